@@ -1,0 +1,219 @@
+"""Plain fp64 attention, RoPE and MLA — the oracle (test infrastructure only; see the package docstring).
+
+Everything is the plain definition written out: scores are materialised, the softmax takes two passes (max, then
+exp-and-sum), RoPE is an explicit cos/sin rotation, the paged cache is gathered with an explicit loop over pages,
+and MLA is computed either in its absorbed form as plain attention or naively through per-head up-projections.
+Library primitives used as steps: numpy matmul, exp, log, sin, cos.
+
+Pages cited (by title, as they appear on the web):
+  [AN]  "Attention" notes, makinaruto.github.io (posts/nlp/llm_learning/attention): sections "FlashAttention",
+        "online-softmax", "Page Attention", "Group-Query Attention", "Multi-Head Latent Attention", "RoPE".
+  [LC]  "DeepSeek 32K to 256K long context" (tqpw.cn): §2.1 RoPE definition, §2.2 frequency code, §2.5 rope cache.
+  [V3]  "DeepSeek-V3 attention guide: einsum vs manual optimisation" (dksg.cn): the naive and the absorbed
+        score einsums quoted from the model's inference code.
+  [AP]  "7 anti-patterns of DeepSeek attention optimisation" (lpnh.cn): §4.2 GQA cache reorder.
+
+Readings taken where the pages are silent or garbled:
+  * online-softmax running max is max(m_old, m_c) ([AN] prints a minus sign inside the max);
+  * the softmax scale multiplies the scores inside the softmax ([V3] "* softmax_scale" on the scores);
+  * query head h reads KV head h // (Hq/Hkv) ([AN] GQA table: Q1..Q4 use K1,K1,K2,K2; [AP] repeat_interleave);
+  * causal: key j is visible to query i iff j <= i (Sq == Sk);
+  * RoPE pairs are adjacent (2i, 2i+1) by default ([LC] §2.1 views the last dim as (-1, 2)); the half-split
+    pairing (i, i + D/2) is available with interleaved=False;
+  * RoPE angle = position * theta**(-2i/D) computed directly from the integer position in fp64 ([LC] §2.5);
+  * an empty key set (sequence length 0) gives O = 0 and lse = -inf.
+"""
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64", "rope_inv_freq", "rope", "attention_prefill", "attention_prefill_rows", "gather_paged",
+    "decode_paged", "mla_decode", "mla_naive",
+]
+
+
+def bf16_bits_to_f64(bits):
+    """Decode IEEE bfloat16 bit patterns (uint16) to float64, exactly: bf16 is the top half of an fp32."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def rope_inv_freq(head_dim, theta):
+    """[LC] §2.1: theta_i = theta ** (-2i/d) for i = 0 .. d/2 - 1 (the rotation frequency of pair i)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return np.float64(theta) ** (-2.0 * i / np.float64(head_dim))
+
+
+def rope(x, positions, theta, interleaved=True):
+    """Rotary position embedding by explicit rotation ([LC] §2.1: each pair (a, b) is multiplied by the
+    matrix [[cos, -sin], [sin, cos]] of angle position * theta_i).
+
+    x: [..., H, D] float (token axes first, then head, then dim). positions: integer array broadcastable to
+    x.shape[:-2]. Returns a new float64 array; nothing is rounded.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    assert d % 2 == 0, "RoPE needs an even head dimension"
+    pos = np.asarray(positions, dtype=np.float64)
+    ang = pos[..., None] * rope_inv_freq(d, theta)           # [..tokens.., D/2], integer position times frequency
+    c = np.cos(ang)[..., None, :]                             # broadcast over the head axis
+    s = np.sin(ang)[..., None, :]
+    if interleaved:
+        a, b = x[..., 0::2], x[..., 1::2]
+    else:
+        a, b = x[..., : d // 2], x[..., d // 2:]
+    ra = a * c - b * s
+    rb = a * s + b * c
+    out = np.empty_like(x)
+    if interleaved:
+        out[..., 0::2], out[..., 1::2] = ra, rb
+    else:
+        out[..., : d // 2], out[..., d // 2:] = ra, rb
+    return out
+
+
+def _softmax_rows_then_v(s, v):
+    """Two-pass softmax over the last axis of materialised scores s [R, T] (pass 1: row max; pass 2: exp and sum),
+    then P @ v. Rows whose every score is -inf (no visible key) give O = 0 and lse = -inf.
+    Returns (o [R, Dv], lse [R])."""
+    m = np.max(s, axis=-1) if s.shape[-1] else np.full(s.shape[:-1], -np.inf)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.exp(s - m_safe[:, None])                           # exp(-inf) = 0 for masked keys
+    l = e.sum(axis=-1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        p = np.where(empty[:, None], 0.0, e / np.where(empty, 1.0, l)[:, None])
+        lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, l)))
+    return p @ v, lse
+
+
+def attention_prefill(q, k, v, causal, scale):
+    """softmax(scale * Q K^T [+ causal mask]) V per (batch, query head), with S materialised ([AN] conventional
+    tiled computation: S = Q K^T, P = softmax(S), O = P V).
+
+    q: [B, S, Hq, D]; k, v: [B, S, Hkv, D] (any float; computed in float64). Query head h reads KV head
+    h // (Hq // Hkv). Returns (o [B, S, Hq, D] float64, lse [B, Hq, S] float64 natural-log sum-exp).
+    """
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
+    bsz, s_len, hq, _ = q.shape
+    hkv = k.shape[2]
+    assert hq % hkv == 0
+    grp = hq // hkv
+    o = np.zeros(q.shape[:3] + (v.shape[-1],), np.float64)
+    lse = np.zeros((bsz, hq, s_len), np.float64)
+    mask = np.triu(np.ones((s_len, s_len), dtype=bool), k=1) if causal else None   # True where key j > query i
+    for b in range(bsz):
+        for h in range(hq):
+            g = h // grp
+            sc = scale * (q[b, :, h, :] @ k[b, :, g, :].T)    # [S, S] materialised
+            if causal:
+                sc[mask] = -np.inf
+            o[b, :, h, :], lse[b, h, :] = _softmax_rows_then_v(sc, v[b, :, g, :])
+    return o, lse
+
+
+def attention_prefill_rows(q, k, v, rows, causal, scale):
+    """attention_prefill restricted to the query positions `rows` (same rows for every batch and head); used where
+    the full S x S score matrix is too large for the CPU. Returns (o [B, R, Hq, Dv], lse [B, Hq, R])."""
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    bsz, s_len, hq, _ = q.shape
+    hkv = k.shape[2]
+    grp = hq // hkv
+    o = np.zeros((bsz, rows.size, hq, v.shape[-1]), np.float64)
+    lse = np.zeros((bsz, hq, rows.size), np.float64)
+    keys = np.arange(s_len)
+    for b in range(bsz):
+        for h in range(hq):
+            g = h // grp
+            sc = scale * (q[b, rows, h, :] @ k[b, :, g, :].T)  # [R, S]
+            if causal:
+                sc[keys[None, :] > rows[:, None]] = -np.inf
+            o[b, :, h, :], lse[b, h, :] = _softmax_rows_then_v(sc, v[b, :, g, :])
+    return o, lse
+
+
+def gather_paged(cache, block_table_row, seq_len):
+    """[AN] Page Attention: logical token t of a sequence lives in physical page block_table_row[t // page_size],
+    slot t % page_size. cache: [num_pages, page_size, ...]. Returns the logical [seq_len, ...] view, gathered with
+    an explicit loop over pages."""
+    page_size = cache.shape[1]
+    out = np.empty((seq_len,) + cache.shape[2:], dtype=cache.dtype)
+    n_pages = (seq_len + page_size - 1) // page_size
+    for j in range(n_pages):
+        phys = int(block_table_row[j])
+        n = min(page_size, seq_len - j * page_size)
+        out[j * page_size: j * page_size + n] = cache[phys, :n]
+    return out
+
+
+def decode_paged(q, k_cache, v_cache, block_table, seq_lens, scale):
+    """One query token per sequence attending all seq_lens[b] cached tokens of a paged KV cache.
+
+    q: [B, Hq, D] (already rotated); k_cache, v_cache: [num_pages, page_size, Hkv, D]; block_table:
+    [B, max_pages] int; seq_lens: [B] int. Query head h reads KV head h // (Hq // Hkv).
+    Returns (o [B, Hq, D] float64, lse [B, Hq] float64).
+    """
+    q = np.asarray(q, np.float64)
+    bsz, hq, _ = q.shape
+    hkv = k_cache.shape[2]
+    grp = hq // hkv
+    o = np.zeros((bsz, hq, v_cache.shape[-1]), np.float64)
+    lse = np.zeros((bsz, hq), np.float64)
+    for b in range(bsz):
+        n = int(seq_lens[b])
+        kb = np.asarray(gather_paged(k_cache, block_table[b], n), np.float64)   # [L, Hkv, D]
+        vb = np.asarray(gather_paged(v_cache, block_table[b], n), np.float64)
+        for h in range(hq):
+            g = h // grp
+            sc = scale * (kb[:, g, :] @ q[b, h, :])[None, :]     # [1, L]
+            ob, lb = _softmax_rows_then_v(sc, vb[:, g, :])
+            o[b, h], lse[b, h] = ob[0], lb[0]
+    return o, lse
+
+
+def mla_decode(q_lat, q_pe, c_kv, k_pe, seq_lens, scale):
+    """MLA decode in the absorbed form, written as plain attention ([V3] absorb-mode scores:
+    scale * (q_nope . kv_cache + q_pe . pe_cache); [AN] MLA: the value up-projection folds into W^O, so the
+    output stays in the latent space: O = P . c_kv).
+
+    q_lat: [B, H, C] (query already projected into the latent space), q_pe: [B, H, R]; c_kv: [B, T, C],
+    k_pe: [B, T, R] (one rope key shared by all heads, [AN] partial RoPE); seq_lens: [B].
+    Every head uses key [c_kv ; k_pe] (C+R wide) and value c_kv. Returns (o [B, H, C], lse [B, H]).
+    """
+    q_lat = np.asarray(q_lat, np.float64); q_pe = np.asarray(q_pe, np.float64)
+    c_kv = np.asarray(c_kv, np.float64); k_pe = np.asarray(k_pe, np.float64)
+    bsz, nh, c = q_lat.shape
+    o = np.zeros((bsz, nh, c), np.float64)
+    lse = np.zeros((bsz, nh), np.float64)
+    for b in range(bsz):
+        n = int(seq_lens[b])
+        keys = np.concatenate([c_kv[b, :n], k_pe[b, :n]], axis=-1)        # [L, C+R]
+        qry = np.concatenate([q_lat[b], q_pe[b]], axis=-1)                  # [H, C+R]
+        sc = scale * (qry @ keys.T)                                         # [H, L] materialised
+        o[b], lse[b] = _softmax_rows_then_v(sc, c_kv[b, :n])
+    return o, lse
+
+
+def mla_naive(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, seq_lens, scale):
+    """MLA with explicit per-head up-projections ([AN] MLA: K = C^KV W^K_up, V = C^KV W^V_up; partial RoPE
+    concatenates a rotated part whose key is shared across heads; [V3] naive-mode score einsum over full keys).
+
+    q_nope: [B, H, Dn], q_pe: [B, H, R], c_kv: [B, T, C], k_pe: [B, T, R], w_uk: [H, C, Dn], w_uv: [H, C, Dv].
+    Head h: key_t = [c_kv_t W_uk[h] ; k_pe_t], value_t = c_kv_t W_uv[h], query [q_nope_h ; q_pe_h].
+    Returns o [B, H, Dv].
+    """
+    q_nope = np.asarray(q_nope, np.float64); q_pe = np.asarray(q_pe, np.float64)
+    c_kv = np.asarray(c_kv, np.float64); k_pe = np.asarray(k_pe, np.float64)
+    w_uk = np.asarray(w_uk, np.float64); w_uv = np.asarray(w_uv, np.float64)
+    bsz, nh, _ = q_nope.shape
+    o = np.zeros((bsz, nh, w_uv.shape[-1]), np.float64)
+    for b in range(bsz):
+        n = int(seq_lens[b])
+        for h in range(nh):
+            k_h = np.concatenate([c_kv[b, :n] @ w_uk[h], k_pe[b, :n]], axis=-1)   # [L, Dn+R]
+            v_h = c_kv[b, :n] @ w_uv[h]                                          # [L, Dv]
+            q_h = np.concatenate([q_nope[b, h], q_pe[b, h]])
+            sc = scale * (k_h @ q_h)[None, :]
+            ob, _ = _softmax_rows_then_v(sc, v_h)
+            o[b, h] = ob[0]
+    return o

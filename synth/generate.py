@@ -1,0 +1,129 @@
+"""Seeded synthetic inputs shared by the oracle tests, the GPU tests and the benchmark.
+
+Holds none of the method's arithmetic: it draws iid N(0, 1) values, rounds them to bfloat16 (round to nearest
+even), and builds block tables, sequence lengths, positions and sampled rows. Every tensor has its own random
+stream: numpy PCG64 seeded by SeedSequence(seed, spawn_key=(tensor id, chunk)), so values do not depend on how many
+threads draw them. bf16 tensors are returned as their uint16 bit patterns, fp32 tensors as float32.
+"""
+from concurrent.futures import ThreadPoolExecutor
+import os
+import zlib
+
+import numpy as np
+
+from .workloads import Prefill, PagedDecode, MLADecode
+
+_CHUNK = 1 << 22          # elements per independently seeded chunk
+
+
+def _tensor_id(name):
+    return zlib.crc32(name.encode()) & 0x7FFFFFFF
+
+
+def f32_to_bf16_bits(x):
+    """Round float32 to bfloat16, nearest-even, returning the uint16 bit pattern (inputs here are finite)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def _workers():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def normal(seed, name, shape, dtype):
+    """iid N(0, 1) of the given shape; dtype "bf16" -> uint16 bits, "fp32" -> float32."""
+    n = int(np.prod(shape, dtype=np.int64))
+    out = np.empty(n, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    tid = _tensor_id(name)
+
+    def fill(ci):
+        lo = ci * _CHUNK
+        hi = min(n, lo + _CHUNK)
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(tid, ci))))
+        vals = rng.standard_normal(hi - lo, dtype=np.float32)
+        out[lo:hi] = f32_to_bf16_bits(vals) if dtype == "bf16" else vals
+
+    n_chunks = (n + _CHUNK - 1) // _CHUNK
+    if n_chunks <= 1:
+        for ci in range(n_chunks):
+            fill(ci)
+    else:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(fill, range(n_chunks)))
+    return out.reshape(shape)
+
+
+def _rng(seed, name):
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(_tensor_id(name),))))
+
+
+def prefill_inputs(w: Prefill, seed=0, seqlen=None, batch=None):
+    """q [B, S, Hq, D], k and v [B, S, Hkv, D]; positions [B*S] int32 (0..S-1 for each sequence).
+    seqlen / batch override the workload's sizes (for scaled-down cases of the same shape family)."""
+    s = w.seqlen if seqlen is None else seqlen
+    b = w.batch if batch is None else batch
+    q = normal(seed, "prefill.q", (b, s, w.hq, w.head_dim), w.dtype)
+    k = normal(seed, "prefill.k", (b, s, w.hkv, w.head_dim), w.dtype)
+    v = normal(seed, "prefill.v", (b, s, w.hkv, w.head_dim), w.dtype)
+    positions = np.tile(np.arange(s, dtype=np.int32), b)
+    return dict(q=q, k=k, v=v, positions=positions)
+
+
+def sampled_rows(seqlen, n, seed=0):
+    """n distinct query positions in [0, seqlen), always including the first and the last, sorted."""
+    if n >= seqlen:
+        return np.arange(seqlen, dtype=np.int64)
+    rng = _rng(seed, "prefill.rows")
+    inner = rng.choice(np.arange(1, seqlen - 1), size=n - 2, replace=False)
+    return np.sort(np.concatenate([[0, seqlen - 1], inner])).astype(np.int64)
+
+
+def paged_decode_inputs(w: PagedDecode, seed=0, batch=None, seq_lens=None, page_size=None, max_len=None):
+    """A paged KV cache placed by a seeded random block table.
+
+    Returns dict with q [B, Hq, D] (not yet rotated), k_cache / v_cache [N_pool, page, Hkv, D], block_table
+    [B, max_pages] int32 (-1 for unused entries), seq_lens [B] int32, positions [B] int32 (= seq_len - 1),
+    spare_pages (physical pages no table references), max_len.
+    Each sequence of length L needs ceil(L / page) pages; a seeded permutation of a pool of N_used + spares
+    pages hands out distinct pages, never shared between sequences.
+    """
+    b = w.batch if batch is None else batch
+    ps = w.page_size if page_size is None else page_size
+    if seq_lens is None:
+        seq_lens = _rng(seed, "decode.lens").integers(w.len_lo, w.len_hi, size=b, endpoint=True)
+    seq_lens = np.asarray(seq_lens, dtype=np.int32)
+    b = seq_lens.size
+    max_len = int(max(w.len_hi, seq_lens.max(initial=0)) if max_len is None else max_len)
+    max_pages = max(1, (max_len + ps - 1) // ps)
+    n_pages = (seq_lens.astype(np.int64) + ps - 1) // ps
+    n_used = int(n_pages.sum())
+    n_pool = n_used + int(np.ceil(n_used * w.spare_frac)) + 1
+    perm = _rng(seed, "decode.perm").permutation(n_pool).astype(np.int32)
+    table = np.full((b, max_pages), -1, dtype=np.int32)
+    off = 0
+    for i in range(b):
+        table[i, : n_pages[i]] = perm[off: off + n_pages[i]]
+        off += int(n_pages[i])
+    spare = np.sort(perm[off:])
+    q = normal(seed, "decode.q", (b, w.hq, w.head_dim), "bf16")
+    kc = normal(seed, "decode.k", (n_pool, ps, w.hkv, w.head_dim), "bf16")
+    vc = normal(seed, "decode.v", (n_pool, ps, w.hkv, w.head_dim), "bf16")
+    return dict(q=q, k_cache=kc, v_cache=vc, block_table=table, seq_lens=seq_lens,
+                positions=(seq_lens - 1).astype(np.int32), spare_pages=spare, max_len=max_len)
+
+
+def mla_inputs(w: MLADecode, seed=0, batch=None, seqlen=None, seq_lens=None):
+    """q_lat [B, H, C], q_pe [B, H, R], c_kv [B, T, C], k_pe [B, T, R] (bf16 bits), seq_lens [B] int32."""
+    b = w.batch if batch is None else batch
+    t = w.seqlen if seqlen is None else seqlen
+    q_lat = normal(seed, "mla.q_lat", (b, w.heads, w.latent), "bf16")
+    q_pe = normal(seed, "mla.q_pe", (b, w.heads, w.rope), "bf16")
+    c_kv = normal(seed, "mla.c_kv", (b, t, w.latent), "bf16")
+    k_pe = normal(seed, "mla.k_pe", (b, t, w.rope), "bf16")
+    lens = np.full(b, t, dtype=np.int32) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
+    return dict(q_lat=q_lat, q_pe=q_pe, c_kv=c_kv, k_pe=k_pe, seq_lens=lens)

@@ -1,0 +1,70 @@
+"""The five workloads: shapes, RoPE base and softmax scale, as constants.
+
+Nothing here computes attention. A workload is named by what it is; `WORKLOADS` maps the short name to its
+description. Long-context RoPE uses the NTK-scaled base 10000 * 4**(128/126) (the base stretched for a 4x longer
+context at head dim 128).
+"""
+from dataclasses import dataclass
+import math
+
+
+@dataclass(frozen=True)
+class Prefill:
+    name: str
+    batch: int
+    seqlen: int
+    hq: int
+    hkv: int
+    head_dim: int
+    dtype: str            # "fp32" or "bf16"
+    theta: float
+    scale: float
+    causal: bool = True
+    sampled_rows: int = 0  # > 0: the oracle checks only this many seeded query rows (for every head)
+
+    @property
+    def flops(self):
+        """Algorithmic flops: QK^T and PV at 2 flop per multiply-add over the unmasked (query, key) pairs."""
+        pairs = self.seqlen * (self.seqlen + 1) // 2 if self.causal else self.seqlen * self.seqlen
+        return 4 * self.batch * self.hq * self.head_dim * pairs
+
+
+@dataclass(frozen=True)
+class PagedDecode:
+    name: str
+    batch: int
+    hq: int
+    hkv: int
+    head_dim: int
+    page_size: int
+    len_lo: int
+    len_hi: int
+    theta: float
+    scale: float
+    spare_frac: float = 0.125   # extra physical pages in the pool, never referenced by a block table
+
+
+@dataclass(frozen=True)
+class MLADecode:
+    name: str
+    batch: int
+    heads: int
+    latent: int            # kv_lora_rank: width of c_kv and of the absorbed query
+    rope: int              # width of the shared rope key k_pe and of q_pe
+    seqlen: int
+    scale: float
+
+
+WORKLOADS = {
+    "mha_fp32_s256": Prefill("mha_fp32_s256", batch=1, seqlen=256, hq=4, hkv=4, head_dim=64, dtype="fp32",
+                             theta=10000.0, scale=1.0 / math.sqrt(64)),
+    "gqa_prefill_s8192": Prefill("gqa_prefill_s8192", batch=2, seqlen=8192, hq=32, hkv=8, head_dim=128,
+                                 dtype="bf16", theta=10000.0, scale=1.0 / math.sqrt(128)),
+    "paged_decode_b64": PagedDecode("paged_decode_b64", batch=64, hq=32, hkv=8, head_dim=128, page_size=64,
+                                    len_lo=1024, len_hi=32768, theta=10000.0, scale=1.0 / math.sqrt(128)),
+    "mla_decode_b32": MLADecode("mla_decode_b32", batch=32, heads=128, latent=512, rope=64, seqlen=32768,
+                                scale=1.0 / math.sqrt(192)),
+    "gqa_prefill_s131072": Prefill("gqa_prefill_s131072", batch=1, seqlen=131072, hq=32, hkv=8, head_dim=128,
+                                   dtype="bf16", theta=10000.0 * 4.0 ** (128.0 / 126.0),
+                                   scale=1.0 / math.sqrt(128), sampled_rows=256),
+}

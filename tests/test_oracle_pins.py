@@ -1,0 +1,381 @@
+"""Pins for the fp64 oracle: each check ties it to something other than itself — values the pages print, closed
+forms, brute force on tiny inputs, invariants the mathematics fixes, and a library routine in a special case.
+Chosen so that a dropped term, a wrong sign or index, or a transposed operand anywhere in the oracle fails one.
+CPU only."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import WORKLOADS
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ----------------------------------------------------------------------------------------------------- RoPE ----
+
+def test_rope_frequencies_match_printed_formula():
+    with open(os.path.join(GOLDEN, "rope_frequencies.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        np.testing.assert_allclose(oracle.rope_inv_freq(case["d"], case["base"]), case["inv_freq"], rtol=1e-15)
+
+
+def test_rope_pair_angles_closed_form():
+    # D = 8, base 10000: pair i rotates by p * 10**(-i). A unit vector (1, 0) in every pair lands on (cos, sin).
+    x = np.zeros((1, 1, 8)); x[..., 0::2] = 1.0
+    for p in (0, 1, 3, 255, 131071):
+        y = oracle.rope(x, np.array([p]), 10000.0)[0, 0]
+        for i in range(4):
+            a = p * 10.0 ** (-i)
+            assert abs(y[2 * i] - math.cos(a)) < 1e-12 and abs(y[2 * i + 1] - math.sin(a)) < 1e-12, (p, i)
+
+
+def test_rope_d2_is_rotation_matrix():
+    x = rnd(1, 5, 3, 2)
+    pos = np.array([0, 1, 7, 1000, 131071])
+    y = oracle.rope(x, pos, 10000.0)
+    for t, p in enumerate(pos):
+        c, s = math.cos(p), math.sin(p)
+        r = np.array([[c, -s], [s, c]])
+        np.testing.assert_allclose(y[t], x[t] @ r.T, atol=1e-13)
+
+
+def test_rope_position_zero_is_identity():
+    x = rnd(2, 4, 3, 64)
+    np.testing.assert_array_equal(oracle.rope(x, np.zeros(4, int), 10000.0), x)
+
+
+def test_rope_preserves_norm():
+    x = rnd(3, 6, 2, 128)
+    pos = np.array([0, 5, 300, 8191, 65536, 131071])
+    for inter in (True, False):
+        y = oracle.rope(x, pos, 40889.94, interleaved=inter)
+        np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+
+
+def test_rope_scores_depend_only_on_relative_position():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((1, 1, 128)); k = rng.standard_normal((1, 1, 128))
+    for _ in range(10):
+        m, n, s = (int(v) for v in rng.integers(0, 131072, 3))
+        for theta in (10000.0, WORKLOADS["gqa_prefill_s131072"].theta):
+            for inter in (True, False):
+                a = np.sum(oracle.rope(q, [m], theta, inter) * oracle.rope(k, [n], theta, inter))
+                b = np.sum(oracle.rope(q, [m + s], theta, inter) * oracle.rope(k, [n + s], theta, inter))
+                assert abs(a - b) < 1e-8 * (1 + abs(a)), (m, n, s)
+
+
+def test_rope_half_split_is_a_permutation_of_interleaved():
+    # Pairing (i, i + D/2) equals pairing (2i, 2i+1) after moving element i -> 2i and i + D/2 -> 2i + 1.
+    d = 16
+    x = rnd(5, 3, 2, d)
+    perm = np.empty(d, int); perm[0::2] = np.arange(d // 2); perm[1::2] = np.arange(d // 2) + d // 2
+    pos = np.array([1, 17, 4000])
+    np.testing.assert_allclose(oracle.rope(x[..., perm], pos, 10000.0, True),
+                               oracle.rope(x, pos, 10000.0, False)[..., perm], atol=1e-14)
+
+
+def test_ntk_base_closed_form():
+    assert abs(WORKLOADS["gqa_prefill_s131072"].theta - 40889.94243248622) < 1e-8
+
+
+# ------------------------------------------------------------------------------------------ softmax/attention ----
+
+def brute_attention(q, k, v, causal, scale):
+    """Nested loops; exp without max subtraction; p = exp(s) / sum exp(s)."""
+    bsz, s_len, hq, _ = q.shape
+    hkv = k.shape[2]
+    o = np.zeros(q.shape[:3] + (v.shape[-1],)); lse = np.zeros((bsz, hq, s_len))
+    for b in range(bsz):
+        for h in range(hq):
+            g = h * hkv // hq
+            for i in range(s_len):
+                w = []
+                for j in range(k.shape[1]):
+                    if causal and j > i:
+                        w.append(0.0)
+                        continue
+                    w.append(math.exp(scale * sum(q[b, i, h, d] * k[b, j, g, d] for d in range(q.shape[-1]))))
+                tot = sum(w)
+                lse[b, h, i] = math.log(tot)
+                for j in range(k.shape[1]):
+                    o[b, i, h] += (w[j] / tot) * v[b, j, g]
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (3, 1)])
+def test_prefill_matches_brute_force(causal, hq, hkv):
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((2, 5, hq, 3)); k = rng.standard_normal((2, 5, hkv, 3)); v = rng.standard_normal((2, 5, hkv, 4))
+    o, lse = oracle.attention_prefill(q, k, v, causal, 0.7)
+    ob, lb = brute_attention(q, k, v, causal, 0.7)
+    np.testing.assert_allclose(o, ob, atol=1e-13)
+    np.testing.assert_allclose(lse, lb, atol=1e-13)
+
+
+def online_softmax_attention(q, k, v, causal, scale, tiles):
+    """Independent fp64 implementation of the page's online-softmax recurrence (block max m_c, block exp-sum l_c;
+    m_new = max(m_old, m_c); l_new = l_old e^(m_old-m_new) + l_c e^(m_c-m_new)), with the output accumulator
+    rescaled by the same factors and divided by l at the end."""
+    bsz, s_len, hq, _ = q.shape
+    hkv = k.shape[2]
+    o = np.zeros(q.shape[:3] + (v.shape[-1],)); lse = np.zeros((bsz, hq, s_len))
+    for b in range(bsz):
+        for h in range(hq):
+            g = h * hkv // hq
+            for i in range(s_len):
+                m, l, acc = -np.inf, 0.0, np.zeros(v.shape[-1])
+                j0 = 0
+                for t in tiles:
+                    j1 = min(j0 + t, s_len)
+                    if j0 >= j1:
+                        break
+                    s = np.array([scale * q[b, i, h] @ k[b, j, g] if (not causal or j <= i) else -np.inf
+                                  for j in range(j0, j1)])
+                    m_c = s.max()
+                    if np.isfinite(m_c):
+                        e = np.exp(s - m_c)
+                        l_c = e.sum()
+                        m_new = max(m, m_c)
+                        a_old = math.exp(m - m_new) if np.isfinite(m) else 0.0
+                        a_c = math.exp(m_c - m_new)
+                        l = l * a_old + l_c * a_c
+                        acc = acc * a_old + a_c * (e @ v[b, j0:j1, g])
+                        m = m_new
+                    j0 = j1
+                o[b, i, h] = acc / l
+                lse[b, h, i] = m + math.log(l)
+    return o, lse
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_online_recurrence_equals_two_pass(causal):
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 37, 4, 8)) * 2; k = rng.standard_normal((1, 37, 2, 8)); v = rng.standard_normal((1, 37, 2, 8))
+    o, lse = oracle.attention_prefill(q, k, v, causal, 0.9)
+    for trial in range(3):
+        tiles = list(rng.integers(1, 12, size=40))
+        o2, l2 = online_softmax_attention(q, k, v, causal, 0.9, tiles)
+        np.testing.assert_allclose(o, o2, atol=1e-12)
+        np.testing.assert_allclose(lse, l2, atol=1e-12)
+
+
+def test_rows_of_p_sum_to_one_and_respect_mask():
+    # With V = identity (value j = e_j) the output row is the probability row itself.
+    s_len = 9
+    q = rnd(8, 1, s_len, 2, 4); k = rnd(9, 1, s_len, 2, 4)
+    v = np.broadcast_to(np.eye(s_len)[None, :, None, :], (1, s_len, 2, s_len)).copy()
+    p, _ = oracle.attention_prefill(q, k, v, True, 1.3)
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-14)
+    assert (p >= 0).all()
+    for i in range(s_len):
+        assert np.all(p[0, i, :, i + 1:] == 0.0)
+
+
+def test_constant_v_gives_constant_o():
+    q = rnd(10, 2, 11, 4, 8); k = rnd(11, 2, 11, 2, 8)
+    c = rnd(12, 8)
+    v = np.broadcast_to(c, (2, 11, 2, 8)).copy()
+    o, _ = oracle.attention_prefill(q, k, v, True, 0.5)
+    np.testing.assert_allclose(o, np.broadcast_to(c, o.shape), atol=1e-14)
+
+
+def test_causal_row_zero_is_v0():
+    q = rnd(13, 1, 6, 4, 8); k = rnd(14, 1, 6, 2, 8); v = rnd(15, 1, 6, 2, 8)
+    o, lse = oracle.attention_prefill(q, k, v, True, 0.35)
+    for h in range(4):
+        np.testing.assert_array_equal(o[0, 0, h], v[0, 0, h // 2])
+        assert abs(lse[0, h, 0] - 0.35 * q[0, 0, h] @ k[0, 0, h // 2]) < 1e-14
+
+
+def test_large_query_along_a_key_selects_its_value():
+    k = np.zeros((1, 4, 1, 4)); k[0, :, 0, :] = np.eye(4)
+    v = rnd(16, 1, 4, 1, 5)
+    q = np.zeros((1, 4, 1, 4)); q[0, 3, 0, 2] = 60.0         # last query points at key 2
+    o, _ = oracle.attention_prefill(q, k, v, True, 1.0)
+    np.testing.assert_allclose(o[0, 3, 0], v[0, 2, 0], atol=1e-20 + 1e-24)
+
+
+def test_gqa_head_mapping_matches_printed_examples():
+    with open(os.path.join(GOLDEN, "gqa_head_mapping.json")) as f:
+        cases = json.load(f)["cases"]
+    for case in cases:
+        hq, hkv = case["hq"], case["hkv"]
+        q = rnd(17, 1, 3, hq, 4); k = rnd(18, 1, 3, hkv, 4)
+        v = np.zeros((1, 3, hkv, 1))
+        for g in range(hkv):
+            v[:, :, g, 0] = 10.0 * (g + 1)                      # each KV head carries a distinct constant
+        o, _ = oracle.attention_prefill(q, k, v, True, 1.0)
+        got = [int(round(o[0, 2, h, 0] / 10.0)) - 1 for h in range(hq)]
+        assert got == case["kv_of_q"], case["cite"]
+
+
+def test_gqa_equals_mha_on_repeated_kv():
+    q = rnd(19, 2, 7, 8, 8); k = rnd(20, 2, 7, 2, 8); v = rnd(21, 2, 7, 2, 8)
+    o, lse = oracle.attention_prefill(q, k, v, True, 0.4)
+    o2, lse2 = oracle.attention_prefill(q, np.repeat(k, 4, axis=2), np.repeat(v, 4, axis=2), True, 0.4)
+    np.testing.assert_allclose(o, o2, atol=1e-15); np.testing.assert_allclose(lse, lse2, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_matches_torch_sdpa_fp64(causal):
+    torch = pytest.importorskip("torch")
+    q = rnd(22, 2, 19, 8, 16); k = rnd(23, 2, 19, 2, 16); v = rnd(24, 2, 19, 2, 16)
+    o, _ = oracle.attention_prefill(q, k, v, causal, 0.3)
+    tq = torch.from_numpy(q).transpose(1, 2)
+    tk = torch.from_numpy(np.repeat(k, 4, axis=2)).transpose(1, 2)
+    tv = torch.from_numpy(np.repeat(v, 4, axis=2)).transpose(1, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.3)
+    np.testing.assert_allclose(o, ref.transpose(1, 2).numpy(), atol=1e-12)
+
+
+def test_prefill_rows_equals_full():
+    q = rnd(25, 2, 40, 4, 8); k = rnd(26, 2, 40, 2, 8); v = rnd(27, 2, 40, 2, 8)
+    o, lse = oracle.attention_prefill(q, k, v, True, 0.6)
+    rows = np.array([0, 3, 17, 39])
+    o_r, lse_r = oracle.attention_prefill_rows(q, k, v, rows, True, 0.6)
+    np.testing.assert_allclose(o_r, o[:, rows], atol=1e-14); np.testing.assert_allclose(lse_r, lse[:, :, rows], atol=1e-14)
+
+
+def test_lse_merge_of_key_splits_equals_unsplit():
+    """Split the keys into random chunks, attend each chunk separately (normalised O_c, lse_c), merge:
+    M = max lse_c, w_c = exp(lse_c - M), O = sum w_c O_c / sum w_c, lse = M + log sum w_c."""
+    rng = np.random.default_rng(28)
+    L = 50
+    q = rng.standard_normal((1, 1, 4, 8)) * 3; k = rng.standard_normal((1, L, 2, 8)); v = rng.standard_normal((1, L, 2, 8))
+    o_full, lse_full = oracle.attention_prefill(q, k, v, False, 0.8)
+    cuts = np.sort(rng.choice(np.arange(1, L), 5, replace=False))
+    bounds = [0, *cuts, L]
+    parts = [oracle.attention_prefill(q, k[:, a:b], v[:, a:b], False, 0.8) for a, b in zip(bounds[:-1], bounds[1:])]
+    lses = np.stack([p[1] for p in parts])                      # [C, 1, H, 1]
+    outs = np.stack([p[0] for p in parts])                      # [C, 1, 1, H, D]
+    mx = lses.max(axis=0)
+    w = np.exp(lses - mx)
+    o = (w.transpose(0, 1, 3, 2)[..., None] * outs).sum(0) / w.sum(0).transpose(0, 2, 1)[..., None]
+    np.testing.assert_allclose(o, o_full, atol=1e-13)
+    np.testing.assert_allclose(mx + np.log(w.sum(0)), lse_full, atol=1e-13)
+
+
+# ------------------------------------------------------------------------------------------------ paged decode ----
+
+def _paged_layout(k_dense, v_dense, page, rng, n_spare=3):
+    """Scatter dense [L, Hkv, D] K/V into a randomly permuted page pool; returns caches and a one-row table."""
+    L = k_dense.shape[0]
+    n_pages = (L + page - 1) // page
+    pool = n_pages + n_spare
+    perm = rng.permutation(pool)
+    kc = rng.standard_normal((pool, page) + k_dense.shape[1:]) * 100
+    vc = rng.standard_normal((pool, page) + v_dense.shape[1:]) * 100
+    for j in range(n_pages):
+        n = min(page, L - j * page)
+        kc[perm[j], :n] = k_dense[j * page: j * page + n]
+        vc[perm[j], :n] = v_dense[j * page: j * page + n]
+    table = np.full((1, n_pages + 2), -1); table[0, :n_pages] = perm[:n_pages]
+    return kc, vc, table
+
+
+def test_decode_equals_last_row_of_causal_prefill():
+    rng = np.random.default_rng(29)
+    for L in (1, 5, 16, 37):
+        k = rng.standard_normal((L, 2, 8)); v = rng.standard_normal((L, 2, 8)); qd = rng.standard_normal((4, 8))
+        kc, vc, table = _paged_layout(k, v, 8, rng)
+        o, lse = oracle.decode_paged(qd[None], kc, vc, table, np.array([L]), 0.5)
+        qfull = np.zeros((1, L, 4, 8)); qfull[0, L - 1] = qd
+        o_ref, lse_ref = oracle.attention_prefill_rows(qfull, k[None], v[None], [L - 1], True, 0.5)
+        np.testing.assert_allclose(o[0], o_ref[0, 0], atol=1e-13); np.testing.assert_allclose(lse[0], lse_ref[0, :, 0], atol=1e-13)
+
+
+def test_decode_is_independent_of_page_placement():
+    rng = np.random.default_rng(30)
+    k = rng.standard_normal((45, 2, 8)); v = rng.standard_normal((45, 2, 8)); qd = rng.standard_normal((1, 4, 8))
+    outs = []
+    for s in range(3):
+        kc, vc, table = _paged_layout(k, v, 16, np.random.default_rng(100 + s))
+        outs.append(oracle.decode_paged(qd, kc, vc, table, np.array([45]), 0.5)[0])
+    np.testing.assert_array_equal(outs[0], outs[1]); np.testing.assert_array_equal(outs[0], outs[2])
+
+
+def test_decode_length_one_gives_v0_and_brute_force():
+    rng = np.random.default_rng(31)
+    kc = rng.standard_normal((4, 8, 2, 4)); vc = rng.standard_normal((4, 8, 2, 4)); q = rng.standard_normal((2, 4, 4))
+    table = np.array([[2, -1, -1], [3, 0, 1]])
+    o, lse = oracle.decode_paged(q, kc, vc, table, np.array([1, 19]), 0.9)
+    for h in range(4):
+        np.testing.assert_array_equal(o[0, h], vc[2, 0, h // 2])
+    # brute force for sequence 1: token t at page table[1][t // 8], slot t % 8
+    for h in range(4):
+        w = [math.exp(0.9 * q[1, h] @ kc[table[1, t // 8], t % 8, h // 2]) for t in range(19)]
+        ref = sum(wi * vc[table[1, t // 8], t % 8, h // 2] for t, wi in enumerate(w)) / sum(w)
+        np.testing.assert_allclose(o[1, h], ref, atol=1e-13)
+        assert abs(lse[1, h] - math.log(sum(w))) < 1e-13
+
+
+def test_empty_key_set_gives_zero_and_minus_inf():
+    kc = np.ones((2, 4, 1, 4)); vc = np.ones((2, 4, 1, 4)); q = np.ones((1, 2, 4))
+    o, lse = oracle.decode_paged(q, kc, vc, np.array([[0, 1]]), np.array([0]), 1.0)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+# ------------------------------------------------------------------------------------------------------ MLA ----
+
+def test_mla_absorbed_equals_naive_up_projection():
+    rng = np.random.default_rng(32)
+    B, H, C, R, Dn, Dv, T = 2, 3, 16, 4, 6, 5, 11
+    q_nope = rng.standard_normal((B, H, Dn)); q_pe = rng.standard_normal((B, H, R))
+    c_kv = rng.standard_normal((B, T, C)); k_pe = rng.standard_normal((B, T, R))
+    w_uk = rng.standard_normal((H, C, Dn)) * 0.3; w_uv = rng.standard_normal((H, C, Dv))
+    lens = np.array([T, 7])
+    o_naive = oracle.mla_naive(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, lens, 0.4)
+    q_lat = np.einsum("hcn,bhn->bhc", w_uk, q_nope)                  # W^K_up absorbed into the query
+    o_lat, _ = oracle.mla_decode(q_lat, q_pe, c_kv, k_pe, lens, 0.4)
+    o_abs = np.einsum("bhc,hcv->bhv", o_lat, w_uv)                   # W^V_up applied after attention
+    np.testing.assert_allclose(o_abs, o_naive, atol=1e-12)
+
+
+def test_mla_scores_match_printed_absorb_einsums():
+    """The absorbed scores written with the page's own einsum index strings, then a softmax and P.c_kv."""
+    rng = np.random.default_rng(33)
+    B, H, C, R, T = 2, 4, 12, 3, 9
+    q_nope = rng.standard_normal((B, 1, H, C)); q_pe = rng.standard_normal((B, 1, H, R))
+    kv = rng.standard_normal((B, T, C)); pe = rng.standard_normal((B, T, R))
+    scores = (np.einsum("bshc,btc->bsht", q_nope, kv) + np.einsum("bshr,btr->bsht", q_pe, pe)) * 0.25
+    p = np.exp(scores - scores.max(-1, keepdims=True)); p /= p.sum(-1, keepdims=True)
+    ref = np.einsum("bsht,btc->bshc", p, kv)[:, 0]
+    o, _ = oracle.mla_decode(q_nope[:, 0], q_pe[:, 0], kv, pe, np.array([T, T]), 0.25)
+    np.testing.assert_allclose(o, ref, atol=1e-13)
+
+
+def test_mla_zero_rope_key_is_single_kv_head_attention():
+    rng = np.random.default_rng(34)
+    B, H, C, R, T = 2, 4, 16, 4, 13
+    q_lat = rng.standard_normal((B, H, C)); q_pe = rng.standard_normal((B, H, R)); c_kv = rng.standard_normal((B, T, C))
+    o, lse = oracle.mla_decode(q_lat, q_pe, c_kv, np.zeros((B, T, R)), np.array([T, T]), 0.3)
+    o_ref, lse_ref = oracle.attention_prefill(q_lat[:, None], c_kv[:, :, None], c_kv[:, :, None], False, 0.3)
+    np.testing.assert_allclose(o, o_ref[:, 0], atol=1e-13); np.testing.assert_allclose(lse, lse_ref[:, :, 0], atol=1e-13)
+
+
+def test_mla_zero_query_averages_latent_cache():
+    rng = np.random.default_rng(35)
+    c_kv = rng.standard_normal((2, 10, 16)); k_pe = rng.standard_normal((2, 10, 4))
+    o, lse = oracle.mla_decode(np.zeros((2, 3, 16)), np.zeros((2, 3, 4)), c_kv, k_pe, np.array([10, 6]), 0.5)
+    np.testing.assert_allclose(o[0], np.broadcast_to(c_kv[0].mean(0), (3, 16)), atol=1e-14)
+    np.testing.assert_allclose(o[1], np.broadcast_to(c_kv[1, :6].mean(0), (3, 16)), atol=1e-14)
+    np.testing.assert_allclose(lse[1], math.log(6), atol=1e-14)
+
+
+def test_bf16_decode_is_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x4049, 0x0000, 0x7F7F, 0x0001], dtype=np.uint16)
+    vals = oracle.bf16_bits_to_f64(bits)
+    assert vals[0] == 1.0 and vals[1] == -1.0 and vals[3] == 0.0
+    assert vals[2] == 3.140625                                        # 0x4049 = 1.5703125 * 2
+    assert vals[4] == (2 - 2 ** -7) * 2.0 ** 127                      # largest finite bf16
+    assert vals[5] == 2.0 ** -133                                     # smallest subnormal bf16
