@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
+
+Primary line: causal GQA prefill, bf16, B=2 Hq=32 Hkv=8 S=8192 D=128 (workload gqa_prefill_s8192). One step is the
+hot path over one batch: RoPE on Q, RoPE on K, then attn_prefill. `value` is the algorithmic attention flops
+(QK^T and PV over the unmasked pairs, 2 flop per multiply-add) per second of wall time over K timed steps,
+with the inputs already resident in HBM. Secondary objects on the same line (same method, HIP events on the
+launch stream): paged GQA decode and MLA absorbed decode in GB/s of algorithmic bytes, and the 131072-token
+prefill in TFLOP/s.
+
+`roofline` describes the dominant kernel of each workload: achieved = algorithmic work per launch / average
+launch duration (HIP events on the stream the kernel runs on), against MI355X's published peaks (bf16 dense MFMA
+2.5 PFLOP/s, HBM 8 TB/s). `traffic` is the counter-measured HBM bytes per launch from the committed rocprofv3
+summary (profiles/traffic.json) when it was taken on the current kernel source, else null.
+
+`cpu_baseline` times the fp64 CPU oracle on a bounded sample of the primary workload (seeded query rows, every
+head): a reported baseline, not a target.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from synth import WORKLOADS, prefill_inputs, paged_decode_inputs, mla_inputs, sampled_rows  # noqa: E402
+
+METRIC = "prefill attention TFLOP/s (% bf16 MFMA peak); decode HBM GB/s (% peak)"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = {
+    "prefill_bf16_kernel": "prefill.hip",
+    "decode_paged_split_kernel": "decode.hip",
+    "mla_split_kernel": "mla.hip",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest(fname):
+    p = os.path.join(ROOT, "transformer_attention_causal_amd", "csrc", fname)
+    h = hashlib.sha256()
+    for f in (p, os.path.join(ROOT, "transformer_attention_causal_amd", "csrc", "device.h")):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from profiles/traffic.json, if measured on the current source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f).get(kernel)
+    if not t or t.get("source_sha") != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def dev_bf16(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class EventTimer:
+    """Average duration of one kernel launch, recorded with events on the launch stream."""
+
+    def __init__(self, torch):
+        self.torch, self.pairs = torch, []
+
+    def start(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs.append([e, None])
+
+    def stop(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record()
+        self.pairs[-1][1] = e
+
+    def mean_ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
+
+
+def roofline_compute(flops, ms, kernel):
+    achieved = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(kernel), "kernel": kernel,
+            "kernel_ms": round(ms, 4)}
+
+
+def roofline_hbm(nbytes, ms, kernel):
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_for(kernel), "kernel": kernel,
+            "kernel_ms": round(ms, 4)}
+
+
+# --------------------------------------------------------------------------------------------------- prefill --
+def bench_prefill(torch, ta, w, steps, warmup, seed=0):
+    log(f"[bench] {w.name}: generating inputs")
+    inp = prefill_inputs(w, seed=seed)
+    q, k, v = (dev_bf16(torch, inp[n]) for n in ("q", "k", "v"))
+    pos = torch.from_numpy(inp["positions"]).cuda()
+    o = torch.empty_like(q)
+    timer = EventTimer(torch)
+
+    def step(timed):
+        ta.attn_rope_apply(q, pos, w.theta)
+        ta.attn_rope_apply(k, pos, w.theta)
+        if timed:
+            timer.start()
+        ta.attn_prefill(q, k, v, causal=True, softmax_scale=w.scale, o=o)
+        if timed:
+            timer.stop()
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: timing {steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    kern_ms = timer.mean_ms()
+    del q, k, v, o
+    torch.cuda.empty_cache()
+    return wall_ms, kern_ms
+
+
+# ---------------------------------------------------------------------------------------------- paged decode --
+def decode_bytes(w, inp):
+    """Algorithmic bytes of one decode step: every cached K and V row of every sequence once, q, o, the used block
+    table entries and the lengths."""
+    tokens = int(inp["seq_lens"].astype(np.int64).sum())
+    pages = int(((inp["seq_lens"].astype(np.int64) + w.page_size - 1) // w.page_size).sum())
+    qo = 2 * inp["q"].size * 2
+    return tokens * w.hkv * w.head_dim * 2 * 2 + qo + pages * 4 + inp["seq_lens"].size * 4
+
+
+def bench_decode(torch, ta, w, steps, warmup, seed=0):
+    log(f"[bench] {w.name}: generating inputs")
+    inp = paged_decode_inputs(w, seed=seed)
+    q = dev_bf16(torch, inp["q"])
+    kc, vc = dev_bf16(torch, inp["k_cache"]), dev_bf16(torch, inp["v_cache"])
+    table = torch.from_numpy(inp["block_table"]).cuda()
+    lens = torch.from_numpy(inp["seq_lens"]).cuda()
+    pos = torch.from_numpy(inp["positions"]).cuda()
+    ta.attn_rope_apply(q, pos, w.theta)
+    o = torch.empty_like(q)
+    ws = torch.empty(ta.attn_decode_paged_workspace_size(w.batch, w.hq, w.head_dim, inp["max_len"]),
+                     dtype=torch.uint8, device="cuda")
+    timer = EventTimer(torch)
+    for i in range(warmup + steps):
+        if i >= warmup:
+            timer.start()
+        ta.attn_decode_paged(q, kc, vc, table, lens, inp["max_len"], softmax_scale=w.scale, o=o, workspace=ws)
+        if i >= warmup:
+            timer.stop()
+    torch.cuda.synchronize()
+    ms = timer.mean_ms()
+    nbytes = decode_bytes(w, inp)
+    del q, kc, vc, o, ws
+    torch.cuda.empty_cache()
+    return ms, nbytes, int(inp["seq_lens"].sum())
+
+
+def mla_bytes(w):
+    return (w.batch * w.seqlen * (w.latent + w.rope) * 2 + w.batch * w.heads * (w.latent + w.rope) * 2
+            + w.batch * w.heads * w.latent * 2 + w.batch * 4)
+
+
+def mla_flops(w):
+    return w.batch * w.heads * w.seqlen * (2 * (w.latent + w.rope) + 2 * w.latent)
+
+
+def bench_mla(torch, ta, w, steps, warmup, seed=0):
+    log(f"[bench] {w.name}: generating inputs")
+    inp = mla_inputs(w, seed=seed)
+    ql, qp, ckv, kpe = (dev_bf16(torch, inp[n]) for n in ("q_lat", "q_pe", "c_kv", "k_pe"))
+    lens = torch.from_numpy(inp["seq_lens"]).cuda()
+    o = torch.empty_like(ql)
+    ws = torch.empty(ta.attn_mla_decode_workspace_size(w.batch, w.heads, w.latent, w.seqlen), dtype=torch.uint8,
+                     device="cuda")
+    timer = EventTimer(torch)
+    for i in range(warmup + steps):
+        if i >= warmup:
+            timer.start()
+        ta.attn_mla_decode(ql, qp, ckv, kpe, lens, w.scale, o=o, workspace=ws)
+        if i >= warmup:
+            timer.stop()
+    torch.cuda.synchronize()
+    ms = timer.mean_ms()
+    del ql, qp, ckv, kpe, o, ws
+    torch.cuda.empty_cache()
+    return ms
+
+
+# ------------------------------------------------------------------------------------------------ cpu oracle --
+def cpu_baseline(w, n_rows=1024, seed=0):
+    """Time the fp64 oracle on `n_rows` seeded query rows (all heads, all batches) of the prefill workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:
+        threads = 1
+    inp = prefill_inputs(w, seed=seed)
+    rows = sampled_rows(w.seqlen, n_rows, seed=seed)
+
+    def f32(b):
+        return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    t0 = time.perf_counter()
+    pos = np.broadcast_to(np.arange(w.seqlen), (w.batch, w.seqlen))
+    k = oracle.rope(f32(inp["k"]), pos, w.theta)
+    v = f32(inp["v"]).astype(np.float64)
+    q = np.zeros((w.batch, w.seqlen, w.hq, w.head_dim))
+    q[:, rows] = oracle.rope(f32(inp["q"][:, rows]), np.broadcast_to(rows, (w.batch, rows.size)), w.theta)
+    oracle.attention_prefill_rows(q, k, v, rows, True, w.scale)
+    dt = time.perf_counter() - t0
+    flops = 4 * w.batch * w.hq * w.head_dim * int((rows + 1).sum())
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows.size} seeded query rows x {w.hq} heads x {w.batch} sequences of {w.name} "
+                      f"(fp64 numpy, scores materialised, {dt:.1f} s)",
+            "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+# ------------------------------------------------------------------------------------------------------ main --
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-secondary", action="store_true", help="only the primary prefill workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration for traffic measurements)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_attention_causal_amd as ta
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ta.load_library()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
+        return
+
+    w = WORKLOADS["gqa_prefill_s8192"]
+    wall_ms, kern_ms = bench_prefill(torch, ta, w, args.steps, args.warmup)
+    value = w.flops / (wall_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall_ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded iid N(0,1), bf16)",
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "hq": w.hq, "hkv": w.hkv,
+                   "head_dim": w.head_dim, "causal": True, "rope_theta": w.theta,
+                   "step": "rope(q) + rope(k) + prefill", "flops_per_step": w.flops},
+        "roofline": roofline_compute(w.flops, kern_ms, "prefill_bf16_kernel"),
+    }
+    line["pct_bf16_peak_step"] = round(value / PEAK_BF16_TFLOPS, 4)
+
+    if not args.no_secondary:
+        wd = WORKLOADS["paged_decode_b64"]
+        ms, nbytes, tokens = bench_decode(torch, ta, wd, max(5, args.steps), args.warmup)
+        line["paged_decode"] = {"workload": wd.name, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                                "ms": round(ms, 4), "bytes": nbytes, "tokens": tokens,
+                                "roofline": roofline_hbm(nbytes, ms, "decode_paged_split_kernel")}
+        wm = WORKLOADS["mla_decode_b32"]
+        ms = bench_mla(torch, ta, wm, max(5, args.steps), args.warmup)
+        nbytes = mla_bytes(wm)
+        line["mla_decode"] = {"workload": wm.name, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+                              "ms": round(ms, 4), "bytes": nbytes,
+                              "tflops": round(mla_flops(wm) / (ms * 1e-3) / 1e12, 1),
+                              "roofline": roofline_hbm(nbytes, ms, "mla_split_kernel")}
+        wl = WORKLOADS["gqa_prefill_s131072"]
+        wall_l, kern_l = bench_prefill(torch, ta, wl, 2, 1)
+        line["long_prefill"] = {"workload": wl.name, "value": round(wl.flops / (wall_l * 1e-3) / 1e12, 2),
+                                "unit": "TFLOP/s", "ms_per_step": round(wall_l, 3),
+                                "roofline": roofline_compute(wl.flops, kern_l, "prefill_bf16_kernel")}
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle sample)")
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

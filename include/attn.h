@@ -1,0 +1,148 @@
+/* attn.h — C ABI of libattn: exact attention with RoPE on MI355X (gfx950).
+ *
+ * Four operations:
+ *   attn_rope_apply    rotary position embedding, in place
+ *   attn_prefill       causal (or full) grouped-query attention over a whole sequence
+ *   attn_decode_paged  one query token per sequence against a paged KV cache (split-KV + log-sum-exp combine)
+ *   attn_mla_decode    multi-head latent attention decode in the absorbed form
+ *
+ * Every result is the exact softmax attention O = softmax(scale * Q K^T [+ mask]) V. The kernels compute it
+ * FlashAttention-style: scores are formed tile by tile on chip, an online softmax keeps a running row max m and
+ * a running exp-sum l and rescales the output accumulator whenever m grows, and S and P are never written to
+ * memory. (Attention notes, makinaruto.github.io, posts/nlp/llm_learning/attention: sections "FlashAttention"
+ * and "online-softmax", update equations for m and l.)
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named as tensors are DEVICE pointers; `stream` is a hipStream_t passed as void* (NULL = the
+ *     default stream). Every call only enqueues work on `stream` and returns; it never synchronises, never
+ *     allocates or frees device memory, never changes the current device, and keeps no state between calls,
+ *     so calls are re-entrant and thread-safe. The caller owns every buffer, including the workspace.
+ *   - Layouts are row-major with the last dimension contiguous. "bf16" is IEEE bfloat16 (results rounded to
+ *     nearest even); arithmetic inside the kernels is fp32.
+ *   - All validation happens on the host before anything is enqueued: on any error nothing is launched and the
+ *     output buffers are untouched. Return value is an attn_status_t:
+ *       ATTN_ERR_INVALID_ARG  a required pointer is NULL, a size is negative or inconsistent (Hq % Hkv != 0,
+ *                             odd head_dim for RoPE), or the scale is not a finite positive number;
+ *       ATTN_ERR_UNSUPPORTED  a valid request this build does not implement (see each function);
+ *       ATTN_ERR_WORKSPACE    workspace smaller than the matching *_workspace_size();
+ *       ATTN_ERR_HIP          the HIP runtime reported an error at launch. Faults inside a kernel surface
+ *                             later, at the caller's synchronisation, as with any HIP kernel.
+ *   - Sizes of zero (no tokens, no sequences) are valid and launch nothing.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1,
+  ATTN_ERR_UNSUPPORTED = 2,
+  ATTN_ERR_WORKSPACE = 3,
+  ATTN_ERR_HIP = 4
+} attn_status_t;
+
+/* Rotary position embedding, in place.
+ * (DeepSeek 32K to 256K long context, tqpw.cn, section 2.1: frequencies theta_i = theta^(-2i/d) and the rotation
+ *  [cos -sin; sin cos] applied to pairs of the last dimension; section 2.5: positions are integers, so angles are
+ *  taken from the integer position directly rather than accumulated.)
+ *   x          [n_tokens, n_heads, head_dim] of `dtype` (ATTN_BF16 or ATTN_FP32), rotated in place. Prefill Q/K in
+ *              [B, S, H, D] layout are n_tokens = B*S rows; decode queries [B, H, D] are n_tokens = B rows.
+ *   positions  [n_tokens] int32 >= 0, the position of each token row.
+ *   theta      RoPE base (10000 for standard RoPE; an NTK-scaled base for stretched contexts), finite, > 1.
+ *   interleaved  1: pairs (2i, 2i+1) — the pairing the page prints; 0: pairs (i, i + head_dim/2).
+ * For pair i of a token at position p the angle is p * theta^(-2i/head_dim), evaluated in fp64 and reduced to
+ * [-pi, pi] before fp32 sin/cos; the rotated values are rounded to `dtype`.
+ * Errors: INVALID_ARG for NULL x/positions (with n_tokens > 0), odd or non-positive head_dim, n_heads <= 0,
+ * theta <= 1 or non-finite; UNSUPPORTED for head_dim > 1024 or another dtype. */
+int attn_rope_apply(void* x, int dtype, int64_t n_tokens, int n_heads, int head_dim, const int32_t* positions,
+                    double theta, int interleaved, void* stream);
+
+/* Prefill attention: every query position of a batch of sequences attends to the keys of its own sequence.
+ * (Attention notes, makinaruto.github.io: "FlashAttention" — intermediates stay on chip, one read and one write
+ *  of HBM; "online-softmax" — running max and exp-sum per block; "Group-Query Attention" derivation table —
+ *  query heads share KV heads in consecutive groups.)
+ *   q          [batch, seqlen, n_heads_q,  head_dim] of dtype (rotated already, see attn_rope_apply)
+ *   k, v       [batch, seqlen, n_heads_kv, head_dim] of dtype
+ *   o          [batch, seqlen, n_heads_q,  head_dim] of dtype, written
+ *   lse        NULL, or [batch, n_heads_q, seqlen] fp32 written with the natural-log sum-exp of each row's
+ *              scaled scores (lse = ln sum_j exp(scale * q.k_j) over the visible keys)
+ *   causal     1: key j is visible to query i iff j <= i; 0: every key is visible.
+ *   softmax_scale  multiplies q.k inside the softmax (1/sqrt(head_dim) for standard attention).
+ * Query head h uses KV head h / (n_heads_q / n_heads_kv).
+ * Supported: dtype ATTN_BF16 (bf16 MFMA, fp32 accumulation) or ATTN_FP32 (fp32 throughout), head_dim 64 or
+ * 128; anything else is UNSUPPORTED. INVALID_ARG: NULL q/k/v/o (with batch*seqlen > 0), n_heads_q % n_heads_kv
+ * != 0, non-positive head counts, bad scale. */
+int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int batch,
+                 int seqlen, int n_heads_q, int n_heads_kv, int head_dim, int causal, float softmax_scale,
+                 void* stream);
+
+/* Bytes of workspace attn_decode_paged needs for these sizes (0 if any size is non-positive). */
+size_t attn_decode_paged_workspace_size(int batch, int n_heads_q, int head_dim, int max_seqlen_kv);
+
+/* Decode over a paged KV cache: one query token per sequence attends to the sequence's seq_lens[b] cached tokens.
+ * (Attention notes, makinaruto.github.io: "Page Attention" — the cache is cut into fixed-size pages addressed
+ *  through a logical-to-physical map; "online-softmax" — the per-chunk (O, m, l) results merge exactly, so the
+ *  keys are split into fixed logical chunks that run in parallel and a second pass combines them by their
+ *  log-sum-exp.)
+ *   q            [batch, n_heads_q, head_dim] bf16, already rotated (attn_rope_apply at position seq_len-1)
+ *   k_cache, v_cache  [num_pages, page_size, n_heads_kv, head_dim] bf16
+ *   block_table  [batch, max_pages_per_seq] int32: logical token t of sequence b lives in physical page
+ *                block_table[b][t / page_size], slot t % page_size. Only entries t < seq_lens[b] are read,
+ *                so unused entries may hold anything (e.g. -1).
+ *   seq_lens     [batch] int32 on the device, 0 <= seq_lens[b] <= max_seqlen_kv and
+ *                <= max_pages_per_seq * page_size. The library never reads it on the host.
+ *   o            [batch, n_heads_q, head_dim] bf16, written; a sequence of length 0 gets O = 0.
+ *   lse          NULL or [batch, n_heads_q] fp32 (-inf for a sequence of length 0).
+ *   workspace    device buffer of at least attn_decode_paged_workspace_size(batch, n_heads_q, head_dim,
+ *                max_seqlen_kv) bytes; its contents need no initialisation and are clobbered.
+ * The result does not depend on where pages sit physically: chunk boundaries are logical, so two block tables
+ * over the same logical K/V give bitwise identical outputs. A page index outside [0, num_pages) in a used entry
+ * is not dereferenced (that chunk of keys is treated as zeros); such a result is meaningless but safe.
+ * Supported: head_dim 128 or 64, n_heads_q / n_heads_kv <= 16, page_size a power of two in [16, 1024].
+ * Otherwise UNSUPPORTED. INVALID_ARG as above, also for max_seqlen_kv < 0 or num_pages <= 0 (with batch > 0). */
+int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                      const int32_t* seq_lens, void* o, float* lse, int batch, int n_heads_q, int n_heads_kv,
+                      int head_dim, int page_size, int max_pages_per_seq, int64_t num_pages, int max_seqlen_kv,
+                      float softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace attn_mla_decode needs for these sizes (0 if any size is non-positive). */
+size_t attn_mla_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int max_seqlen_kv);
+
+/* Multi-head latent attention decode, absorbed form: all heads share one latent cache c_kv and one rope key
+ * k_pe; scores are scale * (q_latent . c_kv_t + q_pe . k_pe_t) and the output stays in the latent space,
+ * O_latent = softmax(scores) . c_kv.
+ * (DeepSeek-V3 attention guide: einsum vs manual optimisation, dksg.cn: the absorb-mode score einsums over
+ *  kv_cache and pe_cache; Attention notes, makinaruto.github.io, "Multi-Head Latent Attention": K = C^KV W^K_up
+ *  and V = C^KV W^V_up, with W^K_up folded into the query side and W^V_up into W^O; "RoPE" compatibility
+ *  section: the rotated part of the key is shared across heads.)
+ *   q_latent     [batch, n_heads, kv_lora_rank] bf16 (the no-RoPE query already multiplied by W^K_up)
+ *   q_pe         [batch, n_heads, rope_dim] bf16 (rotated)
+ *   c_kv         [batch, max_seqlen_kv, kv_lora_rank] bf16
+ *   k_pe         [batch, max_seqlen_kv, rope_dim] bf16 (rotated)
+ *   seq_lens     [batch] int32 on the device, 0 <= seq_lens[b] <= max_seqlen_kv
+ *   o_latent     [batch, n_heads, kv_lora_rank] bf16, written (0 for a sequence of length 0)
+ *   lse          NULL or [batch, n_heads] fp32
+ *   workspace    >= attn_mla_decode_workspace_size(batch, n_heads, kv_lora_rank, max_seqlen_kv) bytes.
+ * Supported: kv_lora_rank 512, rope_dim 64, n_heads a multiple of 32 up to 128 (every wave owns 32 heads).
+ * Otherwise UNSUPPORTED. INVALID_ARG as above. */
+int attn_mla_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
+                    const int32_t* seq_lens, void* o_latent, float* lse, int batch, int n_heads, int kv_lora_rank,
+                    int rope_dim, int max_seqlen_kv, float softmax_scale, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

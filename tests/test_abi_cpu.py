@@ -1,0 +1,156 @@
+"""The C ABI on the CPU: libattn.so loads, exports every function include/attn.h declares, sizes workspaces, and
+rejects invalid arguments with the documented status before any device work (so no GPU is needed here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+LIB = os.path.join(ROOT, "transformer_attention_causal_amd", "libattn.so")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+NULL = None
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libattn.so is not built: run python -m transformer_attention_causal_amd.build")
+    from transformer_attention_causal_amd import load_library
+    return load_library(LIB)
+
+
+def test_header_declares_the_four_operations():
+    names = declared_functions()
+    for n in ("attn_rope_apply", "attn_prefill", "attn_decode_paged", "attn_mla_decode"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from transformer_attention_causal_amd import SIGNATURES
+    names = declared_functions()
+    assert sorted(SIGNATURES) == names, "binding signatures and header disagree"
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code, word in [(0, b"ATTN_OK"), (1, b"INVALID_ARG"), (2, b"UNSUPPORTED"), (3, b"WORKSPACE"), (4, b"HIP")]:
+        assert word in lib.attn_status_string(code)
+    assert lib.attn_status_string(99)
+
+
+def test_workspace_sizes(lib):
+    # decode: [B, Hq, ceil(L/512), D] fp32 partial outputs (256-byte aligned) + [B, Hq, chunks] fp32 lse
+    b, hq, d, lmax = 64, 32, 128, 32768
+    chunks = (lmax + 511) // 512
+    o_bytes = (b * hq * chunks * d * 4 + 255) // 256 * 256
+    assert lib.attn_decode_paged_workspace_size(b, hq, d, lmax) == o_bytes + b * hq * chunks * 4
+    assert lib.attn_decode_paged_workspace_size(0, hq, d, lmax) == 0
+    assert lib.attn_decode_paged_workspace_size(b, hq, d, 0) == 0
+    # MLA: grows with the number of splits, which never exceeds ceil(L/32)
+    assert lib.attn_mla_decode_workspace_size(32, 128, 512, 32768) > 32 * 128 * 512 * 4
+    assert lib.attn_mla_decode_workspace_size(1, 128, 512, 32) == 128 * 512 * 4 + 128 * 4
+    assert lib.attn_mla_decode_workspace_size(-1, 128, 512, 32) == 0
+
+
+def test_rope_validation(lib):
+    f = lib.attn_rope_apply
+    assert f(FAKE, 0, 4, 2, 63, FAKE, 10000.0, 1, NULL) == INVALID        # odd head_dim
+    assert f(FAKE, 0, 4, 0, 64, FAKE, 10000.0, 1, NULL) == INVALID        # no heads
+    assert f(FAKE, 0, -1, 2, 64, FAKE, 10000.0, 1, NULL) == INVALID       # negative tokens
+    assert f(FAKE, 0, 4, 2, 64, FAKE, 1.0, 1, NULL) == INVALID            # base must exceed 1
+    assert f(FAKE, 0, 4, 2, 64, FAKE, float("nan"), 1, NULL) == INVALID
+    assert f(NULL, 0, 4, 2, 64, FAKE, 10000.0, 1, NULL) == INVALID        # null tensor
+    assert f(FAKE, 0, 4, 2, 64, NULL, 10000.0, 1, NULL) == INVALID        # null positions
+    assert f(FAKE, 7, 4, 2, 64, FAKE, 10000.0, 1, NULL) == UNSUPPORTED    # dtype
+    assert f(FAKE, 0, 4, 2, 2048, FAKE, 10000.0, 1, NULL) == UNSUPPORTED  # head_dim > 1024
+    assert f(NULL, 0, 0, 2, 64, NULL, 10000.0, 1, NULL) == OK             # nothing to do
+
+
+def test_prefill_validation(lib):
+    f = lib.attn_prefill
+    args = lambda **kw: dict(dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=NULL, dt=0, b=1, s=16, hq=8, hkv=2, d=128,
+                                  causal=1, scale=0.088), **kw)
+    call = lambda a: f(a["q"], a["k"], a["v"], a["o"], a["lse"], a["dt"], a["b"], a["s"], a["hq"], a["hkv"], a["d"],
+                       a["causal"], a["scale"], NULL)
+    assert call(args(hq=6, hkv=4)) == INVALID            # Hq % Hkv != 0
+    assert call(args(hkv=0)) == INVALID
+    assert call(args(s=-1)) == INVALID
+    assert call(args(scale=0.0)) == INVALID
+    assert call(args(scale=float("inf"))) == INVALID
+    assert call(args(q=NULL)) == INVALID
+    assert call(args(o=NULL)) == INVALID
+    assert call(args(d=96)) == UNSUPPORTED
+    assert call(args(dt=3)) == UNSUPPORTED
+    assert call(args(q=NULL, k=NULL, v=NULL, o=NULL, s=0)) == OK     # empty: nothing launched
+
+
+def test_decode_validation(lib):
+    f = lib.attn_decode_paged
+    ws_need = lib.attn_decode_paged_workspace_size(2, 8, 128, 100)
+
+    def call(**kw):
+        a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=NULL, b=2, hq=8, hkv=2, d=128, ps=64,
+                 maxp=2, npages=4, maxlen=100, scale=0.088, ws=FAKE, wsb=ws_need)
+        a.update(kw)
+        return f(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["o"], a["lse"], a["b"], a["hq"], a["hkv"], a["d"],
+                 a["ps"], a["maxp"], a["npages"], a["maxlen"], a["scale"], a["ws"], a["wsb"], NULL)
+    assert call(hq=6, hkv=4) == INVALID
+    assert call(maxlen=-1) == INVALID
+    assert call(scale=-1.0) == INVALID
+    assert call(ps=0) == INVALID
+    assert call(q=NULL) == INVALID
+    assert call(sl=NULL) == INVALID
+    assert call(bt=NULL) == INVALID
+    assert call(npages=0) == INVALID
+    assert call(d=64) == UNSUPPORTED
+    assert call(hq=64, hkv=2) == UNSUPPORTED             # group of 32 query heads > 16
+    assert call(ps=48) == UNSUPPORTED                    # not a power of two
+    assert call(ps=8) == UNSUPPORTED
+    assert call(wsb=ws_need - 1) == WORKSPACE
+    assert call(ws=NULL) == WORKSPACE
+    assert call(b=0) == OK
+
+
+def test_mla_validation(lib):
+    f = lib.attn_mla_decode
+    ws_need = lib.attn_mla_decode_workspace_size(2, 128, 512, 64)
+
+    def call(**kw):
+        a = dict(ql=FAKE, qp=FAKE, ckv=FAKE, kpe=FAKE, sl=FAKE, o=FAKE, lse=NULL, b=2, h=128, c=512, r=64, t=64,
+                 scale=0.072, ws=FAKE, wsb=ws_need)
+        a.update(kw)
+        return f(a["ql"], a["qp"], a["ckv"], a["kpe"], a["sl"], a["o"], a["lse"], a["b"], a["h"], a["c"], a["r"],
+                 a["t"], a["scale"], a["ws"], a["wsb"], NULL)
+    assert call(h=0) == INVALID
+    assert call(t=-2) == INVALID
+    assert call(scale=float("nan")) == INVALID
+    assert call(ql=NULL) == INVALID
+    assert call(ckv=NULL) == INVALID
+    assert call(c=256) == UNSUPPORTED
+    assert call(r=32) == UNSUPPORTED
+    assert call(h=48) == UNSUPPORTED
+    assert call(h=256) == UNSUPPORTED
+    assert call(wsb=ws_need - 4) == WORKSPACE
+    assert call(b=0) == OK
+
+
+def test_binding_refuses_without_library(tmp_path):
+    from transformer_attention_causal_amd import binding
+    saved = binding._lib
+    binding._lib = None
+    try:
+        with pytest.raises(RuntimeError, match="not built"):
+            binding.load_library(str(tmp_path / "missing.so"))
+    finally:
+        binding._lib = saved

@@ -1,0 +1,173 @@
+"""Thin Python binding over libattn's C ABI (include/attn.h), with the same entry-point names.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels behind the C ABI. PyTorch
+provides device memory and the current stream. If libattn.so is missing or cannot be loaded, every call raises
+(there is no fallback path).
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_BF16, ATTN_FP32 = 0, 1
+STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_WORKSPACE",
+          4: "ATTN_ERR_HIP"}
+
+# (name, restype, argtypes) for every symbol include/attn.h declares.
+_P, _I, _I64, _D, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "attn_rope_apply": (_I, [_P, _I, _I64, _I, _I, _P, _D, _I, _P]),
+    "attn_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_decode_paged_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _I, _F, _P, _SZ, _P]),
+    "attn_mla_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "attn_mla_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
+    "attn_status_string": (ctypes.c_char_p, [_I]),
+}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libattn.so (once) and declare its C signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run `python -m transformer_attention_causal_amd.build` "
+                           "(hipcc, gfx950). There is no fallback implementation.")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise AttnError(fn, status)
+
+
+def _stream(t, stream):
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t, name, dtype=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _code(dtype):
+    if dtype == torch.bfloat16:
+        return ATTN_BF16
+    if dtype == torch.float32:
+        return ATTN_FP32
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+def attn_rope_apply(x, positions, theta, interleaved=True, stream=None):
+    """Rotate x ([..., H, D], bf16 or fp32, contiguous) in place; positions: int32 [prod(x.shape[:-2])]."""
+    lib = load_library()
+    n_tokens = x.numel() // (x.shape[-1] * x.shape[-2]) if x.dim() >= 2 else 0
+    if positions.numel() != n_tokens:
+        raise ValueError("positions must have one entry per token row")
+    _check("attn_rope_apply", lib.attn_rope_apply(_dev(x, "x"), _code(x.dtype), n_tokens, x.shape[-2], x.shape[-1],
+                                                   _dev(positions, "positions", torch.int32), float(theta),
+                                                   1 if interleaved else 0, _stream(x, stream)))
+    return x
+
+
+def attn_prefill(q, k, v, causal=True, softmax_scale=None, o=None, lse=None, return_lse=False, stream=None):
+    """q [B, S, Hq, D], k/v [B, S, Hkv, D] (bf16 or fp32) -> o [B, S, Hq, D] (and lse [B, Hq, S] fp32)."""
+    lib = load_library()
+    bsz, s_len, hq, d = q.shape
+    hkv = k.shape[2]
+    if k.shape != (bsz, s_len, hkv, d) or v.shape != k.shape or k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("k and v must be [B, S, Hkv, D] with q's dtype")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((bsz, hq, s_len), dtype=torch.float32, device=q.device)
+    lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
+    _check("attn_prefill", lib.attn_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o", q.dtype), lse_p,
+                                             _code(q.dtype), bsz, s_len, hq, hkv, d, 1 if causal else 0, scale,
+                                             _stream(q, stream)))
+    return (o, lse) if return_lse else o
+
+
+def attn_decode_paged_workspace_size(batch, n_heads_q, head_dim, max_seqlen_kv):
+    return int(load_library().attn_decode_paged_workspace_size(batch, n_heads_q, head_dim, max_seqlen_kv))
+
+
+def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seqlen_kv, softmax_scale=None, o=None,
+                      lse=None, workspace=None, return_lse=False, stream=None):
+    """q [B, Hq, D] bf16 (rotated); caches [num_pages, page, Hkv, D] bf16; block_table [B, max_pages] int32;
+    seq_lens [B] int32 (device). Returns o [B, Hq, D] bf16 (and lse [B, Hq] fp32)."""
+    lib = load_library()
+    bsz, hq, d = q.shape
+    num_pages, page, hkv, _ = k_cache.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((bsz, hq), dtype=torch.float32, device=q.device)
+    need = attn_decode_paged_workspace_size(bsz, hq, d, max(1, int(max_seqlen_kv)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
+    _check("attn_decode_paged", lib.attn_decode_paged(
+        _dev(q, "q", torch.bfloat16), _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+        _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+        _dev(o, "o", torch.bfloat16), lse_p, bsz, hq, hkv, d, page, block_table.shape[1], num_pages,
+        int(max_seqlen_kv), scale, _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(q, stream)))
+    return (o, lse) if return_lse else o
+
+
+def attn_mla_decode_workspace_size(batch, n_heads, kv_lora_rank, max_seqlen_kv):
+    return int(load_library().attn_mla_decode_workspace_size(batch, n_heads, kv_lora_rank, max_seqlen_kv))
+
+
+def attn_mla_decode(q_latent, q_pe, c_kv, k_pe, seq_lens, softmax_scale, o=None, lse=None, workspace=None,
+                    return_lse=False, stream=None):
+    """q_latent [B, H, C], q_pe [B, H, R], c_kv [B, T, C], k_pe [B, T, R] bf16; seq_lens [B] int32 (device).
+    Returns o_latent [B, H, C] bf16 (and lse [B, H] fp32)."""
+    lib = load_library()
+    bsz, nh, c = q_latent.shape
+    r = q_pe.shape[-1]
+    t = c_kv.shape[1]
+    if o is None:
+        o = torch.empty_like(q_latent)
+    if lse is None and return_lse:
+        lse = torch.empty((bsz, nh), dtype=torch.float32, device=q_latent.device)
+    need = attn_mla_decode_workspace_size(bsz, nh, c, max(1, t))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_latent.device)
+    lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
+    _check("attn_mla_decode", lib.attn_mla_decode(
+        _dev(q_latent, "q_latent", torch.bfloat16), _dev(q_pe, "q_pe", torch.bfloat16),
+        _dev(c_kv, "c_kv", torch.bfloat16), _dev(k_pe, "k_pe", torch.bfloat16),
+        _dev(seq_lens, "seq_lens", torch.int32), _dev(o, "o_latent", torch.bfloat16), lse_p, bsz, nh, c, r, t,
+        float(softmax_scale), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(q_latent, stream)))
+    return (o, lse) if return_lse else o

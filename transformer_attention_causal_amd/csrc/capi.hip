@@ -1,0 +1,107 @@
+// capi.hip — the extern "C" boundary of libattn (declared in include/attn.h).
+//
+// Each entry point validates its arguments on the host BEFORE touching the HIP runtime, so an invalid call
+// returns its status without any device work (and without needing a GPU), then enqueues the kernels on the
+// caller's stream. No allocation, no synchronisation, no state kept between calls.
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/attn.h"
+#include "kernels.h"
+
+#define ATTN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+int hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace
+
+ATTN_EXPORT const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: valid request not implemented by this build";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE: workspace too small";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: HIP runtime error at launch";
+    default: return "unknown attn status";
+  }
+}
+
+ATTN_EXPORT int attn_rope_apply(void* x, int dtype, int64_t n_tokens, int n_heads, int head_dim,
+                                const int32_t* positions, double theta, int interleaved, void* stream) {
+  if (n_tokens < 0 || n_heads <= 0 || head_dim <= 0 || (head_dim & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(theta) || theta <= 1.0) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
+  if (head_dim > 1024) return ATTN_ERR_UNSUPPORTED;
+  if (n_tokens == 0) return ATTN_OK;
+  if (!x || !positions) return ATTN_ERR_INVALID_ARG;
+  return hip_status(attn::launch_rope(x, dtype, n_tokens, n_heads, head_dim, positions, theta, interleaved ? 1 : 0,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+ATTN_EXPORT int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int batch,
+                             int seqlen, int n_heads_q, int n_heads_kv, int head_dim, int causal,
+                             float softmax_scale, void* stream) {
+  if (batch < 0 || seqlen < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0) return ATTN_ERR_INVALID_ARG;
+  if (n_heads_q % n_heads_kv != 0 || !valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_BF16 && dtype != ATTN_FP32) return ATTN_ERR_UNSUPPORTED;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (int64_t(batch) * seqlen == 0) return ATTN_OK;
+  if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == ATTN_BF16)
+    return hip_status(attn::launch_prefill_bf16(q, k, v, o, lse, batch, seqlen, n_heads_q, n_heads_kv, head_dim,
+                                                causal ? 1 : 0, softmax_scale, s));
+  return hip_status(attn::launch_prefill_fp32(q, k, v, o, lse, batch, seqlen, n_heads_q, n_heads_kv, head_dim,
+                                              causal ? 1 : 0, softmax_scale, s));
+}
+
+ATTN_EXPORT size_t attn_decode_paged_workspace_size(int batch, int n_heads_q, int head_dim, int max_seqlen_kv) {
+  return attn::decode_paged_workspace_bytes(batch, n_heads_q, head_dim, max_seqlen_kv);
+}
+
+ATTN_EXPORT int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                                  int batch, int n_heads_q, int n_heads_kv, int head_dim, int page_size,
+                                  int max_pages_per_seq, int64_t num_pages, int max_seqlen_kv,
+                                  float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0 || max_seqlen_kv < 0) return ATTN_ERR_INVALID_ARG;
+  if (n_heads_q % n_heads_kv != 0 || !valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (page_size <= 0 || max_pages_per_seq < 0) return ATTN_ERR_INVALID_ARG;
+  if (head_dim != 128 || n_heads_q / n_heads_kv > 16) return ATTN_ERR_UNSUPPORTED;
+  if (!is_pow2(page_size) || page_size < 16 || page_size > 1024) return ATTN_ERR_UNSUPPORTED;
+  if (batch == 0) return ATTN_OK;
+  if (!q || !seq_lens || !o) return ATTN_ERR_INVALID_ARG;
+  if (max_seqlen_kv > 0 && (!k_cache || !v_cache || !block_table || num_pages <= 0 || max_pages_per_seq <= 0))
+    return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn::decode_paged_workspace_bytes(batch, n_heads_q, head_dim, max(1, max_seqlen_kv));
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  return hip_status(attn::launch_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, batch, n_heads_q,
+                                              n_heads_kv, head_dim, page_size, max_pages_per_seq, num_pages,
+                                              max_seqlen_kv, softmax_scale, workspace,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+ATTN_EXPORT size_t attn_mla_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int max_seqlen_kv) {
+  return attn::mla_decode_workspace_bytes(batch, n_heads, kv_lora_rank, max_seqlen_kv);
+}
+
+ATTN_EXPORT int attn_mla_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
+                                const int32_t* seq_lens, void* o_latent, float* lse, int batch, int n_heads,
+                                int kv_lora_rank, int rope_dim, int max_seqlen_kv, float softmax_scale,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || n_heads <= 0 || kv_lora_rank <= 0 || rope_dim <= 0 || max_seqlen_kv < 0) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (kv_lora_rank != 512 || rope_dim != 64 || n_heads % 32 != 0 || n_heads > 128) return ATTN_ERR_UNSUPPORTED;
+  if (batch == 0) return ATTN_OK;
+  if (!q_latent || !q_pe || !seq_lens || !o_latent) return ATTN_ERR_INVALID_ARG;
+  if (max_seqlen_kv > 0 && (!c_kv || !k_pe)) return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn::mla_decode_workspace_bytes(batch, n_heads, kv_lora_rank, max(1, max_seqlen_kv));
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  return hip_status(attn::launch_mla_decode(q_latent, q_pe, c_kv, k_pe, seq_lens, o_latent, lse, batch, n_heads,
+                                            max_seqlen_kv, softmax_scale, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}

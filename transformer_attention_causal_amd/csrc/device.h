@@ -1,0 +1,93 @@
+// device.h — gfx950 device helpers shared by the attention kernels (vector types, bf16 packing, MFMA
+// wrappers, LDS transpose reads, direct-to-LDS loads, wave64 cross-lane reductions).
+//
+// MFMA operand layouts used throughout (gfx950, wave64; verified on hardware):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds A[l%32][8*(l/32) + s], s = 0..7        B: lane l holds B[8*(l/32) + s][l%32]
+//     D: lane l, register r holds D[8*(r/4) + 4*(l/32) + r%4][l%32]
+//   v_mfma_f32_16x16x32_bf16  D[16x16] += A[16x32] * B[32x16]
+//     A: lane l holds A[l%16][8*(l/16) + s]                   B: lane l holds B[8*(l/16) + s][l%16]
+//     D: lane l, register r holds D[4*(l/16) + r][l%16]
+//   ds_read_b64_tr_b16: within each block of 16 lanes, result lane i, element j is element i%4 of the 8 bytes
+//     addressed by lane 4*j + i/4 of the block. So if block lane 4*j + c addresses row (k0 + j), columns
+//     (n0 + 4c .. n0 + 4c + 3) of a row-major 16-bit matrix, lane i receives column n0 + i, rows k0 .. k0 + 3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// ------------------------------------------------------------------------------------------ bf16 packing --
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two fp32 -> two bf16 (round to nearest even), packed lo | hi << 16 (one v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  bf16x2_t b = __builtin_convertvector(v, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Eight fp32 values -> an 8 x bf16 MFMA operand.
+__device__ __forceinline__ bf16x8_t pack_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                                float a6, float a7) {
+  u32x4_t w = {pack_bf16x2(a0, a1), pack_bf16x2(a2, a3), pack_bf16x2(a4, a5), pack_bf16x2(a6, a7)};
+  return as_bf16x8(w);
+}
+
+// ------------------------------------------------------------------------------------------------ MFMA --
+__device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------------------------------------------- LDS --
+// 16-byte LDS read.
+__device__ __forceinline__ u32x4_t lds_read16(const uint16_t* lds_base, uint32_t byte_off) {
+  return *(const __attribute__((address_space(3))) u32x4_t*)((const __attribute__((address_space(3))) char*)lds_base +
+                                                                byte_off);
+}
+
+// Transposing 8-byte LDS read (see the layout note at the top of this file).
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* lds_base, uint32_t byte_off) {
+  i16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4_t*)((__attribute__((address_space(3))) char*)lds_base + byte_off));
+  return __builtin_bit_cast(u32x2_t, t);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane i's 16 bytes land at lds_wave_base + 16*i, where
+// lds_wave_base must be the same for the whole wave.
+__device__ __forceinline__ void load_lds16(const void* gsrc, uint16_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(const_cast<void*>(gsrc), (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------------------------------- cross-lane --
+__device__ __forceinline__ float xor_lanes(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Online-softmax lazy rescale threshold (log2 units): the running reference max is only moved when the new block
+// max exceeds it by more than this, so unnormalised probabilities stay below 2^kRescaleLog2.
+constexpr float kRescaleLog2 = 8.0f;
+
+}  // namespace attn

@@ -1,0 +1,38 @@
+// kernels.h — internal launchers behind the C ABI (not exported). Arguments are already validated by the
+// caller; every launcher only enqueues on `stream` and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace attn {
+
+// RoPE, in place. dtype: 0 bf16, 1 fp32.
+hipError_t launch_rope(void* x, int dtype, int64_t n_tokens, int n_heads, int head_dim, const int32_t* positions,
+                       double theta, int interleaved, hipStream_t stream);
+
+// Prefill. bf16: MFMA path; fp32: VALU path. head_dim 64 or 128.
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                               int seqlen, int hq, int hkv, int head_dim, int causal, float scale,
+                               hipStream_t stream);
+hipError_t launch_prefill_fp32(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                               int seqlen, int hq, int hkv, int head_dim, int causal, float scale,
+                               hipStream_t stream);
+
+// Paged decode: split-KV partials into the workspace, then the log-sum-exp combine.
+constexpr int kDecodeChunk = 512;  // keys per split (a multiple of 32); split boundaries are logical positions
+size_t decode_paged_workspace_bytes(int batch, int hq, int head_dim, int max_seqlen_kv);
+hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, void* o, float* lse, int batch, int hq, int hkv,
+                               int head_dim, int page_size, int max_pages_per_seq, int64_t num_pages,
+                               int max_seqlen_kv, float scale, void* workspace, hipStream_t stream);
+
+// MLA absorbed decode: split over tokens, then the log-sum-exp combine.
+int mla_num_splits(int batch, int max_seqlen_kv);
+int mla_split_len(int batch, int max_seqlen_kv);
+size_t mla_decode_workspace_bytes(int batch, int n_heads, int kv_lora_rank, int max_seqlen_kv);
+hipError_t launch_mla_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
+                             const int32_t* seq_lens, void* o_latent, float* lse, int batch, int n_heads,
+                             int max_seqlen_kv, float scale, void* workspace, hipStream_t stream);
+
+}  // namespace attn

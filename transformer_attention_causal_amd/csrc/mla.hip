@@ -1,0 +1,263 @@
+// mla.hip — multi-head latent attention decode in the absorbed form.
+//
+// (DeepSeek-V3 attention guide: einsum vs manual optimisation, dksg.cn: absorb-mode scores are
+//  scale * (q_nope . kv_cache + q_pe . pe_cache), two contractions over the latent cache and the shared rope
+//  cache; Attention notes, makinaruto.github.io, "Multi-Head Latent Attention": W^K_up folds into the query and
+//  W^V_up into W^O, so attention runs in the latent space with O_latent = P . C^KV; "RoPE" compatibility section:
+//  the rotated key part is one vector per token shared by every head.)
+//
+// Every head reads the same 576-wide key row [c_kv ; k_pe] and the same 512-wide value row c_kv, so MLA decode is
+// a single-KV-head attention with 128 query rows: the same structure as the prefill kernel with heads in place
+// of query positions.
+//   * One workgroup = (token split, sequence), 8 waves x 16 heads. Token tiles of 32 rows x 576 are copied
+//     straight into LDS (global_load_lds, 16 bytes per lane), double-buffered, one barrier per tile; rows are
+//     unpadded and their 16-byte chunks XOR-swizzled by (row & 7) so both read patterns are conflict-free.
+//   * S^T = Kc Q^T on v_mfma_f32_16x16x32_bf16 (K fragments from LDS, the 576-wide query of the wave's 16 heads
+//     resident in registers). Each lane then holds one head, so the online-softmax statistics and the output
+//     rescale are per-lane scalars plus two exchanges across the four 16-lane groups.
+//   * O^T = c_kv^T P^T: the value operand is the SAME LDS tile read through ds_read_b64_tr_b16 (no second copy),
+//     P^T comes straight from the S^T registers. O^T for 16 heads x 512 stays in registers (128 per lane).
+//   * Splits over tokens write (O / l, lse) partials; the combine kernel merges them by log-sum-exp.
+// HBM-bound in principle (about 240 flop per byte) but close to the MFMA ridge, so both matter.
+#include "device.h"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+constexpr int kC = 512;             // kv_lora_rank
+constexpr int kR = 64;              // rope dim
+constexpr int kDK = kC + kR;        // key width
+constexpr int kRows = 32;           // tokens per tile
+constexpr int kChunks = kDK / 8;    // 72 16-byte chunks per row
+constexpr int kRowBytes = kDK * 2;  // 1152
+constexpr int kTileElems = kRows * kDK;
+constexpr int kTileBlocks = kRows * kChunks / 64;  // 36 wave-instructions of 64 slots
+constexpr int kTargetBlocks = 256;  // one workgroup per compute unit on MI355X
+
+struct MlaArgs {
+  const uint16_t* q_lat;
+  const uint16_t* q_pe;
+  const uint16_t* c_kv;
+  const uint16_t* k_pe;
+  const int32_t* seq_lens;
+  float* ws_o;     // [batch, heads, n_split, 512]
+  float* ws_lse;   // [batch, heads, n_split]
+  int heads, max_len, n_split, split_len;
+  float scale;
+};
+
+// Copy tile rows t_tile .. t_tile+31 (clamped to t_last, a valid token) of sequence b into LDS `dst`.
+__device__ __forceinline__ void mla_issue(uint16_t* dst, const MlaArgs& a, int b, int t_tile, int t_last, int wave,
+                                          int nwaves, int lane) {
+  for (int blk = wave; blk < kTileBlocks; blk += nwaves) {
+    const int slot = blk * 64 + lane;
+    const int row = slot / kChunks;
+    const int lchunk = (slot % kChunks) ^ (row & 7);
+    const int tok = min(t_tile + row, t_last);
+    const int64_t tb = int64_t(b) * a.max_len + tok;
+    const uint16_t* gp = lchunk < kC / 8 ? a.c_kv + tb * kC + lchunk * 8 : a.k_pe + tb * kR + (lchunk - kC / 8) * 8;
+    load_lds16(gp, dst + blk * 512);
+  }
+}
+
+// Heads per wave: 16 (the N dimension of v_mfma_f32_16x16x32_bf16), so a wave keeps its 576-wide query
+// (72 registers) and its O^T = 512 x 16 fp32 (128 registers) resident without spilling; 8 waves cover 128 heads.
+constexpr int kHeadsPerWave = 16;
+
+__global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][kTileElems];
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int nwaves = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, g4 = lane >> 4;
+  const int L = max(0, min(a.seq_lens[b], a.max_len));
+  const int t_begin = split * a.split_len;
+  if (t_begin >= L) return;                           // uniform over the workgroup
+  const int t_end = min(L, t_begin + a.split_len);
+  const int ntiles = (t_end - t_begin + kRows - 1) / kRows;
+  const int h = wave * kHeadsPerWave + n;
+  const float c = a.scale * kLog2e;
+
+  // query [q_lat ; q_pe] of head h: B operands of the 18 k-steps, dims 32*ks + 8*g4 ..
+  bf16x8_t qop[kDK / 32];
+#pragma unroll
+  for (int ks = 0; ks < kDK / 32; ++ks) {
+    const int d = 32 * ks + 8 * g4;
+    const uint16_t* p = d < kC ? a.q_lat + (int64_t(b) * a.heads + h) * kC + d
+                               : a.q_pe + (int64_t(b) * a.heads + h) * kR + (d - kC);
+    qop[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(p));
+  }
+  // O^T: 32 blocks of 16 latent dims; lane holds head n, dims 16*db + 4*g4 + r
+  f32x4_t oacc[kC / 16];
+#pragma unroll
+  for (int db = 0; db < kC / 16; ++db) oacc[db] = f32x4_t{};
+  float m = -INFINITY, l = 0.f;
+
+  // Lane-fixed parts of the swizzled LDS addresses (chunk c of row r sits at 8*(c/8) + ((c%8) ^ (r&7))); the
+  // loops add only compile-time immediates.
+  uint32_t abase[2];                                   // K reads: row n (+16*tb), chunk 4*ks + g4
+#pragma unroll
+  for (int i = 0; i < 2; ++i) abase[i] = uint32_t(n * kRowBytes + 16 * ((4 * i + g4) ^ (n & 7)));
+  const int bl = lane & 15;
+  const int vrow = 4 * g4 + (bl >> 2);                 // V reads: rows vrow (+16), columns 16*db + 4*(bl&3)
+  uint32_t vbase[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    vbase[i] = uint32_t(vrow * kRowBytes + 16 * ((2 * i + ((bl >> 1) & 1)) ^ (vrow & 7)) + 8 * (bl & 1));
+
+  mla_issue(lds[0], a, b, t_begin, t_end - 1, wave, nwaves, lane);
+
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < ntiles) mla_issue(lds[(t + 1) & 1], a, b, t_begin + (t + 1) * kRows, t_end - 1, wave, nwaves, lane);
+    const uint16_t* T = lds[t & 1];
+    const int tok0 = t_begin + t * kRows;
+
+    // S^T = Kc Q^T: two 16-token blocks; lane holds head n, tokens 16*tb + 4*g4 + r
+    f32x4_t sacc[2] = {f32x4_t{}, f32x4_t{}};
+#pragma unroll
+    for (int ks = 0; ks < kDK / 32; ++ks) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+        sacc[tb] = mfma16x16x32(as_bf16x8(lds_read16(T, abase[ks & 1] + 128 * (ks >> 1) + 16 * tb * kRowBytes)),
+                                qop[ks], sacc[tb]);
+      if (ks % 6 == 5) __builtin_amdgcn_sched_barrier(0);   // bound how far LDS reads are hoisted (registers)
+    }
+    if (tok0 + kRows > t_end) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (tok0 + 16 * tb + 4 * g4 + r >= t_end) sacc[tb][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[tb][r]);
+    mx = fmaxf(mx, xor_lanes(mx, 16));
+    mx = fmaxf(mx, xor_lanes(mx, 32));
+    // Lazy rescale: the reference max moves (and O, l are rescaled) only when it grows by more than
+    // 2^kRescaleLog2 for some lane of the wave; otherwise P may exceed 1 by at most that factor. O / l is unchanged.
+    if (__any((mx - m) * c > kRescaleLog2)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2((m - m_new) * c);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < kC / 16; ++db) oacc[db] *= alpha;
+      m = m_new;
+    }
+    const float mc = m * c;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(fmaf(sacc[tb][r], c, -mc));
+        sacc[tb][r] = p;
+        l += p;
+      }
+    const bf16x8_t pb = pack_bf16x8(sacc[0][0], sacc[0][1], sacc[0][2], sacc[0][3], sacc[1][0], sacc[1][1],
+                                    sacc[1][2], sacc[1][3]);
+    // O^T += c_kv^T P^T: the value operand is the same tile read through the transposing LDS read
+#pragma unroll
+    for (int db = 0; db < kC / 16; ++db) {
+      const uint32_t off = vbase[db & 3] + 128 * (db >> 2);
+      const u32x2_t lo = lds_read_tr16(T, off);
+      const u32x2_t hi = lds_read_tr16(T, off + 16 * kRowBytes);
+      const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+      oacc[db] = mfma16x16x32(as_bf16x8(w), pb, oacc[db]);
+      if (db % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  float lt = l + xor_lanes(l, 16);
+  lt += xor_lanes(lt, 32);
+  const float inv = 1.f / lt;
+  const int64_t slot = (int64_t(b) * a.heads + h) * a.n_split + split;
+  float* wo = a.ws_o + slot * kC + 4 * g4;
+#pragma unroll
+  for (int db = 0; db < kC / 16; ++db) {
+    const f32x4_t v = {oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv};
+    *reinterpret_cast<f32x4_t*>(wo + 16 * db) = v;
+  }
+  if (g4 == 0) a.ws_lse[slot] = m * a.scale + logf(lt);
+}
+
+// Merge splits: M = max lse_s, w_s = exp(lse_s - M), O = sum w_s O_s / sum w_s; length 0 -> O = 0, lse = -inf.
+__global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ ws_o,
+    const float* __restrict__ ws_lse, const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ o,
+    float* __restrict__ lse, int heads, int n_split, int split_len, int max_len) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int L = max(0, min(seq_lens[b], max_len));
+  const int ns = (L + split_len - 1) / split_len;
+  const int64_t base = (int64_t(b) * heads + h) * n_split;
+  uint16_t* op = o + (int64_t(b) * heads + h) * kC;
+  const int d0 = 2 * threadIdx.x;
+  if (ns == 0) {
+    *reinterpret_cast<uint32_t*>(op + d0) = 0u;
+    if (lse && threadIdx.x == 0) lse[int64_t(b) * heads + h] = -INFINITY;
+    return;
+  }
+  float mx = -INFINITY;
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ws_lse[base + s]);
+  float a0 = 0.f, a1 = 0.f, wsum = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = expf(ws_lse[base + s] - mx);
+    wsum += w;
+    const f32x2_t v = *reinterpret_cast<const f32x2_t*>(ws_o + (base + s) * kC + d0);
+    a0 = fmaf(w, v[0], a0);
+    a1 = fmaf(w, v[1], a1);
+  }
+  *reinterpret_cast<uint32_t*>(op + d0) = pack_bf16x2(a0 / wsum, a1 / wsum);
+  if (lse && threadIdx.x == 0) lse[int64_t(b) * heads + h] = mx + logf(wsum);
+}
+
+}  // namespace
+
+int mla_num_splits(int batch, int max_seqlen_kv) {
+  if (batch <= 0 || max_seqlen_kv <= 0) return 1;
+  const int by_cu = (kTargetBlocks + batch - 1) / batch;
+  const int by_len = (max_seqlen_kv + kRows - 1) / kRows;
+  return max(1, min(by_cu, by_len));
+}
+
+int mla_split_len(int batch, int max_seqlen_kv) {
+  const int ns = mla_num_splits(batch, max_seqlen_kv);
+  const int per = (max(1, max_seqlen_kv) + ns - 1) / ns;
+  return (per + kRows - 1) / kRows * kRows;
+}
+
+size_t mla_decode_workspace_bytes(int batch, int n_heads, int kv_lora_rank, int max_seqlen_kv) {
+  if (batch <= 0 || n_heads <= 0 || kv_lora_rank <= 0 || max_seqlen_kv <= 0) return 0;
+  const size_t slots = size_t(batch) * size_t(n_heads) * size_t(mla_num_splits(batch, max_seqlen_kv));
+  const size_t o_bytes = (slots * size_t(kv_lora_rank) * sizeof(float) + 255) & ~size_t(255);
+  return o_bytes + slots * sizeof(float);
+}
+
+hipError_t launch_mla_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
+                             const int32_t* seq_lens, void* o_latent, float* lse, int batch, int n_heads,
+                             int max_seqlen_kv, float scale, void* workspace, hipStream_t stream) {
+  MlaArgs a;
+  a.q_lat = static_cast<const uint16_t*>(q_latent);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.c_kv = static_cast<const uint16_t*>(c_kv);
+  a.k_pe = static_cast<const uint16_t*>(k_pe);
+  a.seq_lens = seq_lens;
+  a.heads = n_heads; a.max_len = max_seqlen_kv; a.scale = scale;
+  a.n_split = mla_num_splits(batch, max_seqlen_kv);
+  a.split_len = mla_split_len(batch, max_seqlen_kv);
+  const size_t slots = size_t(batch) * size_t(n_heads) * size_t(a.n_split);
+  const size_t o_bytes = (slots * kC * sizeof(float) + 255) & ~size_t(255);
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  if (max_seqlen_kv > 0)
+    mla_split_kernel<<<dim3(unsigned(a.n_split), unsigned(batch)), dim3(64 * (n_heads / kHeadsPerWave)), 0, stream>>>(a);
+  mla_combine_kernel<<<dim3(unsigned(n_heads), unsigned(batch)), dim3(kC / 2), 0, stream>>>(
+      a.ws_o, a.ws_lse, seq_lens, static_cast<uint16_t*>(o_latent), lse, n_heads, a.n_split, a.split_len,
+      max_seqlen_kv);
+  return hipGetLastError();
+}
+
+}  // namespace attn

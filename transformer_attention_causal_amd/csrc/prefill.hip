@@ -1,0 +1,365 @@
+// prefill.hip — exact causal (or full) grouped-query attention over whole sequences.
+//
+// (Attention notes, makinaruto.github.io, posts/nlp/llm_learning/attention: "FlashAttention" — all intermediate
+//  work stays in fast on-chip memory and HBM is read and written once; "online-softmax" — per block, the block max
+//  m_c and block exp-sum l_c update the running m and l, m_new = max(m_old, m_c), l_new = l_old e^(m_old - m_new)
+//  + l_c e^(m_c - m_new); "Group-Query Attention" derivation table — consecutive query heads share a KV head.)
+//
+// bf16 path, one workgroup = 4 waves:
+//   * Work unit: QW = 32*QB query positions of 4 query heads of one KV group ("heads mode", when the group size
+//     is a multiple of 4: every wave has the same causal range and the K/V tile in LDS feeds 4*QW query rows), or
+//     4 consecutive blocks of QW positions of one query head ("positions mode", any other group size).
+//   * K and V tiles of 64 keys x D are copied straight from global memory into LDS (global_load_lds, 16 bytes
+//     per lane, no register staging), double-buffered, one barrier per tile. LDS rows are unpadded; their
+//     16-byte chunks are XOR-swizzled by (row & 7), which makes both LDS read patterns below conflict-free.
+//   * Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16: K fragments come from LDS (16-byte
+//     reads), Q^T stays in registers for the whole kernel. In the S^T accumulator each lane holds ONE query
+//     (lane % 32) and 16 keys, so the row max and row sum need one cross-lane exchange (lanes l and l ^ 32), and
+//     the output rescale by alpha = exp(m_old - m_new) is a per-lane scalar.
+//   * P^T (bf16) is taken directly from the S^T registers as the B operand of O^T = V^T P^T: the 16 keys a lane
+//     holds are used as its 8+8 contraction slots, and V^T fragments are read with the matching key order by
+//     ds_read_b64_tr_b16 from the row-major V tile. P never leaves registers.
+//   * exp is exp2 with scale*log2(e) folded into one FMA. Tiles fully above the diagonal are skipped; only tiles
+//     that cross the diagonal or the ragged end are masked. Heaviest query blocks are launched first.
+// fp32 path (correctness workload, head_dim 64/128): plain VALU, K/V tiles of 32 keys in LDS, fp32 throughout.
+#include "device.h"
+#include "kernels.h"
+
+namespace attn {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kBN = 64;  // keys per tile
+
+template <int D>
+struct Tile {
+  static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kBytes = kBN * kRowBytes;         // one K or V tile
+  static constexpr int kLoadsPerWave = kBN * kChunks / kThreads;
+  static_assert(kBN * kChunks % kThreads == 0, "tile must split evenly over the workgroup");
+};
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int batch, seqlen, hq, hkv;
+  float scale;
+  int causal;
+  int heads_mode;    // 1: 4 heads x QW positions per workgroup; 0: 1 head x 4*QW positions
+  int n_pblk;        // position blocks per (batch, head group)
+  int n_hgrp;        // head groups: hq/4 in heads mode, hq in positions mode
+};
+
+// Issue the direct-to-LDS copy of one K or V tile (rows key0 .. key0+63 of KV head g) into `dst`.
+// Rows at or past seqlen are clamped to the last row (finite data; their scores are masked and P is 0).
+template <int D>
+__device__ __forceinline__ void issue_tile(uint16_t* dst, const uint16_t* src, int b, int g, int key0,
+                                           const PrefillArgs& a, int wave, int lane) {
+  const int64_t row_stride = int64_t(a.hkv) * D;
+#pragma unroll
+  for (int i = 0; i < Tile<D>::kLoadsPerWave; ++i) {
+    const int blk = i * kWaves + wave;               // 64-slot block this wave instruction fills
+    const int slot = blk * 64 + lane;
+    const int row = slot / Tile<D>::kChunks;
+    const int lchunk = (slot % Tile<D>::kChunks) ^ (row & 7);
+    const int key = min(key0 + row, a.seqlen - 1);
+    const uint16_t* gp = src + (int64_t(b) * a.seqlen + key) * row_stride + int64_t(g) * D + lchunk * 8;
+    load_lds16(gp, dst + blk * 512);
+  }
+}
+
+template <int D, int QB>
+__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
+  constexpr int QW = 32 * QB;
+  constexpr int KS = D / 16;   // k-steps of the QK^T contraction
+  constexpr int DB = D / 32;   // 32-row blocks of O^T
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kBN * D];   // [buffer][K, V]
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lq = lane & 31, lg = lane >> 5;
+  // ---- work unit (heaviest position blocks first; consecutive ids share a position block)
+  const int per_slice = a.batch * a.n_hgrp;
+  const int id = blockIdx.x;
+  const int pblk = a.n_pblk - 1 - id / per_slice;
+  const int rest = id % per_slice;
+  const int b = rest / a.n_hgrp, hgrp = rest % a.n_hgrp;
+  const int grp = a.hq / a.hkv;
+  int h, qpos0, wg_pos0, wg_span;
+  if (a.heads_mode) {
+    h = hgrp * 4 + wave; wg_pos0 = pblk * QW; qpos0 = wg_pos0; wg_span = QW;
+  } else {
+    h = hgrp; wg_pos0 = pblk * 4 * QW; qpos0 = wg_pos0 + wave * QW; wg_span = 4 * QW;
+  }
+  const int g = h / grp;
+  const int S = a.seqlen;
+  const int kend_wg = a.causal ? min(S, wg_pos0 + wg_span) : S;
+  const int kend_w = a.causal ? min(S, qpos0 + QW) : S;
+  const int ntiles = (kend_wg + kBN - 1) / kBN;
+  const float c = a.scale * kLog2e;
+
+  // ---- Q^T operands, resident for the whole kernel: lane holds query (qpos0 + 32*qb + lq), dims 16*ks + 8*lg ..
+  bf16x8_t qop[QB][KS];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qpos = qpos0 + 32 * qb + lq;
+    const uint16_t* qp = a.q + ((int64_t(b) * S + qpos) * a.hq + h) * D + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (qpos < S) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
+      qop[qb][ks] = as_bf16x8(w);
+    }
+  }
+
+  f32x16_t oacc[QB][DB];
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY; l[qb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16_t{};
+  }
+
+  // Lane-fixed parts of the swizzled LDS addresses; the loops add only compile-time immediates.
+  // A chunk c of row r sits at chunk position 8*(c/8) + ((c%8) ^ (r&7)); the XOR key is fixed per lane and
+  // the loops step c by whole residues mod 8 (K reads: 4 residues, V reads: 2).
+  constexpr int RB = Tile<D>::kRowBytes;
+  uint32_t kbase[4];                                   // K: row lq, chunk 2*ks + lg
+#pragma unroll
+  for (int i = 0; i < 4; ++i) kbase[i] = uint32_t(lq * RB + 16 * ((2 * i + lg) ^ (lq & 7)));
+  const int bl = lane & 15, hh = (lane >> 4) & 1;
+  const int vrow = 4 * lg + (bl >> 2);                 // V: rows vrow (+8), columns 16*hh + 4*(bl&3) (+32*db)
+  uint32_t vbase[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    vbase[i] = uint32_t(vrow * RB + 16 * ((4 * i + 2 * hh + ((bl >> 1) & 1)) ^ (vrow & 7)) + 8 * (bl & 1));
+
+  issue_tile<D>(lds[0][0], a.k, b, g, 0, a, wave, lane);
+  issue_tile<D>(lds[0][1], a.v, b, g, 0, a, wave, lane);
+
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmem();
+    __syncthreads();                                   // tile t visible to all; buffer (t+1)&1 free
+    if (t + 1 < ntiles) {
+      issue_tile<D>(lds[(t + 1) & 1][0], a.k, b, g, (t + 1) * kBN, a, wave, lane);
+      issue_tile<D>(lds[(t + 1) & 1][1], a.v, b, g, (t + 1) * kBN, a, wave, lane);
+    }
+    const int key0 = t * kBN;
+    if (key0 >= kend_w) continue;                      // tile entirely above this wave's diagonal
+    const uint16_t* Kt = lds[t & 1][0];
+    const uint16_t* Vt = lds[t & 1][1];
+
+    // ---- S^T = K Q^T for 64 keys (two 32-key blocks)
+    f32x16_t sacc[QB][2];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) { sacc[qb][0] = f32x16_t{}; sacc[qb][1] = f32x16_t{}; }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        // row 32*kb2 + lq, 16-byte chunk 2*ks + lg
+        const bf16x8_t ka = as_bf16x8(lds_read16(Kt, kbase[ks & 3] + 128 * (ks >> 2) + 32 * kb2 * RB));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sacc[qb][kb2] = mfma32x32x16(ka, qop[qb][ks], sacc[qb][kb2]);
+      }
+    }
+
+    // ---- mask: only tiles crossing the diagonal or the ragged end
+    if ((a.causal && key0 + kBN - 1 > qpos0) || key0 + kBN > S) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qpos = qpos0 + 32 * qb + lq;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * kb2 + 8 * (r >> 2) + 4 * lg + (r & 3);
+            if ((a.causal && key > qpos) || key >= S) sacc[qb][kb2][r] = -INFINITY;
+          }
+      }
+    }
+
+    // ---- online softmax (one query per lane; partner lane l ^ 32 holds the other 16 keys)
+    bf16x8_t pb[QB][4];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb2][r]);
+      mx = fmaxf(mx, xor_lanes(mx, 32));
+      // Lazy rescale: move the reference max (rescaling O and l) only when some lane's max grew by more than
+      // 2^kRescaleLog2; otherwise unnormalised P stays below that factor. O / l is unchanged.
+      if (__any((mx - m[qb]) * c > kRescaleLog2)) {
+        const float m_new = fmaxf(m[qb], mx);
+        const float alpha = fast_exp2((m[qb] - m_new) * c);
+        l[qb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
+        m[qb] = m_new;
+      }
+      const float mc = m[qb] * c;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(sacc[qb][kb2][r], c, -mc));
+          sacc[qb][kb2][r] = p;
+          l[qb] += p;
+        }
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const f32x16_t& s = sacc[qb][kb >> 1];
+        const int o8 = 8 * (kb & 1);
+        pb[qb][kb] = pack_bf16x8(s[o8], s[o8 + 1], s[o8 + 2], s[o8 + 3], s[o8 + 4], s[o8 + 5], s[o8 + 6], s[o8 + 7]);
+      }
+    }
+
+    // ---- O^T += V^T P^T: V^T fragments by transposing LDS reads, keys in the same order as the P^T slots
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        // rows 16*kb + vrow (+8), columns 32*db + vcol
+        const uint32_t off = vbase[db & 1] + 128 * (db >> 1) + 16 * kb * RB;
+        const u32x2_t lo = lds_read_tr16(Vt, off);
+        const u32x2_t hi = lds_read_tr16(Vt, off + 8 * RB);
+        const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+        const bf16x8_t va = as_bf16x8(w);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32x32x16(va, pb[qb][kb], oacc[qb][db]);
+      }
+    }
+  }
+
+  // ---- epilogue: O = O^T / l (lane holds query lq, dims 32*db + 8*(r/4) + 4*lg + r%4), lse = scale*m + ln l
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int qpos = qpos0 + 32 * qb + lq;
+    const float lt = l[qb] + xor_lanes(l[qb], 32);
+    if (qpos >= S) continue;
+    const float inv = 1.f / lt;
+    uint16_t* op = a.o + ((int64_t(b) * S + qpos) * a.hq + h) * D + 4 * lg;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const f32x16_t& x = oacc[qb][db];
+        const u32x2_t w = {pack_bf16x2(x[4 * rq] * inv, x[4 * rq + 1] * inv),
+                           pack_bf16x2(x[4 * rq + 2] * inv, x[4 * rq + 3] * inv)};
+        *reinterpret_cast<u32x2_t*>(op + 32 * db + 8 * rq) = w;
+      }
+    if (a.lse && lg == 0) a.lse[(int64_t(b) * a.hq + h) * S + qpos] = m[qb] * a.scale + logf(lt);
+  }
+}
+
+// --------------------------------------------------------------------------------------------- fp32 path --
+constexpr int kF32Keys = 32;     // keys per LDS tile
+constexpr int kF32Queries = 64;  // queries per workgroup
+
+// One workgroup: 64 queries of one head; TPQ = D/16 threads per query, each owning 16 dims of q and O.
+template <int D>
+__global__ __launch_bounds__(kF32Queries * (D / 16)) void prefill_fp32_kernel(const float* __restrict__ q,
+    const float* __restrict__ k, const float* __restrict__ v, float* __restrict__ o, float* __restrict__ lse,
+    int S, int hq, int hkv, int causal, float scale) {
+  constexpr int TPQ = D / 16;
+  constexpr int NT = kF32Queries * TPQ;
+  __shared__ float ks[kF32Keys][D];
+  __shared__ float vs[kF32Keys][D];
+  const int qblk = gridDim.x - 1 - blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (hq / hkv);
+  const int tid = threadIdx.x, part = tid % TPQ;
+  const int qpos = qblk * kF32Queries + tid / TPQ;
+  const float c = scale * kLog2e;
+  float qr[16], acc[16];
+  for (int i = 0; i < 16; ++i) {
+    qr[i] = qpos < S ? q[((int64_t(b) * S + qpos) * hq + h) * D + 16 * part + i] : 0.f;
+    acc[i] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  const int kend = causal ? min(S, (qblk + 1) * kF32Queries) : S;
+  for (int key0 = 0; key0 < kend; key0 += kF32Keys) {
+    __syncthreads();
+    for (int e = tid; e < kF32Keys * D; e += NT) {
+      const int r = e / D, d = e % D;
+      const int key = min(key0 + r, S - 1);
+      const int64_t off = ((int64_t(b) * S + key) * hkv + g) * D + d;
+      ks[r][d] = k[off];
+      vs[r][d] = v[off];
+    }
+    __syncthreads();
+    float s[kF32Keys];
+    float mx = -INFINITY;
+    for (int j = 0; j < kF32Keys; ++j) {
+      float part_dot = 0.f;
+      for (int i = 0; i < 16; ++i) part_dot = fmaf(qr[i], ks[j][16 * part + i], part_dot);
+      for (int w = 1; w < TPQ; w <<= 1) part_dot += xor_lanes(part_dot, w);
+      const int key = key0 + j;
+      s[j] = ((causal && key > qpos) || key >= S) ? -INFINITY : part_dot;
+      mx = fmaxf(mx, s[j]);
+    }
+    const float m_new = fmaxf(m, mx);
+    if (m_new == -INFINITY) continue;                 // every key of this tile is masked for this query
+    const float alpha = exp2f((m - m_new) * c);
+    const float mc = m_new * c;
+    l *= alpha;
+    for (int i = 0; i < 16; ++i) acc[i] *= alpha;
+    for (int j = 0; j < kF32Keys; ++j) {
+      const float p = exp2f(fmaf(s[j], c, -mc));
+      l += p;
+      for (int i = 0; i < 16; ++i) acc[i] = fmaf(p, vs[j][16 * part + i], acc[i]);
+    }
+    m = m_new;
+  }
+  if (qpos < S) {
+    const float inv = 1.f / l;
+    for (int i = 0; i < 16; ++i) o[((int64_t(b) * S + qpos) * hq + h) * D + 16 * part + i] = acc[i] * inv;
+    if (lse && part == 0) lse[(int64_t(b) * hq + h) * S + qpos] = m * scale + logf(l);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                               int seqlen, int hq, int hkv, int head_dim, int causal, float scale,
+                               hipStream_t stream) {
+  constexpr int QB = 1;
+  constexpr int QW = 32 * QB;
+  PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q); a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v); a.o = static_cast<uint16_t*>(o); a.lse = lse;
+  a.batch = batch; a.seqlen = seqlen; a.hq = hq; a.hkv = hkv; a.scale = scale; a.causal = causal;
+  const int grp = hq / hkv;
+  a.heads_mode = (grp % 4 == 0) ? 1 : 0;
+  const int span = a.heads_mode ? QW : 4 * QW;
+  a.n_pblk = (seqlen + span - 1) / span;
+  a.n_hgrp = a.heads_mode ? hq / 4 : hq;
+  const int64_t blocks = int64_t(a.n_pblk) * batch * a.n_hgrp;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+  if (head_dim == 128) prefill_bf16_kernel<128, QB><<<grid, block, 0, stream>>>(a);
+  else prefill_bf16_kernel<64, QB><<<grid, block, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_fp32(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                               int seqlen, int hq, int hkv, int head_dim, int causal, float scale,
+                               hipStream_t stream) {
+  const dim3 grid(unsigned((seqlen + kF32Queries - 1) / kF32Queries), unsigned(hq), unsigned(batch));
+  const float* qf = static_cast<const float*>(q);
+  const float* kf = static_cast<const float*>(k);
+  const float* vf = static_cast<const float*>(v);
+  float* of = static_cast<float*>(o);
+  if (head_dim == 128)
+    prefill_fp32_kernel<128><<<grid, dim3(kF32Queries * 8), 0, stream>>>(qf, kf, vf, of, lse, seqlen, hq, hkv, causal, scale);
+  else
+    prefill_fp32_kernel<64><<<grid, dim3(kF32Queries * 4), 0, stream>>>(qf, kf, vf, of, lse, seqlen, hq, hkv, causal, scale);
+  return hipGetLastError();
+}
+
+}  // namespace attn
