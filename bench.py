@@ -208,7 +208,7 @@ def bench_mla(torch, ta, w, steps, warmup, seed=0):
 
 
 # ------------------------------------------------------------------------------------------------ cpu oracle --
-def cpu_baseline(w, n_rows=1024, seed=0):
+def cpu_baseline(w, n_rows=4096, seed=0):
     """Time the fp64 oracle on `n_rows` seeded query rows (all heads, all batches) of the prefill workload."""
     import oracle
     try:
@@ -243,6 +243,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-secondary", action="store_true", help="only the primary prefill workload")
+    ap.add_argument("--workloads", default="prefill,decode,mla,long",
+                    help="comma list of prefill (primary), decode, mla, long; profiling runs select one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration for traffic measurements)")
@@ -268,7 +270,18 @@ def main():
         print(json.dumps({"copy_bytes": 1 << 30, "launches": 3}))
         return
 
+    sel = set(args.workloads.split(","))
+    if sel - {"prefill", "decode", "mla", "long"}:
+        print(f"unknown workloads {sel}", file=sys.stderr)
+        sys.exit(2)
+    if args.no_secondary:
+        sel &= {"prefill"}
     w = WORKLOADS["gqa_prefill_s8192"]
+    if "prefill" not in sel:          # profiling run of one secondary workload
+        line = {}
+        run_secondary(torch, ta, args, sel, line)
+        print(json.dumps(line))
+        return
     wall_ms, kern_ms = bench_prefill(torch, ta, w, args.steps, args.warmup)
     value = w.flops / (wall_ms * 1e-3) / 1e12
     line = {
@@ -282,12 +295,21 @@ def main():
     }
     line["pct_bf16_peak_step"] = round(value / PEAK_BF16_TFLOPS, 4)
 
-    if not args.no_secondary:
+    run_secondary(torch, ta, args, sel, line)
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (fp64 oracle sample)")
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line))
+
+
+def run_secondary(torch, ta, args, sel, line):
+    if "decode" in sel:
         wd = WORKLOADS["paged_decode_b64"]
         ms, nbytes, tokens = bench_decode(torch, ta, wd, max(5, args.steps), args.warmup)
         line["paged_decode"] = {"workload": wd.name, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                                 "ms": round(ms, 4), "bytes": nbytes, "tokens": tokens,
                                 "roofline": roofline_hbm(nbytes, ms, "decode_paged_split_kernel")}
+    if "mla" in sel:
         wm = WORKLOADS["mla_decode_b32"]
         ms = bench_mla(torch, ta, wm, max(5, args.steps), args.warmup)
         nbytes = mla_bytes(wm)
@@ -295,15 +317,12 @@ def main():
                               "ms": round(ms, 4), "bytes": nbytes,
                               "tflops": round(mla_flops(wm) / (ms * 1e-3) / 1e12, 1),
                               "roofline": roofline_hbm(nbytes, ms, "mla_split_kernel")}
+    if "long" in sel:
         wl = WORKLOADS["gqa_prefill_s131072"]
         wall_l, kern_l = bench_prefill(torch, ta, wl, 2, 1)
         line["long_prefill"] = {"workload": wl.name, "value": round(wl.flops / (wall_l * 1e-3) / 1e12, 2),
                                 "unit": "TFLOP/s", "ms_per_step": round(wall_l, 3),
                                 "roofline": roofline_compute(wl.flops, kern_l, "prefill_bf16_kernel")}
-    if not args.no_cpu_baseline:
-        log("[bench] cpu baseline (fp64 oracle sample)")
-        line["cpu_baseline"] = cpu_baseline(w)
-    print(json.dumps(line))
 
 
 if __name__ == "__main__":
