@@ -56,13 +56,14 @@ def source_digest(fname):
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel):
-    """HBM bytes per launch from profiles/traffic.json, if measured on the current source; else None."""
+def traffic_for(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from profiles/traffic.json (rocprofv3 FETCH_SIZE and WRITE_SIZE,
+    scaled by a plain-copy calibration), if measured on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        t = json.load(f).get(kernel)
+        t = json.load(f).get(f"{kernel}@{workload}")
     if not t or t.get("source_sha") != source_digest(KERNEL_SOURCES[kernel]):
         return None
     return t.get("hbm_bytes_per_launch")
@@ -92,17 +93,17 @@ class EventTimer:
         return sum(a.elapsed_time(b) for a, b in self.pairs) / max(1, len(self.pairs))
 
 
-def roofline_compute(flops, ms, kernel):
+def roofline_compute(flops, ms, kernel, workload):
     achieved = flops / (ms * 1e-3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(kernel), "kernel": kernel,
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic_for(kernel, workload), "kernel": kernel,
             "kernel_ms": round(ms, 4)}
 
 
-def roofline_hbm(nbytes, ms, kernel):
+def roofline_hbm(nbytes, ms, kernel, workload):
     achieved = nbytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_for(kernel), "kernel": kernel,
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_for(kernel, workload), "kernel": kernel,
             "kernel_ms": round(ms, 4)}
 
 
@@ -291,7 +292,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "hq": w.hq, "hkv": w.hkv,
                    "head_dim": w.head_dim, "causal": True, "rope_theta": w.theta,
                    "step": "rope(q) + rope(k) + prefill", "flops_per_step": w.flops},
-        "roofline": roofline_compute(w.flops, kern_ms, "prefill_bf16_kernel"),
+        "roofline": roofline_compute(w.flops, kern_ms, "prefill_bf16_kernel", w.name),
     }
     line["pct_bf16_peak_step"] = round(value / PEAK_BF16_TFLOPS, 4)
 
@@ -308,7 +309,7 @@ def run_secondary(torch, ta, args, sel, line):
         ms, nbytes, tokens = bench_decode(torch, ta, wd, max(5, args.steps), args.warmup)
         line["paged_decode"] = {"workload": wd.name, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                                 "ms": round(ms, 4), "bytes": nbytes, "tokens": tokens,
-                                "roofline": roofline_hbm(nbytes, ms, "decode_paged_split_kernel")}
+                                "roofline": roofline_hbm(nbytes, ms, "decode_paged_split_kernel", wd.name)}
     if "mla" in sel:
         wm = WORKLOADS["mla_decode_b32"]
         ms = bench_mla(torch, ta, wm, max(5, args.steps), args.warmup)
@@ -316,13 +317,13 @@ def run_secondary(torch, ta, args, sel, line):
         line["mla_decode"] = {"workload": wm.name, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                               "ms": round(ms, 4), "bytes": nbytes,
                               "tflops": round(mla_flops(wm) / (ms * 1e-3) / 1e12, 1),
-                              "roofline": roofline_hbm(nbytes, ms, "mla_split_kernel")}
+                              "roofline": roofline_hbm(nbytes, ms, "mla_split_kernel", wm.name)}
     if "long" in sel:
         wl = WORKLOADS["gqa_prefill_s131072"]
         wall_l, kern_l = bench_prefill(torch, ta, wl, 2, 1)
         line["long_prefill"] = {"workload": wl.name, "value": round(wl.flops / (wall_l * 1e-3) / 1e12, 2),
                                 "unit": "TFLOP/s", "ms_per_step": round(wall_l, 3),
-                                "roofline": roofline_compute(wl.flops, kern_l, "prefill_bf16_kernel")}
+                                "roofline": roofline_compute(wl.flops, kern_l, "prefill_bf16_kernel", wl.name)}
 
 
 if __name__ == "__main__":

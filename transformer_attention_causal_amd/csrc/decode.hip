@@ -27,6 +27,11 @@ namespace {
 
 constexpr int kD = 128;
 
+// Build-time choice: software-prefetch the next 32 keys' K/V while computing on the current ones.
+#ifndef ATTN_DECODE_PREFETCH
+#define ATTN_DECODE_PREFETCH 0
+#endif
+
 struct DecodeArgs {
   const uint16_t* q;
   const uint16_t* kc;
@@ -80,8 +85,10 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
   const int64_t row_stride = int64_t(a.hkv) * kD;           // elements between consecutive slots of a page
   const int64_t page_stride = int64_t(page_size) * row_stride;
 
-  for (int t0 = t_begin; t0 < t_end; t0 += 32) {
-    // page of each 16-key half (wave-uniform); out-of-range pages are never dereferenced
+  // K fragments (key t0 + 16*tb + n, dims 8*(4*ks + grp4) ..) and V rows (slot s: key t0 + 16*(s/4) + 4*grp4 + s%4,
+  // dims 8n .. 8n+7) of the 32 keys at t0. Pages are looked up once per 16-key half (wave-uniform); keys at or past
+  // t_end and pages outside [0, num_pages) are never dereferenced (zeros instead).
+  auto load32 = [&](int t0, u32x4_t (&kv)[2][4], u32x4_t (&vv)[8]) {
     int pg[2];
     bool pv[2];
 #pragma unroll
@@ -90,8 +97,6 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
       pg[hf] = trow[tt >> a.page_shift];
       pv[hf] = pg[hf] >= 0 && pg[hf] < a.num_pages;
     }
-    // K fragments: key t0 + 16*tb + n, dims 8*(4*ks + grp4) ..
-    u32x4_t kv[2][4];
 #pragma unroll
     for (int tb = 0; tb < 2; ++tb) {
       const int key = t0 + 16 * tb + n;
@@ -105,8 +110,6 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
         kv[tb][ks] = w;
       }
     }
-    // V rows: slot s holds key t0 + 16*(s/4) + 4*grp4 + s%4, dims 8n .. 8n+7
-    u32x4_t vv[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       const int hf = s >> 2;
@@ -118,6 +121,16 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
                                               int64_t(key & (page_size - 1)) * row_stride + int64_t(g) * kD + 8 * n);
       vv[s] = w;
     }
+  };
+
+  u32x4_t kv[2][4], vv[8];
+  load32(t_begin, kv, vv);
+  for (int t0 = t_begin; t0 < t_end; t0 += 32) {
+#if ATTN_DECODE_PREFETCH
+    // issue the next 32 keys' loads before computing on these (software pipelining, ~64 more registers)
+    u32x4_t kvn[2][4], vvn[8];
+    if (t0 + 32 < t_end) load32(t0 + 32, kvn, vvn);
+#endif
     // S^T[key][head]: lane holds head n, keys t0 + 16*tb + 4*grp4 + r
     f32x4_t sacc[2] = {f32x4_t{}, f32x4_t{}};
 #pragma unroll
@@ -162,6 +175,18 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
                                     sacc[1][2], sacc[1][3]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) oacc[j] = mfma16x16x32(transpose_pick(vv, j), pb, oacc[j]);
+#if ATTN_DECODE_PREFETCH
+    if (t0 + 32 < t_end) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kv[tb][ks] = kvn[tb][ks];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) vv[s] = vvn[s];
+    }
+#else
+    if (t0 + 32 < t_end) load32(t0 + 32, kv, vv);
+#endif
   }
 
   // partial result: O / l and lse for this chunk (lane holds head n, dims 8*(4*grp4 + r) + j)

@@ -20,7 +20,10 @@ hipError_t launch_prefill_fp32(const void* q, const void* k, const void* v, void
                                hipStream_t stream);
 
 // Paged decode: split-KV partials into the workspace, then the log-sum-exp combine.
-constexpr int kDecodeChunk = 512;  // keys per split (a multiple of 32); split boundaries are logical positions
+#ifndef ATTN_DECODE_CHUNK
+#define ATTN_DECODE_CHUNK 512
+#endif
+constexpr int kDecodeChunk = ATTN_DECODE_CHUNK;  // keys per split (a multiple of 32); boundaries are logical positions
 size_t decode_paged_workspace_bytes(int batch, int hq, int head_dim, int max_seqlen_kv);
 hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
                                const int32_t* seq_lens, void* o, float* lse, int batch, int hq, int hkv,
@@ -28,8 +31,8 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
                                int max_seqlen_kv, float scale, void* workspace, hipStream_t stream);
 
 // MLA absorbed decode: split over tokens, then the log-sum-exp combine.
-int mla_num_splits(int batch, int max_seqlen_kv);
-int mla_split_len(int batch, int max_seqlen_kv);
+int mla_num_splits(int batch, int n_heads, int max_seqlen_kv);
+int mla_split_len(int batch, int n_heads, int max_seqlen_kv);
 size_t mla_decode_workspace_bytes(int batch, int n_heads, int kv_lora_rank, int max_seqlen_kv);
 hipError_t launch_mla_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
                              const int32_t* seq_lens, void* o_latent, float* lse, int batch, int n_heads,

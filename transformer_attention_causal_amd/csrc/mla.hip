@@ -9,7 +9,7 @@
 // Every head reads the same 576-wide key row [c_kv ; k_pe] and the same 512-wide value row c_kv, so MLA decode is
 // a single-KV-head attention with 128 query rows: the same structure as the prefill kernel with heads in place
 // of query positions.
-//   * One workgroup = (token split, sequence), 8 waves x 16 heads. Token tiles of 32 rows x 576 are copied
+//   * One workgroup = (token split, sequence), 8 waves x 16 heads. Token tiles of 64 rows x 576 are copied
 //     straight into LDS (global_load_lds, 16 bytes per lane), double-buffered, one barrier per tile; rows are
 //     unpadded and their 16-byte chunks XOR-swizzled by (row & 7) so both read patterns are conflict-free.
 //   * S^T = Kc Q^T on v_mfma_f32_16x16x32_bf16 (K fragments from LDS, the 576-wide query of the wave's 16 heads
@@ -28,18 +28,18 @@ namespace {
 constexpr int kC = 512;             // kv_lora_rank
 constexpr int kR = 64;              // rope dim
 constexpr int kDK = kC + kR;        // key width
-constexpr int kRows = 32;           // tokens per tile
 constexpr int kChunks = kDK / 8;    // 72 16-byte chunks per row
 constexpr int kRowBytes = kDK * 2;  // 1152
-constexpr int kTileElems = kRows * kDK;
-constexpr int kTileBlocks = kRows * kChunks / 64;  // 36 wave-instructions of 64 slots
 constexpr int kTargetBlocks = 256;  // one workgroup per compute unit on MI355X
 
-// Build-time choice of the split kernel: 16 heads per wave (16x16x32 MFMA, 8 waves, 2 per SIMD) or 32 heads per
-// wave (32x32x16 MFMA, 4 waves, 1 per SIMD, half the LDS reads per token).
-#ifndef ATTN_MLA_HEADS_PER_WAVE
-#define ATTN_MLA_HEADS_PER_WAVE 16
+// Tokens per LDS tile = 32 * ATTN_MLA_TILE_HALVES (double-buffered: 72 KiB per 32 tokens).
+#ifndef ATTN_MLA_TILE_HALVES
+#define ATTN_MLA_TILE_HALVES 2
 #endif
+constexpr int kHalves = ATTN_MLA_TILE_HALVES;
+constexpr int kRows = 32 * kHalves;                 // tokens per tile
+constexpr int kTileElems = kRows * kDK;
+constexpr int kTileBlocks = kRows * kChunks / 64;   // wave-instructions of 64 slots per tile
 
 struct MlaArgs {
   const uint16_t* q_lat;
@@ -121,26 +121,29 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
     const uint16_t* T = lds[t & 1];
     const int tok0 = t_begin + t * kRows;
 
-    // S^T = Kc Q^T: two 16-token blocks; lane holds head n, tokens 16*tb + 4*g4 + r
-    f32x4_t sacc[2] = {f32x4_t{}, f32x4_t{}};
+    // S^T = Kc Q^T: 16-token blocks tb; lane holds head n, tokens 16*tb + 4*g4 + r
+    constexpr int TB = 2 * kHalves;
+    f32x4_t sacc[TB];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) sacc[tb] = f32x4_t{};
 #pragma unroll
     for (int ks = 0; ks < kDK / 32; ++ks) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+      for (int tb = 0; tb < TB; ++tb)
         sacc[tb] = mfma16x16x32(as_bf16x8(lds_read16(T, abase[ks & 1] + 128 * (ks >> 1) + 16 * tb * kRowBytes)),
                                 qop[ks], sacc[tb]);
       if (ks % 6 == 5) __builtin_amdgcn_sched_barrier(0);   // bound how far LDS reads are hoisted (registers)
     }
     if (tok0 + kRows > t_end) {
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+      for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          if (tok0 + 16 * tb + 4 * g4 + r >= t_end) sacc[tb][r] = -INFINITY;
+          sacc[tb][r] = tok0 + 16 * tb + 4 * g4 + r >= t_end ? -INFINITY : sacc[tb][r];
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[tb][r]);
     mx = fmaxf(mx, xor_lanes(mx, 16));
@@ -157,23 +160,30 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
     }
     const float mc = m * c;
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float p = fast_exp2(fmaf(sacc[tb][r], c, -mc));
         sacc[tb][r] = p;
         l += p;
       }
-    const bf16x8_t pb = pack_bf16x8(sacc[0][0], sacc[0][1], sacc[0][2], sacc[0][3], sacc[1][0], sacc[1][1],
-                                    sacc[1][2], sacc[1][3]);
+    // P^T operand of each 32-token half: slots 0..3 are tokens 4*g4 + s, slots 4..7 tokens 16 + 4*g4 + s
+    bf16x8_t pb[kHalves];
+#pragma unroll
+    for (int kh = 0; kh < kHalves; ++kh)
+      pb[kh] = pack_bf16x8(sacc[2 * kh][0], sacc[2 * kh][1], sacc[2 * kh][2], sacc[2 * kh][3], sacc[2 * kh + 1][0],
+                           sacc[2 * kh + 1][1], sacc[2 * kh + 1][2], sacc[2 * kh + 1][3]);
     // O^T += c_kv^T P^T: the value operand is the same tile read through the transposing LDS read
 #pragma unroll
     for (int db = 0; db < kC / 16; ++db) {
-      const uint32_t off = vbase[db & 3] + 128 * (db >> 2);
-      const u32x2_t lo = lds_read_tr16(T, off);
-      const u32x2_t hi = lds_read_tr16(T, off + 16 * kRowBytes);
-      const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
-      oacc[db] = mfma16x16x32(as_bf16x8(w), pb, oacc[db]);
+#pragma unroll
+      for (int kh = 0; kh < kHalves; ++kh) {
+        const uint32_t off = vbase[db & 3] + 128 * (db >> 2) + 32 * kh * kRowBytes;
+        const u32x2_t lo = lds_read_tr16(T, off);
+        const u32x2_t hi = lds_read_tr16(T, off + 16 * kRowBytes);
+        const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[db] = mfma16x16x32(as_bf16x8(w), pb[kh], oacc[db]);
+      }
       if (db % 8 == 7) __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -189,118 +199,6 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
     *reinterpret_cast<f32x4_t*>(wo + 16 * db) = v;
   }
   if (g4 == 0) a.ws_lse[slot] = m * a.scale + logf(lt);
-}
-
-// 32 heads per wave on v_mfma_f32_32x32x16_bf16: each K/V fragment read from LDS feeds twice the MFMA work of
-// the 16-head kernel, halving LDS read traffic per token. The wave keeps Q^T (144 VGPRs) and O^T = 512 x 32 fp32
-// (256 registers, accumulated in AGPRs) resident, so it runs at one wave per SIMD (4 waves cover 128 heads).
-__global__ __launch_bounds__(256, 1) void mla_split_kernel_h32(MlaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][kTileElems];
-  const int split = blockIdx.x, b = blockIdx.y;
-  const int nwaves = blockDim.x >> 6;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int lq = lane & 31, lg = lane >> 5;
-  const int L = max(0, min(a.seq_lens[b], a.max_len));
-  const int t_begin = split * a.split_len;
-  if (t_begin >= L) return;                           // uniform over the workgroup
-  const int t_end = min(L, t_begin + a.split_len);
-  const int ntiles = (t_end - t_begin + kRows - 1) / kRows;
-  const int h = wave * 32 + lq;
-  const float c = a.scale * kLog2e;
-
-  // query [q_lat ; q_pe] of head h as 36 B operands (dims 16*ks + 8*lg ..)
-  bf16x8_t qop[kDK / 16];
-#pragma unroll
-  for (int ks = 0; ks < kDK / 16; ++ks) {
-    const int d = 16 * ks + 8 * lg;
-    const uint16_t* p = d < kC ? a.q_lat + (int64_t(b) * a.heads + h) * kC + d
-                               : a.q_pe + (int64_t(b) * a.heads + h) * kR + (d - kC);
-    qop[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(p));
-  }
-  f32x16_t oacc[kC / 32];
-#pragma unroll
-  for (int db = 0; db < kC / 32; ++db) oacc[db] = f32x16_t{};
-  float m = -INFINITY, l = 0.f;
-
-  // Lane-fixed parts of the swizzled LDS addresses (chunk c of row r at 8*(c/8) + ((c%8) ^ (r&7))).
-  uint32_t abase[4];                                   // K reads: row lq, chunk 2*ks + lg
-#pragma unroll
-  for (int i = 0; i < 4; ++i) abase[i] = uint32_t(lq * kRowBytes + 16 * ((2 * i + lg) ^ (lq & 7)));
-  const int bl = lane & 15, hh = (lane >> 4) & 1;
-  const int vrow = 4 * lg + (bl >> 2);                 // V reads: rows vrow (+8, +16*kb), columns 32*db + 16*hh + 4*(bl&3)
-  uint32_t vbase[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    vbase[i] = uint32_t(vrow * kRowBytes + 16 * ((4 * i + 2 * hh + ((bl >> 1) & 1)) ^ (vrow & 7)) + 8 * (bl & 1));
-
-  mla_issue(lds[0], a, b, t_begin, t_end - 1, wave, nwaves, lane);
-  for (int t = 0; t < ntiles; ++t) {
-    wait_vmem();
-    __syncthreads();
-    if (t + 1 < ntiles) mla_issue(lds[(t + 1) & 1], a, b, t_begin + (t + 1) * kRows, t_end - 1, wave, nwaves, lane);
-    const uint16_t* T = lds[t & 1];
-    const int tok0 = t_begin + t * kRows;
-
-    // S^T = Kc Q^T over 576 dims, two interleaved accumulators; lane holds head lq, tokens 8*(r/4) + 4*lg + r%4
-    f32x16_t s0 = f32x16_t{}, s1 = f32x16_t{};
-#pragma unroll
-    for (int ks = 0; ks < kDK / 16; ks += 2) {
-      s0 = mfma32x32x16(as_bf16x8(lds_read16(T, abase[ks & 3] + 128 * (ks >> 2))), qop[ks], s0);
-      s1 = mfma32x32x16(as_bf16x8(lds_read16(T, abase[(ks + 1) & 3] + 128 * ((ks + 1) >> 2))), qop[ks + 1], s1);
-    }
-    f32x16_t sacc = s0 + s1;
-    if (tok0 + kRows > t_end) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (tok0 + 8 * (r >> 2) + 4 * lg + (r & 3) >= t_end) sacc[r] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-    mx = fmaxf(mx, xor_lanes(mx, 32));
-    if (__any((mx - m) * c > kRescaleLog2)) {          // lazy rescale (see the 16-head kernel)
-      const float m_new = fmaxf(m, mx);
-      const float alpha = fast_exp2((m - m_new) * c);
-      l *= alpha;
-#pragma unroll
-      for (int db = 0; db < kC / 32; ++db) oacc[db] *= alpha;
-      m = m_new;
-    }
-    const float mc = m * c;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(fmaf(sacc[r], c, -mc));
-      sacc[r] = p;
-      l += p;
-    }
-    const bf16x8_t pb0 = pack_bf16x8(sacc[0], sacc[1], sacc[2], sacc[3], sacc[4], sacc[5], sacc[6], sacc[7]);
-    const bf16x8_t pb1 = pack_bf16x8(sacc[8], sacc[9], sacc[10], sacc[11], sacc[12], sacc[13], sacc[14], sacc[15]);
-#pragma unroll
-    for (int db = 0; db < kC / 32; ++db) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t off = vbase[db & 1] + 128 * (db >> 1) + 16 * kb * kRowBytes;
-        const u32x2_t lo = lds_read_tr16(T, off);
-        const u32x2_t hi = lds_read_tr16(T, off + 8 * kRowBytes);
-        const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = mfma32x32x16(as_bf16x8(w), kb ? pb1 : pb0, oacc[db]);
-      }
-    }
-  }
-
-  const float lt = l + xor_lanes(l, 32);
-  const float inv = 1.f / lt;
-  const int64_t slot = (int64_t(b) * a.heads + h) * a.n_split + split;
-  float* wo = a.ws_o + slot * kC + 4 * lg;
-#pragma unroll
-  for (int db = 0; db < kC / 32; ++db)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const f32x4_t v = {oacc[db][4 * rq] * inv, oacc[db][4 * rq + 1] * inv, oacc[db][4 * rq + 2] * inv,
-                         oacc[db][4 * rq + 3] * inv};
-      *reinterpret_cast<f32x4_t*>(wo + 32 * db + 8 * rq) = v;
-    }
-  if (lg == 0) a.ws_lse[slot] = m * a.scale + logf(lt);
 }
 
 // Merge splits: M = max lse_s, w_s = exp(lse_s - M), O = sum w_s O_s / sum w_s; length 0 -> O = 0, lse = -inf.
@@ -334,22 +232,23 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
 
 }  // namespace
 
-int mla_num_splits(int batch, int max_seqlen_kv) {
+int mla_num_splits(int batch, int n_heads, int max_seqlen_kv) {
+  (void)n_heads;
   if (batch <= 0 || max_seqlen_kv <= 0) return 1;
   const int by_cu = (kTargetBlocks + batch - 1) / batch;
   const int by_len = (max_seqlen_kv + kRows - 1) / kRows;
   return max(1, min(by_cu, by_len));
 }
 
-int mla_split_len(int batch, int max_seqlen_kv) {
-  const int ns = mla_num_splits(batch, max_seqlen_kv);
+int mla_split_len(int batch, int n_heads, int max_seqlen_kv) {
+  const int ns = mla_num_splits(batch, n_heads, max_seqlen_kv);
   const int per = (max(1, max_seqlen_kv) + ns - 1) / ns;
   return (per + kRows - 1) / kRows * kRows;
 }
 
 size_t mla_decode_workspace_bytes(int batch, int n_heads, int kv_lora_rank, int max_seqlen_kv) {
   if (batch <= 0 || n_heads <= 0 || kv_lora_rank <= 0 || max_seqlen_kv <= 0) return 0;
-  const size_t slots = size_t(batch) * size_t(n_heads) * size_t(mla_num_splits(batch, max_seqlen_kv));
+  const size_t slots = size_t(batch) * size_t(n_heads) * size_t(mla_num_splits(batch, n_heads, max_seqlen_kv));
   const size_t o_bytes = (slots * size_t(kv_lora_rank) * sizeof(float) + 255) & ~size_t(255);
   return o_bytes + slots * sizeof(float);
 }
@@ -364,19 +263,14 @@ hipError_t launch_mla_decode(const void* q_latent, const void* q_pe, const void*
   a.k_pe = static_cast<const uint16_t*>(k_pe);
   a.seq_lens = seq_lens;
   a.heads = n_heads; a.max_len = max_seqlen_kv; a.scale = scale;
-  a.n_split = mla_num_splits(batch, max_seqlen_kv);
-  a.split_len = mla_split_len(batch, max_seqlen_kv);
+  a.n_split = mla_num_splits(batch, n_heads, max_seqlen_kv);
+  a.split_len = mla_split_len(batch, n_heads, max_seqlen_kv);
   const size_t slots = size_t(batch) * size_t(n_heads) * size_t(a.n_split);
   const size_t o_bytes = (slots * kC * sizeof(float) + 255) & ~size_t(255);
   a.ws_o = static_cast<float*>(workspace);
   a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
-  if (max_seqlen_kv > 0) {
-    const dim3 grid(unsigned(a.n_split), unsigned(batch));
-    if (ATTN_MLA_HEADS_PER_WAVE == 32)
-      mla_split_kernel_h32<<<grid, dim3(64 * (n_heads / 32)), 0, stream>>>(a);
-    else
-      mla_split_kernel<<<grid, dim3(64 * (n_heads / kHeadsPerWave)), 0, stream>>>(a);
-  }
+  if (max_seqlen_kv > 0)
+    mla_split_kernel<<<dim3(unsigned(a.n_split), unsigned(batch)), dim3(64 * (n_heads / kHeadsPerWave)), 0, stream>>>(a);
   mla_combine_kernel<<<dim3(unsigned(n_heads), unsigned(batch)), dim3(kC / 2), 0, stream>>>(
       a.ws_o, a.ws_lse, seq_lens, static_cast<uint16_t*>(o_latent), lse, n_heads, a.n_split, a.split_len,
       max_seqlen_kv);

@@ -11,7 +11,8 @@
 //     4 consecutive blocks of QW positions of one query head ("positions mode", any other group size).
 //   * K and V tiles of 64 keys x D are copied straight from global memory into LDS (global_load_lds, 16 bytes
 //     per lane, no register staging), double-buffered, one barrier per tile. LDS rows are unpadded; their
-//     16-byte chunks are XOR-swizzled by (row & 7), which makes both LDS read patterns below conflict-free.
+//     16-byte chunks are XOR-swizzled by a key of the row index (swz_key) that makes both LDS read patterns
+//     below conflict-free on the 64-bank LDS. Two workgroups share a CU (registers capped at 256).
 //   * Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16: K fragments come from LDS (16-byte
 //     reads), Q^T stays in registers for the whole kernel. In the S^T accumulator each lane holds ONE query
 //     (lane % 32) and 16 keys, so the row max and row sum need one cross-lane exchange (lanes l and l ^ 32), and
@@ -31,6 +32,15 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;  // keys per tile
+
+// Build-time tuning: 32-query blocks per wave, and the minimum waves per SIMD the register allocation must
+// allow (2 -> at most 256 registers per lane, so two workgroups share a CU).
+#ifndef ATTN_PREFILL_QB
+#define ATTN_PREFILL_QB 1
+#endif
+#ifndef ATTN_PREFILL_MIN_WAVES_PER_SIMD
+#define ATTN_PREFILL_MIN_WAVES_PER_SIMD 2
+#endif
 
 template <int D>
 struct Tile {
@@ -55,6 +65,17 @@ struct PrefillArgs {
   int n_hgrp;        // head groups: hq/4 in heads mode, hq in positions mode
 };
 
+// LDS swizzle: 16-byte chunk c of tile row r is stored at chunk position c ^ swz_key(r). With 64 four-byte banks,
+// the key must (a) give 16 consecutive rows distinct positions for the same logical chunk (K reads: one row per
+// lane) and (b) give rows 4i..4i+3 disjoint chunk pairs (V^T reads: ds_read_b64_tr_b16 takes 32 bytes from each
+// of 4 rows per 16 lanes). A 4-bit rotation of the row index does both for 256-byte rows (head_dim 128); for
+// 128-byte rows (head_dim 64, two rows per bank window) the rotation acts on the row pair index.
+template <int D>
+__device__ __forceinline__ int swz_key(int r) {
+  if (D == 128) return ((r << 1) | ((r >> 3) & 1)) & 15;
+  return (r & 6) | ((r >> 3) & 1);
+}
+
 // Issue the direct-to-LDS copy of one K or V tile (rows key0 .. key0+63 of KV head g) into `dst`.
 // Rows at or past seqlen are clamped to the last row (finite data; their scores are masked and P is 0).
 template <int D>
@@ -66,7 +87,7 @@ __device__ __forceinline__ void issue_tile(uint16_t* dst, const uint16_t* src, i
     const int blk = i * kWaves + wave;               // 64-slot block this wave instruction fills
     const int slot = blk * 64 + lane;
     const int row = slot / Tile<D>::kChunks;
-    const int lchunk = (slot % Tile<D>::kChunks) ^ (row & 7);
+    const int lchunk = (slot % Tile<D>::kChunks) ^ swz_key<D>(row);
     const int key = min(key0 + row, a.seqlen - 1);
     const uint16_t* gp = src + (int64_t(b) * a.seqlen + key) * row_stride + int64_t(g) * D + lchunk * 8;
     load_lds16(gp, dst + blk * 512);
@@ -74,7 +95,7 @@ __device__ __forceinline__ void issue_tile(uint16_t* dst, const uint16_t* src, i
 }
 
 template <int D, int QB>
-__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int QW = 32 * QB;
   constexpr int KS = D / 16;   // k-steps of the QK^T contraction
   constexpr int DB = D / 32;   // 32-row blocks of O^T
@@ -125,19 +146,21 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
     for (int db = 0; db < DB; ++db) oacc[qb][db] = f32x16_t{};
   }
 
-  // Lane-fixed parts of the swizzled LDS addresses; the loops add only compile-time immediates.
-  // A chunk c of row r sits at chunk position 8*(c/8) + ((c%8) ^ (r&7)); the XOR key is fixed per lane and
-  // the loops step c by whole residues mod 8 (K reads: 4 residues, V reads: 2).
+  // Lane-fixed swizzled LDS addresses: the row parts that vary in the loops (32*kb2 for K, 16*kb for V) leave the
+  // swizzle key unchanged, so every read is one of these bases plus a compile-time immediate.
   constexpr int RB = Tile<D>::kRowBytes;
-  uint32_t kbase[4];                                   // K: row lq, chunk 2*ks + lg
+  uint32_t kbase[KS];                                  // K: row lq (+32*kb2), chunk 2*ks + lg
 #pragma unroll
-  for (int i = 0; i < 4; ++i) kbase[i] = uint32_t(lq * RB + 16 * ((2 * i + lg) ^ (lq & 7)));
+  for (int ks = 0; ks < KS; ++ks) kbase[ks] = uint32_t(lq * RB + 16 * ((2 * ks + lg) ^ swz_key<D>(lq)));
   const int bl = lane & 15, hh = (lane >> 4) & 1;
-  const int vrow = 4 * lg + (bl >> 2);                 // V: rows vrow (+8), columns 16*hh + 4*(bl&3) (+32*db)
-  uint32_t vbase[2];
+  const int vrow = 4 * lg + (bl >> 2);                 // V: rows vrow and vrow + 8 (+16*kb),
+  uint32_t vlo[DB], vhi[DB];                           //    columns 32*db + 16*hh + 4*(bl&3)
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    vbase[i] = uint32_t(vrow * RB + 16 * ((4 * i + 2 * hh + ((bl >> 1) & 1)) ^ (vrow & 7)) + 8 * (bl & 1));
+  for (int db = 0; db < DB; ++db) {
+    const int ch = 4 * db + 2 * hh + ((bl >> 1) & 1);
+    vlo[db] = uint32_t(vrow * RB + 16 * (ch ^ swz_key<D>(vrow)) + 8 * (bl & 1));
+    vhi[db] = uint32_t((vrow + 8) * RB + 16 * (ch ^ swz_key<D>(vrow + 8)) + 8 * (bl & 1));
+  }
 
   issue_tile<D>(lds[0][0], a.k, b, g, 0, a, wave, lane);
   issue_tile<D>(lds[0][1], a.v, b, g, 0, a, wave, lane);
@@ -163,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         // row 32*kb2 + lq, 16-byte chunk 2*ks + lg
-        const bf16x8_t ka = as_bf16x8(lds_read16(Kt, kbase[ks & 3] + 128 * (ks >> 2) + 32 * kb2 * RB));
+        const bf16x8_t ka = as_bf16x8(lds_read16(Kt, kbase[ks] + 32 * kb2 * RB));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sacc[qb][kb2] = mfma32x32x16(ka, qop[qb][ks], sacc[qb][kb2]);
       }
@@ -227,9 +250,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         // rows 16*kb + vrow (+8), columns 32*db + vcol
-        const uint32_t off = vbase[db & 1] + 128 * (db >> 1) + 16 * kb * RB;
-        const u32x2_t lo = lds_read_tr16(Vt, off);
-        const u32x2_t hi = lds_read_tr16(Vt, off + 8 * RB);
+        const u32x2_t lo = lds_read_tr16(Vt, vlo[db] + 16 * kb * RB);
+        const u32x2_t hi = lds_read_tr16(Vt, vhi[db] + 16 * kb * RB);
         const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
         const bf16x8_t va = as_bf16x8(w);
 #pragma unroll
@@ -329,7 +351,7 @@ __global__ __launch_bounds__(kF32Queries * (D / 16)) void prefill_fp32_kernel(co
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
                                int seqlen, int hq, int hkv, int head_dim, int causal, float scale,
                                hipStream_t stream) {
-  constexpr int QB = 1;
+  constexpr int QB = ATTN_PREFILL_QB;
   constexpr int QW = 32 * QB;
   PrefillArgs a;
   a.q = static_cast<const uint16_t*>(q); a.k = static_cast<const uint16_t*>(k);
