@@ -23,6 +23,8 @@
 //   * exp is exp2 with scale*log2(e) folded into one FMA. Tiles fully above the diagonal are skipped; only tiles
 //     that cross the diagonal or the ragged end are masked. Heaviest query blocks are launched first.
 // fp32 path (correctness workload, head_dim 64/128): plain VALU, K/V tiles of 32 keys in LDS, fp32 throughout.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -76,23 +78,46 @@ __device__ __forceinline__ int swz_key(int r) {
   return (r & 6) | ((r >> 3) & 1);
 }
 
-// Issue the direct-to-LDS copy of one K or V tile (rows key0 .. key0+63 of KV head g) into `dst`.
-// Rows at or past seqlen are clamped to the last row (finite data; their scores are masked and P is 0).
-template <int D>
-__device__ __forceinline__ void issue_tile(uint16_t* dst, const uint16_t* src, int b, int g, int key0,
-                                           const PrefillArgs& a, int wave, int lane) {
-  const int64_t row_stride = int64_t(a.hkv) * D;
+// Per-lane element offsets of the direct-to-LDS tile copy by NW waves. Wave instruction i of wave w fills the 64
+// LDS slots of block i*NW + w; slot -> (row, physical chunk) -> logical chunk (physical ^ swz_key(row)). The
+// offsets are relative to row 0 of the tile and the same for K and V (same layout).
+template <int D, int NW>
+struct TileCopy {
+  static constexpr int kLoads = kBN * Tile<D>::kChunks / (64 * NW);
+  static_assert(kBN * Tile<D>::kChunks % (64 * NW) == 0, "tile must split evenly over the waves");
+  uint32_t off[kLoads];
+
+  __device__ __forceinline__ void init(int hkv, int g, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < Tile<D>::kLoadsPerWave; ++i) {
-    const int blk = i * kWaves + wave;               // 64-slot block this wave instruction fills
-    const int slot = blk * 64 + lane;
-    const int row = slot / Tile<D>::kChunks;
-    const int lchunk = (slot % Tile<D>::kChunks) ^ swz_key<D>(row);
-    const int key = min(key0 + row, a.seqlen - 1);
-    const uint16_t* gp = src + (int64_t(b) * a.seqlen + key) * row_stride + int64_t(g) * D + lchunk * 8;
-    load_lds16(gp, dst + blk * 512);
+    for (int i = 0; i < kLoads; ++i) {
+      const int slot = (i * NW + wave) * 64 + lane;
+      const int row = slot / Tile<D>::kChunks;
+      const int lchunk = (slot % Tile<D>::kChunks) ^ swz_key<D>(row);
+      off[i] = uint32_t((row * hkv + g) * D + lchunk * 8);
+    }
   }
-}
+
+  // Copy tile rows key0 .. key0+63 of one K or V tensor (`seq` = row 0 of this sequence) into `dst`. Rows at or
+  // past S are clamped to row S-1 (finite data: their scores are masked and P is exactly 0); only the last,
+  // ragged tile takes that path.
+  __device__ __forceinline__ void issue(uint16_t* dst, const uint16_t* seq, int key0, int S, int hkv, int g, int wave,
+                                        int lane) const {
+    const uint16_t* tb = seq + int64_t(key0) * hkv * D;
+    if (key0 + kBN <= S) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) load_lds16(tb + off[i], dst + (i * NW + wave) * 512);
+    } else {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) {
+        const int slot = (i * NW + wave) * 64 + lane;
+        const int row = slot / Tile<D>::kChunks;
+        const int lchunk = (slot % Tile<D>::kChunks) ^ swz_key<D>(row);
+        const int r = min(row, S - 1 - key0);
+        load_lds16(tb + (r * hkv + g) * D + lchunk * 8, dst + (i * NW + wave) * 512);
+      }
+    }
+  }
+};
 
 template <int D, int QB>
 __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void prefill_bf16_kernel(PrefillArgs a) {
@@ -162,20 +187,16 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
     vhi[db] = uint32_t((vrow + 8) * RB + 16 * (ch ^ swz_key<D>(vrow + 8)) + 8 * (bl & 1));
   }
 
-  issue_tile<D>(lds[0][0], a.k, b, g, 0, a, wave, lane);
-  issue_tile<D>(lds[0][1], a.v, b, g, 0, a, wave, lane);
+  TileCopy<D, kWaves> cp;
+  cp.init(a.hkv, g, wave, lane);
+  const uint16_t* kseq = a.k + int64_t(b) * S * a.hkv * D;
+  const uint16_t* vseq = a.v + int64_t(b) * S * a.hkv * D;
 
-  for (int t = 0; t < ntiles; ++t) {
-    wait_vmem();
-    __syncthreads();                                   // tile t visible to all; buffer (t+1)&1 free
-    if (t + 1 < ntiles) {
-      issue_tile<D>(lds[(t + 1) & 1][0], a.k, b, g, (t + 1) * kBN, a, wave, lane);
-      issue_tile<D>(lds[(t + 1) & 1][1], a.v, b, g, (t + 1) * kBN, a, wave, lane);
-    }
-    const int key0 = t * kBN;
-    if (key0 >= kend_w) continue;                      // tile entirely above this wave's diagonal
-    const uint16_t* Kt = lds[t & 1][0];
-    const uint16_t* Vt = lds[t & 1][1];
+  // One 64-key tile from LDS buffer BUF (a compile-time constant, so LDS addresses are base + immediate).
+  auto tile = [&](auto bufc, int key0) {
+    constexpr int BUF = decltype(bufc)::value;
+    const uint16_t* Kt = lds[BUF][0];
+    const uint16_t* Vt = lds[BUF][1];
 
     // ---- S^T = K Q^T for 64 keys (two 32-key blocks)
     f32x16_t sacc[QB][2];
@@ -216,7 +237,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb2][r]);
-      mx = fmaxf(mx, xor_lanes(mx, 32));
+      mx = max_xor32(mx);
       // Lazy rescale: move the reference max (rescaling O and l) only when some lane's max grew by more than
       // 2^kRescaleLog2; otherwise unnormalised P stays below that factor. O / l is unchanged.
       if (__any((mx - m[qb]) * c > kRescaleLog2)) {
@@ -258,13 +279,34 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
         for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32x32x16(va, pb[qb][kb], oacc[qb][db]);
       }
     }
+  };
+
+  cp.issue(lds[0][0], kseq, 0, S, a.hkv, g, wave, lane);
+  cp.issue(lds[0][1], vseq, 0, S, a.hkv, g, wave, lane);
+  // Two tiles per trip so each tile's LDS buffer is a compile-time constant.
+  for (int t = 0; t < ntiles; t += 2) {
+    wait_vmem();
+    __syncthreads();                                   // tile t visible to all; buffer 1 free
+    if (t + 1 < ntiles) {
+      cp.issue(lds[1][0], kseq, (t + 1) * kBN, S, a.hkv, g, wave, lane);
+      cp.issue(lds[1][1], vseq, (t + 1) * kBN, S, a.hkv, g, wave, lane);
+    }
+    if (t * kBN < kend_w) tile(std::integral_constant<int, 0>{}, t * kBN);
+    if (t + 1 >= ntiles) break;
+    wait_vmem();
+    __syncthreads();                                   // tile t+1 visible to all; buffer 0 free
+    if (t + 2 < ntiles) {
+      cp.issue(lds[0][0], kseq, (t + 2) * kBN, S, a.hkv, g, wave, lane);
+      cp.issue(lds[0][1], vseq, (t + 2) * kBN, S, a.hkv, g, wave, lane);
+    }
+    if ((t + 1) * kBN < kend_w) tile(std::integral_constant<int, 1>{}, (t + 1) * kBN);
   }
 
   // ---- epilogue: O = O^T / l (lane holds query lq, dims 32*db + 8*(r/4) + 4*lg + r%4), lse = scale*m + ln l
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qpos = qpos0 + 32 * qb + lq;
-    const float lt = l[qb] + xor_lanes(l[qb], 32);
+    const float lt = sum_xor32(l[qb]);
     if (qpos >= S) continue;
     const float inv = 1.f / lt;
     uint16_t* op = a.o + ((int64_t(b) * S + qpos) * a.hq + h) * D + 4 * lg;
@@ -352,7 +394,7 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
                                int seqlen, int hq, int hkv, int head_dim, int causal, float scale,
                                hipStream_t stream) {
   constexpr int QB = ATTN_PREFILL_QB;
-  constexpr int QW = 32 * QB;
+  constexpr int QW = 32 * QB;   // query positions per workgroup in heads mode
   PrefillArgs a;
   a.q = static_cast<const uint16_t*>(q); a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v); a.o = static_cast<uint16_t*>(o); a.lse = lse;
@@ -363,9 +405,9 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   a.n_pblk = (seqlen + span - 1) / span;
   a.n_hgrp = a.heads_mode ? hq / 4 : hq;
   const int64_t blocks = int64_t(a.n_pblk) * batch * a.n_hgrp;
-  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
-  if (head_dim == 128) prefill_bf16_kernel<128, QB><<<grid, block, 0, stream>>>(a);
-  else prefill_bf16_kernel<64, QB><<<grid, block, 0, stream>>>(a);
+  const dim3 grid(static_cast<unsigned>(blocks));
+  if (head_dim == 128) prefill_bf16_kernel<128, QB><<<grid, dim3(kThreads), 0, stream>>>(a);
+  else prefill_bf16_kernel<64, QB><<<grid, dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 
