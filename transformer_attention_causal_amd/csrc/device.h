@@ -58,23 +58,41 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
 }
 
 // ------------------------------------------------------------------------------------------------- LDS --
+// LDS reads. The base pointer is __restrict__ so that, once inlined, each read carries alias-scope
+// metadata; without it the compiler treats every LDS read as possibly aliasing an in-flight direct-to-LDS
+// copy and inserts a full vmcnt(0) wait before it, which would stall the copy of the next tile behind the
+// current tile's reads. The kernels order tile copies and reads themselves (vmcnt wait + workgroup barrier
+// before a tile is read; the copy in flight always targets the other buffer).
+//
 // 16-byte LDS read.
-__device__ __forceinline__ u32x4_t lds_read16(const uint16_t* lds_base, uint32_t byte_off) {
+__device__ __forceinline__ u32x4_t lds_read16(const uint16_t* __restrict__ lds_base, uint32_t byte_off) {
   return *(const __attribute__((address_space(3))) u32x4_t*)((const __attribute__((address_space(3))) char*)lds_base +
                                                                 byte_off);
 }
 
 // Transposing 8-byte LDS read (see the layout note at the top of this file).
-__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* lds_base, uint32_t byte_off) {
+__device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* __restrict__ lds_base, uint32_t byte_off) {
   i16x4_t t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) i16x4_t*)((__attribute__((address_space(3))) char*)lds_base + byte_off));
   return __builtin_bit_cast(u32x2_t, t);
 }
 
-// Direct global -> LDS copy of 16 bytes per lane: lane i's 16 bytes land at lds_wave_base + 16*i, where
-// lds_wave_base must be the same for the whole wave.
-__device__ __forceinline__ void load_lds16(const void* gsrc, uint16_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(const_cast<void*>(gsrc), (lds_void_t*)lds_wave_base, 16, 0, 0);
+// Direct global -> LDS copies go through buffer loads (MUBUF with the LDS bit), addressed by a buffer
+// resource plus a 32-bit per-lane byte offset. The FLAT-encoded global_load_lds would do the same copy, but
+// while one is in flight the compiler's wait insertion cannot count LDS reads in order and turns every LDS
+// wait into lgkmcnt(0), which serialises software-pipelined LDS reads behind their MFMAs.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
+
+// Raw buffer resource over `bytes` bytes at `base` (stride 0, 32-bit dword data format); loads at offsets
+// >= bytes return zero.
+__device__ __forceinline__ buf_rsrc_t make_buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// 16 bytes per lane from `rsrc` at byte offset `voff` into LDS: lane i's bytes land at lds_wave_base + 16*i,
+// where lds_wave_base must be the same for the whole wave.
+__device__ __forceinline__ void load_lds16(buf_rsrc_t rsrc, uint32_t voff, uint16_t* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_wave_base, 16, static_cast<int>(voff), 0, 0, 0);
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

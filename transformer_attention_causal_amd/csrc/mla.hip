@@ -28,18 +28,23 @@ namespace {
 constexpr int kC = 512;             // kv_lora_rank
 constexpr int kR = 64;              // rope dim
 constexpr int kDK = kC + kR;        // key width
-constexpr int kChunks = kDK / 8;    // 72 16-byte chunks per row
-constexpr int kRowBytes = kDK * 2;  // 1152
 constexpr int kTargetBlocks = 256;  // one workgroup per compute unit on MI355X
 
-// Tokens per LDS tile = 32 * ATTN_MLA_TILE_HALVES (double-buffered: 72 KiB per 32 tokens).
+// Tokens per LDS tile = 32 * ATTN_MLA_TILE_HALVES.
 #ifndef ATTN_MLA_TILE_HALVES
 #define ATTN_MLA_TILE_HALVES 2
 #endif
 constexpr int kHalves = ATTN_MLA_TILE_HALVES;
 constexpr int kRows = 32 * kHalves;                 // tokens per tile
-constexpr int kTileElems = kRows * kDK;
-constexpr int kTileBlocks = kRows * kChunks / 64;   // wave-instructions of 64 slots per tile
+// LDS tile: the latent rows first, each padded to 1056 bytes (1024 + 32), then the rope rows, 128 bytes each.
+//   latent: chunk c (16 bytes) of row r sits at physical chunk c ^ ((r >> 3) & 1). The 32-byte pad shifts
+//           consecutive rows by 8 banks, so the transposing value reads (8 rows x 32 bytes per half-wave) hit
+//           64 distinct banks, and the flipped chunk bit separates rows r and r + 8 for the 16-row K reads.
+//   rope:   chunk c of row r sits at c ^ ((r >> 1) & 7), which spreads the 16-row K reads over all banks.
+constexpr int kCkvStride = 2 * kC + 32;             // bytes per latent row in LDS
+constexpr int kPeOff = kRows * kCkvStride;          // byte offset of the rope rows
+constexpr int kTileBytes = kPeOff + kRows * kR * 2;
+constexpr int kCopies = kRows + kRows / 8;          // wave instructions per tile copy (one per latent row, 8 rope rows)
 
 struct MlaArgs {
   const uint16_t* q_lat;
@@ -53,17 +58,24 @@ struct MlaArgs {
   float scale;
 };
 
-// Copy tile rows t_tile .. t_tile+31 (clamped to t_last, a valid token) of sequence b into LDS `dst`.
-__device__ __forceinline__ void mla_issue(uint16_t* dst, const MlaArgs& a, int b, int t_tile, int t_last, int wave,
+// Copy tokens t_tile .. t_tile + kRows - 1 of sequence b into the LDS tile at `dst`; tokens at or past t_end come
+// from token t_end - 1 (finite data; their scores are masked and P is exactly 0). Instruction i < kRows copies
+// latent row i (1024 contiguous bytes); the others copy 8 rope rows each (1024 contiguous bytes).
+__device__ __forceinline__ void mla_issue(char* dst, const MlaArgs& a, int b, int t_tile, int t_end, int wave,
                                           int nwaves, int lane) {
-  for (int blk = wave; blk < kTileBlocks; blk += nwaves) {
-    const int slot = blk * 64 + lane;
-    const int row = slot / kChunks;
-    const int lchunk = (slot % kChunks) ^ (row & 7);
-    const int tok = min(t_tile + row, t_last);
-    const int64_t tb = int64_t(b) * a.max_len + tok;
-    const uint16_t* gp = lchunk < kC / 8 ? a.c_kv + tb * kC + lchunk * 8 : a.k_pe + tb * kR + (lchunk - kC / 8) * 8;
-    load_lds16(gp, dst + blk * 512);
+  const int rows = min(kRows, t_end - t_tile);
+  const int64_t tok0 = int64_t(b) * a.max_len + t_tile;
+  const buf_rsrc_t rc = make_buf_rsrc(a.c_kv + tok0 * kC, uint32_t(rows * kC * 2));
+  const buf_rsrc_t rp = make_buf_rsrc(a.k_pe + tok0 * kR, uint32_t(rows * kR * 2));
+  for (int i = wave; i < kCopies; i += nwaves) {
+    if (i < kRows) {
+      const uint32_t off = uint32_t(min(i, rows - 1) * kC * 2 + 16 * (lane ^ ((i >> 3) & 1)));
+      load_lds16(rc, off, reinterpret_cast<uint16_t*>(dst + i * kCkvStride));
+    } else {
+      const int r = 8 * (i - kRows) + (lane >> 3);
+      const uint32_t off = uint32_t(min(r, rows - 1) * kR * 2 + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
+      load_lds16(rp, off, reinterpret_cast<uint16_t*>(dst + kPeOff + (i - kRows) * 1024));
+    }
   }
 }
 
@@ -71,8 +83,19 @@ __device__ __forceinline__ void mla_issue(uint16_t* dst, const MlaArgs& a, int b
 // (72 registers) and its O^T = 512 x 16 fp32 (128 registers) resident without spilling; 8 waves cover 128 heads.
 constexpr int kHeadsPerWave = 16;
 
+// LDS fragments in flight ahead of the MFMA that consumes them (4 registers each).
+#ifndef ATTN_MLA_PIPE
+#define ATTN_MLA_PIPE 3
+#endif
+constexpr int kPipe = ATTN_MLA_PIPE;
+// 1: pin the read/MFMA interleave with scheduling groups; 0: leave the order to the compiler.
+#ifndef ATTN_MLA_SGB
+#define ATTN_MLA_SGB 1
+#endif
+#define MLA_SGB(mask, n) do { if (ATTN_MLA_SGB) __builtin_amdgcn_sched_group_barrier(mask, n, 0); } while (0)
+
 __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][kTileElems];
+  __shared__ __attribute__((aligned(16))) char lds[2][kTileBytes];
   const int split = blockIdx.x, b = blockIdx.y;
   const int nwaves = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -100,39 +123,50 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
   for (int db = 0; db < kC / 16; ++db) oacc[db] = f32x4_t{};
   float m = -INFINITY, l = 0.f;
 
-  // Lane-fixed parts of the swizzled LDS addresses (chunk c of row r sits at 8*(c/8) + ((c%8) ^ (r&7))); the
-  // loops add only compile-time immediates.
-  uint32_t abase[2];                                   // K reads: row n (+16*tb), chunk 4*ks + g4
+  // Lane-fixed parts of the LDS addresses (layout above); the loops add only compile-time immediates.
+  //   K reads (A operand): token row n (+16*tb), chunk 4*ks + g4.
+  const uint32_t abase = uint32_t(n * kCkvStride + 16 * (g4 ^ ((n >> 3) & 1)));
+  uint32_t pbase[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) abase[i] = uint32_t(n * kRowBytes + 16 * ((4 * i + g4) ^ (n & 7)));
+  for (int j = 0; j < 2; ++j) pbase[j] = uint32_t(kPeOff + n * kR * 2 + 16 * ((4 * j + g4) ^ ((n >> 1) & 7)));
+  //   value reads (transposing): rows vrow (+16), latent columns 16*db + 4*(bl&3) .. +3.
   const int bl = lane & 15;
-  const int vrow = 4 * g4 + (bl >> 2);                 // V reads: rows vrow (+16), columns 16*db + 4*(bl&3)
-  uint32_t vbase[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    vbase[i] = uint32_t(vrow * kRowBytes + 16 * ((2 * i + ((bl >> 1) & 1)) ^ (vrow & 7)) + 8 * (bl & 1));
+  const int vrow = 4 * g4 + (bl >> 2);
+  const uint32_t vbase = uint32_t(vrow * kCkvStride + 16 * (((bl >> 1) & 1) ^ ((vrow >> 3) & 1)) + 8 * (bl & 1));
 
-  mla_issue(lds[0], a, b, t_begin, t_end - 1, wave, nwaves, lane);
+  mla_issue(lds[0], a, b, t_begin, t_end, wave, nwaves, lane);
 
   for (int t = 0; t < ntiles; ++t) {
     wait_vmem();
     __syncthreads();
-    if (t + 1 < ntiles) mla_issue(lds[(t + 1) & 1], a, b, t_begin + (t + 1) * kRows, t_end - 1, wave, nwaves, lane);
-    const uint16_t* T = lds[t & 1];
+    if (t + 1 < ntiles) mla_issue(lds[(t + 1) & 1], a, b, t_begin + (t + 1) * kRows, t_end, wave, nwaves, lane);
+    const uint16_t* T = reinterpret_cast<const uint16_t*>(lds[t & 1]);
     const int tok0 = t_begin + t * kRows;
 
-    // S^T = Kc Q^T: 16-token blocks tb; lane holds head n, tokens 16*tb + 4*g4 + r
+    // S^T = Kc Q^T: 16-token blocks tb; lane holds head n, tokens 16*tb + 4*g4 + r. The K fragments are
+    // software-pipelined kPipe MFMAs ahead (one wave-uniform order pinned by scheduling groups), so LDS latency
+    // overlaps the MFMAs instead of stalling each one.
     constexpr int TB = 2 * kHalves;
+    constexpr int NQ = (kDK / 32) * TB;                // MFMAs of the score contraction
     f32x4_t sacc[TB];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) sacc[tb] = f32x4_t{};
+    auto kfrag = [&](int j) {                           // j = ks * TB + tb
+      const int ks = j / TB, tb = j % TB;
+      return as_bf16x8(ks < kC / 32 ? lds_read16(T, abase + 64 * ks + 16 * tb * kCkvStride)
+                                    : lds_read16(T, pbase[ks - kC / 32] + 16 * tb * kR * 2));
+    };
+    bf16x8_t kf[kPipe];
 #pragma unroll
-    for (int ks = 0; ks < kDK / 32; ++ks) {
+    for (int j = 0; j < kPipe; ++j) kf[j] = kfrag(j);
+    MLA_SGB(0x100, kPipe);
 #pragma unroll
-      for (int tb = 0; tb < TB; ++tb)
-        sacc[tb] = mfma16x16x32(as_bf16x8(lds_read16(T, abase[ks & 1] + 128 * (ks >> 1) + 16 * tb * kRowBytes)),
-                                qop[ks], sacc[tb]);
-      if (ks % 6 == 5) __builtin_amdgcn_sched_barrier(0);   // bound how far LDS reads are hoisted (registers)
+    for (int j = 0; j < NQ; ++j) {
+      const bf16x8_t cur = kf[j % kPipe];
+      if (j + kPipe < NQ) kf[j % kPipe] = kfrag(j + kPipe);
+      sacc[j % TB] = mfma16x16x32(cur, qop[j / TB], sacc[j % TB]);
+      MLA_SGB(0x008, 1);
+      if (j + kPipe < NQ) MLA_SGB(0x100, 1);
     }
     if (tok0 + kRows > t_end) {
 #pragma unroll
@@ -173,18 +207,28 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
     for (int kh = 0; kh < kHalves; ++kh)
       pb[kh] = pack_bf16x8(sacc[2 * kh][0], sacc[2 * kh][1], sacc[2 * kh][2], sacc[2 * kh][3], sacc[2 * kh + 1][0],
                            sacc[2 * kh + 1][1], sacc[2 * kh + 1][2], sacc[2 * kh + 1][3]);
-    // O^T += c_kv^T P^T: the value operand is the same tile read through the transposing LDS read
+    // O^T += c_kv^T P^T: the value operand is the same tile read through the transposing LDS read; 32-token
+    // halves outer so consecutive MFMAs use independent accumulators; value fragments pipelined like K.
+    constexpr int NV = kHalves * (kC / 16);
+    auto vfrag = [&](int j) {                           // j = kh * 32 + db
+      const int kh = j / (kC / 16), db = j % (kC / 16);
+      const uint32_t off = vbase + 32 * db + 32 * kh * kCkvStride;
+      const u32x2_t lo = lds_read_tr16(T, off);
+      const u32x2_t hi = lds_read_tr16(T, off + 16 * kCkvStride);
+      const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
+      return as_bf16x8(w);
+    };
+    bf16x8_t vf[kPipe];
 #pragma unroll
-    for (int db = 0; db < kC / 16; ++db) {
+    for (int j = 0; j < kPipe; ++j) vf[j] = vfrag(j);
+    MLA_SGB(0x100, 2 * kPipe);
 #pragma unroll
-      for (int kh = 0; kh < kHalves; ++kh) {
-        const uint32_t off = vbase[db & 3] + 128 * (db >> 2) + 32 * kh * kRowBytes;
-        const u32x2_t lo = lds_read_tr16(T, off);
-        const u32x2_t hi = lds_read_tr16(T, off + 16 * kRowBytes);
-        const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
-        oacc[db] = mfma16x16x32(as_bf16x8(w), pb[kh], oacc[db]);
-      }
-      if (db % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < NV; ++j) {
+      const bf16x8_t cur = vf[j % kPipe];
+      if (j + kPipe < NV) vf[j % kPipe] = vfrag(j + kPipe);
+      oacc[j % (kC / 16)] = mfma16x16x32(cur, pb[j / (kC / 16)], oacc[j % (kC / 16)]);
+      MLA_SGB(0x008, 1);
+      if (j + kPipe < NV) MLA_SGB(0x100, 2);
     }
   }
 

@@ -9,8 +9,8 @@
 //   * Work unit: QW = 32*QB query positions of 4 query heads of one KV group ("heads mode", when the group size
 //     is a multiple of 4: every wave has the same causal range and the K/V tile in LDS feeds 4*QW query rows), or
 //     4 consecutive blocks of QW positions of one query head ("positions mode", any other group size).
-//   * K and V tiles of 64 keys x D are copied straight from global memory into LDS (global_load_lds, 16 bytes
-//     per lane, no register staging), double-buffered, one barrier per tile. LDS rows are unpadded; their
+//   * K and V tiles of 64 keys x D are copied straight from global memory into LDS (buffer loads with the LDS
+//     bit, 16 bytes per lane, no register staging), double-buffered, one barrier per tile. LDS rows are unpadded; their
 //     16-byte chunks are XOR-swizzled by a key of the row index (swz_key) that makes both LDS read patterns
 //     below conflict-free on the 64-bank LDS. Two workgroups share a CU (registers capped at 256).
 //   * Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16: K fragments come from LDS (16-byte
@@ -78,42 +78,43 @@ __device__ __forceinline__ int swz_key(int r) {
   return (r & 6) | ((r >> 3) & 1);
 }
 
-// Per-lane element offsets of the direct-to-LDS tile copy by NW waves. Wave instruction i of wave w fills the 64
-// LDS slots of block i*NW + w; slot -> (row, physical chunk) -> logical chunk (physical ^ swz_key(row)). The
-// offsets are relative to row 0 of the tile and the same for K and V (same layout).
+// Per-lane byte offsets of the direct-to-LDS tile copy by NW waves. Wave instruction i of wave w fills the 64 LDS
+// slots of block i*NW + w; slot -> (row, physical chunk) -> logical chunk (physical ^ swz_key(row)). The offsets
+// are relative to row 0 of the tile and the same for K and V (same layout).
 template <int D, int NW>
 struct TileCopy {
   static constexpr int kLoads = kBN * Tile<D>::kChunks / (64 * NW);
   static_assert(kBN * Tile<D>::kChunks % (64 * NW) == 0, "tile must split evenly over the waves");
   uint32_t off[kLoads];
 
+  __device__ __forceinline__ static uint32_t byte_off(int row, int slot, int hkv, int g) {
+    const int lchunk = (slot % Tile<D>::kChunks) ^ swz_key<D>(slot / Tile<D>::kChunks);
+    return uint32_t(((row * hkv + g) * D + lchunk * 8) * 2);
+  }
+
   __device__ __forceinline__ void init(int hkv, int g, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int slot = (i * NW + wave) * 64 + lane;
-      const int row = slot / Tile<D>::kChunks;
-      const int lchunk = (slot % Tile<D>::kChunks) ^ swz_key<D>(row);
-      off[i] = uint32_t((row * hkv + g) * D + lchunk * 8);
+      off[i] = byte_off(slot / Tile<D>::kChunks, slot, hkv, g);
     }
   }
 
   // Copy tile rows key0 .. key0+63 of one K or V tensor (`seq` = row 0 of this sequence) into `dst`. Rows at or
   // past S are clamped to row S-1 (finite data: their scores are masked and P is exactly 0); only the last,
-  // ragged tile takes that path.
+  // ragged tile takes that path. The buffer resource spans exactly the tile's valid rows.
   __device__ __forceinline__ void issue(uint16_t* dst, const uint16_t* seq, int key0, int S, int hkv, int g, int wave,
                                         int lane) const {
-    const uint16_t* tb = seq + int64_t(key0) * hkv * D;
-    if (key0 + kBN <= S) {
+    const int rows = min(kBN, S - key0);
+    const buf_rsrc_t rs = make_buf_rsrc(seq + int64_t(key0) * hkv * D, uint32_t(rows * hkv * D * 2));
+    if (rows == kBN) {
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) load_lds16(tb + off[i], dst + (i * NW + wave) * 512);
+      for (int i = 0; i < kLoads; ++i) load_lds16(rs, off[i], dst + (i * NW + wave) * 512);
     } else {
 #pragma unroll
       for (int i = 0; i < kLoads; ++i) {
         const int slot = (i * NW + wave) * 64 + lane;
-        const int row = slot / Tile<D>::kChunks;
-        const int lchunk = (slot % Tile<D>::kChunks) ^ swz_key<D>(row);
-        const int r = min(row, S - 1 - key0);
-        load_lds16(tb + (r * hkv + g) * D + lchunk * 8, dst + (i * NW + wave) * 512);
+        load_lds16(rs, byte_off(min(slot / Tile<D>::kChunks, rows - 1), slot, hkv, g), dst + (i * NW + wave) * 512);
       }
     }
   }
