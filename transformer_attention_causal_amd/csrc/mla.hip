@@ -37,9 +37,12 @@ constexpr int kTargetBlocks = 256;  // one workgroup per compute unit on MI355X
 constexpr int kHalves = ATTN_MLA_TILE_HALVES;
 constexpr int kRows = 32 * kHalves;                 // tokens per tile
 // LDS tile: the latent rows first, each padded to 1056 bytes (1024 + 32), then the rope rows, 128 bytes each.
-//   latent: chunk c (16 bytes) of row r sits at physical chunk c ^ ((r >> 3) & 1). The 32-byte pad shifts
-//           consecutive rows by 8 banks, so the transposing value reads (8 rows x 32 bytes per half-wave) hit
-//           64 distinct banks, and the flipped chunk bit separates rows r and r + 8 for the 16-row K reads.
+// LDS has 64 four-byte banks; measured on gfx950, ds_read_b128 serves the lane sets {0-7, 24-31}, {8-15, 16-23},
+// {32-39, 56-63}, {40-47, 48-55} one per cycle and ds_read_b64_tr_b16 32 consecutive lanes per cycle; a set is
+// conflict-free when its lanes hit distinct slots modulo 256 bytes.
+//   latent: unswizzled. The 32-byte pad shifts row r by 2r 16-byte slots: the transposing value reads (rows
+//           r0..r0+7 x 32 bytes per 32 lanes) fill all 64 banks, and each K-read set (8 rows at one chunk, the
+//           other 8 of the 16 rows at the next chunk) lands on the even and the odd slots.
 //   rope:   chunk c of row r sits at c ^ ((r >> 1) & 7), which spreads the 16-row K reads over all banks.
 constexpr int kCkvStride = 2 * kC + 32;             // bytes per latent row in LDS
 constexpr int kPeOff = kRows * kCkvStride;          // byte offset of the rope rows
@@ -69,7 +72,7 @@ __device__ __forceinline__ void mla_issue(char* dst, const MlaArgs& a, int b, in
   const buf_rsrc_t rp = make_buf_rsrc(a.k_pe + tok0 * kR, uint32_t(rows * kR * 2));
   for (int i = wave; i < kCopies; i += nwaves) {
     if (i < kRows) {
-      const uint32_t off = uint32_t(min(i, rows - 1) * kC * 2 + 16 * (lane ^ ((i >> 3) & 1)));
+      const uint32_t off = uint32_t(min(i, rows - 1) * kC * 2 + 16 * lane);
       load_lds16(rc, off, reinterpret_cast<uint16_t*>(dst + i * kCkvStride));
     } else {
       const int r = 8 * (i - kRows) + (lane >> 3);
@@ -125,14 +128,14 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
 
   // Lane-fixed parts of the LDS addresses (layout above); the loops add only compile-time immediates.
   //   K reads (A operand): token row n (+16*tb), chunk 4*ks + g4.
-  const uint32_t abase = uint32_t(n * kCkvStride + 16 * (g4 ^ ((n >> 3) & 1)));
+  const uint32_t abase = uint32_t(n * kCkvStride + 16 * g4);
   uint32_t pbase[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) pbase[j] = uint32_t(kPeOff + n * kR * 2 + 16 * ((4 * j + g4) ^ ((n >> 1) & 7)));
   //   value reads (transposing): rows vrow (+16), latent columns 16*db + 4*(bl&3) .. +3.
   const int bl = lane & 15;
   const int vrow = 4 * g4 + (bl >> 2);
-  const uint32_t vbase = uint32_t(vrow * kCkvStride + 16 * (((bl >> 1) & 1) ^ ((vrow >> 3) & 1)) + 8 * (bl & 1));
+  const uint32_t vbase = uint32_t(vrow * kCkvStride + 8 * (bl & 3));
 
   mla_issue(lds[0], a, b, t_begin, t_end, wave, nwaves, lane);
 

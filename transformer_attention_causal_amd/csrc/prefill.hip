@@ -67,15 +67,20 @@ struct PrefillArgs {
   int n_hgrp;        // head groups: hq/4 in heads mode, hq in positions mode
 };
 
-// LDS swizzle: 16-byte chunk c of tile row r is stored at chunk position c ^ swz_key(r). With 64 four-byte banks,
-// the key must (a) give 16 consecutive rows distinct positions for the same logical chunk (K reads: one row per
-// lane) and (b) give rows 4i..4i+3 disjoint chunk pairs (V^T reads: ds_read_b64_tr_b16 takes 32 bytes from each
-// of 4 rows per 16 lanes). A 4-bit rotation of the row index does both for 256-byte rows (head_dim 128); for
-// 128-byte rows (head_dim 64, two rows per bank window) the rotation acts on the row pair index.
+// LDS swizzle: 16-byte chunk c of tile row r is stored at chunk position c ^ swz_key(r). LDS has 64 four-byte
+// banks (256 bytes per cycle). Measured on gfx950: ds_read_b128 serves 16 lanes per cycle, in the lane sets
+// {0-7, 24-31}, {8-15, 16-23}, {32-39, 56-63}, {40-47, 48-55}; ds_read_b64(_tr_b16) serves 32 consecutive lanes
+// per cycle. A set is conflict-free when its lanes hit distinct 16-byte (8-byte) slots modulo 256 bytes.
+//   K reads (A operand of the 32x32x16 MFMA): lane l reads row l%32, so each b128 set holds rows {0-7, 24-31} or
+//     {8-15, 16-23} at one logical chunk: the key must be distinct over each of those row sets.
+//   V^T reads (ds_read_b64_tr_b16): 32 lanes read 4 consecutive rows (aligned to 4) x 4 consecutive chunks: the
+//     key must send the 4 rows to 4 different groups of 4 chunk slots.
+// 256-byte rows (head_dim 128): key = (r%4)*4 + (r/4)%4. 128-byte rows (head_dim 64; two rows per 256 bytes, so
+// row parity already separates half the slots): key = ((r/2)%2)*4 + (r/4)%4. Both depend on r mod 16 only.
 template <int D>
 __device__ __forceinline__ int swz_key(int r) {
-  if (D == 128) return ((r << 1) | ((r >> 3) & 1)) & 15;
-  return (r & 6) | ((r >> 3) & 1);
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 // Per-lane byte offsets of the direct-to-LDS tile copy by NW waves. Wave instruction i of wave w fills the 64 LDS
