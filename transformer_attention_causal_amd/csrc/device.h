@@ -81,18 +81,30 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* __restrict__ ld
 // resource plus a 32-bit per-lane byte offset. The FLAT-encoded global_load_lds would do the same copy, but
 // while one is in flight the compiler's wait insertion cannot count LDS reads in order and turns every LDS
 // wait into lgkmcnt(0), which serialises software-pipelined LDS reads behind their MFMAs.
-typedef __amdgpu_buffer_rsrc_t buf_rsrc_t;
+// Buffer resource (V#) as four dwords. The resource is built from wave-uniform words so it lives in scalar
+// registers; the opaque __amdgpu_buffer_rsrc_t form is assembled in vector registers and makes the compiler wrap
+// every load in a per-lane waterfall loop.
+typedef int buf_rsrc_t __attribute__((ext_vector_type(4)));
+
+// The LLVM raw buffer load-to-LDS intrinsic, taking the resource as 4 x i32.
+__device__ void raw_buffer_load_lds(buf_rsrc_t rsrc, lds_void_t* lds, int size, int voffset, int soffset, int offset,
+                                    int aux) __asm("llvm.amdgcn.raw.buffer.load.lds");
 
 // Raw buffer resource over `bytes` bytes at `base` (stride 0, 32-bit dword data format); loads at offsets
-// >= bytes return zero.
+// >= bytes return zero. `base` and `bytes` must be wave-uniform.
 __device__ __forceinline__ buf_rsrc_t make_buf_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  buf_rsrc_t r = {__builtin_amdgcn_readfirstlane(static_cast<int>(uint32_t(p))),
+                  __builtin_amdgcn_readfirstlane(static_cast<int>(uint32_t(p >> 32) & 0xffffu)),
+                  __builtin_amdgcn_readfirstlane(static_cast<int>(bytes)), 0x00020000};
+  return r;
 }
 
-// 16 bytes per lane from `rsrc` at byte offset `voff` into LDS: lane i's bytes land at lds_wave_base + 16*i,
-// where lds_wave_base must be the same for the whole wave.
-__device__ __forceinline__ void load_lds16(buf_rsrc_t rsrc, uint32_t voff, uint16_t* lds_wave_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_wave_base, 16, static_cast<int>(voff), 0, 0, 0);
+// 16 bytes per lane from `rsrc` at byte offset voff + soff into LDS: lane i's bytes land at lds_wave_base + 16*i,
+// where lds_wave_base and soff must be the same for the whole wave. Only voff is range-checked against the
+// resource size, so soff must keep the access inside the resource whenever voff is in range.
+__device__ __forceinline__ void load_lds16(buf_rsrc_t rsrc, uint32_t voff, void* lds_wave_base, uint32_t soff = 0) {
+  raw_buffer_load_lds(rsrc, (lds_void_t*)lds_wave_base, 16, static_cast<int>(voff), static_cast<int>(soff), 0, 0);
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }

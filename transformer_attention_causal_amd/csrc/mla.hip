@@ -61,24 +61,33 @@ struct MlaArgs {
   float scale;
 };
 
-// Copy tokens t_tile .. t_tile + kRows - 1 of sequence b into the LDS tile at `dst`; tokens at or past t_end come
-// from token t_end - 1 (finite data; their scores are masked and P is exactly 0). Instruction i < kRows copies
-// latent row i (1024 contiguous bytes); the others copy 8 rope rows each (1024 contiguous bytes).
-__device__ __forceinline__ void mla_issue(char* dst, const MlaArgs& a, int b, int t_tile, int t_end, int wave,
-                                          int nwaves, int lane) {
-  const int rows = min(kRows, t_end - t_tile);
-  const int64_t tok0 = int64_t(b) * a.max_len + t_tile;
-  const buf_rsrc_t rc = make_buf_rsrc(a.c_kv + tok0 * kC, uint32_t(rows * kC * 2));
-  const buf_rsrc_t rp = make_buf_rsrc(a.k_pe + tok0 * kR, uint32_t(rows * kR * 2));
-  for (int i = wave; i < kCopies; i += nwaves) {
-    if (i < kRows) {
-      const uint32_t off = uint32_t(min(i, rows - 1) * kC * 2 + 16 * lane);
-      load_lds16(rc, off, reinterpret_cast<uint16_t*>(dst + i * kCkvStride));
-    } else {
-      const int r = 8 * (i - kRows) + (lane >> 3);
-      const uint32_t off = uint32_t(min(r, rows - 1) * kR * 2 + 16 * ((lane & 7) ^ ((r >> 1) & 7)));
-      load_lds16(rp, off, reinterpret_cast<uint16_t*>(dst + kPeOff + (i - kRows) * 1024));
-    }
+// One tile copy: tokens t_tile .. t_tile + kRows - 1 of sequence b. Copy instruction i < kRows moves latent row
+// i (1024 contiguous bytes), the others 8 rope rows each (1024 contiguous bytes). Tokens at or past t_end come from
+// token t_end - 1 (finite data; their scores are masked and P is exactly 0). The buffer resources span exactly the
+// valid rows; a tile past the end gets none, so its copy instructions read nothing (out of range: zeros).
+struct MlaCopy {
+  buf_rsrc_t rc, rp;
+  int rows;
+};
+
+__device__ __forceinline__ MlaCopy mla_copy_setup(const MlaArgs& a, int b, int t_tile, int t_end) {
+  MlaCopy cp;
+  cp.rows = max(0, min(kRows, t_end - t_tile));
+  const int64_t tok0 = int64_t(b) * a.max_len + min(t_tile, t_end - 1);
+  cp.rc = make_buf_rsrc(a.c_kv + tok0 * kC, uint32_t(cp.rows * kC * 2));
+  cp.rp = make_buf_rsrc(a.k_pe + tok0 * kR, uint32_t(cp.rows * kR * 2));
+  return cp;
+}
+
+// Copy instruction i (wave-uniform) of a tile copy into the LDS tile at `dst`.
+__device__ __forceinline__ void mla_copy_one(char* dst, const MlaCopy& cp, int i, int lane) {
+  if (i < kRows) {
+    const int row = max(0, min(i, cp.rows - 1));       // uniform: goes in the scalar offset
+    load_lds16(cp.rc, uint32_t(16 * lane), dst + i * kCkvStride, uint32_t(row * kC * 2));
+  } else {
+    const int r = 8 * (i - kRows) + (lane >> 3);
+    const int row = max(0, min(r, cp.rows - 1));
+    load_lds16(cp.rp, uint32_t(row * kR * 2 + 16 * ((lane & 7) ^ ((r >> 1) & 7))), dst + kPeOff + (i - kRows) * 1024);
   }
 }
 
@@ -97,11 +106,19 @@ constexpr int kPipe = ATTN_MLA_PIPE;
 #endif
 #define MLA_SGB(mask, n) do { if (ATTN_MLA_SGB) __builtin_amdgcn_sched_group_barrier(mask, n, 0); } while (0)
 
+// NW waves per workgroup (16 heads each). Each wave issues kCopies / NW copy instructions per tile, spread over
+// its score MFMAs (one every NW), so the copy of tile t+1 overlaps tile t's work instead of stalling every wave
+// on a burst of vector-memory issues right after the barrier.
+template <int NW>
 __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
+  static_assert(kCopies % NW == 0, "copy instructions must split evenly over the waves");
+  constexpr int NC = kCopies / NW;
   __shared__ __attribute__((aligned(16))) char lds[2][kTileBytes];
   const int split = blockIdx.x, b = blockIdx.y;
-  const int nwaves = blockDim.x >> 6;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // Wave index in a scalar register, with its range [0, NW) visible to the compiler (resolves at compile time
+  // whether each copy instruction moves a latent or a rope block).
+  const int wave = int(unsigned(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) % unsigned(NW));
+  const int lane = threadIdx.x & 63;
   const int n = lane & 15, g4 = lane >> 4;
   const int L = max(0, min(a.seq_lens[b], a.max_len));
   const int t_begin = split * a.split_len;
@@ -137,12 +154,17 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
   const int vrow = 4 * g4 + (bl >> 2);
   const uint32_t vbase = uint32_t(vrow * kCkvStride + 8 * (bl & 3));
 
-  mla_issue(lds[0], a, b, t_begin, t_end, wave, nwaves, lane);
+  {
+    const MlaCopy cp0 = mla_copy_setup(a, b, t_begin, t_end);
+#pragma unroll
+    for (int k = 0; k < NC; ++k) mla_copy_one(lds[0], cp0, wave + k * NW, lane);
+  }
 
   for (int t = 0; t < ntiles; ++t) {
     wait_vmem();
-    __syncthreads();
-    if (t + 1 < ntiles) mla_issue(lds[(t + 1) & 1], a, b, t_begin + (t + 1) * kRows, t_end, wave, nwaves, lane);
+    __syncthreads();                                   // tile t visible to all; buffer (t+1)&1 free
+    const MlaCopy cpn = mla_copy_setup(a, b, t_begin + (t + 1) * kRows, t_end);
+    char* nbuf = lds[(t + 1) & 1];
     const uint16_t* T = reinterpret_cast<const uint16_t*>(lds[t & 1]);
     const int tok0 = t_begin + t * kRows;
 
@@ -170,6 +192,10 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
       sacc[j % TB] = mfma16x16x32(cur, qop[j / TB], sacc[j % TB]);
       MLA_SGB(0x008, 1);
       if (j + kPipe < NQ) MLA_SGB(0x100, 1);
+      if (j % NW == 0 && j / NW < NC) {                // next tile's copy, one instruction every NW MFMAs
+        mla_copy_one(nbuf, cpn, wave + (j / NW) * NW, lane);
+        MLA_SGB(0x020, 1);
+      }
     }
     if (tok0 + kRows > t_end) {
 #pragma unroll
@@ -316,8 +342,15 @@ hipError_t launch_mla_decode(const void* q_latent, const void* q_pe, const void*
   const size_t o_bytes = (slots * kC * sizeof(float) + 255) & ~size_t(255);
   a.ws_o = static_cast<float*>(workspace);
   a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
-  if (max_seqlen_kv > 0)
-    mla_split_kernel<<<dim3(unsigned(a.n_split), unsigned(batch)), dim3(64 * (n_heads / kHeadsPerWave)), 0, stream>>>(a);
+  if (max_seqlen_kv > 0) {
+    const dim3 grid(unsigned(a.n_split), unsigned(batch)), block(64 * (n_heads / kHeadsPerWave));
+    switch (n_heads / kHeadsPerWave) {
+      case 2: mla_split_kernel<2><<<grid, block, 0, stream>>>(a); break;
+      case 4: mla_split_kernel<4><<<grid, block, 0, stream>>>(a); break;
+      case 6: mla_split_kernel<6><<<grid, block, 0, stream>>>(a); break;
+      default: mla_split_kernel<8><<<grid, block, 0, stream>>>(a); break;
+    }
+  }
   mla_combine_kernel<<<dim3(unsigned(n_heads), unsigned(batch)), dim3(kC / 2), 0, stream>>>(
       a.ws_o, a.ws_lse, seq_lens, static_cast<uint16_t*>(o_latent), lse, n_heads, a.n_split, a.split_len,
       max_seqlen_kv);

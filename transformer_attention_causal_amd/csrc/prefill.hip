@@ -132,7 +132,8 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   constexpr int DB = D / 32;   // 32-row blocks of O^T
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kBN * D];   // [buffer][K, V]
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar register)
+  const int lane = threadIdx.x & 63;
   const int lq = lane & 31, lg = lane >> 5;
   // ---- work unit (heaviest position blocks first; consecutive ids share a position block)
   const int per_slice = a.batch * a.n_hgrp;
