@@ -5,14 +5,15 @@
 //  m_c and block exp-sum l_c update the running m and l, m_new = max(m_old, m_c), l_new = l_old e^(m_old - m_new)
 //  + l_c e^(m_c - m_new); "Group-Query Attention" derivation table — consecutive query heads share a KV head.)
 //
-// bf16 path, one workgroup = 4 waves:
-//   * Work unit: QW = 32*QB query positions of 4 query heads of one KV group ("heads mode", when the group size
-//     is a multiple of 4: every wave has the same causal range and the K/V tile in LDS feeds 4*QW query rows), or
-//     4 consecutive blocks of QW positions of one query head ("positions mode", any other group size).
+// bf16 path, one workgroup = 12 waves (one per CU, three per SIMD: registers capped at 168 per lane):
+//   * Work unit: 3 blocks of 32 query positions x 4 query heads of one KV group ("heads mode", when the group
+//     size is a multiple of 4: each K/V tile in LDS feeds 384 query rows), or 12 consecutive 32-position blocks of
+//     one query head ("positions mode", any other group size). Each wave owns 32 queries of one head.
 //   * K and V tiles of 64 keys x D are copied straight from global memory into LDS (buffer loads with the LDS
-//     bit, 16 bytes per lane, no register staging), double-buffered, one barrier per tile. LDS rows are unpadded; their
-//     16-byte chunks are XOR-swizzled by a key of the row index (swz_key) that makes both LDS read patterns
-//     below conflict-free on the 64-bank LDS. Two workgroups share a CU (registers capped at 256).
+//     bit, 16 bytes per lane, no register staging), double-buffered, one barrier per tile. LDS rows are unpadded;
+//     their 16-byte chunks are XOR-swizzled by a key of the row index (swz_key) that makes both LDS read patterns
+//     below conflict-free on the 64-bank LDS. Three waves per SIMD let one wave's MFMAs overlap another's
+//     softmax and LDS waits; sharing each tile over 12 waves keeps the L2-to-LDS copy rate well below its limit.
 //   * Scores are formed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16: K fragments come from LDS (16-byte
 //     reads), Q^T stays in registers for the whole kernel. In the S^T accumulator each lane holds ONE query
 //     (lane % 32) and 16 keys, so the row max and row sum need one cross-lane exchange (lanes l and l ^ 32), and
@@ -31,17 +32,22 @@
 namespace attn {
 namespace {
 
-constexpr int kWaves = 4;
+// Waves per workgroup: in heads mode 4 heads x (kWaves/4) blocks of 32 positions share each K/V tile in LDS.
+#ifndef ATTN_PREFILL_WAVES
+#define ATTN_PREFILL_WAVES 12
+#endif
+constexpr int kWaves = ATTN_PREFILL_WAVES;
+constexpr int kPosBlocks = kWaves / 4;   // 32-position blocks per workgroup in heads mode
 constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 64;  // keys per tile
 
 // Build-time tuning: 32-query blocks per wave, and the minimum waves per SIMD the register allocation must
-// allow (2 -> at most 256 registers per lane, so two workgroups share a CU).
+// allow (3 -> at most 168 registers per lane).
 #ifndef ATTN_PREFILL_QB
 #define ATTN_PREFILL_QB 1
 #endif
 #ifndef ATTN_PREFILL_MIN_WAVES_PER_SIMD
-#define ATTN_PREFILL_MIN_WAVES_PER_SIMD 2
+#define ATTN_PREFILL_MIN_WAVES_PER_SIMD 3
 #endif
 
 template <int D>
@@ -49,8 +55,6 @@ struct Tile {
   static constexpr int kChunks = D / 8;                  // 16-byte chunks per row
   static constexpr int kRowBytes = D * 2;
   static constexpr int kBytes = kBN * kRowBytes;         // one K or V tile
-  static constexpr int kLoadsPerWave = kBN * kChunks / kThreads;
-  static_assert(kBN * kChunks % kThreads == 0, "tile must split evenly over the workgroup");
 };
 
 struct PrefillArgs {
@@ -83,54 +87,51 @@ __device__ __forceinline__ int swz_key(int r) {
   return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-// Per-lane byte offsets of the direct-to-LDS tile copy by NW waves. Wave instruction i of wave w fills the 64 LDS
-// slots of block i*NW + w; slot -> (row, physical chunk) -> logical chunk (physical ^ swz_key(row)). The offsets
-// are relative to row 0 of the tile and the same for K and V (same layout).
-template <int D, int NW>
+// Per-lane byte offsets of the direct-to-LDS copy of a ROWS-row tile by NW waves. Wave instruction i of wave w
+// fills the 64 LDS slots of block i*NW + w; slot -> (row, physical chunk) -> logical chunk (physical ^
+// swz_key(row)). The offsets are relative to row 0 of the tile and the same for K and V (same layout).
+template <int D, int NW, int ROWS>
 struct TileCopy {
-  static constexpr int kLoads = kBN * Tile<D>::kChunks / (64 * NW);
-  static_assert(kBN * Tile<D>::kChunks % (64 * NW) == 0, "tile must split evenly over the waves");
+  static constexpr int kBlocks = ROWS * Tile<D>::kChunks / 64;   // 64-slot blocks per tile
+  static constexpr int kLoads = (kBlocks + NW - 1) / NW;         // per wave (the last round may be partial)
+  static_assert(ROWS * Tile<D>::kChunks % 64 == 0, "tile must split into 64-slot blocks");
   uint32_t off[kLoads];
-
-  __device__ __forceinline__ static uint32_t byte_off(int row, int slot, int hkv, int g) {
-    const int lchunk = (slot % Tile<D>::kChunks) ^ swz_key<D>(slot / Tile<D>::kChunks);
-    return uint32_t(((row * hkv + g) * D + lchunk * 8) * 2);
-  }
 
   __device__ __forceinline__ void init(int hkv, int g, int wave, int lane) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int slot = (i * NW + wave) * 64 + lane;
-      off[i] = byte_off(slot / Tile<D>::kChunks, slot, hkv, g);
+      const int row = slot / Tile<D>::kChunks;
+      const int lchunk = (slot % Tile<D>::kChunks) ^ swz_key<D>(row);
+      off[i] = uint32_t(((row * hkv + g) * D + lchunk * 8) * 2);
     }
   }
 
-  // Copy tile rows key0 .. key0+63 of one K or V tensor (`seq` = row 0 of this sequence) into `dst`. Rows at or
-  // past S are clamped to row S-1 (finite data: their scores are masked and P is exactly 0); only the last,
-  // ragged tile takes that path. The buffer resource spans exactly the tile's valid rows.
-  __device__ __forceinline__ void issue(uint16_t* dst, const uint16_t* seq, int key0, int S, int hkv, int g, int wave,
-                                        int lane) const {
-    const int rows = min(kBN, S - key0);
-    const buf_rsrc_t rs = make_buf_rsrc(seq + int64_t(key0) * hkv * D, uint32_t(rows * hkv * D * 2));
-    if (rows == kBN) {
+  // Copy tile rows key0 .. key0+ROWS-1 of one K or V tensor (`seq` = row 0 of this sequence) into `dst`. The
+  // buffer resource spans exactly the rows below S; rows past the end read as zeros (measured: an out-of-range
+  // lane of a buffer load-to-LDS writes 0), which are finite, so their masked scores and P = 0 stay exact.
+  __device__ __forceinline__ void issue(uint16_t* dst, const uint16_t* seq, int key0, int S, int hkv, int wave) const {
+    const int rows = max(0, min(ROWS, S - key0));
+    const buf_rsrc_t rs = make_buf_rsrc(seq + int64_t(min(key0, S - 1)) * hkv * D, uint32_t(rows * hkv * D * 2));
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) load_lds16(rs, off[i], dst + (i * NW + wave) * 512);
-    } else {
-#pragma unroll
-      for (int i = 0; i < kLoads; ++i) {
-        const int slot = (i * NW + wave) * 64 + lane;
-        load_lds16(rs, byte_off(min(slot / Tile<D>::kChunks, rows - 1), slot, hkv, g), dst + (i * NW + wave) * 512);
-      }
-    }
+    for (int i = 0; i < kLoads; ++i)
+      if (kBlocks % NW == 0 || i * NW + wave < kBlocks) load_lds16(rs, off[i], dst + (i * NW + wave) * 512);
   }
 };
+
+// 64-key sub-tiles per LDS tile (one barrier and one copy round per tile).
+#ifndef ATTN_PREFILL_SUB
+#define ATTN_PREFILL_SUB 1
+#endif
+constexpr int kSub = ATTN_PREFILL_SUB;
+constexpr int kTileKeys = kSub * kBN;
 
 template <int D, int QB>
 __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int QW = 32 * QB;
   constexpr int KS = D / 16;   // k-steps of the QK^T contraction
   constexpr int DB = D / 32;   // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kBN * D];   // [buffer][K, V]
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTileKeys * D];   // [buffer][K, V]
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar register)
   const int lane = threadIdx.x & 63;
@@ -144,15 +145,16 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   const int grp = a.hq / a.hkv;
   int h, qpos0, wg_pos0, wg_span;
   if (a.heads_mode) {
-    h = hgrp * 4 + wave; wg_pos0 = pblk * QW; qpos0 = wg_pos0; wg_span = QW;
+    h = hgrp * 4 + (wave & 3); wg_pos0 = pblk * kPosBlocks * QW; qpos0 = wg_pos0 + (wave >> 2) * QW;
+    wg_span = kPosBlocks * QW;
   } else {
-    h = hgrp; wg_pos0 = pblk * 4 * QW; qpos0 = wg_pos0 + wave * QW; wg_span = 4 * QW;
+    h = hgrp; wg_pos0 = pblk * kWaves * QW; qpos0 = wg_pos0 + wave * QW; wg_span = kWaves * QW;
   }
   const int g = h / grp;
   const int S = a.seqlen;
   const int kend_wg = a.causal ? min(S, wg_pos0 + wg_span) : S;
   const int kend_w = a.causal ? min(S, qpos0 + QW) : S;
-  const int ntiles = (kend_wg + kBN - 1) / kBN;
+  const int ntiles = (kend_wg + kTileKeys - 1) / kTileKeys;
   const float c = a.scale * kLog2e;
 
   // ---- Q^T operands, resident for the whole kernel: lane holds query (qpos0 + 32*qb + lq), dims 16*ks + 8*lg ..
@@ -194,16 +196,17 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
     vhi[db] = uint32_t((vrow + 8) * RB + 16 * (ch ^ swz_key<D>(vrow + 8)) + 8 * (bl & 1));
   }
 
-  TileCopy<D, kWaves> cp;
+  TileCopy<D, kWaves, kTileKeys> cp;
   cp.init(a.hkv, g, wave, lane);
   const uint16_t* kseq = a.k + int64_t(b) * S * a.hkv * D;
   const uint16_t* vseq = a.v + int64_t(b) * S * a.hkv * D;
 
   // One 64-key tile from LDS buffer BUF (a compile-time constant, so LDS addresses are base + immediate).
-  auto tile = [&](auto bufc, int key0) {
+  auto tile = [&](auto bufc, auto subc, int key0) {
     constexpr int BUF = decltype(bufc)::value;
-    const uint16_t* Kt = lds[BUF][0];
-    const uint16_t* Vt = lds[BUF][1];
+    constexpr int SUB = decltype(subc)::value;
+    const uint16_t* Kt = lds[BUF][0] + SUB * kBN * D;
+    const uint16_t* Vt = lds[BUF][1] + SUB * kBN * D;
 
     // ---- S^T = K Q^T for 64 keys (two 32-key blocks)
     f32x16_t sacc[QB][2];
@@ -288,25 +291,33 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
     }
   };
 
-  cp.issue(lds[0][0], kseq, 0, S, a.hkv, g, wave, lane);
-  cp.issue(lds[0][1], vseq, 0, S, a.hkv, g, wave, lane);
+  // All sub-tiles of one LDS tile (compile-time buffer and sub-tile indices, so LDS addresses are immediates);
+  // sub-tiles entirely above this wave's diagonal are skipped.
+  auto tiles = [&](auto bufc, int t) {
+    tile(bufc, std::integral_constant<int, 0>{}, t * kTileKeys);
+    if (kSub > 1 && t * kTileKeys + kBN < kend_w) tile(bufc, std::integral_constant<int, kSub - 1>{}, t * kTileKeys + kBN);
+  };
+  static_assert(kSub == 1 || kSub == 2, "one or two sub-tiles per LDS tile");
+
+  cp.issue(lds[0][0], kseq, 0, S, a.hkv, wave);
+  cp.issue(lds[0][1], vseq, 0, S, a.hkv, wave);
   // Two tiles per trip so each tile's LDS buffer is a compile-time constant.
   for (int t = 0; t < ntiles; t += 2) {
     wait_vmem();
     __syncthreads();                                   // tile t visible to all; buffer 1 free
     if (t + 1 < ntiles) {
-      cp.issue(lds[1][0], kseq, (t + 1) * kBN, S, a.hkv, g, wave, lane);
-      cp.issue(lds[1][1], vseq, (t + 1) * kBN, S, a.hkv, g, wave, lane);
+      cp.issue(lds[1][0], kseq, (t + 1) * kTileKeys, S, a.hkv, wave);
+      cp.issue(lds[1][1], vseq, (t + 1) * kTileKeys, S, a.hkv, wave);
     }
-    if (t * kBN < kend_w) tile(std::integral_constant<int, 0>{}, t * kBN);
+    if (t * kTileKeys < kend_w) tiles(std::integral_constant<int, 0>{}, t);
     if (t + 1 >= ntiles) break;
     wait_vmem();
     __syncthreads();                                   // tile t+1 visible to all; buffer 0 free
     if (t + 2 < ntiles) {
-      cp.issue(lds[0][0], kseq, (t + 2) * kBN, S, a.hkv, g, wave, lane);
-      cp.issue(lds[0][1], vseq, (t + 2) * kBN, S, a.hkv, g, wave, lane);
+      cp.issue(lds[0][0], kseq, (t + 2) * kTileKeys, S, a.hkv, wave);
+      cp.issue(lds[0][1], vseq, (t + 2) * kTileKeys, S, a.hkv, wave);
     }
-    if ((t + 1) * kBN < kend_w) tile(std::integral_constant<int, 1>{}, (t + 1) * kBN);
+    if ((t + 1) * kTileKeys < kend_w) tiles(std::integral_constant<int, 1>{}, t + 1);
   }
 
   // ---- epilogue: O = O^T / l (lane holds query lq, dims 32*db + 8*(r/4) + 4*lg + r%4), lse = scale*m + ln l
@@ -408,7 +419,7 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   a.batch = batch; a.seqlen = seqlen; a.hq = hq; a.hkv = hkv; a.scale = scale; a.causal = causal;
   const int grp = hq / hkv;
   a.heads_mode = (grp % 4 == 0) ? 1 : 0;
-  const int span = a.heads_mode ? QW : 4 * QW;
+  const int span = a.heads_mode ? kPosBlocks * QW : kWaves * QW;
   a.n_pblk = (seqlen + span - 1) / span;
   a.n_hgrp = a.heads_mode ? hq / 4 : hq;
   const int64_t blocks = int64_t(a.n_pblk) * batch * a.n_hgrp;
