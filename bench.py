@@ -100,11 +100,12 @@ def roofline_compute(flops, ms, kernel, workload):
             "kernel_ms": round(ms, 4)}
 
 
-def roofline_hbm(nbytes, ms, kernel, workload):
+def roofline_hbm(nbytes, ms, kernel, workload, timed=None):
+    """`ms` times one library call; `timed` names the kernels it launches when there is more than `kernel`."""
     achieved = nbytes / (ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic_for(kernel, workload), "kernel": kernel,
-            "kernel_ms": round(ms, 4)}
+            "timed": timed or kernel, "kernel_ms": round(ms, 4)}
 
 
 # --------------------------------------------------------------------------------------------------- prefill --
@@ -242,7 +243,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # Warm-up long enough (about 0.1 s of work) for the GPU clock to settle before the timed steps.
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-secondary", action="store_true", help="only the primary prefill workload")
     ap.add_argument("--workloads", default="prefill,decode,mla,long",
                     help="comma list of prefill (primary), decode, mla, long; profiling runs select one")
@@ -306,18 +308,20 @@ def main():
 def run_secondary(torch, ta, args, sel, line):
     if "decode" in sel:
         wd = WORKLOADS["paged_decode_b64"]
-        ms, nbytes, tokens = bench_decode(torch, ta, wd, max(5, args.steps), args.warmup)
+        ms, nbytes, tokens = bench_decode(torch, ta, wd, max(20, args.steps), max(100, args.warmup))
         line["paged_decode"] = {"workload": wd.name, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                                 "ms": round(ms, 4), "bytes": nbytes, "tokens": tokens,
-                                "roofline": roofline_hbm(nbytes, ms, "decode_paged_split_kernel", wd.name)}
+                                "roofline": roofline_hbm(nbytes, ms, "decode_paged_split_kernel", wd.name,
+                                                         "decode_paged_split_kernel + decode_combine_kernel")}
     if "mla" in sel:
         wm = WORKLOADS["mla_decode_b32"]
-        ms = bench_mla(torch, ta, wm, max(5, args.steps), args.warmup)
+        ms = bench_mla(torch, ta, wm, max(20, args.steps), max(300, args.warmup))
         nbytes = mla_bytes(wm)
         line["mla_decode"] = {"workload": wm.name, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                               "ms": round(ms, 4), "bytes": nbytes,
                               "tflops": round(mla_flops(wm) / (ms * 1e-3) / 1e12, 1),
-                              "roofline": roofline_hbm(nbytes, ms, "mla_split_kernel", wm.name)}
+                              "roofline": roofline_hbm(nbytes, ms, "mla_split_kernel", wm.name,
+                                                       "mla_split_kernel + mla_combine_kernel")}
     if "long" in sel:
         wl = WORKLOADS["gqa_prefill_s131072"]
         wall_l, kern_l = bench_prefill(torch, ta, wl, 2, 1)
