@@ -222,9 +222,12 @@ __global__ __launch_bounds__(kD) void decode_combine_kernel(const float* __restr
     if (lse && d == 0) lse[int64_t(b) * hq + h] = -INFINITY;
     return;
   }
+  // Unrolled so that several independent partial loads are in flight (the loop is latency-bound otherwise).
   float mx = -INFINITY;
+#pragma unroll 8
   for (int ci = 0; ci < nc; ++ci) mx = fmaxf(mx, ws_lse[base + ci]);
   float acc = 0.f, wsum = 0.f;
+#pragma unroll 8
   for (int ci = 0; ci < nc; ++ci) {
     const float w = expf(ws_lse[base + ci] - mx);
     wsum += w;

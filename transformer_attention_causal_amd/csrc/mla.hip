@@ -289,9 +289,12 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
     if (lse && threadIdx.x == 0) lse[int64_t(b) * heads + h] = -INFINITY;
     return;
   }
+  // Unrolled so that several independent partial loads are in flight (the loop is latency-bound otherwise).
   float mx = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ws_lse[base + s]);
   float a0 = 0.f, a1 = 0.f, wsum = 0.f;
+#pragma unroll 8
   for (int s = 0; s < ns; ++s) {
     const float w = expf(ws_lse[base + s] - mx);
     wsum += w;

@@ -39,7 +39,14 @@ namespace {
 constexpr int kWaves = ATTN_PREFILL_WAVES;
 constexpr int kPosBlocks = kWaves / 4;   // 32-position blocks per workgroup in heads mode
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBN = 64;  // keys per tile
+// Keys per compute tile (32 or 64).
+#ifndef ATTN_PREFILL_BN
+#define ATTN_PREFILL_BN 64
+#endif
+constexpr int kBN = ATTN_PREFILL_BN;
+constexpr int kKB2 = kBN / 32;   // 32-key blocks of S^T per tile
+constexpr int kKB = kBN / 16;    // 16-key contraction blocks of P.V per tile
+static_assert(kBN == 32 || kBN == 64, "tile of 32 or 64 keys");
 
 // Build-time tuning: 32-query blocks per wave, and the minimum waves per SIMD the register allocation must
 // allow (3 -> at most 168 registers per lane).
@@ -201,21 +208,23 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   const uint16_t* kseq = a.k + int64_t(b) * S * a.hkv * D;
   const uint16_t* vseq = a.v + int64_t(b) * S * a.hkv * D;
 
-  // One 64-key tile from LDS buffer BUF (a compile-time constant, so LDS addresses are base + immediate).
+  // One kBN-key tile from LDS buffer BUF (a compile-time constant, so LDS addresses are base + immediate).
   auto tile = [&](auto bufc, auto subc, int key0) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr int SUB = decltype(subc)::value;
     const uint16_t* Kt = lds[BUF][0] + SUB * kBN * D;
     const uint16_t* Vt = lds[BUF][1] + SUB * kBN * D;
 
-    // ---- S^T = K Q^T for 64 keys (two 32-key blocks)
-    f32x16_t sacc[QB][2];
+    // ---- S^T = K Q^T for the tile's keys (32-key blocks kb2)
+    f32x16_t sacc[QB][kKB2];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) { sacc[qb][0] = f32x16_t{}; sacc[qb][1] = f32x16_t{}; }
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb2 = 0; kb2 < kKB2; ++kb2) sacc[qb][kb2] = f32x16_t{};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < kKB2; ++kb2) {
         // row 32*kb2 + lq, 16-byte chunk 2*ks + lg
         const bf16x8_t ka = as_bf16x8(lds_read16(Kt, kbase[ks] + 32 * kb2 * RB));
 #pragma unroll
@@ -229,7 +238,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
       for (int qb = 0; qb < QB; ++qb) {
         const int qpos = qpos0 + 32 * qb + lq;
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < kKB2; ++kb2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = key0 + 32 * kb2 + 8 * (r >> 2) + 4 * lg + (r & 3);
@@ -239,12 +248,12 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
     }
 
     // ---- online softmax (one query per lane; partner lane l ^ 32 holds the other 16 keys)
-    bf16x8_t pb[QB][4];
+    bf16x8_t pb[QB][kKB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < kKB2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[qb][kb2][r]);
       mx = max_xor32(mx);
@@ -260,7 +269,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
       }
       const float mc = m[qb] * c;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < kKB2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float p = fast_exp2(fmaf(sacc[qb][kb2][r], c, -mc));
@@ -268,7 +277,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
           l[qb] += p;
         }
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < kKB; ++kb) {
         const f32x16_t& s = sacc[qb][kb >> 1];
         const int o8 = 8 * (kb & 1);
         pb[qb][kb] = pack_bf16x8(s[o8], s[o8 + 1], s[o8 + 2], s[o8 + 3], s[o8 + 4], s[o8 + 5], s[o8 + 6], s[o8 + 7]);
@@ -277,7 +286,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
 
     // ---- O^T += V^T P^T: V^T fragments by transposing LDS reads, keys in the same order as the P^T slots
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
+    for (int kb = 0; kb < kKB; ++kb) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         // rows 16*kb + vrow (+8), columns 32*db + vcol
