@@ -26,7 +26,13 @@ namespace attn {
 namespace {
 
 constexpr int kD = 128;
+static_assert(kDecodeChunk % 32 == 0 && kDecodeChunk / 16 <= 64, "a chunk's pages (>= 16 keys each) fit one wave");
 
+// Grid order: 1 = the KV heads of one chunk are consecutive workgroups (they read interleaved 256-byte pieces
+// of the same page slots at the same time); 0 = the chunks of one head are consecutive.
+#ifndef ATTN_DECODE_HEAD_MAJOR
+#define ATTN_DECODE_HEAD_MAJOR 0
+#endif
 // Build-time choice: software-prefetch the next 32 keys' K/V while computing on the current ones.
 #ifndef ATTN_DECODE_PREFETCH
 #define ATTN_DECODE_PREFETCH 0
@@ -57,7 +63,11 @@ __device__ __forceinline__ bf16x8_t transpose_pick(const u32x4_t* vv, int j) {
 }
 
 __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
+#if ATTN_DECODE_HEAD_MAJOR
+  const int g = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
+#else
   const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+#endif
   const int page_size = 1 << a.page_shift;
   const int L = clamp_len(a.seq_lens[b], a.max_len, a.max_pages * page_size);
   const int t_begin = chunk * kDecodeChunk;
@@ -82,6 +92,11 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
   for (int j = 0; j < 8; ++j) oacc[j] = f32x4_t{};
   float m = -INFINITY, l = 0.f;
   const int32_t* trow = a.table + int64_t(b) * a.max_pages;
+  // The chunk's page numbers, read once: lane i holds the entry of the chunk's i-th page (a chunk spans at most
+  // 512/16 = 32 pages), fetched per 16 keys with a lane read instead of a dependent table load per iteration.
+  const int first_page = t_begin >> a.page_shift;
+  const int last_page = (t_end - 1) >> a.page_shift;
+  const int pg_lane = (lane <= last_page - first_page) ? trow[first_page + lane] : -1;
   const int64_t row_stride = int64_t(a.hkv) * kD;           // elements between consecutive slots of a page
   const int64_t page_stride = int64_t(page_size) * row_stride;
 
@@ -94,7 +109,7 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int tt = min(t0 + 16 * hf, t_end - 1);
-      pg[hf] = trow[tt >> a.page_shift];
+      pg[hf] = __builtin_amdgcn_readlane(pg_lane, (tt >> a.page_shift) - first_page);
       pv[hf] = pg[hf] >= 0 && pg[hf] < a.num_pages;
     }
 #pragma unroll
@@ -268,7 +283,9 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
   a.page_shift = shift; a.max_pages = max_pages_per_seq; a.max_len = max_seqlen_kv; a.n_chunks = n_chunks;
   a.num_pages = num_pages; a.scale = scale;
   if (max_seqlen_kv > 0)
-    decode_paged_split_kernel<<<dim3(unsigned(n_chunks), unsigned(hkv), unsigned(batch)), dim3(64), 0, stream>>>(a);
+    decode_paged_split_kernel<<<ATTN_DECODE_HEAD_MAJOR ? dim3(unsigned(hkv), unsigned(n_chunks), unsigned(batch))
+                                                       : dim3(unsigned(n_chunks), unsigned(hkv), unsigned(batch)),
+                                dim3(64), 0, stream>>>(a);
   decode_combine_kernel<<<dim3(unsigned(hq), unsigned(batch)), dim3(kD), 0, stream>>>(
       a.ws_o, a.ws_lse, seq_lens, static_cast<uint16_t*>(o), lse, hq, n_chunks, max_seqlen_kv,
       max_pages_per_seq * page_size);
