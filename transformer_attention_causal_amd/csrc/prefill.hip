@@ -37,7 +37,13 @@ namespace {
 #define ATTN_PREFILL_WAVES 12
 #endif
 constexpr int kWaves = ATTN_PREFILL_WAVES;
-constexpr int kPosBlocks = kWaves / 4;   // 32-position blocks per workgroup in heads mode
+// Query heads per workgroup in heads mode (they share one KV head; the group size must be a multiple).
+#ifndef ATTN_PREFILL_HEADS
+#define ATTN_PREFILL_HEADS 4
+#endif
+constexpr int kHeads = ATTN_PREFILL_HEADS;
+constexpr int kPosBlocks = kWaves / kHeads;   // 32-position blocks per workgroup in heads mode
+static_assert(kWaves % kHeads == 0, "waves split into heads x position blocks");
 constexpr int kThreads = 64 * kWaves;
 // Keys per compute tile (32 or 64).
 #ifndef ATTN_PREFILL_BN
@@ -73,7 +79,7 @@ struct PrefillArgs {
   int batch, seqlen, hq, hkv;
   float scale;
   int causal;
-  int heads_mode;    // 1: 4 heads x QW positions per workgroup; 0: 1 head x 4*QW positions
+  int heads_mode;    // 1: kHeads heads x kPosBlocks*32 positions per workgroup; 0: 1 head x kWaves*32 positions
   int n_pblk;        // position blocks per (batch, head group)
   int n_hgrp;        // head groups: hq/4 in heads mode, hq in positions mode
 };
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   const int grp = a.hq / a.hkv;
   int h, qpos0, wg_pos0, wg_span;
   if (a.heads_mode) {
-    h = hgrp * 4 + (wave & 3); wg_pos0 = pblk * kPosBlocks * QW; qpos0 = wg_pos0 + (wave >> 2) * QW;
+    h = hgrp * kHeads + wave % kHeads; wg_pos0 = pblk * kPosBlocks * QW; qpos0 = wg_pos0 + (wave / kHeads) * QW;
     wg_span = kPosBlocks * QW;
   } else {
     h = hgrp; wg_pos0 = pblk * kWaves * QW; qpos0 = wg_pos0 + wave * QW; wg_span = kWaves * QW;
@@ -427,10 +433,10 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   a.v = static_cast<const uint16_t*>(v); a.o = static_cast<uint16_t*>(o); a.lse = lse;
   a.batch = batch; a.seqlen = seqlen; a.hq = hq; a.hkv = hkv; a.scale = scale; a.causal = causal;
   const int grp = hq / hkv;
-  a.heads_mode = (grp % 4 == 0) ? 1 : 0;
+  a.heads_mode = (grp % kHeads == 0) ? 1 : 0;
   const int span = a.heads_mode ? kPosBlocks * QW : kWaves * QW;
   a.n_pblk = (seqlen + span - 1) / span;
-  a.n_hgrp = a.heads_mode ? hq / 4 : hq;
+  a.n_hgrp = a.heads_mode ? hq / kHeads : hq;
   const int64_t blocks = int64_t(a.n_pblk) * batch * a.n_hgrp;
   const dim3 grid(static_cast<unsigned>(blocks));
   if (head_dim == 128) prefill_bf16_kernel<128, QB><<<grid, dim3(kThreads), 0, stream>>>(a);
