@@ -17,4 +17,6 @@ from .attention import (  # noqa: F401
     decode_paged,
     mla_decode,
     mla_naive,
+    kv_append_paged,
+    prefill_paged,
 )

@@ -21,13 +21,17 @@ Readings taken where the pages are silent or garbled:
   * RoPE pairs are adjacent (2i, 2i+1) by default ([LC] §2.1 views the last dim as (-1, 2)); the half-split
     pairing (i, i + D/2) is available with interleaved=False;
   * RoPE angle = position * theta**(-2i/D) computed directly from the integer position in fp64 ([LC] §2.5);
-  * an empty key set (sequence length 0) gives O = 0 and lse = -inf.
+  * an empty key set (sequence length 0) gives O = 0 and lse = -inf;
+  * chunked prefill from a paged cache: the new tokens of a sequence follow its cached ones, new token i sits at
+    absolute position cache_len + i and sees keys 0 .. cache_len + i ([AN]: later tokens attend to all earlier
+    ones; with fewer queries than keys the mask is aligned to the last query, the bottom-right corner); appended
+    keys are rotated at that absolute position and values are copied unrotated.
 """
 import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64", "rope_inv_freq", "rope", "attention_prefill", "attention_prefill_rows", "gather_paged",
-    "decode_paged", "mla_decode", "mla_naive",
+    "decode_paged", "mla_decode", "mla_naive", "kv_append_paged", "prefill_paged",
 ]
 
 
@@ -217,3 +221,55 @@ def mla_naive(q_nope, q_pe, c_kv, k_pe, w_uk, w_uv, seq_lens, scale):
             ob, _ = _softmax_rows_then_v(sc, v_h)
             o[b, h] = ob[0]
     return o
+
+
+def kv_append_paged(k_cache, v_cache, block_table, cache_lens, k_new, v_new, cu_new, theta, interleaved=True):
+    """Append new tokens to a paged KV cache ([AN] Page Attention: logical token t of a sequence lives in page
+    block_table[b][t // page_size], slot t % page_size). New token i of sequence b (rows cu_new[b] .. cu_new[b+1]-1
+    of k_new / v_new) has absolute position cache_lens[b] + i; its key is rotated at that position ([LC] §2.1, §2.5:
+    the angle comes straight from the integer position) and its value is stored as is.
+
+    k_cache, v_cache: [num_pages, page_size, Hkv, D]; k_new, v_new: [total_new, Hkv, D]; cu_new: [B+1];
+    cache_lens: [B]. Returns new float64 caches (the inputs are not modified); slots not written keep their values.
+    """
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    page_size = kc.shape[1]
+    for b in range(len(cache_lens)):
+        for row in range(int(cu_new[b]), int(cu_new[b + 1])):
+            pos = int(cache_lens[b]) + row - int(cu_new[b])
+            page, slot = int(block_table[b][pos // page_size]), pos % page_size
+            kc[page, slot] = rope(np.asarray(k_new[row], np.float64)[None], np.array([pos]), theta, interleaved)[0]
+            vc[page, slot] = v_new[row]
+    return kc, vc
+
+
+def prefill_paged(q, k_cache, v_cache, block_table, cu_new, cache_lens, scale):
+    """Chunked / variable-length causal prefill against a paged KV cache that already holds, for each sequence b,
+    its cache_lens[b] earlier tokens followed by its n_b = cu_new[b+1] - cu_new[b] new ones. The new tokens are the
+    queries: query i of sequence b (row cu_new[b] + i of q, already rotated) sits at absolute position
+    cache_lens[b] + i and sees keys 0 .. cache_lens[b] + i. Scores are materialised per (sequence, head).
+
+    q: [total_new, Hq, D]; caches: [num_pages, page_size, Hkv, D]. Query head h reads KV head h // (Hq // Hkv).
+    Returns (o [total_new, Hq, D] float64, lse [Hq, total_new] float64).
+    """
+    q = np.asarray(q, np.float64)
+    total, hq, _ = q.shape
+    hkv = k_cache.shape[2]
+    grp = hq // hkv
+    o = np.zeros((total, hq, v_cache.shape[-1]), np.float64)
+    lse = np.zeros((hq, total), np.float64)
+    for b in range(len(cache_lens)):
+        r0, r1 = int(cu_new[b]), int(cu_new[b + 1])
+        n, ctx = r1 - r0, int(cache_lens[b])
+        if n == 0:
+            continue
+        kb = np.asarray(gather_paged(k_cache, block_table[b], ctx + n), np.float64)    # [ctx + n, Hkv, D]
+        vb = np.asarray(gather_paged(v_cache, block_table[b], ctx + n), np.float64)
+        hidden = np.arange(ctx + n)[None, :] > (ctx + np.arange(n))[:, None]           # key after the query
+        for h in range(hq):
+            g = h // grp
+            sc = scale * (q[r0:r1, h, :] @ kb[:, g, :].T)                               # [n, ctx + n]
+            sc[hidden] = -np.inf
+            o[r0:r1, h, :], lse[h, r0:r1] = _softmax_rows_then_v(sc, vb[:, g, :])
+    return o, lse

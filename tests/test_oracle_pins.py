@@ -325,6 +325,127 @@ def test_empty_key_set_gives_zero_and_minus_inf():
     assert np.all(o == 0) and np.all(np.isneginf(lse))
 
 
+# ------------------------------------------------------------------------------ chunked prefill from pages ----
+
+def _paged_multi(seqs_k, seqs_v, page, rng, n_spare=4):
+    """Scatter dense per-sequence K/V [L_b, Hkv, D] into one randomly permuted pool of distinct pages (junk
+    elsewhere); returns caches and the block table (-1 past each sequence's pages)."""
+    n_pages = [(k.shape[0] + page - 1) // page for k in seqs_k]
+    pool = sum(n_pages) + n_spare
+    perm = rng.permutation(pool)
+    kc = rng.standard_normal((pool, page) + seqs_k[0].shape[1:]) * 100
+    vc = rng.standard_normal((pool, page) + seqs_v[0].shape[1:]) * 100
+    table = np.full((len(seqs_k), max(n_pages) + 1), -1)
+    used = 0
+    for b, (k, v) in enumerate(zip(seqs_k, seqs_v)):
+        for j in range(n_pages[b]):
+            phys = perm[used]; used += 1
+            n = min(page, k.shape[0] - j * page)
+            kc[phys, :n] = k[j * page: j * page + n]
+            vc[phys, :n] = v[j * page: j * page + n]
+            table[b, j] = phys
+    return kc, vc, table
+
+
+CHUNKS = [(0, 7), (5, 1), (13, 11), (20, 20), (8, 9)]    # (cached tokens, new tokens) per sequence
+
+
+def _chunked_case(seed, hq=4, hkv=2, d=8, page=8):
+    rng = np.random.default_rng(seed)
+    ks = [rng.standard_normal((c + n, hkv, d)) for c, n in CHUNKS]
+    vs = [rng.standard_normal((c + n, hkv, d)) for c, n in CHUNKS]
+    qs = [rng.standard_normal((c + n, hq, d)) for c, n in CHUNKS]
+    kc, vc, table = _paged_multi(ks, vs, page, rng)
+    cu = np.concatenate([[0], np.cumsum([n for _, n in CHUNKS])])
+    ctx = np.array([c for c, _ in CHUNKS])
+    q_new = np.concatenate([qs[b][c:] for b, (c, _) in enumerate(CHUNKS)])
+    return ks, vs, qs, kc, vc, table, cu, ctx, q_new
+
+
+def test_chunked_prefill_equals_tail_rows_of_full_prefill():
+    # The last n of c + n tokens as queries against all c + n keys are rows c .. c+n-1 of the ordinary causal
+    # prefill over the whole sequence (where the mask j <= i is exact because Sq == Sk).
+    ks, vs, qs, kc, vc, table, cu, ctx, q_new = _chunked_case(40)
+    o, lse = oracle.prefill_paged(q_new, kc, vc, table, cu, ctx, 0.6)
+    for b, (c, n) in enumerate(CHUNKS):
+        o_ref, lse_ref = oracle.attention_prefill(qs[b][None], ks[b][None], vs[b][None], True, 0.6)
+        np.testing.assert_allclose(o[cu[b]:cu[b + 1]], o_ref[0, c:], atol=1e-12)
+        np.testing.assert_allclose(lse[:, cu[b]:cu[b + 1]], lse_ref[0, :, c:], atol=1e-12)
+
+
+def test_chunked_prefill_of_one_new_token_is_decode():
+    rng = np.random.default_rng(41)
+    lens = [1, 9, 17, 33]
+    ks = [rng.standard_normal((L, 2, 8)) for L in lens]; vs = [rng.standard_normal((L, 2, 8)) for L in lens]
+    kc, vc, table = _paged_multi(ks, vs, 8, rng)
+    q = rng.standard_normal((len(lens), 4, 8))
+    o, lse = oracle.prefill_paged(q, kc, vc, table, np.arange(len(lens) + 1), np.array(lens) - 1, 0.7)
+    o_d, lse_d = oracle.decode_paged(q, kc, vc, table, np.array(lens), 0.7)
+    np.testing.assert_allclose(o, o_d, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_d.T, atol=1e-13)
+
+
+def test_chunked_prefill_brute_force_tiny():
+    # explicit loops: 3 cached + 2 new tokens, one KV head shared by 2 query heads, keys after the query hidden
+    rng = np.random.default_rng(42)
+    k = rng.standard_normal((5, 1, 4)); v = rng.standard_normal((5, 1, 4)); q = rng.standard_normal((2, 2, 4))
+    kc, vc, table = _paged_multi([k], [v], 4, rng)
+    o, lse = oracle.prefill_paged(q, kc, vc, table, np.array([0, 2]), np.array([3]), 0.9)
+    for i in range(2):
+        for h in range(2):
+            w = [math.exp(0.9 * q[i, h] @ k[j, 0]) for j in range(3 + i + 1)]
+            ref = sum(wj * v[j, 0] for j, wj in enumerate(w)) / sum(w)
+            np.testing.assert_allclose(o[i, h], ref, atol=1e-13)
+            assert abs(lse[h, i] - math.log(sum(w))) < 1e-13
+
+
+def test_chunked_prefill_with_no_new_tokens_leaves_other_rows():
+    ks, vs, qs, kc, vc, table, cu, ctx, q_new = _chunked_case(43)
+    cu2 = np.concatenate([cu[:2], cu[1:]])             # insert an empty sequence after the first one
+    table2 = np.concatenate([table[:1], table[:1], table[1:]])
+    ctx2 = np.concatenate([ctx[:1], [4], ctx[1:]])
+    o, lse = oracle.prefill_paged(q_new, kc, vc, table, cu, ctx, 0.5)
+    o2, lse2 = oracle.prefill_paged(q_new, kc, vc, table2, cu2, ctx2, 0.5)
+    np.testing.assert_array_equal(o, o2); np.testing.assert_array_equal(lse, lse2)
+
+
+def test_kv_append_places_rotated_keys_at_absolute_positions():
+    rng = np.random.default_rng(44)
+    page, hkv, d, theta = 8, 2, 8, 500.0
+    ctx = np.array([0, 6, 13]); n = np.array([5, 9, 3])
+    dense_k = [rng.standard_normal((c, hkv, d)) for c in ctx]; dense_v = [rng.standard_normal((c, hkv, d)) for c in ctx]
+    # reserve pages for the final lengths; the cached prefix is already in place
+    full = [np.concatenate([dk, np.zeros((m, hkv, d))]) for dk, m in zip(dense_k, n)]
+    kc, vc, table = _paged_multi(full, [np.concatenate([dv, np.zeros((m, hkv, d))]) for dv, m in zip(dense_v, n)],
+                                 page, rng)
+    k_new = rng.standard_normal((n.sum(), hkv, d)); v_new = rng.standard_normal((n.sum(), hkv, d))
+    cu = np.concatenate([[0], np.cumsum(n)])
+    kc2, vc2 = oracle.kv_append_paged(kc, vc, table, ctx, k_new, v_new, cu, theta)
+    for b in range(3):
+        L = ctx[b] + n[b]
+        kg = oracle.gather_paged(kc2, table[b], L); vg = oracle.gather_paged(vc2, table[b], L)
+        np.testing.assert_array_equal(kg[:ctx[b]], dense_k[b]); np.testing.assert_array_equal(vg[:ctx[b]], dense_v[b])
+        # one vectorised rotation of the whole new block at positions ctx .. ctx+n-1
+        np.testing.assert_allclose(kg[ctx[b]:], oracle.rope(k_new[cu[b]:cu[b + 1]], np.arange(ctx[b], L), theta),
+                                   atol=1e-14)
+        np.testing.assert_array_equal(vg[ctx[b]:], v_new[cu[b]:cu[b + 1]])
+    used = set(table[table >= 0].tolist())
+    for p in range(kc.shape[0]):
+        if p not in used:
+            np.testing.assert_array_equal(kc2[p], kc[p]); np.testing.assert_array_equal(vc2[p], vc[p])
+
+
+def test_kv_append_in_two_chunks_equals_one():
+    rng = np.random.default_rng(45)
+    kc = rng.standard_normal((6, 4, 1, 4)); vc = rng.standard_normal((6, 4, 1, 4))
+    table = np.array([[4, 1, 5, 0]])
+    k_new = rng.standard_normal((9, 1, 4)); v_new = rng.standard_normal((9, 1, 4))
+    one = oracle.kv_append_paged(kc, vc, table, np.array([3]), k_new, v_new, np.array([0, 9]), 1000.0)
+    a = oracle.kv_append_paged(kc, vc, table, np.array([3]), k_new[:4], v_new[:4], np.array([0, 4]), 1000.0)
+    two = oracle.kv_append_paged(a[0], a[1], table, np.array([7]), k_new[4:], v_new[4:], np.array([0, 5]), 1000.0)
+    np.testing.assert_array_equal(one[0], two[0]); np.testing.assert_array_equal(one[1], two[1])
+
+
 # ------------------------------------------------------------------------------------------------------ MLA ----
 
 def test_mla_absorbed_equals_naive_up_projection():
