@@ -1,10 +1,12 @@
 /* attn.h — C ABI of libattn: exact attention with RoPE on MI355X (gfx950).
  *
- * Four operations:
- *   attn_rope_apply    rotary position embedding, in place
- *   attn_prefill       causal (or full) grouped-query attention over a whole sequence
- *   attn_decode_paged  one query token per sequence against a paged KV cache (split-KV + log-sum-exp combine)
- *   attn_mla_decode    multi-head latent attention decode in the absorbed form
+ * Operations:
+ *   attn_rope_apply       rotary position embedding, in place
+ *   attn_prefill          causal (or full) grouped-query attention over a whole sequence
+ *   attn_decode_paged     one query token per sequence against a paged KV cache (split-KV + log-sum-exp combine)
+ *   attn_mla_decode       multi-head latent attention decode in the absorbed form
+ *   attn_kv_append_paged  write new tokens' keys (rotated) and values into a paged KV cache
+ *   attn_prefill_paged    chunked / variable-length causal prefill of new tokens against a paged KV cache
  *
  * Every result is the exact softmax attention O = softmax(scale * Q K^T [+ mask]) V. The kernels compute it
  * FlashAttention-style: scores are formed tile by tile on chip, an online softmax keeps a running row max m and
@@ -137,6 +139,49 @@ int attn_mla_decode(const void* q_latent, const void* q_pe, const void* c_kv, co
                     const int32_t* seq_lens, void* o_latent, float* lse, int batch, int n_heads, int kv_lora_rank,
                     int rope_dim, int max_seqlen_kv, float softmax_scale, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* Append new tokens to a paged KV cache, rotating the keys.
+ * (Attention notes, makinaruto.github.io, "Page Attention": logical token t of a sequence lives in physical page
+ *  block_table[t / page_size], slot t % page_size; DeepSeek 32K to 256K long context, tqpw.cn, sections 2.1 and
+ *  2.5: RoPE at the token's integer position.)
+ *   k_new, v_new  [total_new, n_heads_kv, head_dim] bf16: the new tokens of all sequences, packed in order; the rows
+ *                 of sequence b are cu_new[b] .. cu_new[b+1]-1. 16-byte aligned.
+ *   cu_new       [batch + 1] int32, non-decreasing, cu_new[0] = 0, cu_new[batch] = total_new.
+ *   cache_lens   [batch] int32 >= 0: tokens already in sequence b's cache. New row r of sequence b goes to
+ *                absolute position p = cache_lens[b] + r - cu_new[b]: page block_table[b][p / page_size], slot
+ *                p % page_size. Its key is rotated at position p with base `theta` (pairing as attn_rope_apply's
+ *                `interleaved`); its value is copied.
+ *   k_cache, v_cache  [num_pages, page_size, n_heads_kv, head_dim] bf16, written in place (16-byte aligned).
+ *   block_table  [batch, max_pages_per_seq] int32; the entries covering the new positions must name pages in
+ *                [0, num_pages). A row whose page entry is out of range, or whose position is past the table, is
+ *                not written.
+ * Unsupported: head_dim not a multiple of 16 or above 1024, page_size not a power of two. */
+int attn_kv_append_paged(const void* k_new, const void* v_new, const int32_t* cu_new, const int32_t* cache_lens,
+                         void* k_cache, void* v_cache, const int32_t* block_table, int batch, int total_new,
+                         int n_heads_kv, int head_dim, int page_size, int max_pages_per_seq, int64_t num_pages,
+                         double theta, int interleaved, void* stream);
+
+/* Chunked / variable-length causal prefill from a paged KV cache.
+ * The cache already holds, for each sequence b, its cache_lens[b] earlier tokens followed by its
+ * n_b = cu_new[b+1] - cu_new[b] new tokens (attn_kv_append_paged). The new tokens are the queries: query i of
+ * sequence b sits at absolute position cache_lens[b] + i and attends keys 0 .. cache_lens[b] + i. With fewer
+ * queries than keys the causal mask is aligned to the last query (bottom-right). (Attention notes,
+ * makinaruto.github.io: later tokens attend to all earlier ones; "Page Attention" for the cache mapping;
+ * "FlashAttention" / "online-softmax" for the computation.)
+ *   q            [total_new, n_heads_q, head_dim] bf16, already rotated at the absolute positions.
+ *   k_cache, v_cache  [num_pages, page_size, n_heads_kv, head_dim] bf16; block_table [batch, max_pages_per_seq]
+ *                int32, entries covering positions 0 .. cache_lens[b] + n_b - 1 in [0, num_pages) (an entry outside
+ *                that range, or a position past max_pages_per_seq * page_size, reads as zero keys and values).
+ *   cu_new, cache_lens  as for attn_kv_append_paged.
+ *   max_new      >= every n_b (and <= total_new): sizes the grid; rows of queries past max_new are not written.
+ *   o            [total_new, n_heads_q, head_dim] bf16.
+ *   lse          [n_heads_q, total_new] fp32 (natural log) or NULL.
+ * Query head h reads KV head h / (n_heads_q / n_heads_kv).
+ * Unsupported: head_dim not 64 or 128; page_size not a power of two of at least 64. */
+int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                       const int32_t* cu_new, const int32_t* cache_lens, void* o, float* lse, int batch, int total_new,
+                       int max_new, int n_heads_q, int n_heads_kv, int head_dim, int page_size, int max_pages_per_seq,
+                       int64_t num_pages, float softmax_scale, void* stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* attn_status_string(int status);

@@ -127,3 +127,42 @@ def mla_inputs(w: MLADecode, seed=0, batch=None, seqlen=None, seq_lens=None):
     k_pe = normal(seed, "mla.k_pe", (b, t, w.rope), "bf16")
     lens = np.full(b, t, dtype=np.int32) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
     return dict(q_lat=q_lat, q_pe=q_pe, c_kv=c_kv, k_pe=k_pe, seq_lens=lens)
+
+
+def chunked_prefill_inputs(w, seed=0, ctx_lens=None, new_lens=None, page_size=None, hq=None, hkv=None,
+                           head_dim=None):
+    """A paged cache holding ctx_lens[b] tokens per sequence (already-rotated keys: the N(0,1) values), placed by a
+    seeded random block table with room for the new tokens, plus the new tokens' q, k, v (not yet rotated).
+
+    Returns dict with q [T, Hq, D], k_new / v_new [T, Hkv, D] (T = total new tokens, sequences packed in order),
+    k_cache / v_cache [N_pool, page, Hkv, D], block_table [B, max_pages] int32 (-1 unused), cu_new [B+1],
+    ctx_lens [B], positions [T] (absolute position of each new token), spare_pages, max_new.
+    """
+    ctx = np.asarray(w.ctx_lens if ctx_lens is None else ctx_lens, dtype=np.int32)
+    new = np.asarray(w.new_lens if new_lens is None else new_lens, dtype=np.int32)
+    ps = w.page_size if page_size is None else page_size
+    hq = w.hq if hq is None else hq
+    hkv = w.hkv if hkv is None else hkv
+    d = w.head_dim if head_dim is None else head_dim
+    b = ctx.size
+    total = (ctx + new).astype(np.int64)
+    n_pages = (total + ps - 1) // ps
+    max_pages = max(1, int(n_pages.max(initial=1)))
+    n_used = int(n_pages.sum())
+    n_pool = n_used + int(np.ceil(n_used * w.spare_frac)) + 1
+    perm = _rng(seed, "chunked.perm").permutation(n_pool).astype(np.int32)
+    table = np.full((b, max_pages), -1, dtype=np.int32)
+    off = 0
+    for i in range(b):
+        table[i, : n_pages[i]] = perm[off: off + n_pages[i]]
+        off += int(n_pages[i])
+    cu = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    t = int(cu[-1])
+    positions = np.concatenate([np.arange(c, c + n) for c, n in zip(ctx, new)] or [np.zeros(0)]).astype(np.int32)
+    return dict(q=normal(seed, "chunked.q", (t, hq, d), "bf16"),
+                k_new=normal(seed, "chunked.k_new", (t, hkv, d), "bf16"),
+                v_new=normal(seed, "chunked.v_new", (t, hkv, d), "bf16"),
+                k_cache=normal(seed, "chunked.k", (n_pool, ps, hkv, d), "bf16"),
+                v_cache=normal(seed, "chunked.v", (n_pool, ps, hkv, d), "bf16"),
+                block_table=table, cu_new=cu, ctx_lens=ctx, positions=positions,
+                spare_pages=np.sort(perm[off:]), max_new=int(new.max(initial=0)))

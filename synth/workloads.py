@@ -1,4 +1,4 @@
-"""The five workloads: shapes, RoPE base and softmax scale, as constants.
+"""The workloads: shapes, RoPE base and softmax scale, as constants.
 
 Nothing here computes attention. A workload is named by what it is; `WORKLOADS` maps the short name to its
 description. Long-context RoPE uses the NTK-scaled base 10000 * 4**(128/126) (the base stretched for a 4x longer
@@ -55,6 +55,33 @@ class MLADecode:
     scale: float
 
 
+@dataclass(frozen=True)
+class ChunkedPrefill:
+    """New tokens of several sequences appended to a paged cache that already holds ctx_lens[b] tokens each, then
+    attending (causally, bottom-right aligned) to everything before them."""
+    name: str
+    hq: int
+    hkv: int
+    head_dim: int
+    page_size: int
+    ctx_lens: tuple        # tokens already cached per sequence
+    new_lens: tuple        # new tokens per sequence (the queries)
+    theta: float
+    scale: float
+    spare_frac: float = 0.125
+
+    @property
+    def batch(self):
+        return len(self.ctx_lens)
+
+    @property
+    def flops(self):
+        """Algorithmic flops: QK^T and PV at 2 flop per multiply-add over the unmasked (query, key) pairs; new token
+        i of a sequence with c cached tokens sees c + i + 1 keys."""
+        pairs = sum(n * c + n * (n + 1) // 2 for c, n in zip(self.ctx_lens, self.new_lens))
+        return 4 * self.hq * self.head_dim * pairs
+
+
 WORKLOADS = {
     "mha_fp32_s256": Prefill("mha_fp32_s256", batch=1, seqlen=256, hq=4, hkv=4, head_dim=64, dtype="fp32",
                              theta=10000.0, scale=1.0 / math.sqrt(64)),
@@ -64,6 +91,9 @@ WORKLOADS = {
                                     len_lo=1024, len_hi=32768, theta=10000.0, scale=1.0 / math.sqrt(128)),
     "mla_decode_b32": MLADecode("mla_decode_b32", batch=32, heads=128, latent=512, rope=64, seqlen=32768,
                                 scale=1.0 / math.sqrt(192)),
+    "chunked_prefill_b4": ChunkedPrefill("chunked_prefill_b4", hq=32, hkv=8, head_dim=128, page_size=64,
+                                         ctx_lens=(0, 4096, 8192, 14336), new_lens=(2048, 2048, 2048, 2048),
+                                         theta=10000.0, scale=1.0 / math.sqrt(128)),
     "gqa_prefill_s131072": Prefill("gqa_prefill_s131072", batch=1, seqlen=131072, hq=32, hkv=8, head_dim=128,
                                    dtype="bf16", theta=10000.0 * 4.0 ** (128.0 / 126.0),
                                    scale=1.0 / math.sqrt(128), sampled_rows=256),

@@ -154,3 +154,40 @@ def test_binding_refuses_without_library(tmp_path):
             binding.load_library(str(tmp_path / "missing.so"))
     finally:
         binding._lib = saved
+
+
+def test_kv_append_validation(lib):
+    f = lib.attn_kv_append_paged
+    A = ctypes.c_void_p(0x10000)                    # 16-byte aligned fake pointer (never dereferenced)
+    U = ctypes.c_void_p(0x10008)                    # misaligned
+    args = lambda **kw: [kw.get(n, d) for n, d in [
+        ("k_new", A), ("v_new", A), ("cu", FAKE), ("lens", FAKE), ("kc", A), ("vc", A), ("table", FAKE),
+        ("batch", 2), ("total", 10), ("hkv", 8), ("d", 128), ("page", 64), ("maxp", 4), ("npages", 16),
+        ("theta", 10000.0), ("inter", 1), ("stream", NULL)]]
+    assert f(*args(d=127)) == INVALID
+    assert f(*args(batch=-1)) == INVALID
+    assert f(*args(theta=0.5)) == INVALID
+    assert f(*args(k_new=NULL)) == INVALID
+    assert f(*args(k_new=U)) == INVALID               # rows must be 16-byte aligned
+    assert f(*args(npages=0)) == INVALID
+    assert f(*args(d=72)) == UNSUPPORTED              # not a multiple of 16
+    assert f(*args(page=48)) == UNSUPPORTED           # not a power of two
+    assert f(*args(total=0, k_new=NULL)) == OK        # nothing to append
+
+
+def test_prefill_paged_validation(lib):
+    f = lib.attn_prefill_paged
+    args = lambda **kw: [kw.get(n, d) for n, d in [
+        ("q", FAKE), ("kc", FAKE), ("vc", FAKE), ("table", FAKE), ("cu", FAKE), ("lens", FAKE), ("o", FAKE),
+        ("lse", NULL), ("batch", 2), ("total", 100), ("maxnew", 60), ("hq", 32), ("hkv", 8), ("d", 128),
+        ("page", 64), ("maxp", 8), ("npages", 32), ("scale", 0.088), ("stream", NULL)]]
+    assert f(*args(hq=30)) == INVALID                 # Hq % Hkv
+    assert f(*args(scale=0.0)) == INVALID
+    assert f(*args(maxnew=101)) == INVALID            # more than the total
+    assert f(*args(q=NULL)) == INVALID
+    assert f(*args(cu=NULL)) == INVALID
+    assert f(*args(npages=0)) == INVALID
+    assert f(*args(d=96)) == UNSUPPORTED
+    assert f(*args(page=32)) == UNSUPPORTED           # tiles of 64 keys may not straddle pages
+    assert f(*args(page=96)) == UNSUPPORTED
+    assert f(*args(total=0, maxnew=0, q=NULL)) == OK

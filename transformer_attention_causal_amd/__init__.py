@@ -1,5 +1,5 @@
-"""Exact attention on MI355X (gfx950): RoPE, causal grouped-query prefill, paged-KV decode and MLA absorbed decode,
-as hand-written HIP kernels behind a C ABI (include/attn.h). This package holds the kernels (csrc/), the build
+"""Exact attention on MI355X (gfx950): RoPE, causal grouped-query prefill, paged-KV decode, MLA absorbed decode, and
+chunked prefill from a paged cache with RoPE-on-append, as hand-written HIP kernels behind a C ABI (include/attn.h). This package holds the kernels (csrc/), the build
 step (build.py) and a thin ctypes binding with the same entry-point names (binding.py).
 """
 from .binding import (  # noqa: F401
@@ -8,9 +8,11 @@ from .binding import (  # noqa: F401
     SIGNATURES,
     attn_decode_paged,
     attn_decode_paged_workspace_size,
+    attn_kv_append_paged,
     attn_mla_decode,
     attn_mla_decode_workspace_size,
     attn_prefill,
+    attn_prefill_paged,
     attn_rope_apply,
     load_library,
 )

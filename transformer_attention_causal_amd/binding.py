@@ -26,6 +26,8 @@ SIGNATURES = {
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _I, _F, _P, _SZ, _P]),
     "attn_mla_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "attn_mla_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
+    "attn_kv_append_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _D, _I, _P]),
+    "attn_prefill_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I64, _F, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -170,4 +172,45 @@ def attn_mla_decode(q_latent, q_pe, c_kv, k_pe, seq_lens, softmax_scale, o=None,
         _dev(seq_lens, "seq_lens", torch.int32), _dev(o, "o_latent", torch.bfloat16), lse_p, bsz, nh, c, r, t,
         float(softmax_scale), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(q_latent, stream)))
+    return (o, lse) if return_lse else o
+
+
+def attn_kv_append_paged(k_new, v_new, cu_new, cache_lens, k_cache, v_cache, block_table, theta, interleaved=True,
+                         stream=None):
+    """Write new rows k_new/v_new [total_new, Hkv, D] bf16 into the paged caches [num_pages, page, Hkv, D] bf16 at
+    positions cache_lens[b] + i (keys rotated with base theta); cu_new [B+1] and cache_lens [B] are int32 device
+    tensors, block_table [B, max_pages] int32. The caches are updated in place."""
+    lib = load_library()
+    total, hkv, d = k_new.shape
+    num_pages, page = k_cache.shape[0], k_cache.shape[1]
+    if v_new.shape != k_new.shape or k_cache.shape[2:] != (hkv, d) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_new/v_new [total, Hkv, D] and caches [num_pages, page, Hkv, D] must agree")
+    _check("attn_kv_append_paged", lib.attn_kv_append_paged(
+        _dev(k_new, "k_new", torch.bfloat16), _dev(v_new, "v_new", torch.bfloat16), _dev(cu_new, "cu_new", torch.int32),
+        _dev(cache_lens, "cache_lens", torch.int32), _dev(k_cache, "k_cache", torch.bfloat16),
+        _dev(v_cache, "v_cache", torch.bfloat16), _dev(block_table, "block_table", torch.int32), cu_new.numel() - 1,
+        total, hkv, d, page, block_table.shape[1], num_pages, float(theta), 1 if interleaved else 0,
+        _stream(k_new, stream)))
+    return k_cache, v_cache
+
+
+def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_new, cache_lens, max_new, softmax_scale=None, o=None,
+                       lse=None, return_lse=False, stream=None):
+    """q [total_new, Hq, D] bf16 (rotated at absolute positions) against the paged caches that already hold each
+    sequence's cache_lens[b] earlier tokens plus its new ones. Returns o [total_new, Hq, D] bf16 (and lse
+    [Hq, total_new] fp32). max_new (host int) must be at least every sequence's number of new tokens."""
+    lib = load_library()
+    total, hq, d = q.shape
+    num_pages, page, hkv, _ = k_cache.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, total), dtype=torch.float32, device=q.device)
+    lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
+    _check("attn_prefill_paged", lib.attn_prefill_paged(
+        _dev(q, "q", torch.bfloat16), _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+        _dev(block_table, "block_table", torch.int32), _dev(cu_new, "cu_new", torch.int32),
+        _dev(cache_lens, "cache_lens", torch.int32), _dev(o, "o", torch.bfloat16), lse_p, cu_new.numel() - 1, total,
+        int(max_new), hq, hkv, d, page, block_table.shape[1], num_pages, scale, _stream(q, stream)))
     return (o, lse) if return_lse else o

@@ -105,3 +105,44 @@ ATTN_EXPORT int attn_mla_decode(const void* q_latent, const void* q_pe, const vo
                                             max_seqlen_kv, softmax_scale, workspace,
                                             static_cast<hipStream_t>(stream)));
 }
+
+ATTN_EXPORT int attn_kv_append_paged(const void* k_new, const void* v_new, const int32_t* cu_new,
+                                     const int32_t* cache_lens, void* k_cache, void* v_cache,
+                                     const int32_t* block_table, int batch, int total_new, int n_heads_kv,
+                                     int head_dim, int page_size, int max_pages_per_seq, int64_t num_pages,
+                                     double theta, int interleaved, void* stream) {
+  if (batch < 0 || total_new < 0 || n_heads_kv <= 0 || head_dim <= 0 || (head_dim & 1)) return ATTN_ERR_INVALID_ARG;
+  if (page_size <= 0 || max_pages_per_seq < 0 || num_pages < 0) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(theta) || theta <= 1.0) return ATTN_ERR_INVALID_ARG;
+  if (head_dim % 16 != 0 || head_dim > 1024 || !is_pow2(page_size)) return ATTN_ERR_UNSUPPORTED;
+  if (batch == 0 || total_new == 0) return ATTN_OK;
+  if (!k_new || !v_new || !cu_new || !cache_lens || !k_cache || !v_cache || !block_table) return ATTN_ERR_INVALID_ARG;
+  if (max_pages_per_seq <= 0 || num_pages <= 0) return ATTN_ERR_INVALID_ARG;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(k_new) | reinterpret_cast<uintptr_t>(v_new) |
+                          reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache);
+  if (align % 16 != 0) return ATTN_ERR_INVALID_ARG;
+  return hip_status(attn::launch_kv_append_paged(k_new, v_new, cu_new, cache_lens, k_cache, v_cache, block_table,
+                                                 batch, total_new, n_heads_kv, head_dim, page_size, max_pages_per_seq,
+                                                 num_pages, theta, interleaved ? 1 : 0,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+ATTN_EXPORT int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                   const int32_t* cu_new, const int32_t* cache_lens, void* o, float* lse, int batch,
+                                   int total_new, int max_new, int n_heads_q, int n_heads_kv, int head_dim,
+                                   int page_size, int max_pages_per_seq, int64_t num_pages, float softmax_scale,
+                                   void* stream) {
+  if (batch < 0 || total_new < 0 || max_new < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (n_heads_q % n_heads_kv != 0 || !valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (page_size <= 0 || max_pages_per_seq < 0 || num_pages < 0 || max_new > total_new) return ATTN_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!is_pow2(page_size) || page_size < 64) return ATTN_ERR_UNSUPPORTED;
+  if (batch == 0 || total_new == 0 || max_new == 0) return ATTN_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !cu_new || !cache_lens || !o) return ATTN_ERR_INVALID_ARG;
+  if (max_pages_per_seq <= 0 || num_pages <= 0) return ATTN_ERR_INVALID_ARG;
+  return hip_status(attn::launch_prefill_paged(q, k_cache, v_cache, block_table, cu_new, cache_lens, o, lse, batch,
+                                               total_new, max_new, n_heads_q, n_heads_kv, head_dim, page_size,
+                                               max_pages_per_seq, num_pages, softmax_scale,
+                                               static_cast<hipStream_t>(stream)));
+}

@@ -15,6 +15,17 @@ hipError_t launch_rope(void* x, int dtype, int64_t n_tokens, int n_heads, int he
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
                                int seqlen, int hq, int hkv, int head_dim, int causal, float scale,
                                hipStream_t stream);
+// Chunked / variable-length causal prefill from a paged cache (bf16, head_dim 64 or 128, page size a power of two
+// that is a multiple of 64).
+hipError_t launch_prefill_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                const int32_t* cu_new, const int32_t* ctx_lens, void* o, float* lse, int batch,
+                                int total_new, int max_new, int hq, int hkv, int head_dim, int page_size,
+                                int max_pages_per_seq, int64_t num_pages, float scale, hipStream_t stream);
+// Append new K (rotated at its absolute positions) and V rows to a paged cache (bf16).
+hipError_t launch_kv_append_paged(const void* k_new, const void* v_new, const int32_t* cu_new,
+                                  const int32_t* ctx_lens, void* k_cache, void* v_cache, const int32_t* block_table,
+                                  int batch, int total_new, int hkv, int head_dim, int page_size, int max_pages_per_seq,
+                                  int64_t num_pages, double theta, int interleaved, hipStream_t stream);
 hipError_t launch_prefill_fp32(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
                                int seqlen, int hq, int hkv, int head_dim, int causal, float scale,
                                hipStream_t stream);

@@ -82,6 +82,14 @@ struct PrefillArgs {
   int heads_mode;    // 1: kHeads heads x kPosBlocks*32 positions per workgroup; 0: 1 head x kWaves*32 positions
   int n_pblk;        // position blocks per (batch, head group)
   int n_hgrp;        // head groups: hq/4 in heads mode, hq in positions mode
+  // Chunked prefill from a paged cache (the PAGED kernel): the queries of sequence b are rows cu_new[b] ..
+  // cu_new[b+1]-1 of q and o, query i sits at absolute position ctx_lens[b] + i, and the keys are the first
+  // ctx_lens[b] + n_b tokens of the paged caches [num_pages, page_size, hkv, D]; lse is [hq, total rows].
+  const int32_t* cu_new;
+  const int32_t* ctx_lens;
+  const int32_t* table;
+  int page_shift, max_pages, total_new;
+  int64_t num_pages;
 };
 
 // LDS swizzle: 16-byte chunk c of tile row r is stored at chunk position c ^ swz_key(r). LDS has 64 four-byte
@@ -120,12 +128,11 @@ struct TileCopy {
     }
   }
 
-  // Copy tile rows key0 .. key0+ROWS-1 of one K or V tensor (`seq` = row 0 of this sequence) into `dst`. The
-  // buffer resource spans exactly the rows below S; rows past the end read as zeros (measured: an out-of-range
-  // lane of a buffer load-to-LDS writes 0), which are finite, so their masked scores and P = 0 stay exact.
-  __device__ __forceinline__ void issue(uint16_t* dst, const uint16_t* seq, int key0, int S, int hkv, int wave) const {
-    const int rows = max(0, min(ROWS, S - key0));
-    const buf_rsrc_t rs = make_buf_rsrc(seq + int64_t(min(key0, S - 1)) * hkv * D, uint32_t(rows * hkv * D * 2));
+  // Copy `rows` tile rows starting at `base` (row 0 of the tile, head 0) into `dst`. The buffer resource spans
+  // exactly those rows; the others read as zeros (measured: an out-of-range lane of a buffer load-to-LDS writes 0),
+  // which are finite, so their masked scores and P = 0 stay exact.
+  __device__ __forceinline__ void issue(uint16_t* dst, const uint16_t* base, int rows, int hkv, int wave) const {
+    const buf_rsrc_t rs = make_buf_rsrc(base, uint32_t(max(0, min(ROWS, rows)) * hkv * D * 2));
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
       if (kBlocks % NW == 0 || i * NW + wave < kBlocks) load_lds16(rs, off[i], dst + (i * NW + wave) * 512);
@@ -139,7 +146,82 @@ struct TileCopy {
 constexpr int kSub = ATTN_PREFILL_SUB;
 constexpr int kTileKeys = kSub * kBN;
 
-template <int D, int QB>
+// ---- chunked prefill schedule. Work unit (b, p) of a sequence with S_b new tokens on ctx_b cached ones takes
+// queries p*span .. min(S_b, (p+1)*span) - 1 and reads keys 0 .. kend - 1, kend = ctx_b + min(S_b, (p+1)*span):
+// its cost is proportional to kend, and the contexts (device data) can differ by orders of magnitude between
+// sequences. Rank r picks the unit with the r-th largest kend (ties: lower b first), so the heaviest units start
+// first and the light ones fill the tail. Every wave computes the same answer from wave-wide reductions over the
+// batch (64 sequences per step); no synchronisation, no workspace.
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 32; o; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ bool pick_chunked_unit(const PrefillArgs& a, int span, int r, int& b_out, int& p_out) {
+  const int lane = threadIdx.x & 63;
+  auto seq = [&](int b, int& S, int& ctx) {
+    S = min(a.cu_new[b + 1] - a.cu_new[b], a.seqlen);
+    ctx = max(0, a.ctx_lens[b]);
+  };
+  // number of units with kend > X
+  auto count_above = [&](int X) {
+    int c = 0;
+    for (int b = lane; b < a.batch; b += 64) {
+      int S, ctx;
+      seq(b, S, ctx);
+      if (S > 0 && ctx + S > X) {
+        const int nb = (S + span - 1) / span;
+        c += X < ctx ? nb : max(1, nb - (X - ctx) / span);
+      }
+    }
+    return wave_sum_i(c);
+  };
+  int hi = 0;
+  for (int b = lane; b < a.batch; b += 64) {
+    int S, ctx;
+    seq(b, S, ctx);
+    if (S > 0) hi = max(hi, ctx + S);
+  }
+  hi = wave_max_i(hi);
+  if (r >= count_above(-1)) return false;
+  int lo = 0;                                    // smallest X with count_above(X) <= r is the unit's kend
+  while (lo < hi) {
+    const int mid = lo + (hi - lo) / 2;
+    if (count_above(mid) <= r) hi = mid; else lo = mid + 1;
+  }
+  const int K = lo;
+  int m = r - count_above(K);                    // among the units with kend == K (one per sequence at most)
+  for (int b0 = 0; b0 < a.batch; b0 += 64) {
+    const int b = b0 + lane;
+    bool has = false;
+    int p = 0;
+    if (b < a.batch) {
+      int S, ctx;
+      seq(b, S, ctx);
+      has = S > 0 && ctx < K && K <= ctx + S && (K == ctx + S || (K - ctx) % span == 0);
+      p = (K - ctx + span - 1) / span - 1;
+    }
+    uint64_t mask = __ballot(has);
+    const int cnt = __popcll(mask);
+    if (m < cnt) {
+      for (int i = 0; i < m; ++i) mask &= mask - 1;
+      const int src = __builtin_ctzll(mask);
+      b_out = __builtin_amdgcn_readfirstlane(b0 + src);
+      p_out = __builtin_amdgcn_readfirstlane(__shfl(p, src, 64));
+      return true;
+    }
+    m -= cnt;
+  }
+  return false;                                  // unreachable for consistent inputs
+}
+
+template <int D, int QB, bool PAGED>
 __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void prefill_bf16_kernel(PrefillArgs a) {
   constexpr int QW = 32 * QB;
   constexpr int KS = D / 16;   // k-steps of the QK^T contraction
@@ -150,11 +232,24 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   const int lane = threadIdx.x & 63;
   const int lq = lane & 31, lg = lane >> 5;
   // ---- work unit (heaviest position blocks first; consecutive ids share a position block)
-  const int per_slice = a.batch * a.n_hgrp;
+  // (chunked prefill: heaviest units first by the device-side ranking above; head groups innermost, so the
+  // blocks of one unit land on consecutive XCDs and each XCD keeps to a fixed set of KV heads)
   const int id = blockIdx.x;
-  const int pblk = a.n_pblk - 1 - id / per_slice;
-  const int rest = id % per_slice;
-  const int b = rest / a.n_hgrp, hgrp = rest % a.n_hgrp;
+  int pblk, b, hgrp;
+  if constexpr (PAGED) {
+    hgrp = id % a.n_hgrp;
+    const int span = a.heads_mode ? kPosBlocks * QW : kWaves * QW;
+    int bb, pp;
+    if (!pick_chunked_unit(a, span, id / a.n_hgrp, bb, pp)) return;
+    // one scalar for both (measured: keeps the D=128 kernel within its register budget, no spills)
+    const int code = __builtin_amdgcn_readfirstlane(bb * a.n_pblk + pp);
+    b = code / a.n_pblk; pblk = code % a.n_pblk;
+  } else {
+    const int per_slice = a.batch * a.n_hgrp;
+    pblk = a.n_pblk - 1 - id / per_slice;
+    const int rest = id % per_slice;
+    b = rest / a.n_hgrp; hgrp = rest % a.n_hgrp;
+  }
   const int grp = a.hq / a.hkv;
   int h, qpos0, wg_pos0, wg_span;
   if (a.heads_mode) {
@@ -164,9 +259,18 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
     h = hgrp; wg_pos0 = pblk * kWaves * QW; qpos0 = wg_pos0 + wave * QW; wg_span = kWaves * QW;
   }
   const int g = h / grp;
-  const int S = a.seqlen;
-  const int kend_wg = a.causal ? min(S, wg_pos0 + wg_span) : S;
-  const int kend_w = a.causal ? min(S, qpos0 + QW) : S;
+  // S queries (positions 0 .. S-1 in this workgroup's numbering) at absolute positions koff .., T keys.
+  int S, koff, T;
+  int64_t qrow0;                                       // row of query 0 in q and o
+  if constexpr (PAGED) {
+    const int r0 = a.cu_new[b];
+    S = min(a.cu_new[b + 1] - r0, a.seqlen); koff = max(0, a.ctx_lens[b]); T = koff + S; qrow0 = r0;
+  } else {
+    S = a.seqlen; koff = 0; T = S; qrow0 = int64_t(b) * S;
+  }
+  if (wg_pos0 >= S) return;                            // uniform: a block past this sequence's queries
+  const int kend_wg = a.causal ? min(T, koff + wg_pos0 + wg_span) : T;
+  const int kend_w = a.causal ? min(T, koff + qpos0 + QW) : T;
   const int ntiles = (kend_wg + kTileKeys - 1) / kTileKeys;
   const float c = a.scale * kLog2e;
 
@@ -175,7 +279,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qpos = qpos0 + 32 * qb + lq;
-    const uint16_t* qp = a.q + ((int64_t(b) * S + qpos) * a.hq + h) * D + 8 * lg;
+    const uint16_t* qp = a.q + ((qrow0 + min(qpos, S - 1)) * a.hq + h) * D + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4_t w = {0u, 0u, 0u, 0u};
@@ -211,8 +315,28 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
 
   TileCopy<D, kWaves, kTileKeys> cp;
   cp.init(a.hkv, g, wave, lane);
-  const uint16_t* kseq = a.k + int64_t(b) * S * a.hkv * D;
-  const uint16_t* vseq = a.v + int64_t(b) * S * a.hkv * D;
+  // Row 0 of the K or V tile at key0 and its valid row count. Paged: tiles never straddle pages (page size a
+  // multiple of the tile); a page number outside [0, num_pages), or a tile past the table's max_pages entries,
+  // gives no rows (zeros, no memory access).
+  auto tile_src = [&](const uint16_t* kv, int key0, int& rows) -> const uint16_t* {
+    rows = max(0, min(kTileKeys, T - key0));
+    if constexpr (PAGED) {
+      const int pi = key0 >> a.page_shift;
+      const int page = pi < a.max_pages ? a.table[int64_t(b) * a.max_pages + pi] : -1;
+      if (page < 0 || page >= a.num_pages) rows = 0;
+      const int64_t slot0 = (int64_t(max(page, 0)) << a.page_shift) + (key0 & ((1 << a.page_shift) - 1));
+      return kv + slot0 * a.hkv * D;
+    } else {
+      return kv + (int64_t(b) * S + min(key0, T - 1)) * a.hkv * D;
+    }
+  };
+  auto copy_tile = [&](int buf, int t) {
+    int rows;
+    const uint16_t* kb = tile_src(a.k, t * kTileKeys, rows);
+    cp.issue(lds[buf][0], kb, rows, a.hkv, wave);
+    const uint16_t* vb = tile_src(a.v, t * kTileKeys, rows);
+    cp.issue(lds[buf][1], vb, rows, a.hkv, wave);
+  };
 
   // One kBN-key tile from LDS buffer BUF (a compile-time constant, so LDS addresses are base + immediate).
   auto tile = [&](auto bufc, auto subc, int key0) {
@@ -239,7 +363,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
     }
 
     // ---- mask: only tiles crossing the diagonal or the ragged end
-    if ((a.causal && key0 + kBN - 1 > qpos0) || key0 + kBN > S) {
+    if ((a.causal && key0 + kBN - 1 > koff + qpos0) || key0 + kBN > T) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int qpos = qpos0 + 32 * qb + lq;
@@ -248,7 +372,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = key0 + 32 * kb2 + 8 * (r >> 2) + 4 * lg + (r & 3);
-            if ((a.causal && key > qpos) || key >= S) sacc[qb][kb2][r] = -INFINITY;
+            if ((a.causal && key > koff + qpos) || key >= T) sacc[qb][kb2][r] = -INFINITY;
           }
       }
     }
@@ -314,24 +438,17 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   };
   static_assert(kSub == 1 || kSub == 2, "one or two sub-tiles per LDS tile");
 
-  cp.issue(lds[0][0], kseq, 0, S, a.hkv, wave);
-  cp.issue(lds[0][1], vseq, 0, S, a.hkv, wave);
+  copy_tile(0, 0);
   // Two tiles per trip so each tile's LDS buffer is a compile-time constant.
   for (int t = 0; t < ntiles; t += 2) {
     wait_vmem();
     __syncthreads();                                   // tile t visible to all; buffer 1 free
-    if (t + 1 < ntiles) {
-      cp.issue(lds[1][0], kseq, (t + 1) * kTileKeys, S, a.hkv, wave);
-      cp.issue(lds[1][1], vseq, (t + 1) * kTileKeys, S, a.hkv, wave);
-    }
+    if (t + 1 < ntiles) copy_tile(1, t + 1);
     if (t * kTileKeys < kend_w) tiles(std::integral_constant<int, 0>{}, t);
     if (t + 1 >= ntiles) break;
     wait_vmem();
     __syncthreads();                                   // tile t+1 visible to all; buffer 0 free
-    if (t + 2 < ntiles) {
-      cp.issue(lds[0][0], kseq, (t + 2) * kTileKeys, S, a.hkv, wave);
-      cp.issue(lds[0][1], vseq, (t + 2) * kTileKeys, S, a.hkv, wave);
-    }
+    if (t + 2 < ntiles) copy_tile(0, t + 2);
     if ((t + 1) * kTileKeys < kend_w) tiles(std::integral_constant<int, 1>{}, t + 1);
   }
 
@@ -342,7 +459,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
     const float lt = sum_xor32(l[qb]);
     if (qpos >= S) continue;
     const float inv = 1.f / lt;
-    uint16_t* op = a.o + ((int64_t(b) * S + qpos) * a.hq + h) * D + 4 * lg;
+    uint16_t* op = a.o + ((qrow0 + qpos) * a.hq + h) * D + 4 * lg;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -352,7 +469,10 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
                            pack_bf16x2(x[4 * rq + 2] * inv, x[4 * rq + 3] * inv)};
         *reinterpret_cast<u32x2_t*>(op + 32 * db + 8 * rq) = w;
       }
-    if (a.lse && lg == 0) a.lse[(int64_t(b) * a.hq + h) * S + qpos] = m[qb] * a.scale + logf(lt);
+    if (a.lse && lg == 0) {
+      const int64_t li = PAGED ? int64_t(h) * a.total_new + qrow0 + qpos : (int64_t(b) * a.hq + h) * S + qpos;
+      a.lse[li] = m[qb] * a.scale + logf(lt);
+    }
   }
 }
 
@@ -423,24 +543,46 @@ __global__ __launch_bounds__(kF32Queries * (D / 16)) void prefill_fp32_kernel(co
 
 }  // namespace
 
+namespace {
+// Shared launch geometry: n_pblk position blocks (heaviest first) x batch x head groups.
+PrefillArgs prefill_args(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int max_q,
+                         int hq, int hkv, int causal, float scale) {
+  PrefillArgs a = {};
+  a.q = static_cast<const uint16_t*>(q); a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v); a.o = static_cast<uint16_t*>(o); a.lse = lse;
+  a.batch = batch; a.seqlen = max_q; a.hq = hq; a.hkv = hkv; a.scale = scale; a.causal = causal;
+  const int grp = hq / hkv;
+  a.heads_mode = (grp % kHeads == 0) ? 1 : 0;
+  const int span = a.heads_mode ? kPosBlocks * 32 : kWaves * 32;
+  a.n_pblk = (max_q + span - 1) / span;
+  a.n_hgrp = a.heads_mode ? hq / kHeads : hq;
+  return a;
+}
+}  // namespace
+
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
                                int seqlen, int hq, int hkv, int head_dim, int causal, float scale,
                                hipStream_t stream) {
-  constexpr int QB = ATTN_PREFILL_QB;
-  constexpr int QW = 32 * QB;   // query positions per workgroup in heads mode
-  PrefillArgs a;
-  a.q = static_cast<const uint16_t*>(q); a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v); a.o = static_cast<uint16_t*>(o); a.lse = lse;
-  a.batch = batch; a.seqlen = seqlen; a.hq = hq; a.hkv = hkv; a.scale = scale; a.causal = causal;
-  const int grp = hq / hkv;
-  a.heads_mode = (grp % kHeads == 0) ? 1 : 0;
-  const int span = a.heads_mode ? kPosBlocks * QW : kWaves * QW;
-  a.n_pblk = (seqlen + span - 1) / span;
-  a.n_hgrp = a.heads_mode ? hq / kHeads : hq;
-  const int64_t blocks = int64_t(a.n_pblk) * batch * a.n_hgrp;
-  const dim3 grid(static_cast<unsigned>(blocks));
-  if (head_dim == 128) prefill_bf16_kernel<128, QB><<<grid, dim3(kThreads), 0, stream>>>(a);
-  else prefill_bf16_kernel<64, QB><<<grid, dim3(kThreads), 0, stream>>>(a);
+  const PrefillArgs a = prefill_args(q, k, v, o, lse, batch, seqlen, hq, hkv, causal, scale);
+  const dim3 grid(static_cast<unsigned>(int64_t(a.n_pblk) * batch * a.n_hgrp));
+  if (head_dim == 128) prefill_bf16_kernel<128, 1, false><<<grid, dim3(kThreads), 0, stream>>>(a);
+  else prefill_bf16_kernel<64, 1, false><<<grid, dim3(kThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                                const int32_t* cu_new, const int32_t* ctx_lens, void* o, float* lse, int batch,
+                                int total_new, int max_new, int hq, int hkv, int head_dim, int page_size,
+                                int max_pages_per_seq, int64_t num_pages, float scale, hipStream_t stream) {
+  if (max_new <= 0 || total_new <= 0) return hipSuccess;
+  PrefillArgs a = prefill_args(q, k_cache, v_cache, o, lse, batch, max_new, hq, hkv, 1, scale);
+  a.cu_new = cu_new; a.ctx_lens = ctx_lens; a.table = block_table;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  a.page_shift = shift; a.max_pages = max_pages_per_seq; a.total_new = total_new; a.num_pages = num_pages;
+  const dim3 grid(static_cast<unsigned>(int64_t(a.n_pblk) * batch * a.n_hgrp));
+  if (head_dim == 128) prefill_bf16_kernel<128, 1, true><<<grid, dim3(kThreads), 0, stream>>>(a);
+  else prefill_bf16_kernel<64, 1, true><<<grid, dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 

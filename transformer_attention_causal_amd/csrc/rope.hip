@@ -162,7 +162,117 @@ hipError_t launch_typed(T* x, int64_t n_tokens, int n_heads, int head_dim, const
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------ paged KV append --
+// (Attention notes, makinaruto.github.io, "Page Attention": logical token t of a sequence lives in page
+//  block_table[t / page_size], slot t % page_size.) New row r of k_new / v_new belongs to the sequence b with
+// cu_new[b] <= r < cu_new[b+1] and has absolute position ctx_lens[b] + r - cu_new[b]. Its key is rotated at that
+// position (same fp64 table as above) and written with its value to the page slot. Rows whose page number is
+// outside [0, num_pages) or past the table are not written.
+
+// The sequence of row r: the last b with cu_new[b] <= r (binary search over the batch offsets).
+__device__ __forceinline__ int seq_of_row(const int32_t* cu_new, int batch, int64_t r) {
+  int lo = 0, hi = batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_new[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+template <bool kInterleaved>
+__global__ __launch_bounds__(kRopeThreads) void kv_append_kernel(const uint16_t* __restrict__ k_new,
+    const uint16_t* __restrict__ v_new, const int32_t* __restrict__ cu_new, const int32_t* __restrict__ ctx_lens,
+    uint16_t* __restrict__ kc, uint16_t* __restrict__ vc, const int32_t* __restrict__ table, int batch,
+    int64_t total_new, int hkv, int head_dim, int page_shift, int max_pages, int64_t num_pages, double theta) {
+  __shared__ float2 cs[kTokens][kMaxPairs];
+  __shared__ double inv_freq[kMaxPairs];
+  __shared__ int32_t pos[kTokens];
+  __shared__ int64_t dst_row[kTokens];                  // destination slot row (page * page_size + slot), or -1
+  const int64_t t0 = int64_t(blockIdx.x) * kTokens;
+  if (threadIdx.x < kTokens) {
+    const int64_t r = t0 + threadIdx.x;
+    int32_t p = 0;
+    int64_t dst = -1;
+    if (r < total_new) {
+      const int b = seq_of_row(cu_new, batch, r);
+      p = ctx_lens[b] + int32_t(r - cu_new[b]);
+      const int pi = p >> page_shift;
+      if (p >= 0 && pi < max_pages) {
+        const int page = table[int64_t(b) * max_pages + pi];
+        if (page >= 0 && page < num_pages) dst = (int64_t(page) << page_shift) + (p & ((1 << page_shift) - 1));
+      }
+    }
+    pos[threadIdx.x] = p;
+    dst_row[threadIdx.x] = dst;
+  }
+  __syncthreads();
+  build_table(cs, inv_freq, pos, 0, kTokens, head_dim, theta);
+  constexpr int N = 8;                                   // bf16 per 16 bytes
+  const int row = hkv * head_dim;
+  const int units = kInterleaved ? row / N : row / (2 * N);
+  for (int u = threadIdx.x; u < kTokens * units; u += kRopeThreads) {
+    const int tok = u / units, w = u % units;
+    if (t0 + tok >= total_new || dst_row[tok] < 0) continue;
+    const uint16_t* src = k_new + (t0 + tok) * int64_t(row);
+    uint16_t* dst = kc + dst_row[tok] * row;
+    float a[N], b[N];
+    if (kInterleaved) {
+      const int e0 = w * N, d0 = e0 % head_dim;
+      Vec16<uint16_t>::unpack(*reinterpret_cast<const u32x4_t*>(src + e0), a);
+      for (int k = 0; k < N / 2; ++k) {
+        const float2 t = cs[tok][d0 / 2 + k];
+        b[2 * k] = fmaf(a[2 * k], t.x, -a[2 * k + 1] * t.y);
+        b[2 * k + 1] = fmaf(a[2 * k], t.y, a[2 * k + 1] * t.x);
+      }
+      *reinterpret_cast<u32x4_t*>(dst + e0) = Vec16<uint16_t>::pack(b);
+    } else {
+      const int per_head = head_dim / (2 * N);
+      const int h = w / per_head, d0 = (w % per_head) * N;
+      const int e0 = h * head_dim + d0, e1 = e0 + head_dim / 2;
+      Vec16<uint16_t>::unpack(*reinterpret_cast<const u32x4_t*>(src + e0), a);
+      Vec16<uint16_t>::unpack(*reinterpret_cast<const u32x4_t*>(src + e1), b);
+      float ra[N], rb[N];
+      for (int k = 0; k < N; ++k) {
+        const float2 t = cs[tok][d0 + k];
+        ra[k] = fmaf(a[k], t.x, -b[k] * t.y);
+        rb[k] = fmaf(a[k], t.y, b[k] * t.x);
+      }
+      *reinterpret_cast<u32x4_t*>(dst + e0) = Vec16<uint16_t>::pack(ra);
+      *reinterpret_cast<u32x4_t*>(dst + e1) = Vec16<uint16_t>::pack(rb);
+    }
+  }
+  // values: plain 16-byte copies
+  const int vunits = row / N;
+  for (int u = threadIdx.x; u < kTokens * vunits; u += kRopeThreads) {
+    const int tok = u / vunits, w = u % vunits;
+    if (t0 + tok >= total_new || dst_row[tok] < 0) continue;
+    *reinterpret_cast<u32x4_t*>(vc + dst_row[tok] * row + w * N) =
+        *reinterpret_cast<const u32x4_t*>(v_new + (t0 + tok) * int64_t(row) + w * N);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_kv_append_paged(const void* k_new, const void* v_new, const int32_t* cu_new,
+                                  const int32_t* ctx_lens, void* k_cache, void* v_cache, const int32_t* block_table,
+                                  int batch, int total_new, int hkv, int head_dim, int page_size, int max_pages_per_seq,
+                                  int64_t num_pages, double theta, int interleaved, hipStream_t stream) {
+  if (total_new <= 0) return hipSuccess;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  const dim3 grid(static_cast<unsigned>((int64_t(total_new) + kTokens - 1) / kTokens)), block(kRopeThreads);
+  const uint16_t* kn = static_cast<const uint16_t*>(k_new);
+  const uint16_t* vn = static_cast<const uint16_t*>(v_new);
+  uint16_t* kc = static_cast<uint16_t*>(k_cache);
+  uint16_t* vc = static_cast<uint16_t*>(v_cache);
+  if (interleaved)
+    kv_append_kernel<true><<<grid, block, 0, stream>>>(kn, vn, cu_new, ctx_lens, kc, vc, block_table, batch, total_new,
+                                                        hkv, head_dim, shift, max_pages_per_seq, num_pages, theta);
+  else
+    kv_append_kernel<false><<<grid, block, 0, stream>>>(kn, vn, cu_new, ctx_lens, kc, vc, block_table, batch, total_new,
+                                                         hkv, head_dim, shift, max_pages_per_seq, num_pages, theta);
+  return hipGetLastError();
+}
 
 hipError_t launch_rope(void* x, int dtype, int64_t n_tokens, int n_heads, int head_dim, const int32_t* positions,
                        double theta, int interleaved, hipStream_t stream) {
