@@ -7,8 +7,9 @@ Primary line: causal GQA prefill, bf16, B=2 Hq=32 Hkv=8 S=8192 D=128 (workload g
 hot path over one batch: RoPE on Q, RoPE on K, then attn_prefill. `value` is the algorithmic attention flops
 (QK^T and PV over the unmasked pairs, 2 flop per multiply-add) per second of wall time over K timed steps,
 with the inputs already resident in HBM. Secondary objects on the same line (same method, HIP events on the
-launch stream): paged GQA decode and MLA absorbed decode in GB/s of algorithmic bytes, and the 131072-token
-prefill in TFLOP/s.
+launch stream): paged GQA decode and MLA absorbed decode in GB/s of algorithmic bytes, the 131072-token prefill
+and the chunked prefill from a paged cache (four 2048-token chunks on 0 / 4096 / 8192 / 14336 cached tokens; one
+step = append with RoPE on K, RoPE on Q, attend) in TFLOP/s.
 
 `roofline` describes the dominant kernel of each workload: achieved = algorithmic work per launch / average
 launch duration (HIP events on the stream the kernel runs on), against MI355X's published peaks (bf16 dense MFMA
@@ -31,7 +32,8 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from synth import WORKLOADS, prefill_inputs, paged_decode_inputs, mla_inputs, sampled_rows  # noqa: E402
+from synth import (WORKLOADS, prefill_inputs, paged_decode_inputs, mla_inputs, sampled_rows,  # noqa: E402
+                   chunked_prefill_inputs)
 
 METRIC = "prefill attention TFLOP/s (% bf16 MFMA peak); decode HBM GB/s (% peak)"
 PEAK_BF16_TFLOPS = 2500.0
@@ -209,6 +211,41 @@ def bench_mla(torch, ta, w, steps, warmup, seed=0):
     return ms
 
 
+# ------------------------------------------------------------------------------------------- chunked prefill --
+def bench_chunked(torch, ta, w, steps, warmup, seed=0):
+    log(f"[bench] {w.name}: generating inputs")
+    inp = chunked_prefill_inputs(w, seed=seed)
+    q, kn, vn = (dev_bf16(torch, inp[n]) for n in ("q", "k_new", "v_new"))
+    kc, vc = dev_bf16(torch, inp["k_cache"]), dev_bf16(torch, inp["v_cache"])
+    table, cu, ctx, pos = (torch.from_numpy(inp[n]).cuda() for n in ("block_table", "cu_new", "ctx_lens",
+                                                                     "positions"))
+    o = torch.empty_like(q)
+    timer = EventTimer(torch)
+
+    def step(timed):
+        ta.attn_kv_append_paged(kn, vn, cu, ctx, kc, vc, table, w.theta)
+        ta.attn_rope_apply(q, pos, w.theta)
+        if timed:
+            timer.start()
+        ta.attn_prefill_paged(q, kc, vc, table, cu, ctx, inp["max_new"], softmax_scale=w.scale, o=o)
+        if timed:
+            timer.stop()
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: timing {steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    kern_ms = timer.mean_ms()
+    del q, kn, vn, kc, vc, o
+    torch.cuda.empty_cache()
+    return wall_ms, kern_ms
+
+
 # ------------------------------------------------------------------------------------------------ cpu oracle --
 def cpu_baseline(w, n_rows=4096, seed=0):
     """Time the fp64 oracle on `n_rows` seeded query rows (all heads, all batches) of the prefill workload."""
@@ -246,8 +283,8 @@ def main():
     # Warm-up long enough (about 0.1 s of work) for the GPU clock to settle before the timed steps.
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-secondary", action="store_true", help="only the primary prefill workload")
-    ap.add_argument("--workloads", default="prefill,decode,mla,long",
-                    help="comma list of prefill (primary), decode, mla, long; profiling runs select one")
+    ap.add_argument("--workloads", default="prefill,decode,mla,long,chunked",
+                    help="comma list of prefill (primary), decode, mla, long, chunked; profiling runs select one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration for traffic measurements)")
@@ -274,7 +311,7 @@ def main():
         return
 
     sel = set(args.workloads.split(","))
-    if sel - {"prefill", "decode", "mla", "long"}:
+    if sel - {"prefill", "decode", "mla", "long", "chunked"}:
         print(f"unknown workloads {sel}", file=sys.stderr)
         sys.exit(2)
     if args.no_secondary:
@@ -328,6 +365,14 @@ def run_secondary(torch, ta, args, sel, line):
         line["long_prefill"] = {"workload": wl.name, "value": round(wl.flops / (wall_l * 1e-3) / 1e12, 2),
                                 "unit": "TFLOP/s", "ms_per_step": round(wall_l, 3),
                                 "roofline": roofline_compute(wl.flops, kern_l, "prefill_bf16_kernel", wl.name)}
+    if "chunked" in sel:
+        wc = WORKLOADS["chunked_prefill_b4"]
+        wall_c, kern_c = bench_chunked(torch, ta, wc, max(20, args.steps), max(100, args.warmup))
+        line["chunked_prefill"] = {"workload": wc.name, "value": round(wc.flops / (wall_c * 1e-3) / 1e12, 2),
+                                   "unit": "TFLOP/s", "ms_per_step": round(wall_c, 4),
+                                   "ctx_lens": list(wc.ctx_lens), "new_lens": list(wc.new_lens),
+                                   "step": "kv_append_paged (rope k) + rope(q) + prefill_paged",
+                                   "roofline": roofline_compute(wc.flops, kern_c, "prefill_bf16_kernel", wc.name)}
 
 
 if __name__ == "__main__":
