@@ -19,4 +19,7 @@ from .attention import (  # noqa: F401
     mla_naive,
     kv_append_paged,
     prefill_paged,
+    dsa_indexer_scores,
+    topk_indices,
+    mla_sparse_decode,
 )

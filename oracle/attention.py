@@ -12,6 +12,8 @@ Pages cited (by title, as they appear on the web):
   [V3]  "DeepSeek-V3 attention guide: einsum vs manual optimisation" (dksg.cn): the naive and the absorbed
         score einsums quoted from the model's inference code.
   [AP]  "7 anti-patterns of DeepSeek attention optimisation" (lpnh.cn): §4.2 GQA cache reorder.
+  [AN-LI] the "Lighting Indexer" section of [AN]: DeepSeek Sparse Attention scores every earlier token with
+        sum over indexer heads j of w_j * ReLU(q_j . k_s) and attends only the most relevant tokens.
 
 Readings taken where the pages are silent or garbled:
   * online-softmax running max is max(m_old, m_c) ([AN] prints a minus sign inside the max);
@@ -25,13 +27,19 @@ Readings taken where the pages are silent or garbled:
   * chunked prefill from a paged cache: the new tokens of a sequence follow its cached ones, new token i sits at
     absolute position cache_len + i and sees keys 0 .. cache_len + i ([AN]: later tokens attend to all earlier
     ones; with fewer queries than keys the mask is aligned to the last query, the bottom-right corner); appended
-    keys are rotated at that absolute position and values are copied unrotated.
+    keys are rotated at that absolute position and values are copied unrotated;
+  * the indexer ([AN-LI]) is taken literally: no scale and no rotation beyond what its inputs already carry, one
+    key per token shared by all indexer heads, one weight per (query token, indexer head); "the most relevant
+    tokens" are the top_k largest scores, ties broken towards the lower token index (the page names no rule);
+    a sequence with at most top_k tokens keeps all of them; sparse attention is the absorbed MLA attention
+    restricted to the selected tokens.
 """
 import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64", "rope_inv_freq", "rope", "attention_prefill", "attention_prefill_rows", "gather_paged",
-    "decode_paged", "mla_decode", "mla_naive", "kv_append_paged", "prefill_paged",
+    "decode_paged", "mla_decode", "mla_naive", "kv_append_paged", "prefill_paged", "dsa_indexer_scores",
+    "topk_indices", "mla_sparse_decode",
 ]
 
 
@@ -272,4 +280,57 @@ def prefill_paged(q, k_cache, v_cache, block_table, cu_new, cache_lens, scale):
             sc = scale * (q[r0:r1, h, :] @ kb[:, g, :].T)                               # [n, ctx + n]
             sc[hidden] = -np.inf
             o[r0:r1, h, :], lse[h, r0:r1] = _softmax_rows_then_v(sc, vb[:, g, :])
+    return o, lse
+
+
+def dsa_indexer_scores(q_idx, w, k_idx, seq_lens):
+    """Lightning-indexer scores of one query token per sequence against every cached token ([AN-LI]):
+    I[b, s] = sum_j w[b, j] * ReLU(q_idx[b, j] . k_idx[b, s]) for s < seq_lens[b], -inf past the length.
+
+    q_idx: [B, H_I, D_I] (indexer queries), w: [B, H_I] (per-head weights), k_idx: [B, T, D_I] (one indexer key per
+    token). Returns [B, T] float64.
+    """
+    q_idx = np.asarray(q_idx, np.float64); w = np.asarray(w, np.float64); k_idx = np.asarray(k_idx, np.float64)
+    bsz, t = k_idx.shape[0], k_idx.shape[1]
+    out = np.full((bsz, t), -np.inf)
+    for b in range(bsz):
+        n = int(seq_lens[b])
+        dots = k_idx[b, :n] @ q_idx[b].T                  # [L, H_I]: q_j . k_s for every head and token
+        out[b, :n] = np.maximum(dots, 0.0) @ w[b]         # weighted sum of the ReLU'd dots over the heads
+    return out
+
+
+def topk_indices(scores, seq_lens, k):
+    """Indices of the k largest scores among the first seq_lens[b] of each row ([AN-LI]: keep the most relevant
+    tokens). Ties at the cut go to the lower index. All min(k, L) selected indices are returned in ascending order,
+    the rest of the k slots hold -1. Returns int32 [B, k].
+    """
+    scores = np.asarray(scores)
+    out = np.full((scores.shape[0], k), -1, np.int32)
+    for b in range(scores.shape[0]):
+        n = int(seq_lens[b])
+        idx = np.arange(n)
+        order = np.lexsort((idx, -scores[b, :n].astype(np.float64)))   # by descending score, then by index
+        sel = np.sort(order[: min(k, n)])
+        out[b, : sel.size] = sel
+    return out
+
+
+def mla_sparse_decode(q_lat, q_pe, c_kv, k_pe, seq_lens, indices, scale):
+    """Absorbed MLA decode over the selected tokens only (DeepSeek Sparse Attention, [AN-LI]): for sequence b the
+    keys and values are the rows indices[b, i] of its caches, for the entries with 0 <= index < seq_lens[b]
+    (others, e.g. -1 padding, are ignored). Otherwise exactly mla_decode. Returns (o [B, H, C], lse [B, H]).
+    """
+    q_lat = np.asarray(q_lat, np.float64); q_pe = np.asarray(q_pe, np.float64)
+    c_kv = np.asarray(c_kv, np.float64); k_pe = np.asarray(k_pe, np.float64)
+    bsz, nh, c = q_lat.shape
+    o = np.zeros((bsz, nh, c), np.float64)
+    lse = np.zeros((bsz, nh), np.float64)
+    for b in range(bsz):
+        n = int(seq_lens[b])
+        sel = np.array([int(i) for i in indices[b] if 0 <= int(i) < n], dtype=np.int64)
+        keys = np.concatenate([c_kv[b, sel], k_pe[b, sel]], axis=-1)        # [n_sel, C+R], gathered rows
+        qry = np.concatenate([q_lat[b], q_pe[b]], axis=-1)
+        sc = scale * (qry @ keys.T)
+        o[b], lse[b] = _softmax_rows_then_v(sc, c_kv[b, sel])
     return o, lse

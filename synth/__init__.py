@@ -1,6 +1,6 @@
 """Seeded synthetic inputs and workload shapes (no attention arithmetic here)."""
-from .workloads import WORKLOADS, Prefill, PagedDecode, MLADecode, ChunkedPrefill  # noqa: F401
+from .workloads import WORKLOADS, Prefill, PagedDecode, MLADecode, ChunkedPrefill, DSADecode  # noqa: F401
 from .generate import (  # noqa: F401
     f32_to_bf16_bits, normal, prefill_inputs, sampled_rows, paged_decode_inputs, mla_inputs,
-    chunked_prefill_inputs,
+    chunked_prefill_inputs, dsa_inputs,
 )

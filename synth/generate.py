@@ -166,3 +166,15 @@ def chunked_prefill_inputs(w, seed=0, ctx_lens=None, new_lens=None, page_size=No
                 v_cache=normal(seed, "chunked.v", (n_pool, ps, hkv, d), "bf16"),
                 block_table=table, cu_new=cu, ctx_lens=ctx, positions=positions,
                 spare_pages=np.sort(perm[off:]), max_new=int(new.max(initial=0)))
+
+
+def dsa_inputs(w, seed=0, batch=None, seqlen=None, seq_lens=None):
+    """The MLA decode inputs (q_lat, q_pe, c_kv, k_pe, seq_lens as mla_inputs) plus the lightning indexer's:
+    q_idx [B, H_I, D_I] and k_idx [B, T, D_I] bf16 bits, head weights w_idx [B, H_I] float32; all iid N(0, 1)."""
+    b = w.batch if batch is None else batch
+    t = w.seqlen if seqlen is None else seqlen
+    out = mla_inputs(w, seed=seed, batch=b, seqlen=t, seq_lens=seq_lens)
+    out["q_idx"] = normal(seed, "dsa.q_idx", (b, w.idx_heads, w.idx_dim), "bf16")
+    out["k_idx"] = normal(seed, "dsa.k_idx", (b, t, w.idx_dim), "bf16")
+    out["w_idx"] = normal(seed, "dsa.w_idx", (b, w.idx_heads), "fp32")
+    return out

@@ -82,6 +82,22 @@ class ChunkedPrefill:
         return 4 * self.hq * self.head_dim * pairs
 
 
+@dataclass(frozen=True)
+class DSADecode:
+    """DeepSeek Sparse Attention decode: a lightning indexer scores every cached token of each sequence, the top_k
+    are kept, and absorbed MLA attends only those (latent / rope widths as MLADecode)."""
+    name: str
+    batch: int
+    heads: int
+    latent: int
+    rope: int
+    seqlen: int
+    idx_heads: int         # indexer heads H_I
+    idx_dim: int           # indexer query / key width D_I
+    topk: int
+    scale: float
+
+
 WORKLOADS = {
     "mha_fp32_s256": Prefill("mha_fp32_s256", batch=1, seqlen=256, hq=4, hkv=4, head_dim=64, dtype="fp32",
                              theta=10000.0, scale=1.0 / math.sqrt(64)),
@@ -91,6 +107,8 @@ WORKLOADS = {
                                     len_lo=1024, len_hi=32768, theta=10000.0, scale=1.0 / math.sqrt(128)),
     "mla_decode_b32": MLADecode("mla_decode_b32", batch=32, heads=128, latent=512, rope=64, seqlen=32768,
                                 scale=1.0 / math.sqrt(192)),
+    "dsa_decode_b32": DSADecode("dsa_decode_b32", batch=32, heads=128, latent=512, rope=64, seqlen=32768,
+                                idx_heads=64, idx_dim=128, topk=2048, scale=1.0 / math.sqrt(192)),
     "chunked_prefill_b4": ChunkedPrefill("chunked_prefill_b4", hq=32, hkv=8, head_dim=128, page_size=64,
                                          ctx_lens=(0, 4096, 8192, 14336), new_lens=(2048, 2048, 2048, 2048),
                                          theta=10000.0, scale=1.0 / math.sqrt(128)),

@@ -500,3 +500,117 @@ def test_bf16_decode_is_exact():
     assert vals[2] == 3.140625                                        # 0x4049 = 1.5703125 * 2
     assert vals[4] == (2 - 2 ** -7) * 2.0 ** 127                      # largest finite bf16
     assert vals[5] == 2.0 ** -133                                     # smallest subnormal bf16
+
+
+# ------------------------------------------------------------------------------ DSA indexer, top-k, sparse MLA ----
+
+def test_indexer_brute_force_loops():
+    """The page's formula with explicit loops: sum over heads j of w_j * max(0, sum_d q_jd * k_sd)."""
+    rng = np.random.default_rng(50)
+    B, H, D, T = 2, 3, 4, 6
+    q = rng.standard_normal((B, H, D)); w = rng.standard_normal((B, H)); k = rng.standard_normal((B, T, D))
+    lens = np.array([6, 4])
+    got = oracle.dsa_indexer_scores(q, w, k, lens)
+    for b in range(B):
+        for s in range(T):
+            if s >= lens[b]:
+                assert got[b, s] == -np.inf
+                continue
+            ref = 0.0
+            for j in range(H):
+                dot = sum(q[b, j, d] * k[b, s, d] for d in range(D))
+                ref += w[b, j] * (dot if dot > 0 else 0.0)
+            assert abs(got[b, s] - ref) < 1e-13
+
+
+def test_indexer_relu_and_weights():
+    # one head with w = 1 is ReLU(q . k); a head whose dots are all negative contributes nothing; w is linear
+    rng = np.random.default_rng(51)
+    q = rng.standard_normal((1, 1, 8)); k = rng.standard_normal((1, 20, 8))
+    got = oracle.dsa_indexer_scores(q, np.ones((1, 1)), k, [20])
+    np.testing.assert_allclose(got[0], np.maximum(k[0] @ q[0, 0], 0), atol=1e-14)
+    q2 = np.concatenate([q, np.zeros_like(q)], axis=1)          # second head: q = 0, so ReLU(q . k) = 0
+    got2 = oracle.dsa_indexer_scores(q2, np.array([[1.0, 5.0]]), k, [20])
+    np.testing.assert_allclose(got2, got, atol=1e-14)
+    w = rng.standard_normal((1, 2)); qq = rng.standard_normal((1, 2, 8))
+    a = oracle.dsa_indexer_scores(qq, w, k, [20]); b2 = oracle.dsa_indexer_scores(qq, -2.5 * w, k, [20])
+    np.testing.assert_allclose(b2, -2.5 * a, atol=1e-13)
+    # heads are an unordered sum: permuting heads together with their weights changes nothing
+    perm = [1, 0]
+    np.testing.assert_allclose(oracle.dsa_indexer_scores(qq[:, perm], w[:, perm], k, [20]), a, atol=1e-13)
+
+
+def test_topk_distinct_values_is_argsort():
+    rng = np.random.default_rng(52)
+    x = rng.standard_normal((3, 50))
+    lens = np.array([50, 30, 7])
+    got = oracle.topk_indices(x, lens, 10)
+    for b in range(3):
+        ref = np.sort(np.argsort(-x[b, :lens[b]], kind="stable")[:10])
+        n = min(10, lens[b])
+        np.testing.assert_array_equal(got[b, :n], ref)
+        assert np.all(got[b, n:] == -1)
+        sel = np.zeros(lens[b], bool); sel[got[b, :n]] = True
+        if n < lens[b]:
+            assert x[b, :lens[b]][sel].min() > x[b, :lens[b]][~sel].max()
+
+
+def test_topk_ties_and_short_rows():
+    x = np.array([[3.0, 1.0, 3.0, 3.0, 0.0, 7.0], [2.0, 2.0, 2.0, 2.0, 2.0, 2.0]])
+    got = oracle.topk_indices(x, [5, 6], 3)
+    np.testing.assert_array_equal(got[0], [0, 2, 3])           # 7.0 is past the length; three 3.0 ties fill it
+    np.testing.assert_array_equal(got[1], [0, 1, 2])           # all equal: the lowest indices
+    got = oracle.topk_indices(x, [2, 0], 4)
+    np.testing.assert_array_equal(got[0], [0, 1, -1, -1])      # fewer tokens than k: all of them
+    np.testing.assert_array_equal(got[1], [-1, -1, -1, -1])
+
+
+def _mla_case(seed, B=2, H=3, C=16, R=4, T=12):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, H, C)), rng.standard_normal((B, H, R)), rng.standard_normal((B, T, C)),
+            rng.standard_normal((B, T, R)))
+
+
+def test_sparse_mla_with_every_token_is_dense():
+    q_lat, q_pe, c_kv, k_pe = _mla_case(53)
+    lens = np.array([12, 5])
+    idx = np.array([np.arange(12), np.concatenate([np.arange(5), -np.ones(7, int)])])
+    o, lse = oracle.mla_sparse_decode(q_lat, q_pe, c_kv, k_pe, lens, idx, 0.35)
+    o_ref, lse_ref = oracle.mla_decode(q_lat, q_pe, c_kv, k_pe, lens, 0.35)
+    np.testing.assert_allclose(o, o_ref, atol=1e-13); np.testing.assert_allclose(lse, lse_ref, atol=1e-13)
+
+
+def test_sparse_mla_equals_dense_on_a_compacted_cache():
+    q_lat, q_pe, c_kv, k_pe = _mla_case(54)
+    lens = np.array([12, 9])
+    idx = np.array([[7, 2, 11, -1, 0, 40], [8, 3, 9, 5, -1, 1]])  # unordered, padding, entries at / past the length
+    o, lse = oracle.mla_sparse_decode(q_lat, q_pe, c_kv, k_pe, lens, idx, 0.35)
+    for b in range(2):
+        keep = [i for i in idx[b] if 0 <= i < lens[b]]
+        ck = np.zeros((1, len(keep), c_kv.shape[2])); kp = np.zeros((1, len(keep), k_pe.shape[2]))
+        for j, i in enumerate(keep):                              # explicit copy of the selected rows
+            ck[0, j] = c_kv[b, i]; kp[0, j] = k_pe[b, i]
+        o_ref, lse_ref = oracle.mla_decode(q_lat[b:b + 1], q_pe[b:b + 1], ck, kp, [len(keep)], 0.35)
+        np.testing.assert_allclose(o[b], o_ref[0], atol=1e-13); np.testing.assert_allclose(lse[b], lse_ref[0], atol=1e-13)
+    # the order of the index list does not matter
+    o2, _ = oracle.mla_sparse_decode(q_lat, q_pe, c_kv, k_pe, lens, idx[:, ::-1], 0.35)
+    np.testing.assert_allclose(o2, o, atol=1e-13)
+
+
+def test_sparse_mla_with_nothing_selected_is_empty():
+    q_lat, q_pe, c_kv, k_pe = _mla_case(55)
+    o, lse = oracle.mla_sparse_decode(q_lat, q_pe, c_kv, k_pe, np.array([12, 3]), np.array([[-1, -1], [5, 7]]), 0.3)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+def test_dsa_pipeline_with_large_k_is_dense_mla():
+    # top_k >= L keeps every token, so indexer -> top-k -> sparse attention is dense MLA whatever the scores are
+    q_lat, q_pe, c_kv, k_pe = _mla_case(56)
+    rng = np.random.default_rng(57)
+    lens = np.array([12, 10])
+    sc = oracle.dsa_indexer_scores(rng.standard_normal((2, 4, 8)), rng.standard_normal((2, 4)),
+                                   rng.standard_normal((2, 12, 8)), lens)
+    idx = oracle.topk_indices(sc, lens, 16)
+    o, _ = oracle.mla_sparse_decode(q_lat, q_pe, c_kv, k_pe, lens, idx, 0.3)
+    o_ref, _ = oracle.mla_decode(q_lat, q_pe, c_kv, k_pe, lens, 0.3)
+    np.testing.assert_allclose(o, o_ref, atol=1e-13)
