@@ -7,6 +7,9 @@
  *   attn_mla_decode       multi-head latent attention decode in the absorbed form
  *   attn_kv_append_paged  write new tokens' keys (rotated) and values into a paged KV cache
  *   attn_prefill_paged    chunked / variable-length causal prefill of new tokens against a paged KV cache
+ *   attn_dsa_indexer      DeepSeek Sparse Attention: lightning-indexer relevance score of every cached token
+ *   attn_topk             the indices of the top-k scores of each sequence
+ *   attn_mla_sparse_decode  absorbed MLA decode over a list of selected tokens per sequence
  *
  * Every result is the exact softmax attention O = softmax(scale * Q K^T [+ mask]) V. The kernels compute it
  * FlashAttention-style: scores are formed tile by tile on chip, an online softmax keeps a running row max m and
@@ -182,6 +185,49 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, 
                        const int32_t* cu_new, const int32_t* cache_lens, void* o, float* lse, int batch, int total_new,
                        int max_new, int n_heads_q, int n_heads_kv, int head_dim, int page_size, int max_pages_per_seq,
                        int64_t num_pages, float softmax_scale, void* stream);
+
+/* DeepSeek Sparse Attention, step 1: lightning-indexer scores for one query token per sequence.
+ * (Attention notes, makinaruto.github.io, "Lighting Indexer": each earlier token s is scored by the sum over the
+ *  indexer heads j of w_j * ReLU(q_j . k_s); the highest-scoring tokens are the ones attended.)
+ *   q_idx     [batch, n_heads_idx, idx_dim] bf16: the indexer queries of the current token (16-byte aligned)
+ *   w_idx     [batch, n_heads_idx] fp32: the per-head weights of the current token
+ *   k_idx     [batch, max_seqlen_kv, idx_dim] bf16: one indexer key per cached token (16-byte aligned)
+ *   seq_lens  [batch] int32 on the device, 0 <= seq_lens[b] <= max_seqlen_kv
+ *   scores    [batch, max_seqlen_kv] fp32, written: scores[b][s] = sum_j w_j * max(0, q_j . k_s) for s < seq_lens[b]
+ *             (fp32 accumulation of bf16 products), -inf for s >= seq_lens[b].
+ * Nothing is scaled or rotated here: any scale or position encoding is already in the inputs.
+ * Supported: n_heads_idx 32 or 64, idx_dim 64 or 128; otherwise UNSUPPORTED. */
+int attn_dsa_indexer(const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* seq_lens,
+                     float* scores, int batch, int n_heads_idx, int idx_dim, int max_seqlen_kv, void* stream);
+
+/* DeepSeek Sparse Attention, step 2: the top-k tokens of each sequence by score ("only the most relevant tokens",
+ * Attention notes, "Lighting Indexer").
+ *   scores    [batch, max_seqlen_kv] fp32 (e.g. from attn_dsa_indexer); only the first seq_lens[b] of row b are
+ *             read. NaN is ordered above +inf.
+ *   indices   [batch, topk] int32, written: the min(topk, seq_lens[b]) selected token indices in ascending order,
+ *             then -1. Selected = the topk largest scores; at equal scores the lower index wins, so the result is
+ *             unique. A sequence with at most topk tokens keeps all of them.
+ * INVALID_ARG for topk <= 0. */
+int attn_topk(const float* scores, const int32_t* seq_lens, int32_t* indices, int batch, int max_seqlen_kv, int topk,
+              void* stream);
+
+/* Bytes of workspace attn_mla_sparse_decode needs for these sizes (0 if any size is non-positive). */
+size_t attn_mla_sparse_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int topk);
+
+/* DeepSeek Sparse Attention, step 3: absorbed MLA decode (as attn_mla_decode) restricted, for each sequence b, to
+ * the tokens indices[b][0 .. topk-1] (Attention notes, "Lighting Indexer": attention over the selected tokens only;
+ * the MLA passages as cited for attn_mla_decode).
+ *   indices   [batch, topk] int32 on the device: token indices into sequence b's caches. Entries outside
+ *             [0, seq_lens[b]) (e.g. the -1 padding of attn_topk) are ignored; a repeated index counts twice.
+ *   The other arguments are those of attn_mla_decode; max_seqlen_kv is the caches' token dimension (> 0).
+ *   o_latent  0 and lse -inf for a sequence with no valid index.
+ *   workspace >= attn_mla_sparse_decode_workspace_size(batch, n_heads, kv_lora_rank, topk) bytes.
+ * Only the selected tokens' rows are read. Supported as attn_mla_decode, with max_seqlen_kv * kv_lora_rank * 2
+ * <= 2^31. */
+int attn_mla_sparse_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
+                           const int32_t* seq_lens, const int32_t* indices, void* o_latent, float* lse, int batch,
+                           int n_heads, int kv_lora_rank, int rope_dim, int max_seqlen_kv, int topk,
+                           float softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* attn_status_string(int status);

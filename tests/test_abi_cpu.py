@@ -29,9 +29,10 @@ def lib():
     return load_library(LIB)
 
 
-def test_header_declares_the_four_operations():
+def test_header_declares_the_operations():
     names = declared_functions()
-    for n in ("attn_rope_apply", "attn_prefill", "attn_decode_paged", "attn_mla_decode"):
+    for n in ("attn_rope_apply", "attn_prefill", "attn_decode_paged", "attn_mla_decode", "attn_kv_append_paged",
+              "attn_prefill_paged", "attn_dsa_indexer", "attn_topk", "attn_mla_sparse_decode"):
         assert n in names
 
 
@@ -191,3 +192,51 @@ def test_prefill_paged_validation(lib):
     assert f(*args(page=32)) == UNSUPPORTED           # tiles of 64 keys may not straddle pages
     assert f(*args(page=96)) == UNSUPPORTED
     assert f(*args(total=0, maxnew=0, q=NULL)) == OK
+
+
+def test_dsa_indexer_validation(lib):
+    f = lib.attn_dsa_indexer
+    A = ctypes.c_void_p(0x10000)
+    U = ctypes.c_void_p(0x10004)
+    args = lambda **kw: [kw.get(n, d) for n, d in [
+        ("q", A), ("w", FAKE), ("k", A), ("lens", FAKE), ("scores", FAKE), ("batch", 2), ("hi", 64), ("di", 128),
+        ("t", 1000), ("stream", NULL)]]
+    assert f(*args(batch=-1)) == INVALID
+    assert f(*args(t=-1)) == INVALID
+    assert f(*args(hi=0)) == INVALID
+    assert f(*args(w=NULL)) == INVALID
+    assert f(*args(scores=NULL)) == INVALID
+    assert f(*args(k=U)) == INVALID                   # 16-byte rows
+    assert f(*args(hi=48)) == UNSUPPORTED
+    assert f(*args(di=96)) == UNSUPPORTED
+    assert f(*args(t=0, q=NULL)) == OK                # no tokens: nothing to score
+
+
+def test_topk_validation(lib):
+    f = lib.attn_topk
+    args = lambda **kw: [kw.get(n, d) for n, d in [
+        ("scores", FAKE), ("lens", FAKE), ("out", FAKE), ("batch", 2), ("t", 100), ("k", 10), ("stream", NULL)]]
+    assert f(*args(k=0)) == INVALID
+    assert f(*args(batch=-2)) == INVALID
+    assert f(*args(out=NULL)) == INVALID
+    assert f(*args(scores=NULL)) == INVALID
+    assert f(*args(batch=0, out=NULL)) == OK
+
+
+def test_mla_sparse_validation(lib):
+    f = lib.attn_mla_sparse_decode
+    need = lib.attn_mla_sparse_decode_workspace_size(2, 128, 512, 256)
+    assert need == lib.attn_mla_decode_workspace_size(2, 128, 512, 256)
+    args = lambda **kw: [kw.get(n, d) for n, d in [
+        ("ql", FAKE), ("qp", FAKE), ("ckv", FAKE), ("kpe", FAKE), ("lens", FAKE), ("idx", FAKE), ("o", FAKE),
+        ("lse", NULL), ("b", 2), ("h", 128), ("c", 512), ("r", 64), ("t", 4096), ("k", 256), ("scale", 0.07),
+        ("ws", FAKE), ("wsb", need), ("stream", NULL)]]
+    assert f(*args(k=0)) == INVALID
+    assert f(*args(t=0)) == INVALID
+    assert f(*args(idx=NULL)) == INVALID
+    assert f(*args(scale=-1.0)) == INVALID
+    assert f(*args(c=256)) == UNSUPPORTED
+    assert f(*args(h=40)) == UNSUPPORTED
+    assert f(*args(t=1 << 23)) == UNSUPPORTED         # latent rows of one sequence beyond a 32-bit resource
+    assert f(*args(wsb=need - 1)) == WORKSPACE
+    assert f(*args(b=0)) == OK

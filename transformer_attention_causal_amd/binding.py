@@ -28,6 +28,10 @@ SIGNATURES = {
     "attn_mla_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "attn_kv_append_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _D, _I, _P]),
     "attn_prefill_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I64, _F, _P]),
+    "attn_dsa_indexer": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
+    "attn_topk": (_I, [_P, _P, _P, _I, _I, _I, _P]),
+    "attn_mla_sparse_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
+    "attn_mla_sparse_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "attn_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -213,4 +217,63 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_new, cache_lens, max
         _dev(block_table, "block_table", torch.int32), _dev(cu_new, "cu_new", torch.int32),
         _dev(cache_lens, "cache_lens", torch.int32), _dev(o, "o", torch.bfloat16), lse_p, cu_new.numel() - 1, total,
         int(max_new), hq, hkv, d, page, block_table.shape[1], num_pages, scale, _stream(q, stream)))
+    return (o, lse) if return_lse else o
+
+
+def attn_dsa_indexer(q_idx, w_idx, k_idx, seq_lens, scores=None, stream=None):
+    """q_idx [B, H_I, D_I] bf16, w_idx [B, H_I] fp32, k_idx [B, T, D_I] bf16, seq_lens [B] int32 (device).
+    Returns scores [B, T] fp32 (-inf past each sequence's length)."""
+    lib = load_library()
+    bsz, hi, di = q_idx.shape
+    t = k_idx.shape[1]
+    if k_idx.shape != (bsz, t, di) or tuple(w_idx.shape) != (bsz, hi):
+        raise ValueError("shape mismatch between q_idx, w_idx and k_idx")
+    if scores is None:
+        scores = torch.empty((bsz, t), dtype=torch.float32, device=q_idx.device)
+    _check("attn_dsa_indexer", lib.attn_dsa_indexer(
+        _dev(q_idx, "q_idx", torch.bfloat16), _dev(w_idx, "w_idx", torch.float32), _dev(k_idx, "k_idx", torch.bfloat16),
+        _dev(seq_lens, "seq_lens", torch.int32), _dev(scores, "scores", torch.float32), bsz, hi, di, t,
+        _stream(q_idx, stream)))
+    return scores
+
+
+def attn_topk(scores, seq_lens, topk, indices=None, stream=None):
+    """scores [B, T] fp32, seq_lens [B] int32 (device) -> indices [B, topk] int32: the selected tokens ascending,
+    then -1."""
+    lib = load_library()
+    bsz, t = scores.shape
+    if indices is None:
+        indices = torch.empty((bsz, topk), dtype=torch.int32, device=scores.device)
+    _check("attn_topk", lib.attn_topk(_dev(scores, "scores", torch.float32), _dev(seq_lens, "seq_lens", torch.int32),
+                                      _dev(indices, "indices", torch.int32), bsz, t, int(topk),
+                                      _stream(scores, stream)))
+    return indices
+
+
+def attn_mla_sparse_decode_workspace_size(batch, n_heads, kv_lora_rank, topk):
+    return int(load_library().attn_mla_sparse_decode_workspace_size(batch, n_heads, kv_lora_rank, topk))
+
+
+def attn_mla_sparse_decode(q_latent, q_pe, c_kv, k_pe, seq_lens, indices, softmax_scale, o=None, lse=None,
+                           workspace=None, return_lse=False, stream=None):
+    """As attn_mla_decode, over the tokens indices [B, topk] int32 (device) of each sequence only."""
+    lib = load_library()
+    bsz, nh, c = q_latent.shape
+    r = q_pe.shape[-1]
+    t = c_kv.shape[1]
+    topk = indices.shape[1]
+    if o is None:
+        o = torch.empty_like(q_latent)
+    if lse is None and return_lse:
+        lse = torch.empty((bsz, nh), dtype=torch.float32, device=q_latent.device)
+    need = attn_mla_sparse_decode_workspace_size(bsz, nh, c, topk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_latent.device)
+    lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
+    _check("attn_mla_sparse_decode", lib.attn_mla_sparse_decode(
+        _dev(q_latent, "q_latent", torch.bfloat16), _dev(q_pe, "q_pe", torch.bfloat16),
+        _dev(c_kv, "c_kv", torch.bfloat16), _dev(k_pe, "k_pe", torch.bfloat16),
+        _dev(seq_lens, "seq_lens", torch.int32), _dev(indices, "indices", torch.int32),
+        _dev(o, "o_latent", torch.bfloat16), lse_p, bsz, nh, c, r, t, topk, float(softmax_scale),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(q_latent, stream)))
     return (o, lse) if return_lse else o

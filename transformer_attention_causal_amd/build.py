@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
-SOURCES = ["rope.hip", "prefill.hip", "decode.hip", "mla.hip", "capi.hip"]
+SOURCES = ["rope.hip", "prefill.hip", "decode.hip", "mla.hip", "dsa.hip", "capi.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -146,3 +146,48 @@ ATTN_EXPORT int attn_prefill_paged(const void* q, const void* k_cache, const voi
                                                max_pages_per_seq, num_pages, softmax_scale,
                                                static_cast<hipStream_t>(stream)));
 }
+
+ATTN_EXPORT int attn_dsa_indexer(const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* seq_lens,
+                                 float* scores, int batch, int n_heads_idx, int idx_dim, int max_seqlen_kv,
+                                 void* stream) {
+  if (batch < 0 || n_heads_idx <= 0 || idx_dim <= 0 || max_seqlen_kv < 0) return ATTN_ERR_INVALID_ARG;
+  if ((n_heads_idx != 32 && n_heads_idx != 64) || (idx_dim != 64 && idx_dim != 128)) return ATTN_ERR_UNSUPPORTED;
+  if (batch == 0 || max_seqlen_kv == 0) return ATTN_OK;
+  if (!q_idx || !w_idx || !k_idx || !seq_lens || !scores) return ATTN_ERR_INVALID_ARG;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(q_idx) | reinterpret_cast<uintptr_t>(k_idx);
+  if (align % 16 != 0) return ATTN_ERR_INVALID_ARG;
+  return hip_status(attn::launch_dsa_indexer(q_idx, w_idx, k_idx, seq_lens, scores, batch, n_heads_idx, idx_dim,
+                                             max_seqlen_kv, static_cast<hipStream_t>(stream)));
+}
+
+ATTN_EXPORT int attn_topk(const float* scores, const int32_t* seq_lens, int32_t* indices, int batch,
+                          int max_seqlen_kv, int topk, void* stream) {
+  if (batch < 0 || max_seqlen_kv < 0 || topk <= 0) return ATTN_ERR_INVALID_ARG;
+  if (batch == 0) return ATTN_OK;
+  if (!seq_lens || !indices || (max_seqlen_kv > 0 && !scores)) return ATTN_ERR_INVALID_ARG;
+  return hip_status(attn::launch_topk(scores, seq_lens, indices, batch, max_seqlen_kv, topk,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+ATTN_EXPORT size_t attn_mla_sparse_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int topk) {
+  return attn::mla_decode_workspace_bytes(batch, n_heads, kv_lora_rank, topk);
+}
+
+ATTN_EXPORT int attn_mla_sparse_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
+                                       const int32_t* seq_lens, const int32_t* indices, void* o_latent, float* lse,
+                                       int batch, int n_heads, int kv_lora_rank, int rope_dim, int max_seqlen_kv,
+                                       int topk, float softmax_scale, void* workspace, size_t workspace_bytes,
+                                       void* stream) {
+  if (batch < 0 || n_heads <= 0 || kv_lora_rank <= 0 || rope_dim <= 0 || max_seqlen_kv <= 0 || topk <= 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (kv_lora_rank != 512 || rope_dim != 64 || n_heads % 32 != 0 || n_heads > 128) return ATTN_ERR_UNSUPPORTED;
+  if (batch == 0) return ATTN_OK;
+  if (!q_latent || !q_pe || !c_kv || !k_pe || !seq_lens || !indices || !o_latent) return ATTN_ERR_INVALID_ARG;
+  if (int64_t(max_seqlen_kv) * kv_lora_rank * 2 > (int64_t(1) << 31)) return ATTN_ERR_UNSUPPORTED;
+  const size_t need = attn::mla_decode_workspace_bytes(batch, n_heads, kv_lora_rank, topk);
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  return hip_status(attn::launch_mla_sparse_decode(q_latent, q_pe, c_kv, k_pe, seq_lens, indices, o_latent, lse,
+                                                   batch, n_heads, max_seqlen_kv, topk, softmax_scale, workspace,
+                                                   static_cast<hipStream_t>(stream)));
+}

@@ -107,6 +107,11 @@ __device__ __forceinline__ void load_lds16(buf_rsrc_t rsrc, uint32_t voff, void*
   raw_buffer_load_lds(rsrc, (lds_void_t*)lds_wave_base, 16, static_cast<int>(voff), static_cast<int>(soff), 0, 0);
 }
 
+// 4 bytes per lane: lane i's dword lands at lds_wave_base + 4*i (same addressing rules as load_lds16).
+__device__ __forceinline__ void load_lds4(buf_rsrc_t rsrc, uint32_t voff, void* lds_wave_base, uint32_t soff = 0) {
+  raw_buffer_load_lds(rsrc, (lds_void_t*)lds_wave_base, 4, static_cast<int>(voff), static_cast<int>(soff), 0, 0);
+}
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------------------- cross-lane --

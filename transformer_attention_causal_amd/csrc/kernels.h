@@ -49,4 +49,19 @@ hipError_t launch_mla_decode(const void* q_latent, const void* q_pe, const void*
                              const int32_t* seq_lens, void* o_latent, float* lse, int batch, int n_heads,
                              int max_seqlen_kv, float scale, void* workspace, hipStream_t stream);
 
+// Sparse MLA decode over a [batch, topk] list of token indices per sequence (same workspace layout as the dense
+// form with topk in place of max_seqlen_kv).
+hipError_t launch_mla_sparse_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
+                                    const int32_t* seq_lens, const int32_t* indices, void* o_latent, float* lse,
+                                    int batch, int n_heads, int max_seqlen_kv, int topk, float scale, void* workspace,
+                                    hipStream_t stream);
+
+// DeepSeek Sparse Attention selection: lightning-indexer scores [batch, max_seqlen_kv] fp32, then the top-k
+// token indices per sequence. Indexer: n_heads_idx 32 or 64, idx_dim 64 or 128, bf16 inputs, fp32 weights.
+hipError_t launch_dsa_indexer(const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* seq_lens,
+                              float* scores, int batch, int n_heads_idx, int idx_dim, int max_seqlen_kv,
+                              hipStream_t stream);
+hipError_t launch_topk(const float* scores, const int32_t* seq_lens, int32_t* indices, int batch, int max_seqlen_kv,
+                       int k, hipStream_t stream);
+
 }  // namespace attn

@@ -18,6 +18,10 @@
 //   * O^T = c_kv^T P^T: the value operand is the SAME LDS tile read through ds_read_b64_tr_b16 (no second copy),
 //     P^T comes straight from the S^T registers. O^T for 16 heads x 512 stays in registers (128 per lane).
 //   * Splits over tokens write (O / l, lse) partials; the combine kernel merges them by log-sum-exp.
+//   * Sparse form (DeepSeek Sparse Attention, Attention notes "Lighting Indexer": only the selected tokens take
+//     part): the same kernel over a list of token indices per sequence. The splits cut the list; each copy
+//     instruction of a latent row takes its token from the list (a lane read of the tile's index vector into the
+//     scalar offset), the rope rows take theirs per lane; list entries outside [0, L) are masked like the tail.
 // HBM-bound in principle (about 240 flop per byte) but close to the MFMA ridge, so both matter.
 #include "device.h"
 #include "kernels.h"
@@ -59,6 +63,8 @@ struct MlaArgs {
   float* ws_lse;   // [batch, heads, n_split]
   int heads, max_len, n_split, split_len;
   float scale;
+  const int32_t* idx;   // sparse form: [batch, topk] token indices (entries outside [0, L) are ignored)
+  int topk;
 };
 
 // One tile copy: tokens t_tile .. t_tile + kRows - 1 of sequence b. Copy instruction i < kRows moves latent row
@@ -77,6 +83,37 @@ __device__ __forceinline__ MlaCopy mla_copy_setup(const MlaArgs& a, int b, int t
   cp.rc = make_buf_rsrc(a.c_kv + tok0 * kC, uint32_t(cp.rows * kC * 2));
   cp.rp = make_buf_rsrc(a.k_pe + tok0 * kR, uint32_t(cp.rows * kR * 2));
   return cp;
+}
+
+// Sparse form. The token list of a tile (64 entries) is staged in LDS by one 4-byte-per-lane load-to-LDS; slot
+// position q holds the entry of tile row (q % 8) * 8 + q / 8 (an 8 x 8 transpose: the map is its own inverse).
+// The resources span the whole sequence. A row whose entry is outside [0, L), or past the end of the list, is
+// copied from an out-of-range offset, so it reads as zeros (finite, masked, P = 0) and no unselected token is
+// ever read.
+__device__ __forceinline__ int idx_pos(int row) { return (row & 7) * 8 + (row >> 3); }
+
+__device__ __forceinline__ MlaCopy mla_copy_setup_sparse(const MlaArgs& a, int b) {
+  MlaCopy cp;
+  cp.rows = kRows;
+  cp.rc = make_buf_rsrc(a.c_kv + int64_t(b) * a.max_len * kC, uint32_t(a.max_len * kC * 2));
+  cp.rp = make_buf_rsrc(a.k_pe + int64_t(b) * a.max_len * kR, uint32_t(a.max_len * kR * 2));
+  return cp;
+}
+
+// `nrows` = list entries in this tile; `oob` = a byte offset at or past both resources' ends.
+__device__ __forceinline__ void mla_copy_one_sparse(char* dst, const MlaCopy& cp, int i, int lane,
+                                                    const int32_t* slot, int L, int nrows, uint32_t oob) {
+  if (i < kRows) {
+    const int id = __builtin_amdgcn_readfirstlane(slot[idx_pos(i)]);   // uniform: scalar offset
+    const bool ok = i < nrows && id >= 0 && id < L;
+    load_lds16(cp.rc, uint32_t(16 * lane) + (ok ? 0u : oob), dst + i * kCkvStride, ok ? uint32_t(id * kC * 2) : 0u);
+  } else {
+    const int r = 8 * (i - kRows) + (lane >> 3);
+    const int id = slot[idx_pos(r)];
+    const bool ok = r < nrows && id >= 0 && id < L;
+    load_lds16(cp.rp, (ok ? uint32_t(id * kR * 2) : oob) + uint32_t(16 * ((lane & 7) ^ ((r >> 1) & 7))),
+               dst + kPeOff + (i - kRows) * 1024);
+  }
 }
 
 // Copy instruction i (wave-uniform) of a tile copy into the LDS tile at `dst`.
@@ -109,11 +146,14 @@ constexpr int kPipe = ATTN_MLA_PIPE;
 // NW waves per workgroup (16 heads each). Each wave issues kCopies / NW copy instructions per tile, spread over
 // its score MFMAs (one every NW), so the copy of tile t+1 overlaps tile t's work instead of stalling every wave
 // on a burst of vector-memory issues right after the barrier.
-template <int NW>
+template <int NW, bool SPARSE>
 __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
+  // LDS fragments in flight (the sparse form keeps two: its token-list handling needs the registers)
+  constexpr int kP = SPARSE ? 2 : kPipe;
   static_assert(kCopies % NW == 0, "copy instructions must split evenly over the waves");
   constexpr int NC = kCopies / NW;
   __shared__ __attribute__((aligned(16))) char lds[2][kTileBytes];
+  __shared__ int32_t lds_idx[SPARSE ? 4 : 1][64];     // sparse: token lists of tiles t .. t+3 (slot t & 3)
   const int split = blockIdx.x, b = blockIdx.y;
   // Wave index in a scalar register, with its range [0, NW) visible to the compiler (resolves at compile time
   // whether each copy instruction moves a latent or a rope block).
@@ -122,8 +162,9 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
   const int n = lane & 15, g4 = lane >> 4;
   const int L = max(0, min(a.seq_lens[b], a.max_len));
   const int t_begin = split * a.split_len;
-  if (t_begin >= L) return;                           // uniform over the workgroup
-  const int t_end = min(L, t_begin + a.split_len);
+  // dense: tokens t_begin .. t_end-1; sparse: list positions t_begin .. t_end-1 (every split writes a partial)
+  if (!SPARSE && t_begin >= L) return;                // uniform over the workgroup
+  const int t_end = min(SPARSE ? a.topk : L, t_begin + a.split_len);
   const int ntiles = (t_end - t_begin + kRows - 1) / kRows;
   const int h = wave * kHeadsPerWave + n;
   const float c = a.scale * kLog2e;
@@ -154,7 +195,28 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
   const int vrow = 4 * g4 + (bl >> 2);
   const uint32_t vbase = uint32_t(vrow * kCkvStride + 8 * (bl & 3));
 
-  {
+  // Sparse form: wave 0 stages the token list of tile u into lds_idx[u & 3] (entries past the split read 0;
+  // validity also checks the list position).
+  MlaCopy cps;
+  buf_rsrc_t ri;
+  const uint32_t oob = uint32_t(a.max_len) * kC * 2;  // past the end of both sparse resources
+  auto stage_idx = [&](int u) {
+    if (wave == 0 && u < ntiles)
+      load_lds4(ri, uint32_t(4 * (u * kRows + idx_pos(lane))), lds_idx[u & 3]);
+  };
+  if constexpr (SPARSE) {
+    cps = mla_copy_setup_sparse(a, b);
+    ri = make_buf_rsrc(a.idx + int64_t(b) * a.topk + t_begin, uint32_t(max(0, t_end - t_begin) * 4));
+    stage_idx(0);
+    stage_idx(1);
+    wait_vmem();
+    __syncthreads();
+    if (ntiles > 0) {
+#pragma unroll
+      for (int k = 0; k < NC; ++k)
+        mla_copy_one_sparse(lds[0], cps, wave + k * NW, lane, lds_idx[0], L, t_end - t_begin, oob);
+    }
+  } else {
     const MlaCopy cp0 = mla_copy_setup(a, b, t_begin, t_end);
 #pragma unroll
     for (int k = 0; k < NC; ++k) mla_copy_one(lds[0], cp0, wave + k * NW, lane);
@@ -163,13 +225,19 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
   for (int t = 0; t < ntiles; ++t) {
     wait_vmem();
     __syncthreads();                                   // tile t visible to all; buffer (t+1)&1 free
-    const MlaCopy cpn = mla_copy_setup(a, b, t_begin + (t + 1) * kRows, t_end);
+    uint64_t valid = ~0ull;                            // sparse: rows of tile t holding a token of the sequence
+    if constexpr (SPARSE) {
+      const int id = lds_idx[t & 3][idx_pos(lane)];    // tile row `lane`
+      valid = __ballot(t * kRows + lane < t_end - t_begin && id >= 0 && id < L);
+      stage_idx(t + 2);                                // lands with this iteration's copies
+    }
+    const MlaCopy cpn = SPARSE ? cps : mla_copy_setup(a, b, t_begin + (t + 1) * kRows, t_end);
     char* nbuf = lds[(t + 1) & 1];
     const uint16_t* T = reinterpret_cast<const uint16_t*>(lds[t & 1]);
     const int tok0 = t_begin + t * kRows;
 
     // S^T = Kc Q^T: 16-token blocks tb; lane holds head n, tokens 16*tb + 4*g4 + r. The K fragments are
-    // software-pipelined kPipe MFMAs ahead (one wave-uniform order pinned by scheduling groups), so LDS latency
+    // software-pipelined kP MFMAs ahead (one wave-uniform order pinned by scheduling groups), so LDS latency
     // overlaps the MFMAs instead of stalling each one.
     constexpr int TB = 2 * kHalves;
     constexpr int NQ = (kDK / 32) * TB;                // MFMAs of the score contraction
@@ -181,23 +249,37 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
       return as_bf16x8(ks < kC / 32 ? lds_read16(T, abase + 64 * ks + 16 * tb * kCkvStride)
                                     : lds_read16(T, pbase[ks - kC / 32] + 16 * tb * kR * 2));
     };
-    bf16x8_t kf[kPipe];
+    bf16x8_t kf[kP];
 #pragma unroll
-    for (int j = 0; j < kPipe; ++j) kf[j] = kfrag(j);
-    MLA_SGB(0x100, kPipe);
+    for (int j = 0; j < kP; ++j) kf[j] = kfrag(j);
+    MLA_SGB(0x100, kP);
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      const bf16x8_t cur = kf[j % kPipe];
-      if (j + kPipe < NQ) kf[j % kPipe] = kfrag(j + kPipe);
+      const bf16x8_t cur = kf[j % kP];
+      if (j + kP < NQ) kf[j % kP] = kfrag(j + kP);
       sacc[j % TB] = mfma16x16x32(cur, qop[j / TB], sacc[j % TB]);
       MLA_SGB(0x008, 1);
-      if (j + kPipe < NQ) MLA_SGB(0x100, 1);
+      if (j + kP < NQ) MLA_SGB(0x100, 1);
       if (j % NW == 0 && j / NW < NC) {                // next tile's copy, one instruction every NW MFMAs
-        mla_copy_one(nbuf, cpn, wave + (j / NW) * NW, lane);
+        if constexpr (SPARSE) {
+          if (t + 1 < ntiles)
+            mla_copy_one_sparse(nbuf, cpn, wave + (j / NW) * NW, lane, lds_idx[(t + 1) & 3], L,
+                                t_end - t_begin - (t + 1) * kRows, oob);
+        } else {
+          mla_copy_one(nbuf, cpn, wave + (j / NW) * NW, lane);
+        }
         MLA_SGB(0x020, 1);
       }
     }
-    if (tok0 + kRows > t_end) {
+    if constexpr (SPARSE) {
+      if (valid != ~0ull) {
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            sacc[tb][r] = (uint32_t(valid >> (16 * tb + r)) >> (4 * g4)) & 1 ? sacc[tb][r] : -INFINITY;
+      }
+    } else if (tok0 + kRows > t_end) {
 #pragma unroll
       for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
@@ -221,7 +303,8 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
       for (int db = 0; db < kC / 16; ++db) oacc[db] *= alpha;
       m = m_new;
     }
-    const float mc = m * c;
+    // (sparse: until a selected token is seen m is -inf and every P is 0)
+    const float mc = (SPARSE && m == -INFINITY) ? 0.f : m * c;
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
@@ -247,23 +330,23 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
       const u32x4_t w = {lo[0], lo[1], hi[0], hi[1]};
       return as_bf16x8(w);
     };
-    bf16x8_t vf[kPipe];
+    bf16x8_t vf[kP];
 #pragma unroll
-    for (int j = 0; j < kPipe; ++j) vf[j] = vfrag(j);
-    MLA_SGB(0x100, 2 * kPipe);
+    for (int j = 0; j < kP; ++j) vf[j] = vfrag(j);
+    MLA_SGB(0x100, 2 * kP);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      const bf16x8_t cur = vf[j % kPipe];
-      if (j + kPipe < NV) vf[j % kPipe] = vfrag(j + kPipe);
+      const bf16x8_t cur = vf[j % kP];
+      if (j + kP < NV) vf[j % kP] = vfrag(j + kP);
       oacc[j % (kC / 16)] = mfma16x16x32(cur, pb[j / (kC / 16)], oacc[j % (kC / 16)]);
       MLA_SGB(0x008, 1);
-      if (j + kPipe < NV) MLA_SGB(0x100, 2);
+      if (j + kP < NV) MLA_SGB(0x100, 2);
     }
   }
 
   float lt = l + xor_lanes(l, 16);
   lt += xor_lanes(lt, 32);
-  const float inv = 1.f / lt;
+  const float inv = (SPARSE && lt == 0.f) ? 0.f : 1.f / lt;   // sparse: a split may select nothing
   const int64_t slot = (int64_t(b) * a.heads + h) * a.n_split + split;
   float* wo = a.ws_o + slot * kC + 4 * g4;
 #pragma unroll
@@ -271,16 +354,17 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
     const f32x4_t v = {oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv};
     *reinterpret_cast<f32x4_t*>(wo + 16 * db) = v;
   }
-  if (g4 == 0) a.ws_lse[slot] = m * a.scale + logf(lt);
+  if (g4 == 0) a.ws_lse[slot] = (SPARSE && lt == 0.f) ? -INFINITY : m * a.scale + logf(lt);
 }
 
 // Merge splits: M = max lse_s, w_s = exp(lse_s - M), O = sum w_s O_s / sum w_s; length 0 -> O = 0, lse = -inf.
 __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ ws_o,
     const float* __restrict__ ws_lse, const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ o,
-    float* __restrict__ lse, int heads, int n_split, int split_len, int max_len) {
+    float* __restrict__ lse, int heads, int n_split, int split_len, int max_len, int sparse) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int L = max(0, min(seq_lens[b], max_len));
-  const int ns = (L + split_len - 1) / split_len;
+  // dense: the splits that cover tokens below L; sparse: every split (an empty one has lse = -inf, O = 0)
+  const int ns = sparse ? n_split : (L + split_len - 1) / split_len;
   const int64_t base = (int64_t(b) * heads + h) * n_split;
   uint16_t* op = o + (int64_t(b) * heads + h) * kC;
   const int d0 = 2 * threadIdx.x;
@@ -293,6 +377,11 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
   float mx = -INFINITY;
 #pragma unroll 8
   for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ws_lse[base + s]);
+  if (mx == -INFINITY) {                               // sparse: nothing selected at all
+    *reinterpret_cast<uint32_t*>(op + d0) = 0u;
+    if (lse && threadIdx.x == 0) lse[int64_t(b) * heads + h] = -INFINITY;
+    return;
+  }
   float a0 = 0.f, a1 = 0.f, wsum = 0.f;
 #pragma unroll 8
   for (int s = 0; s < ns; ++s) {
@@ -332,7 +421,7 @@ size_t mla_decode_workspace_bytes(int batch, int n_heads, int kv_lora_rank, int 
 hipError_t launch_mla_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
                              const int32_t* seq_lens, void* o_latent, float* lse, int batch, int n_heads,
                              int max_seqlen_kv, float scale, void* workspace, hipStream_t stream) {
-  MlaArgs a;
+  MlaArgs a = {};
   a.q_lat = static_cast<const uint16_t*>(q_latent);
   a.q_pe = static_cast<const uint16_t*>(q_pe);
   a.c_kv = static_cast<const uint16_t*>(c_kv);
@@ -348,15 +437,47 @@ hipError_t launch_mla_decode(const void* q_latent, const void* q_pe, const void*
   if (max_seqlen_kv > 0) {
     const dim3 grid(unsigned(a.n_split), unsigned(batch)), block(64 * (n_heads / kHeadsPerWave));
     switch (n_heads / kHeadsPerWave) {
-      case 2: mla_split_kernel<2><<<grid, block, 0, stream>>>(a); break;
-      case 4: mla_split_kernel<4><<<grid, block, 0, stream>>>(a); break;
-      case 6: mla_split_kernel<6><<<grid, block, 0, stream>>>(a); break;
-      default: mla_split_kernel<8><<<grid, block, 0, stream>>>(a); break;
+      case 2: mla_split_kernel<2, false><<<grid, block, 0, stream>>>(a); break;
+      case 4: mla_split_kernel<4, false><<<grid, block, 0, stream>>>(a); break;
+      case 6: mla_split_kernel<6, false><<<grid, block, 0, stream>>>(a); break;
+      default: mla_split_kernel<8, false><<<grid, block, 0, stream>>>(a); break;
     }
   }
   mla_combine_kernel<<<dim3(unsigned(n_heads), unsigned(batch)), dim3(kC / 2), 0, stream>>>(
       a.ws_o, a.ws_lse, seq_lens, static_cast<uint16_t*>(o_latent), lse, n_heads, a.n_split, a.split_len,
-      max_seqlen_kv);
+      max_seqlen_kv, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_sparse_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
+                                    const int32_t* seq_lens, const int32_t* indices, void* o_latent, float* lse,
+                                    int batch, int n_heads, int max_seqlen_kv, int topk, float scale, void* workspace,
+                                    hipStream_t stream) {
+  MlaArgs a = {};
+  a.q_lat = static_cast<const uint16_t*>(q_latent);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.c_kv = static_cast<const uint16_t*>(c_kv);
+  a.k_pe = static_cast<const uint16_t*>(k_pe);
+  a.seq_lens = seq_lens;
+  a.idx = indices;
+  a.topk = topk;
+  a.heads = n_heads; a.max_len = max_seqlen_kv; a.scale = scale;
+  a.n_split = mla_num_splits(batch, n_heads, topk);
+  a.split_len = mla_split_len(batch, n_heads, topk);
+  const size_t slots = size_t(batch) * size_t(n_heads) * size_t(a.n_split);
+  const size_t o_bytes = (slots * kC * sizeof(float) + 255) & ~size_t(255);
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  const dim3 grid(unsigned(a.n_split), unsigned(batch)), block(64 * (n_heads / kHeadsPerWave));
+  switch (n_heads / kHeadsPerWave) {
+    case 2: mla_split_kernel<2, true><<<grid, block, 0, stream>>>(a); break;
+    case 4: mla_split_kernel<4, true><<<grid, block, 0, stream>>>(a); break;
+    case 6: mla_split_kernel<6, true><<<grid, block, 0, stream>>>(a); break;
+    default: mla_split_kernel<8, true><<<grid, block, 0, stream>>>(a); break;
+  }
+  mla_combine_kernel<<<dim3(unsigned(n_heads), unsigned(batch)), dim3(kC / 2), 0, stream>>>(
+      a.ws_o, a.ws_lse, seq_lens, static_cast<uint16_t*>(o_latent), lse, n_heads, a.n_split, a.split_len,
+      max_seqlen_kv, 1);
   return hipGetLastError();
 }
 
