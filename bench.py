@@ -9,7 +9,8 @@ hot path over one batch: RoPE on Q, RoPE on K, then attn_prefill. `value` is the
 with the inputs already resident in HBM. Secondary objects on the same line (same method, HIP events on the
 launch stream): paged GQA decode and MLA absorbed decode in GB/s of algorithmic bytes, the 131072-token prefill
 and the chunked prefill from a paged cache (four 2048-token chunks on 0 / 4096 / 8192 / 14336 cached tokens; one
-step = append with RoPE on K, RoPE on Q, attend) in TFLOP/s.
+step = append with RoPE on K, RoPE on Q, attend) in TFLOP/s, and DeepSeek Sparse Attention decode (lightning indexer
+over 32768 cached tokens, top-2048 selection, sparse MLA) in GB/s of algorithmic bytes.
 
 `roofline` describes the dominant kernel of each workload: achieved = algorithmic work per launch / average
 launch duration (HIP events on the stream the kernel runs on), against MI355X's published peaks (bf16 dense MFMA
@@ -33,7 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from synth import (WORKLOADS, prefill_inputs, paged_decode_inputs, mla_inputs, sampled_rows,  # noqa: E402
-                   chunked_prefill_inputs)
+                   chunked_prefill_inputs, dsa_inputs)
 
 METRIC = "prefill attention TFLOP/s (% bf16 MFMA peak); decode HBM GB/s (% peak)"
 PEAK_BF16_TFLOPS = 2500.0
@@ -42,6 +43,7 @@ KERNEL_SOURCES = {
     "prefill_bf16_kernel": "prefill.hip",
     "decode_paged_split_kernel": "decode.hip",
     "mla_split_kernel": "mla.hip",
+    "dsa_indexer_kernel": "dsa.hip",
 }
 
 
@@ -246,6 +248,59 @@ def bench_chunked(torch, ta, w, steps, warmup, seed=0):
     return wall_ms, kern_ms
 
 
+# ---------------------------------------------------------------------------------------- sparse attention --
+def dsa_bytes(w):
+    """Algorithmic bytes of each DSA kernel: the indexer reads every indexer key, its queries and weights, and
+    writes one fp32 score per token; top-k reads the scores and writes the indices; sparse MLA reads the selected
+    [c_kv ; k_pe] rows, the queries, and writes the latent output."""
+    b, t = w.batch, w.seqlen
+    idx = b * t * w.idx_dim * 2 + b * w.idx_heads * (w.idx_dim * 2 + 4) + b * t * 4
+    topk = b * t * 4 + b * w.topk * 4 + b * 4
+    sparse = (b * w.topk * (w.latent + w.rope) * 2 + b * w.heads * (w.latent + w.rope) * 2 + b * w.heads * w.latent * 2
+              + b * w.topk * 4)
+    return {"indexer": idx, "topk": topk, "sparse_mla": sparse}
+
+
+def bench_dsa(torch, ta, w, steps, warmup, seed=0):
+    log(f"[bench] {w.name}: generating inputs")
+    inp = dsa_inputs(w, seed=seed)
+    qi, ki = dev_bf16(torch, inp["q_idx"]), dev_bf16(torch, inp["k_idx"])
+    wi = torch.from_numpy(inp["w_idx"]).cuda()
+    ql, qp, ckv, kpe = (dev_bf16(torch, inp[n]) for n in ("q_lat", "q_pe", "c_kv", "k_pe"))
+    lens = torch.from_numpy(inp["seq_lens"]).cuda()
+    scores = torch.empty((w.batch, w.seqlen), dtype=torch.float32, device="cuda")
+    idx = torch.empty((w.batch, w.topk), dtype=torch.int32, device="cuda")
+    o = torch.empty_like(ql)
+    ws = torch.empty(ta.attn_mla_sparse_decode_workspace_size(w.batch, w.heads, w.latent, w.topk), dtype=torch.uint8,
+                     device="cuda")
+    timers = {k: EventTimer(torch) for k in ("indexer", "topk", "sparse_mla")}
+
+    def step(timed):
+        for name, fn in (("indexer", lambda: ta.attn_dsa_indexer(qi, wi, ki, lens, scores=scores)),
+                         ("topk", lambda: ta.attn_topk(scores, lens, w.topk, indices=idx)),
+                         ("sparse_mla", lambda: ta.attn_mla_sparse_decode(ql, qp, ckv, kpe, lens, idx, w.scale, o=o,
+                                                                         workspace=ws))):
+            if timed:
+                timers[name].start()
+            fn()
+            if timed:
+                timers[name].stop()
+
+    for _ in range(warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: timing {steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms = {k: t.mean_ms() for k, t in timers.items()}
+    del qi, ki, wi, ql, qp, ckv, kpe, scores, idx, o, ws
+    torch.cuda.empty_cache()
+    return wall_ms, ms
+
+
 # ------------------------------------------------------------------------------------------------ cpu oracle --
 def cpu_baseline(w, n_rows=4096, seed=0):
     """Time the fp64 oracle on `n_rows` seeded query rows (all heads, all batches) of the prefill workload."""
@@ -283,8 +338,8 @@ def main():
     # Warm-up long enough (about 0.1 s of work) for the GPU clock to settle before the timed steps.
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-secondary", action="store_true", help="only the primary prefill workload")
-    ap.add_argument("--workloads", default="prefill,decode,mla,long,chunked",
-                    help="comma list of prefill (primary), decode, mla, long, chunked; profiling runs select one")
+    ap.add_argument("--workloads", default="prefill,decode,mla,long,chunked,dsa",
+                    help="comma list of prefill (primary), decode, mla, long, chunked, dsa; profiling runs select one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration for traffic measurements)")
@@ -311,7 +366,7 @@ def main():
         return
 
     sel = set(args.workloads.split(","))
-    if sel - {"prefill", "decode", "mla", "long", "chunked"}:
+    if sel - {"prefill", "decode", "mla", "long", "chunked", "dsa"}:
         print(f"unknown workloads {sel}", file=sys.stderr)
         sys.exit(2)
     if args.no_secondary:
@@ -373,6 +428,18 @@ def run_secondary(torch, ta, args, sel, line):
                                    "ctx_lens": list(wc.ctx_lens), "new_lens": list(wc.new_lens),
                                    "step": "kv_append_paged (rope k) + rope(q) + prefill_paged",
                                    "roofline": roofline_compute(wc.flops, kern_c, "prefill_bf16_kernel", wc.name)}
+    if "dsa" in sel:
+        ws_ = WORKLOADS["dsa_decode_b32"]
+        wall_s, ms = bench_dsa(torch, ta, ws_, max(20, args.steps), max(100, args.warmup))
+        nb = dsa_bytes(ws_)
+        total = sum(nb.values())
+        line["dsa_decode"] = {
+            "workload": ws_.name, "value": round(total / (wall_s * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "ms_per_step": round(wall_s, 4), "bytes_per_step": total, "topk": ws_.topk, "seqlen": ws_.seqlen,
+            "step": "dsa_indexer + topk + mla_sparse_decode",
+            "kernels": {k: {"ms": round(v, 4), "bytes": nb[k], "GB/s": round(nb[k] / (v * 1e-3) / 1e9, 1)}
+                        for k, v in ms.items()},
+            "roofline": roofline_hbm(nb["indexer"], ms["indexer"], "dsa_indexer_kernel", ws_.name)}
 
 
 if __name__ == "__main__":

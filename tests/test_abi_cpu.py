@@ -226,7 +226,7 @@ def test_topk_validation(lib):
 def test_mla_sparse_validation(lib):
     f = lib.attn_mla_sparse_decode
     need = lib.attn_mla_sparse_decode_workspace_size(2, 128, 512, 256)
-    assert need == lib.attn_mla_decode_workspace_size(2, 128, 512, 256)
+    assert need >= 2 * 128 * 512 * 4                 # at least one fp32 partial per (sequence, head)
     args = lambda **kw: [kw.get(n, d) for n, d in [
         ("ql", FAKE), ("qp", FAKE), ("ckv", FAKE), ("kpe", FAKE), ("lens", FAKE), ("idx", FAKE), ("o", FAKE),
         ("lse", NULL), ("b", 2), ("h", 128), ("c", 512), ("r", 64), ("t", 4096), ("k", 256), ("scale", 0.07),

@@ -95,6 +95,19 @@ def test_topk_ties_signed_zeros_and_infinities():
         np.testing.assert_array_equal(got, ref, err_msg=f"k={k}")
 
 
+def test_topk_long_rows_in_rounds():
+    """Rows longer than one register-resident round (32768 scores), with ties spread across rounds."""
+    ta = require_gpu()
+    rng = np.random.default_rng(69)
+    lens = [70000, 32769, 32768, 65536]
+    sc = rng.standard_normal((4, 70000)).astype(np.float32)
+    sc[1] = rng.integers(0, 50, 70000).astype(np.float32)             # ties everywhere
+    sc[3] = np.round(sc[3] * 4) / 4
+    for k in (5, 2048, 40000):
+        say(f"topk rounds k={k} lens={lens}")
+        np.testing.assert_array_equal(run_topk(ta, sc, lens, k), oracle.topk_indices(sc, lens, k), err_msg=f"k={k}")
+
+
 def run_sparse(ta, w, inp, idx):
     o, lse = ta.attn_mla_sparse_decode(dev_bf16(inp["q_lat"]), dev_bf16(inp["q_pe"]), dev_bf16(inp["c_kv"]),
                                        dev_bf16(inp["k_pe"]), dev(inp["seq_lens"]), dev(np.asarray(idx, np.int32)),

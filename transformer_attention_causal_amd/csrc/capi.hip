@@ -170,7 +170,7 @@ ATTN_EXPORT int attn_topk(const float* scores, const int32_t* seq_lens, int32_t*
 }
 
 ATTN_EXPORT size_t attn_mla_sparse_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int topk) {
-  return attn::mla_decode_workspace_bytes(batch, n_heads, kv_lora_rank, topk);
+  return attn::mla_sparse_workspace_bytes(batch, n_heads, kv_lora_rank, topk);
 }
 
 ATTN_EXPORT int attn_mla_sparse_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
@@ -185,7 +185,7 @@ ATTN_EXPORT int attn_mla_sparse_decode(const void* q_latent, const void* q_pe, c
   if (batch == 0) return ATTN_OK;
   if (!q_latent || !q_pe || !c_kv || !k_pe || !seq_lens || !indices || !o_latent) return ATTN_ERR_INVALID_ARG;
   if (int64_t(max_seqlen_kv) * kv_lora_rank * 2 > (int64_t(1) << 31)) return ATTN_ERR_UNSUPPORTED;
-  const size_t need = attn::mla_decode_workspace_bytes(batch, n_heads, kv_lora_rank, topk);
+  const size_t need = attn::mla_sparse_workspace_bytes(batch, n_heads, kv_lora_rank, topk);
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   return hip_status(attn::launch_mla_sparse_decode(q_latent, q_pe, c_kv, k_pe, seq_lens, indices, o_latent, lse,
                                                    batch, n_heads, max_seqlen_kv, topk, softmax_scale, workspace,

@@ -13,10 +13,11 @@
 // token: ReLU, times the head weight, summed in registers, then one exchange with lane l^32. HBM-bound: every key
 // row is read once (256 bytes per token at D_I = 128) and one fp32 score written.
 //
-// Top-k. One workgroup per sequence finds the k-th largest score by radix selection on an order-preserving 32-bit
-// key (four 8-bit digits from the top; LDS histograms with wave-aggregated atomics for the heavily shared leading
-// digits), then writes the indices above the threshold and the lowest-index ties at it, in ascending order, with
-// two block-wide prefix sums. Deterministic; no workspace.
+// Top-k. One workgroup per sequence holds the sequence's scores in registers (32 per lane for up to 32768 tokens;
+// longer sequences are taken in rounds of 32768) as order-preserving 32-bit keys, finds the k-th largest key by
+// radix selection (four 8-bit digits from the top; LDS histograms in 16 lane-interleaved copies so that the
+// heavily shared leading digits do not serialise the atomics), then writes the indices above the threshold and the
+// lowest-index ties at it, in ascending order, from wave-wide ballot counts. Deterministic; no workspace.
 #include "device.h"
 #include "kernels.h"
 
@@ -97,6 +98,13 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void dsa_indexer_kernel(const ui
 // ---------------------------------------------------------------------------------------------------- top-k --
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kTopkPer = 32;                          // scores per lane held in registers per round
+constexpr int kTopkRound = kTopkThreads * kTopkPer;   // 32768 scores per round (one round for <= 32768 tokens)
+// The digit histogram is kept in kHistCopies copies, lane l counting into copy l % kHistCopies: the leading
+// digits are shared by most keys, and same-address LDS atomics serialise. Copy stride 257 words puts the copies of
+// one bin in distinct banks.
+constexpr int kHistCopies = 16;
+constexpr int kHistStride = 257;
 
 // Order-preserving key: a larger float gives a larger unsigned key (-0 is taken as +0).
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -104,35 +112,22 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum over the workgroup (threads in order); `total` gets the sum. Uses red[0..kTopkWaves).
-__device__ int block_exclusive_scan(int v, int* red, int& total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) red[wave] = x;
-  __syncthreads();
-  int before = 0, sum = 0;
-  for (int i = 0; i < kTopkWaves; ++i) {
-    const int t = red[i];
-    if (i < wave) before += t;
-    sum += t;
-  }
-  __syncthreads();                                     // red is free again
-  total = sum;
-  return before + x - v;
+// Number of set bits of `m` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return int(__builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u)));
 }
 
+// Round r covers scores [r*kTopkRound, (r+1)*kTopkRound); in it wave w owns the contiguous segment of 64*kTopkPer
+// scores starting at w*64*kTopkPer, and lane i holds its scores 64*j + i (j < kTopkPer) as keys in registers, so
+// every pass over a resident round reads registers only and the ordered write-out needs only wave-wide counts.
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
     const int32_t* __restrict__ seq_lens, int32_t* __restrict__ out, int max_len, int k) {
-  __shared__ uint32_t hist[256];
-  __shared__ int red[kTopkWaves];
+  __shared__ uint32_t hist[kHistCopies * kHistStride];
+  __shared__ int wtot[2][kTopkWaves];
   __shared__ uint32_t sel_digit, sel_above;
   const int b = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = max(0, min(seq_lens[b], max_len));
   const int kk = min(k, n);
   const float* s = scores + int64_t(b) * max_len;
@@ -141,33 +136,31 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     for (int i = tid; i < k; i += kTopkThreads) o[i] = i < n ? i : -1;
     return;
   }
+  const int rounds = (n + kTopkRound - 1) / kTopkRound;
+  uint32_t x[kTopkPer];
+  auto first = [&](int r) { return r * kTopkRound + wave * (64 * kTopkPer) + lane; };   // index of x[0]
+  auto load_round = [&](int r) {
+    const int i0 = first(r);
+#pragma unroll
+    for (int j = 0; j < kTopkPer; ++j) x[j] = order_key(s[min(i0 + 64 * j, n - 1)]);   // unconditional: all in flight
+  };
+  if (rounds == 1) load_round(0);
 
   // ---- radix selection of the kk-th largest key: after digit pass p the top 8(p+1) bits of the threshold are
-  // known (prefix under mask) and krem more elements with that prefix must be taken.
+  // known (prefix under mask) and krem more keys with that prefix must be taken.
   uint32_t prefix = 0, mask = 0;
   int krem = kk;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 24 - 8 * pass;
-    if (tid < 256) hist[tid] = 0;
+    for (int i = tid; i < kHistCopies * kHistStride; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
-    for (int i0 = 0; i0 < n; i0 += kTopkThreads) {     // uniform trip count: every lane takes part in the ballots
-      const int i = i0 + tid;
-      uint32_t key = 0;
-      bool act = false;
-      if (i < n) {
-        key = order_key(s[i]);
-        act = (key & mask) == prefix;
-      }
-      const uint32_t d = (key >> shift) & 255u;
-      const uint64_t am = __ballot(act);
-      if (am) {
-        // the digit of the first active lane is counted with one atomic (leading digits are shared by most
-        // keys, and same-address LDS atomics serialise); the others individually
-        const int leader = __builtin_ctzll(am);
-        const uint32_t d0 = __shfl(d, leader, 64);
-        const uint64_t same = __ballot(act && d == d0);
-        if (lane == leader) atomicAdd(&hist[d0], uint32_t(__popcll(same)));
-        if (act && d != d0) atomicAdd(&hist[d], 1u);
+    uint32_t* my_hist = hist + (lane % kHistCopies) * kHistStride;
+    for (int r = 0; r < rounds; ++r) {
+      if (rounds > 1) load_round(r);
+      const int i0 = first(r);
+#pragma unroll
+      for (int j = 0; j < kTopkPer; ++j) {
+        if (i0 + 64 * j < n && (x[j] & mask) == prefix) atomicAdd(&my_hist[(x[j] >> shift) & 255u], 1u);
       }
     }
     __syncthreads();
@@ -175,7 +168,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
       // bins in descending order: lane j takes bins 255-4j .. 252-4j
       uint32_t c[4], t = 0;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) { c[q] = hist[255 - 4 * lane - q]; t += c[q]; }
+      for (int q = 0; q < 4; ++q) {
+        c[q] = 0;
+        for (int cp = 0; cp < kHistCopies; ++cp) c[q] += hist[cp * kHistStride + 255 - 4 * lane - q];
+        t += c[q];
+      }
       uint32_t incl = t;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
@@ -197,26 +194,42 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   }
   const uint32_t thr = prefix;                          // the kk-th largest key; krem ties at thr are taken
 
-  // ---- ordered compaction: thread t owns elements [t*E, (t+1)*E)
-  const int E = (n + kTopkThreads - 1) / kTopkThreads;
-  const int lo = min(n, tid * E), hi = min(n, lo + E);
-  int gt = 0, eq = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = order_key(s[i]);
-    gt += key > thr;
-    eq += key == thr;
-  }
-  int tot;
-  const int eq_before = block_exclusive_scan(eq, red, tot);
-  const int take_eq = max(0, min(eq, krem - eq_before));
-  int pos = block_exclusive_scan(gt + take_eq, red, tot);
-  int taken = 0;
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t key = order_key(s[i]);
-    if (key > thr || (key == thr && taken < take_eq)) {
-      taken += key == thr;
-      if (pos < kk) o[pos] = i;                        // always true for a consistent selection; keeps writes in the row
-      ++pos;
+  // ---- ordered write-out, round by round: keys above thr, and the first krem keys equal to thr (by index).
+  int eq_carry = 0, sel_carry = 0;                      // ties and selections in earlier rounds
+  for (int r = 0; r < rounds; ++r) {
+    if (rounds > 1) load_round(r);
+    const int i0 = first(r);
+    int gtc = 0, eqc = 0;
+#pragma unroll
+    for (int j = 0; j < kTopkPer; ++j) {
+      const bool v = i0 + 64 * j < n;
+      gtc += __popcll(__ballot(v && x[j] > thr));
+      eqc += __popcll(__ballot(v && x[j] == thr));
+    }
+    if (lane == 0) { wtot[0][wave] = gtc; wtot[1][wave] = eqc; }
+    __syncthreads();
+    int eq_seen = eq_carry, pos = sel_carry, eq_run = eq_carry, sel_run = sel_carry;
+    for (int v = 0; v < kTopkWaves; ++v) {              // segments in index order
+      const int g = wtot[0][v], e = wtot[1][v];
+      if (v == wave) { eq_seen = eq_run; pos = sel_run; }
+      sel_run += g + max(0, min(e, krem - eq_run));
+      eq_run += e;
+    }
+    __syncthreads();                                   // wtot is rewritten by the next round
+    eq_carry = eq_run;
+    sel_carry = sel_run;
+#pragma unroll
+    for (int j = 0; j < kTopkPer; ++j) {
+      const int i = i0 + 64 * j;
+      const bool v = i < n;
+      const bool above = v && x[j] > thr, tie = v && x[j] == thr;
+      const uint64_t em = __ballot(tie);
+      const bool sel = above || (tie && eq_seen + lanes_below(em) < krem);
+      const uint64_t sm = __ballot(sel);
+      const int p = pos + lanes_below(sm);
+      if (sel && p < kk) o[p] = i;                     // p < kk always holds for a consistent selection
+      pos += __popcll(sm);
+      eq_seen += __popcll(em);
     }
   }
   for (int i = kk + tid; i < k; i += kTopkThreads) o[i] = -1;

@@ -42,9 +42,10 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
                                int max_seqlen_kv, float scale, void* workspace, hipStream_t stream);
 
 // MLA absorbed decode: split over tokens, then the log-sum-exp combine.
-int mla_num_splits(int batch, int n_heads, int max_seqlen_kv);
-int mla_split_len(int batch, int n_heads, int max_seqlen_kv);
+int mla_num_splits(int batch, int n_heads, int max_seqlen_kv, int target_blocks);
+int mla_split_len(int batch, int n_heads, int max_seqlen_kv, int target_blocks);
 size_t mla_decode_workspace_bytes(int batch, int n_heads, int kv_lora_rank, int max_seqlen_kv);
+size_t mla_sparse_workspace_bytes(int batch, int n_heads, int kv_lora_rank, int topk);
 hipError_t launch_mla_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
                              const int32_t* seq_lens, void* o_latent, float* lse, int batch, int n_heads,
                              int max_seqlen_kv, float scale, void* workspace, hipStream_t stream);

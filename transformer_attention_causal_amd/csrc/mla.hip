@@ -397,25 +397,41 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restric
 
 }  // namespace
 
-int mla_num_splits(int batch, int n_heads, int max_seqlen_kv) {
+// Workgroups the sparse form aims for: its splits are short (top-k tokens), so each split's partial output
+// (heads x 512 fp32) is a large share of its traffic.
+#ifndef ATTN_MLA_SPARSE_TARGET
+#define ATTN_MLA_SPARSE_TARGET 256
+#endif
+
+int mla_num_splits(int batch, int n_heads, int max_seqlen_kv, int target) {
   (void)n_heads;
   if (batch <= 0 || max_seqlen_kv <= 0) return 1;
-  const int by_cu = (kTargetBlocks + batch - 1) / batch;
+  const int by_cu = (target + batch - 1) / batch;
   const int by_len = (max_seqlen_kv + kRows - 1) / kRows;
   return max(1, min(by_cu, by_len));
 }
 
-int mla_split_len(int batch, int n_heads, int max_seqlen_kv) {
-  const int ns = mla_num_splits(batch, n_heads, max_seqlen_kv);
+int mla_split_len(int batch, int n_heads, int max_seqlen_kv, int target) {
+  const int ns = mla_num_splits(batch, n_heads, max_seqlen_kv, target);
   const int per = (max(1, max_seqlen_kv) + ns - 1) / ns;
   return (per + kRows - 1) / kRows * kRows;
 }
 
-size_t mla_decode_workspace_bytes(int batch, int n_heads, int kv_lora_rank, int max_seqlen_kv) {
-  if (batch <= 0 || n_heads <= 0 || kv_lora_rank <= 0 || max_seqlen_kv <= 0) return 0;
-  const size_t slots = size_t(batch) * size_t(n_heads) * size_t(mla_num_splits(batch, n_heads, max_seqlen_kv));
+namespace {
+size_t workspace_bytes(int batch, int n_heads, int kv_lora_rank, int len, int target) {
+  if (batch <= 0 || n_heads <= 0 || kv_lora_rank <= 0 || len <= 0) return 0;
+  const size_t slots = size_t(batch) * size_t(n_heads) * size_t(mla_num_splits(batch, n_heads, len, target));
   const size_t o_bytes = (slots * size_t(kv_lora_rank) * sizeof(float) + 255) & ~size_t(255);
   return o_bytes + slots * sizeof(float);
+}
+}  // namespace
+
+size_t mla_decode_workspace_bytes(int batch, int n_heads, int kv_lora_rank, int max_seqlen_kv) {
+  return workspace_bytes(batch, n_heads, kv_lora_rank, max_seqlen_kv, kTargetBlocks);
+}
+
+size_t mla_sparse_workspace_bytes(int batch, int n_heads, int kv_lora_rank, int topk) {
+  return workspace_bytes(batch, n_heads, kv_lora_rank, topk, ATTN_MLA_SPARSE_TARGET);
 }
 
 hipError_t launch_mla_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
@@ -428,8 +444,8 @@ hipError_t launch_mla_decode(const void* q_latent, const void* q_pe, const void*
   a.k_pe = static_cast<const uint16_t*>(k_pe);
   a.seq_lens = seq_lens;
   a.heads = n_heads; a.max_len = max_seqlen_kv; a.scale = scale;
-  a.n_split = mla_num_splits(batch, n_heads, max_seqlen_kv);
-  a.split_len = mla_split_len(batch, n_heads, max_seqlen_kv);
+  a.n_split = mla_num_splits(batch, n_heads, max_seqlen_kv, kTargetBlocks);
+  a.split_len = mla_split_len(batch, n_heads, max_seqlen_kv, kTargetBlocks);
   const size_t slots = size_t(batch) * size_t(n_heads) * size_t(a.n_split);
   const size_t o_bytes = (slots * kC * sizeof(float) + 255) & ~size_t(255);
   a.ws_o = static_cast<float*>(workspace);
@@ -462,8 +478,8 @@ hipError_t launch_mla_sparse_decode(const void* q_latent, const void* q_pe, cons
   a.idx = indices;
   a.topk = topk;
   a.heads = n_heads; a.max_len = max_seqlen_kv; a.scale = scale;
-  a.n_split = mla_num_splits(batch, n_heads, topk);
-  a.split_len = mla_split_len(batch, n_heads, topk);
+  a.n_split = mla_num_splits(batch, n_heads, topk, ATTN_MLA_SPARSE_TARGET);
+  a.split_len = mla_split_len(batch, n_heads, topk, ATTN_MLA_SPARSE_TARGET);
   const size_t slots = size_t(batch) * size_t(n_heads) * size_t(a.n_split);
   const size_t o_bytes = (slots * kC * sizeof(float) + 255) & ~size_t(255);
   a.ws_o = static_cast<float*>(workspace);
