@@ -7,10 +7,11 @@ Primary line: causal GQA prefill, bf16, B=2 Hq=32 Hkv=8 S=8192 D=128 (workload g
 hot path over one batch: RoPE on Q, RoPE on K, then attn_prefill. `value` is the algorithmic attention flops
 (QK^T and PV over the unmasked pairs, 2 flop per multiply-add) per second of wall time over K timed steps,
 with the inputs already resident in HBM. Secondary objects on the same line (same method, HIP events on the
-launch stream): paged GQA decode and MLA absorbed decode in GB/s of algorithmic bytes, the 131072-token prefill
-and the chunked prefill from a paged cache (four 2048-token chunks on 0 / 4096 / 8192 / 14336 cached tokens; one
-step = append with RoPE on K, RoPE on Q, attend) in TFLOP/s, and DeepSeek Sparse Attention decode (lightning indexer
-over 32768 cached tokens, top-2048 selection, sparse MLA) in GB/s of algorithmic bytes.
+launch stream): paged GQA decode (bf16, FP8 E4M3 and int8 caches) and MLA absorbed decode in GB/s of algorithmic
+bytes, the 131072-token prefill and the chunked prefill from a paged cache (four 2048-token chunks on 0 / 4096 /
+8192 / 14336 cached tokens; one step = append with RoPE on K, RoPE on Q, attend) in TFLOP/s, and DeepSeek Sparse
+Attention decode (lightning indexer over 32768 cached tokens, top-2048 selection, sparse MLA) in GB/s of
+algorithmic bytes.
 
 `roofline` describes the dominant kernel of each workload: achieved = algorithmic work per launch / average
 launch duration (HIP events on the stream the kernel runs on), against MI355X's published peaks (bf16 dense MFMA
@@ -147,19 +148,25 @@ def bench_prefill(torch, ta, w, steps, warmup, seed=0):
 
 # ---------------------------------------------------------------------------------------------- paged decode --
 def decode_bytes(w, inp):
-    """Algorithmic bytes of one decode step: every cached K and V row of every sequence once, q, o, the used block
-    table entries and the lengths."""
+    """Algorithmic bytes of one decode step: every cached K and V row of every sequence once (2 bytes per element,
+    or 1 for an 8-bit cache, plus its scales), q, o, the used block table entries and the lengths."""
     tokens = int(inp["seq_lens"].astype(np.int64).sum())
     pages = int(((inp["seq_lens"].astype(np.int64) + w.page_size - 1) // w.page_size).sum())
     qo = 2 * inp["q"].size * 2
-    return tokens * w.hkv * w.head_dim * 2 * 2 + qo + pages * 4 + inp["seq_lens"].size * 4
+    elem = 1 if inp.get("kv", "bf16") != "bf16" else 2
+    scales = 2 * w.hkv * w.head_dim * 4 if elem == 1 else 0
+    return tokens * w.hkv * w.head_dim * 2 * elem + qo + pages * 4 + inp["seq_lens"].size * 4 + scales
 
 
-def bench_decode(torch, ta, w, steps, warmup, seed=0):
-    log(f"[bench] {w.name}: generating inputs")
-    inp = paged_decode_inputs(w, seed=seed)
+def bench_decode(torch, ta, w, steps, warmup, seed=0, kv="bf16"):
+    log(f"[bench] {w.name} ({kv} cache): generating inputs")
+    inp = paged_decode_inputs(w, seed=seed, kv=kv)
     q = dev_bf16(torch, inp["q"])
-    kc, vc = dev_bf16(torch, inp["k_cache"]), dev_bf16(torch, inp["v_cache"])
+    if kv == "bf16":
+        kc, vc = dev_bf16(torch, inp["k_cache"]), dev_bf16(torch, inp["v_cache"])
+    else:
+        kc, vc = torch.from_numpy(inp["k_cache"]).cuda(), torch.from_numpy(inp["v_cache"]).cuda()
+        ksc, vsc = torch.from_numpy(inp["k_scale"]).cuda(), torch.from_numpy(inp["v_scale"]).cuda()
     table = torch.from_numpy(inp["block_table"]).cuda()
     lens = torch.from_numpy(inp["seq_lens"]).cuda()
     pos = torch.from_numpy(inp["positions"]).cuda()
@@ -171,7 +178,11 @@ def bench_decode(torch, ta, w, steps, warmup, seed=0):
     for i in range(warmup + steps):
         if i >= warmup:
             timer.start()
-        ta.attn_decode_paged(q, kc, vc, table, lens, inp["max_len"], softmax_scale=w.scale, o=o, workspace=ws)
+        if kv == "bf16":
+            ta.attn_decode_paged(q, kc, vc, table, lens, inp["max_len"], softmax_scale=w.scale, o=o, workspace=ws)
+        else:
+            ta.attn_decode_paged_q8(q, kc, vc, ksc, vsc, kv, table, lens, inp["max_len"], softmax_scale=w.scale, o=o,
+                                    workspace=ws)
         if i >= warmup:
             timer.stop()
     torch.cuda.synchronize()
@@ -338,8 +349,9 @@ def main():
     # Warm-up long enough (about 0.1 s of work) for the GPU clock to settle before the timed steps.
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-secondary", action="store_true", help="only the primary prefill workload")
-    ap.add_argument("--workloads", default="prefill,decode,mla,long,chunked,dsa",
-                    help="comma list of prefill (primary), decode, mla, long, chunked, dsa; profiling runs select one")
+    ap.add_argument("--workloads", default="prefill,decode,mla,long,chunked,dsa,decode_fp8,decode_int8",
+                    help="comma list of prefill (primary), decode, mla, long, chunked, dsa, decode_fp8, decode_int8; "
+                         "profiling runs select one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration for traffic measurements)")
@@ -366,7 +378,7 @@ def main():
         return
 
     sel = set(args.workloads.split(","))
-    if sel - {"prefill", "decode", "mla", "long", "chunked", "dsa"}:
+    if sel - {"prefill", "decode", "mla", "long", "chunked", "dsa", "decode_fp8", "decode_int8"}:
         print(f"unknown workloads {sel}", file=sys.stderr)
         sys.exit(2)
     if args.no_secondary:
@@ -405,6 +417,16 @@ def run_secondary(torch, ta, args, sel, line):
                                 "ms": round(ms, 4), "bytes": nbytes, "tokens": tokens,
                                 "roofline": roofline_hbm(nbytes, ms, "decode_paged_split_kernel", wd.name,
                                                          "decode_paged_split_kernel + decode_combine_kernel")}
+    for kv in ("fp8", "int8"):
+        if f"decode_{kv}" not in sel:
+            continue
+        wd = WORKLOADS["paged_decode_b64"]
+        ms, nbytes, tokens = bench_decode(torch, ta, wd, max(20, args.steps), max(100, args.warmup), kv=kv)
+        line[f"paged_decode_{kv}"] = {
+            "workload": wd.name, "kv_cache": kv, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+            "ms": round(ms, 4), "bytes": nbytes, "tokens": tokens,
+            "roofline": roofline_hbm(nbytes, ms, "decode_paged_split_kernel", f"{wd.name}_{kv}",
+                                     "decode_paged_split_kernel + decode_combine_kernel")}
     if "mla" in sel:
         wm = WORKLOADS["mla_decode_b32"]
         ms = bench_mla(torch, ta, wm, max(20, args.steps), max(300, args.warmup))

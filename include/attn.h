@@ -4,6 +4,7 @@
  *   attn_rope_apply       rotary position embedding, in place
  *   attn_prefill          causal (or full) grouped-query attention over a whole sequence
  *   attn_decode_paged     one query token per sequence against a paged KV cache (split-KV + log-sum-exp combine)
+ *   attn_decode_paged_q8  the same over 8-bit (FP8 E4M3 or int8) K/V caches with per-channel scales
  *   attn_mla_decode       multi-head latent attention decode in the absorbed form
  *   attn_kv_append_paged  write new tokens' keys (rotated) and values into a paged KV cache
  *   attn_prefill_paged    chunked / variable-length causal prefill of new tokens against a paged KV cache
@@ -45,6 +46,9 @@ extern "C" {
 #endif
 
 typedef enum { ATTN_BF16 = 0, ATTN_FP32 = 1 } attn_dtype_t;
+
+/* 8-bit KV cache element kinds (attn_decode_paged_q8). */
+typedef enum { ATTN_KV_FP8_E4M3 = 1, ATTN_KV_INT8 = 2 } attn_kv8_t;
 
 typedef enum {
   ATTN_OK = 0,
@@ -117,6 +121,22 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, c
                       const int32_t* seq_lens, void* o, float* lse, int batch, int n_heads_q, int n_heads_kv,
                       int head_dim, int page_size, int max_pages_per_seq, int64_t num_pages, int max_seqlen_kv,
                       float softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Paged decode over 8-bit K/V caches: attn_decode_paged where each cached value is code * scale[kv_head][channel].
+ * ("DeepSeek 32K to 256K long context", tqpw.cn, section 2.5: K and V kept as int8 with per-channel scales;
+ *  "7 anti-patterns of DeepSeek attention optimisation", lpnh.cn, section 3.3: FP8 E4M3, largest value 448.)
+ *   k_cache, v_cache  [num_pages, page_size, n_heads_kv, head_dim] bytes: OCP FP8 E4M3 codes (kv_kind
+ *                ATTN_KV_FP8_E4M3; the NaN code S.1111.111 must not occur) or int8 (ATTN_KV_INT8), 16-byte aligned.
+ *   k_scale, v_scale  [n_heads_kv, head_dim] fp32 per-channel scales (16-byte aligned).
+ *   Everything else as attn_decode_paged (same workspace size). The K scale is folded into the query, rounded to
+ *   bf16 once per query; the V scale multiplies the output channels in fp32.
+ * Supported and INVALID_ARG as attn_decode_paged, plus INVALID_ARG for a misaligned pointer and UNSUPPORTED for
+ * another kv_kind. */
+int attn_decode_paged_q8(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                         const float* v_scale, int kv_kind, const int32_t* block_table, const int32_t* seq_lens,
+                         void* o, float* lse, int batch, int n_heads_q, int n_heads_kv, int head_dim, int page_size,
+                         int max_pages_per_seq, int64_t num_pages, int max_seqlen_kv, float softmax_scale,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace attn_mla_decode needs for these sizes (0 if any size is non-positive). */
 size_t attn_mla_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int max_seqlen_kv);

@@ -22,4 +22,8 @@ from .attention import (  # noqa: F401
     dsa_indexer_scores,
     topk_indices,
     mla_sparse_decode,
+    fp8_e4m3_decode,
+    int8_decode,
+    dequantize_kv,
+    decode_paged_q8,
 )

@@ -12,6 +12,8 @@ Pages cited (by title, as they appear on the web):
   [V3]  "DeepSeek-V3 attention guide: einsum vs manual optimisation" (dksg.cn): the naive and the absorbed
         score einsums quoted from the model's inference code.
   [AP]  "7 anti-patterns of DeepSeek attention optimisation" (lpnh.cn): §4.2 GQA cache reorder.
+  [LC-KV] [LC] §2.5, KV-cache compression: keys and values stored as 8-bit integers with a per-channel scale.
+  [AP-F8] [AP] §3.3: FP8 E4M3, whose largest finite value is 448.
   [AN-LI] the "Lighting Indexer" section of [AN]: DeepSeek Sparse Attention scores every earlier token with
         sum over indexer heads j of w_j * ReLU(q_j . k_s) and attends only the most relevant tokens.
 
@@ -32,14 +34,18 @@ Readings taken where the pages are silent or garbled:
     key per token shared by all indexer heads, one weight per (query token, indexer head); "the most relevant
     tokens" are the top_k largest scores, ties broken towards the lower token index (the page names no rule);
     a sequence with at most top_k tokens keeps all of them; sparse attention is the absorbed MLA attention
-    restricted to the selected tokens.
+    restricted to the selected tokens;
+  * 8-bit KV caches ([LC-KV], [AP-F8]): a cached value is code * scale[kv_head, channel], the code being an int8
+    (two's complement) or an OCP FP8 E4M3 byte (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is
+    subnormal; no infinities, S.1111.111 is NaN) and the scale an fp32 per (KV head, channel) for K and for V;
+    attention is then exactly decode_paged on the dequantised caches.
 """
 import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64", "rope_inv_freq", "rope", "attention_prefill", "attention_prefill_rows", "gather_paged",
     "decode_paged", "mla_decode", "mla_naive", "kv_append_paged", "prefill_paged", "dsa_indexer_scores",
-    "topk_indices", "mla_sparse_decode",
+    "topk_indices", "mla_sparse_decode", "fp8_e4m3_decode", "int8_decode", "dequantize_kv", "decode_paged_q8",
 ]
 
 
@@ -334,3 +340,33 @@ def mla_sparse_decode(q_lat, q_pe, c_kv, k_pe, seq_lens, indices, scale):
         sc = scale * (qry @ keys.T)
         o[b], lse[b] = _softmax_rows_then_v(sc, c_kv[b, sel])
     return o, lse
+
+
+def fp8_e4m3_decode(codes):
+    """Value of each OCP FP8 E4M3 byte ([AP-F8]): bit 7 sign, bits 6..3 exponent e (bias 7), bits 2..0 mantissa m;
+    e = 0 is subnormal (m/8 * 2^-6), otherwise (1 + m/8) * 2^(e-7); e = 15 with m = 7 is NaN (no infinities, so
+    the largest finite value is 1.75 * 2^8 = 448). Returns float64."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2((e - 7).astype(np.float64)))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return sign * mag
+
+
+def int8_decode(codes):
+    """Value of each int8 byte (two's complement). Returns float64."""
+    return np.asarray(codes, np.uint8).view(np.int8).astype(np.float64)
+
+
+def dequantize_kv(codes, scale, kind):
+    """8-bit cache [num_pages, page_size, Hkv, D] -> float64 values code * scale[kv_head, channel] ([LC-KV])."""
+    dec = fp8_e4m3_decode(codes) if kind == "fp8" else int8_decode(codes)
+    return dec * np.asarray(scale, np.float64)[None, None]
+
+
+def decode_paged_q8(q, k_codes, v_codes, k_scale, v_scale, kind, block_table, seq_lens, scale):
+    """Paged decode over 8-bit K/V caches: decode_paged on the dequantised caches. kind: "fp8" or "int8"."""
+    return decode_paged(q, dequantize_kv(k_codes, k_scale, kind), dequantize_kv(v_codes, v_scale, kind), block_table,
+                        seq_lens, scale)

@@ -1,7 +1,8 @@
 """Seeded synthetic inputs shared by the oracle tests, the GPU tests and the benchmark.
 
 Holds none of the method's arithmetic: it draws iid N(0, 1) values, rounds them to bfloat16 (round to nearest
-even), and builds block tables, sequence lengths, positions and sampled rows. Every tensor has its own random
+even) or encodes them as 8-bit cache codes (FP8 E4M3 or int8, nearest-even, with per-channel scales), and builds
+block tables, sequence lengths, positions and sampled rows. Every tensor has its own random
 stream: numpy PCG64 seeded by SeedSequence(seed, spawn_key=(tensor id, chunk)), so values do not depend on how many
 threads draw them. bf16 tensors are returned as their uint16 bit patterns, fp32 tensors as float32.
 """
@@ -35,18 +36,45 @@ def _workers():
     return max(1, min(16, n))
 
 
-def normal(seed, name, shape, dtype):
-    """iid N(0, 1) of the given shape; dtype "bf16" -> uint16 bits, "fp32" -> float32."""
+def f32_to_e4m3_bits(x):
+    """Round float32 to the OCP FP8 E4M3 byte, nearest-even, saturating at +-448 (never produces the NaN code)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    sign = (x.view(np.uint32) >> np.uint32(24)) & np.uint32(0x80)
+    a = np.abs(x)
+    u = a.view(np.uint32)
+    lsb = (u >> np.uint32(20)) & np.uint32(1)
+    r = (u + np.uint32(0x7FFFF) + lsb) >> np.uint32(20)           # float32 exponent and top 3 mantissa bits, rounded
+    normal_code = np.minimum(r.astype(np.int64) - (120 << 3), 0x7E)  # rebias 127 -> 7; saturate at 448
+    sub_code = np.rint(a * np.float32(512.0)).astype(np.int64)       # below 2^-6: m * 2^-9, m = 0..8
+    code = np.where(a < np.float32(2.0 ** -6), sub_code, normal_code)
+    return (code.astype(np.uint32) | sign).astype(np.uint8)
+
+
+def f32_to_int8_bits(x):
+    """Round float32 to int8, nearest-even, clipped to [-127, 127]; returned as the uint8 byte."""
+    return np.clip(np.rint(np.asarray(x, np.float32)), -127, 127).astype(np.int8).view(np.uint8)
+
+
+def normal(seed, name, shape, dtype, q8=None):
+    """iid N(0, 1) of the given shape; dtype "bf16" -> uint16 bits, "fp32" -> float32. With q8 = (scale, kind) the
+    values are divided by scale (broadcast over the trailing dimensions) and stored as 8-bit codes, kind "fp8"
+    (E4M3) or "int8"."""
     n = int(np.prod(shape, dtype=np.int64))
-    out = np.empty(n, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    out = np.empty(n, dtype=np.uint8 if q8 else (np.uint16 if dtype == "bf16" else np.float32))
     tid = _tensor_id(name)
+    if q8:
+        inv = (1.0 / np.asarray(q8[0], np.float64)).astype(np.float32).ravel()
+        enc = f32_to_e4m3_bits if q8[1] == "fp8" else f32_to_int8_bits
 
     def fill(ci):
         lo = ci * _CHUNK
         hi = min(n, lo + _CHUNK)
         rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=(tid, ci))))
         vals = rng.standard_normal(hi - lo, dtype=np.float32)
-        out[lo:hi] = f32_to_bf16_bits(vals) if dtype == "bf16" else vals
+        if q8:
+            out[lo:hi] = enc(vals * inv[np.arange(lo, hi) % inv.size])
+        else:
+            out[lo:hi] = f32_to_bf16_bits(vals) if dtype == "bf16" else vals
 
     n_chunks = (n + _CHUNK - 1) // _CHUNK
     if n_chunks <= 1:
@@ -83,7 +111,15 @@ def sampled_rows(seqlen, n, seed=0):
     return np.sort(np.concatenate([[0, seqlen - 1], inner])).astype(np.int64)
 
 
-def paged_decode_inputs(w: PagedDecode, seed=0, batch=None, seq_lens=None, page_size=None, max_len=None):
+def kv_scales(seed, w, kind):
+    """Per-(KV head, channel) fp32 scales for an 8-bit cache of N(0,1) values: 4 / code_max times a seeded factor in
+    [0.75, 1.25] (so about 4 standard deviations fill the code range), as k_scale, v_scale [Hkv, D]."""
+    top = 448.0 if kind == "fp8" else 127.0
+    f = _rng(seed, "decode.kv_scale").uniform(0.75, 1.25, size=(2, w.hkv, w.head_dim))
+    return (4.0 / top * f).astype(np.float32)
+
+
+def paged_decode_inputs(w: PagedDecode, seed=0, batch=None, seq_lens=None, page_size=None, max_len=None, kv="bf16"):
     """A paged KV cache placed by a seeded random block table.
 
     Returns dict with q [B, Hq, D] (not yet rotated), k_cache / v_cache [N_pool, page, Hkv, D], block_table
@@ -111,10 +147,16 @@ def paged_decode_inputs(w: PagedDecode, seed=0, batch=None, seq_lens=None, page_
         off += int(n_pages[i])
     spare = np.sort(perm[off:])
     q = normal(seed, "decode.q", (b, w.hq, w.head_dim), "bf16")
-    kc = normal(seed, "decode.k", (n_pool, ps, w.hkv, w.head_dim), "bf16")
-    vc = normal(seed, "decode.v", (n_pool, ps, w.hkv, w.head_dim), "bf16")
-    return dict(q=q, k_cache=kc, v_cache=vc, block_table=table, seq_lens=seq_lens,
-                positions=(seq_lens - 1).astype(np.int32), spare_pages=spare, max_len=max_len)
+    out = dict(q=q, block_table=table, seq_lens=seq_lens, positions=(seq_lens - 1).astype(np.int32),
+               spare_pages=spare, max_len=max_len)
+    shape = (n_pool, ps, w.hkv, w.head_dim)
+    if kv == "bf16":
+        out.update(k_cache=normal(seed, "decode.k", shape, "bf16"), v_cache=normal(seed, "decode.v", shape, "bf16"))
+    else:                     # 8-bit codes of the same N(0,1) draws, with per-channel scales
+        sk, sv = kv_scales(seed, w, kv)
+        out.update(k_cache=normal(seed, "decode.k", shape, None, q8=(sk, kv)),
+                   v_cache=normal(seed, "decode.v", shape, None, q8=(sv, kv)), k_scale=sk, v_scale=sv, kv=kv)
+    return out
 
 
 def mla_inputs(w: MLADecode, seed=0, batch=None, seqlen=None, seq_lens=None):

@@ -32,7 +32,7 @@ def lib():
 def test_header_declares_the_operations():
     names = declared_functions()
     for n in ("attn_rope_apply", "attn_prefill", "attn_decode_paged", "attn_mla_decode", "attn_kv_append_paged",
-              "attn_prefill_paged", "attn_dsa_indexer", "attn_topk", "attn_mla_sparse_decode"):
+              "attn_prefill_paged", "attn_dsa_indexer", "attn_topk", "attn_mla_sparse_decode", "attn_decode_paged_q8"):
         assert n in names
 
 
@@ -238,5 +238,25 @@ def test_mla_sparse_validation(lib):
     assert f(*args(c=256)) == UNSUPPORTED
     assert f(*args(h=40)) == UNSUPPORTED
     assert f(*args(t=1 << 23)) == UNSUPPORTED         # latent rows of one sequence beyond a 32-bit resource
+    assert f(*args(wsb=need - 1)) == WORKSPACE
+    assert f(*args(b=0)) == OK
+
+
+def test_decode_q8_validation(lib):
+    f = lib.attn_decode_paged_q8
+    A = ctypes.c_void_p(0x10000)
+    U = ctypes.c_void_p(0x10008)
+    need = lib.attn_decode_paged_workspace_size(2, 32, 128, 4096)
+    args = lambda **kw: [kw.get(n, d) for n, d in [
+        ("q", A), ("kc", A), ("vc", A), ("ks", A), ("vs", A), ("kind", 1), ("table", FAKE), ("lens", FAKE),
+        ("o", FAKE), ("lse", NULL), ("b", 2), ("hq", 32), ("hkv", 8), ("d", 128), ("page", 64), ("maxp", 64),
+        ("npages", 200), ("t", 4096), ("scale", 0.088), ("ws", FAKE), ("wsb", need), ("stream", NULL)]]
+    assert f(*args(hq=30)) == INVALID
+    assert f(*args(ks=NULL)) == INVALID
+    assert f(*args(kc=U)) == INVALID                  # 16-byte aligned rows
+    assert f(*args(scale=0.0)) == INVALID
+    assert f(*args(kind=0)) == UNSUPPORTED            # bf16 caches go through attn_decode_paged
+    assert f(*args(kind=3)) == UNSUPPORTED
+    assert f(*args(d=64)) == UNSUPPORTED
     assert f(*args(wsb=need - 1)) == WORKSPACE
     assert f(*args(b=0)) == OK

@@ -614,3 +614,59 @@ def test_dsa_pipeline_with_large_k_is_dense_mla():
     o, _ = oracle.mla_sparse_decode(q_lat, q_pe, c_kv, k_pe, lens, idx, 0.3)
     o_ref, _ = oracle.mla_decode(q_lat, q_pe, c_kv, k_pe, lens, 0.3)
     np.testing.assert_allclose(o, o_ref, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------------------------- 8-bit KV ----
+
+def test_fp8_e4m3_printed_maximum_and_closed_forms():
+    v = oracle.fp8_e4m3_decode
+    assert v([0x7E])[0] == 448.0 and v([0xFE])[0] == -448.0          # the largest finite E4M3 value the page prints
+    assert v([0x38])[0] == 1.0 and v([0x40])[0] == 2.0 and v([0x30])[0] == 0.5
+    assert v([0x08])[0] == 2.0 ** -6 and v([0x01])[0] == 2.0 ** -9    # smallest normal, smallest subnormal
+    assert v([0x07])[0] == 7 * 2.0 ** -9                              # largest subnormal
+    assert np.isnan(v([0x7F])[0]) and np.isnan(v([0xFF])[0])
+    assert v([0x80])[0] == 0.0 and np.signbit(v([0x80])[0])
+
+
+def test_fp8_e4m3_all_codes_match_torch_and_are_monotone():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = oracle.fp8_e4m3_decode(codes)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    np.testing.assert_array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    pos = got[:0x7F]                                                   # 0x00 .. 0x7E increase strictly
+    assert np.all(np.diff(pos) > 0)
+
+
+def test_int8_decode_is_twos_complement():
+    np.testing.assert_array_equal(oracle.int8_decode([0, 1, 127, 128, 255, 0x81]), [0, 1, 127, -128, -1, -127])
+
+
+def test_q8_decode_scales_are_per_channel_and_linear():
+    """Scaling K's channel d by s_d equals scaling the query's channel d; scaling V's channel d scales output
+    channel d; with unit scales the 8-bit decode is decode_paged on the decoded codes."""
+    rng = np.random.default_rng(70)
+    B, Hq, Hkv, D, page, T = 2, 4, 2, 8, 4, 10
+    lens = np.array([10, 7])
+    kc = rng.integers(0, 256, (6, page, Hkv, D)).astype(np.uint8)
+    vc = rng.integers(0, 256, (6, page, Hkv, D)).astype(np.uint8)
+    kc[(kc & 0x7F) == 0x7F] = 0x3C                                       # no NaN codes
+    vc[(vc & 0x7F) == 0x7F] = 0x3C
+    table = np.array([[0, 3, 5], [1, 4, -1]], np.int32)
+    q = rng.standard_normal((B, Hq, D))
+    ones = np.ones((Hkv, D))
+    sk = rng.uniform(0.01, 0.1, (Hkv, D)); sv = rng.uniform(0.01, 0.1, (Hkv, D))
+    for kind in ("fp8", "int8"):
+        dec = oracle.fp8_e4m3_decode if kind == "fp8" else oracle.int8_decode
+        o1, l1 = oracle.decode_paged_q8(q, kc, vc, ones, ones, kind, table, lens, 0.3)
+        o2, l2 = oracle.decode_paged(q, dec(kc), dec(vc), table, lens, 0.3)
+        np.testing.assert_array_equal(o1, o2); np.testing.assert_array_equal(l1, l2)
+        # K scale == query scaled per channel by the scale of its KV head
+        o3, l3 = oracle.decode_paged_q8(q, kc, vc, sk, ones, kind, table, lens, 0.3)
+        qs = q * sk[np.arange(Hq) // (Hq // Hkv)][None]
+        o4, l4 = oracle.decode_paged_q8(qs, kc, vc, ones, ones, kind, table, lens, 0.3)
+        np.testing.assert_allclose(o3, o4, atol=1e-13); np.testing.assert_allclose(l3, l4, atol=1e-13)
+        # V scale == output scaled per channel
+        o5, _ = oracle.decode_paged_q8(q, kc, vc, ones, sv, kind, table, lens, 0.3)
+        np.testing.assert_allclose(o5, o1 * sv[np.arange(Hq) // (Hq // Hkv)][None], atol=1e-13)

@@ -8,6 +8,7 @@ from .binding import (  # noqa: F401
     LIB_PATH,
     SIGNATURES,
     attn_decode_paged,
+    attn_decode_paged_q8,
     attn_decode_paged_workspace_size,
     attn_dsa_indexer,
     attn_kv_append_paged,

@@ -14,6 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
 
 ATTN_BF16, ATTN_FP32 = 0, 1
+ATTN_KV_FP8_E4M3, ATTN_KV_INT8 = 1, 2
 STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_WORKSPACE",
           4: "ATTN_ERR_HIP"}
 
@@ -24,6 +25,8 @@ SIGNATURES = {
     "attn_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "attn_decode_paged_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _I, _F, _P, _SZ, _P]),
+    "attn_decode_paged_q8": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _I, _F, _P, _SZ,
+                                  _P]),
     "attn_mla_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "attn_mla_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "attn_kv_append_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _D, _I, _P]),
@@ -276,4 +279,31 @@ def attn_mla_sparse_decode(q_latent, q_pe, c_kv, k_pe, seq_lens, indices, softma
         _dev(seq_lens, "seq_lens", torch.int32), _dev(indices, "indices", torch.int32),
         _dev(o, "o_latent", torch.bfloat16), lse_p, bsz, nh, c, r, t, topk, float(softmax_scale),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(q_latent, stream)))
+    return (o, lse) if return_lse else o
+
+
+def attn_decode_paged_q8(q, k_cache, v_cache, k_scale, v_scale, kv_kind, block_table, seq_lens, max_seqlen_kv,
+                         softmax_scale=None, o=None, lse=None, workspace=None, return_lse=False, stream=None):
+    """As attn_decode_paged over 8-bit caches: k_cache / v_cache uint8 [num_pages, page, Hkv, D] holding FP8 E4M3
+    (kv_kind "fp8") or int8 ("int8") codes, k_scale / v_scale fp32 [Hkv, D]."""
+    lib = load_library()
+    bsz, hq, d = q.shape
+    num_pages, page, hkv, _ = k_cache.shape
+    kind = {"fp8": ATTN_KV_FP8_E4M3, "int8": ATTN_KV_INT8}[kv_kind]
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((bsz, hq), dtype=torch.float32, device=q.device)
+    need = attn_decode_paged_workspace_size(bsz, hq, d, max(1, int(max_seqlen_kv)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
+    _check("attn_decode_paged_q8", lib.attn_decode_paged_q8(
+        _dev(q, "q", torch.bfloat16), _dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32), kind,
+        _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+        _dev(o, "o", torch.bfloat16), lse_p, bsz, hq, hkv, d, page, block_table.shape[1], num_pages,
+        int(max_seqlen_kv), scale, _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(q, stream)))
     return (o, lse) if return_lse else o

@@ -85,6 +85,34 @@ ATTN_EXPORT int attn_decode_paged(const void* q, const void* k_cache, const void
                                               static_cast<hipStream_t>(stream)));
 }
 
+ATTN_EXPORT int attn_decode_paged_q8(const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                                     const float* v_scale, int kv_kind, const int32_t* block_table,
+                                     const int32_t* seq_lens, void* o, float* lse, int batch, int n_heads_q,
+                                     int n_heads_kv, int head_dim, int page_size, int max_pages_per_seq,
+                                     int64_t num_pages, int max_seqlen_kv, float softmax_scale, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (batch < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0 || max_seqlen_kv < 0) return ATTN_ERR_INVALID_ARG;
+  if (n_heads_q % n_heads_kv != 0 || !valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (page_size <= 0 || max_pages_per_seq < 0) return ATTN_ERR_INVALID_ARG;
+  if (kv_kind != ATTN_KV_FP8_E4M3 && kv_kind != ATTN_KV_INT8) return ATTN_ERR_UNSUPPORTED;
+  if (head_dim != 128 || n_heads_q / n_heads_kv > 16) return ATTN_ERR_UNSUPPORTED;
+  if (!is_pow2(page_size) || page_size < 16 || page_size > 1024) return ATTN_ERR_UNSUPPORTED;
+  if (batch == 0) return ATTN_OK;
+  if (!q || !seq_lens || !o || !k_scale || !v_scale) return ATTN_ERR_INVALID_ARG;
+  if (max_seqlen_kv > 0 && (!k_cache || !v_cache || !block_table || num_pages <= 0 || max_pages_per_seq <= 0))
+    return ATTN_ERR_INVALID_ARG;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_cache) |
+                          reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(k_scale) |
+                          reinterpret_cast<uintptr_t>(v_scale);
+  if (align % 16 != 0) return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn::decode_paged_workspace_bytes(batch, n_heads_q, head_dim, max(1, max_seqlen_kv));
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  return hip_status(attn::launch_decode_paged_q8(kv_kind == ATTN_KV_FP8_E4M3 ? 1 : 0, q, k_cache, v_cache, k_scale,
+                                                 v_scale, block_table, seq_lens, o, lse, batch, n_heads_q, n_heads_kv,
+                                                 page_size, max_pages_per_seq, num_pages, max_seqlen_kv, softmax_scale,
+                                                 workspace, static_cast<hipStream_t>(stream)));
+}
+
 ATTN_EXPORT size_t attn_mla_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, int max_seqlen_kv) {
   return attn::mla_decode_workspace_bytes(batch, n_heads, kv_lora_rank, max_seqlen_kv);
 }

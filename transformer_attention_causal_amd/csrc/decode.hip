@@ -19,6 +19,16 @@
 //   * Pages are looked up once per 16 keys (page size is a power of two >= 16, so 16 aligned keys share a page).
 //   * Partial (O / l, lse) per chunk goes to the workspace; the combine kernel merges a sequence's chunks.
 // Split boundaries are logical key positions, so the result does not depend on physical page placement.
+//
+// 8-bit caches ("7 anti-patterns of DeepSeek attention optimisation", lpnh.cn, section 3.3: FP8 E4M3, largest
+// value 448; "DeepSeek 32K to 256K long context", tqpw.cn, section 2.5: int8 K/V with per-channel scales): the
+// same kernel reads one byte per element. Every E4M3 and int8 value is exact in bf16, so codes become MFMA
+// operands by exact conversion (v_cvt_scalef32_pk_bf16_fp8 with scale 1; int8 through float). The per-channel K
+// scale is folded into the query (q_d * k_scale_d, rounded to bf16 once per query); the per-channel V scale
+// multiplies the output channels at the end. For the K loads the contraction order over the 128 dims is
+// permuted (k-steps 2i and 2i+1 of lane group g take dims 64i + 16g .. +15) so a lane loads 16 contiguous bytes.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -33,15 +43,16 @@ static_assert(kDecodeChunk % 32 == 0 && kDecodeChunk / 16 <= 64, "a chunk's page
 #ifndef ATTN_DECODE_HEAD_MAJOR
 #define ATTN_DECODE_HEAD_MAJOR 0
 #endif
-// Build-time choice: software-prefetch the next 32 keys' K/V while computing on the current ones.
-#ifndef ATTN_DECODE_PREFETCH
-#define ATTN_DECODE_PREFETCH 0
-#endif
+
+// Cache element kinds: 0 bf16, 1 FP8 E4M3 codes, 2 int8 codes (the 8-bit kinds carry per-channel scales).
+constexpr int kKvBf16 = 0, kKvFp8 = 1, kKvInt8 = 2;
 
 struct DecodeArgs {
   const uint16_t* q;
-  const uint16_t* kc;
-  const uint16_t* vc;
+  const void* kc;
+  const void* vc;
+  const float* k_scale;    // 8-bit caches: [hkv, D]
+  const float* v_scale;
   const int32_t* table;
   const int32_t* seq_lens;
   float* ws_o;      // [batch, hq, n_chunks, D]
@@ -62,6 +73,27 @@ __device__ __forceinline__ bf16x8_t transpose_pick(const u32x4_t* vv, int j) {
   return as_bf16x8(w);
 }
 
+// Two 8-bit codes (bytes 0-1, or 2-3 when hi) of `w` as two bf16 (exact).
+template <int KV>
+__device__ __forceinline__ uint32_t codes_to_bf16x2(uint32_t w, bool hi) {
+  if constexpr (KV == kKvFp8) {
+    return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  } else {
+    const uint32_t u = w ^ 0x80808080u;               // biased bytes: code + 128
+    const int sh = hi ? 16 : 0;
+    return pack_bf16x2(float((u >> sh) & 255u) - 128.f, float((u >> (sh + 8)) & 255u) - 128.f);
+  }
+}
+
+// Eight 8-bit codes (two dwords) as eight bf16 (four dwords), in order.
+template <int KV>
+__device__ __forceinline__ u32x4_t codes_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return u32x4_t{codes_to_bf16x2<KV>(w0, false), codes_to_bf16x2<KV>(w0, true), codes_to_bf16x2<KV>(w1, false),
+                 codes_to_bf16x2<KV>(w1, true)};
+}
+
+template <int KV>
 __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
 #if ATTN_DECODE_HEAD_MAJOR
   const int g = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
@@ -79,12 +111,20 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
   const bool hv = n < G;
   const float c = a.scale * kLog2e;
 
-  // Q^T operand: lane holds head n, dims 8*(4*ks + grp4) .. +7 for k-step ks.
+  // Q^T operand: lane holds head n, dims kdim(ks) .. +7 for k-step ks (8-bit caches: times the K scale).
+  auto kdim = [&](int ks) { return KV == kKvBf16 ? 8 * (4 * ks + grp4) : 64 * (ks >> 1) + 16 * grp4 + 8 * (ks & 1); };
   bf16x8_t qop[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     u32x4_t w = {0u, 0u, 0u, 0u};
-    if (hv) w = *reinterpret_cast<const u32x4_t*>(a.q + (int64_t(b) * a.hq + h) * kD + 8 * (4 * ks + grp4));
+    if (hv) w = *reinterpret_cast<const u32x4_t*>(a.q + (int64_t(b) * a.hq + h) * kD + kdim(ks));
+    if constexpr (KV != kKvBf16) {
+      const float* ks_p = a.k_scale + g * kD + kdim(ks);
+      w = u32x4_t{pack_bf16x2(bf16lo_to_f32(w[0]) * ks_p[0], bf16hi_to_f32(w[0]) * ks_p[1]),
+                  pack_bf16x2(bf16lo_to_f32(w[1]) * ks_p[2], bf16hi_to_f32(w[1]) * ks_p[3]),
+                  pack_bf16x2(bf16lo_to_f32(w[2]) * ks_p[4], bf16hi_to_f32(w[2]) * ks_p[5]),
+                  pack_bf16x2(bf16lo_to_f32(w[3]) * ks_p[6], bf16hi_to_f32(w[3]) * ks_p[7])};
+    }
     qop[ks] = as_bf16x8(w);
   }
   f32x4_t oacc[8];
@@ -103,6 +143,44 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
   // K fragments (key t0 + 16*tb + n, dims 8*(4*ks + grp4) ..) and V rows (slot s: key t0 + 16*(s/4) + 4*grp4 + s%4,
   // dims 8n .. 8n+7) of the 32 keys at t0. Pages are looked up once per 16-key half (wave-uniform); keys at or past
   // t_end and pages outside [0, num_pages) are never dereferenced (zeros instead).
+  using E = std::conditional_t<KV == kKvBf16, uint16_t, uint8_t>;
+  const E* kcache = static_cast<const E*>(a.kc);
+  const E* vcache = static_cast<const E*>(a.vc);
+  // 8-bit caches: K of key 16*tb + n as two 16-byte pieces (dims 16*grp4 .., 64 + 16*grp4 ..), V rows as 8 bytes.
+  auto load32_q8 = [&](int t0, u32x4_t (&kv8)[2][2], u32x2_t (&vv8)[8]) {
+    int pg[2];
+    bool pv[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int tt = min(t0 + 16 * hf, t_end - 1);
+      pg[hf] = __builtin_amdgcn_readlane(pg_lane, (tt >> a.page_shift) - first_page);
+      pv[hf] = pg[hf] >= 0 && pg[hf] < a.num_pages;
+    }
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb) {
+      const int key = t0 + 16 * tb + n;
+      const bool ok = key < t_end && pv[tb];
+      const E* kp = kcache + int64_t(pg[tb]) * page_stride + int64_t(key & (page_size - 1)) * row_stride +
+                    int64_t(g) * kD + 16 * grp4;
+#pragma unroll
+      for (int hk = 0; hk < 2; ++hk) {
+        u32x4_t w = {0u, 0u, 0u, 0u};
+        if (ok) w = *reinterpret_cast<const u32x4_t*>(kp + 64 * hk);
+        kv8[tb][hk] = w;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int hf = s >> 2;
+      const int key = t0 + 16 * hf + 4 * grp4 + (s & 3);
+      const bool ok = key < t_end && pv[hf];
+      u32x2_t w = {0u, 0u};
+      if (ok)
+        w = *reinterpret_cast<const u32x2_t*>(vcache + int64_t(pg[hf]) * page_stride +
+                                              int64_t(key & (page_size - 1)) * row_stride + int64_t(g) * kD + 8 * n);
+      vv8[s] = w;
+    }
+  };
   auto load32 = [&](int t0, u32x4_t (&kv)[2][4], u32x4_t (&vv)[8]) {
     int pg[2];
     bool pv[2];
@@ -116,8 +194,8 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
     for (int tb = 0; tb < 2; ++tb) {
       const int key = t0 + 16 * tb + n;
       const bool ok = key < t_end && pv[tb];
-      const uint16_t* kp = a.kc + int64_t(pg[tb]) * page_stride + int64_t(key & (page_size - 1)) * row_stride +
-                           int64_t(g) * kD + 8 * grp4;
+      const E* kp = kcache + int64_t(pg[tb]) * page_stride + int64_t(key & (page_size - 1)) * row_stride +
+                    int64_t(g) * kD + 8 * grp4;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         u32x4_t w = {0u, 0u, 0u, 0u};
@@ -132,20 +210,24 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
       const bool ok = key < t_end && pv[hf];
       u32x4_t w = {0u, 0u, 0u, 0u};
       if (ok)
-        w = *reinterpret_cast<const u32x4_t*>(a.vc + int64_t(pg[hf]) * page_stride +
+        w = *reinterpret_cast<const u32x4_t*>(vcache + int64_t(pg[hf]) * page_stride +
                                               int64_t(key & (page_size - 1)) * row_stride + int64_t(g) * kD + 8 * n);
       vv[s] = w;
     }
   };
+  // 8-bit codes -> the bf16 operands the loop uses (K in the permuted k-step order, V rows in order)
+  auto widen = [&](const u32x4_t (&kv8)[2][2], const u32x2_t (&vv8)[8], u32x4_t (&kv)[2][4], u32x4_t (&vv)[8]) {
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        kv[tb][ks] = codes_to_bf16x8<KV>(kv8[tb][ks >> 1][2 * (ks & 1)], kv8[tb][ks >> 1][2 * (ks & 1) + 1]);
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) vv[s2] = codes_to_bf16x8<KV>(vv8[s2][0], vv8[s2][1]);
+  };
 
-  u32x4_t kv[2][4], vv[8];
-  load32(t_begin, kv, vv);
-  for (int t0 = t_begin; t0 < t_end; t0 += 32) {
-#if ATTN_DECODE_PREFETCH
-    // issue the next 32 keys' loads before computing on these (software pipelining, ~64 more registers)
-    u32x4_t kvn[2][4], vvn[8];
-    if (t0 + 32 < t_end) load32(t0 + 32, kvn, vvn);
-#endif
+  // One block of 32 keys: S^T = K Q^T, online softmax, O^T += V^T P^T (K and V as bf16 operands in kv, vv).
+  auto block = [&](int t0, const u32x4_t (&kv)[2][4], const u32x4_t (&vv)[8]) {
     // S^T[key][head]: lane holds head n, keys t0 + 16*tb + 4*grp4 + r
     f32x4_t sacc[2] = {f32x4_t{}, f32x4_t{}};
 #pragma unroll
@@ -190,18 +272,31 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
                                     sacc[1][2], sacc[1][3]);
 #pragma unroll
     for (int j = 0; j < 8; ++j) oacc[j] = mfma16x16x32(transpose_pick(vv, j), pb, oacc[j]);
-#if ATTN_DECODE_PREFETCH
-    if (t0 + 32 < t_end) {
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kv[tb][ks] = kvn[tb][ks];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) vv[s] = vvn[s];
+  };
+
+  u32x4_t kv[2][4], vv[8];
+  if constexpr (KV == kKvBf16) {
+    load32(t_begin, kv, vv);
+    for (int t0 = t_begin; t0 < t_end; t0 += 32) {
+      block(t0, kv, vv);
+      if (t0 + 32 < t_end) load32(t0 + 32, kv, vv);
     }
-#else
-    if (t0 + 32 < t_end) load32(t0 + 32, kv, vv);
-#endif
+  } else {
+    // 8-bit codes take half the registers: two blocks of codes in flight (ring of two), widened to bf16 operands
+    // just before use.
+    u32x4_t ka[2][2], kb[2][2];
+    u32x2_t va[8], vb[8];
+    load32_q8(t_begin, ka, va);
+    if (t_begin + 32 < t_end) load32_q8(t_begin + 32, kb, vb);
+    for (int t0 = t_begin; t0 < t_end; t0 += 64) {
+      widen(ka, va, kv, vv);
+      if (t0 + 64 < t_end) load32_q8(t0 + 64, ka, va);
+      block(t0, kv, vv);
+      if (t0 + 32 >= t_end) break;
+      widen(kb, vb, kv, vv);
+      if (t0 + 96 < t_end) load32_q8(t0 + 96, kb, vb);
+      block(t0 + 32, kv, vv);
+    }
   }
 
   // partial result: O / l and lse for this chunk (lane holds head n, dims 8*(4*grp4 + r) + j)
@@ -216,6 +311,11 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
     const int d0 = 8 * (4 * grp4 + r);
     f32x4_t lo = {oacc[0][r] * inv, oacc[1][r] * inv, oacc[2][r] * inv, oacc[3][r] * inv};
     f32x4_t hi = {oacc[4][r] * inv, oacc[5][r] * inv, oacc[6][r] * inv, oacc[7][r] * inv};
+    if constexpr (KV != kKvBf16) {                     // per-channel V scale
+      const f32x4_t* vs = reinterpret_cast<const f32x4_t*>(a.v_scale + g * kD + d0);
+      lo *= vs[0];
+      hi *= vs[1];
+    }
     *reinterpret_cast<f32x4_t*>(wo + d0) = lo;
     *reinterpret_cast<f32x4_t*>(wo + d0 + 4) = hi;
   }
@@ -262,18 +362,20 @@ size_t decode_paged_workspace_bytes(int batch, int hq, int head_dim, int max_seq
   return o_bytes + slots * sizeof(float);
 }
 
-hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
-                               const int32_t* seq_lens, void* o, float* lse, int batch, int hq, int hkv,
-                               int head_dim, int page_size, int max_pages_per_seq, int64_t num_pages,
-                               int max_seqlen_kv, float scale, void* workspace, hipStream_t stream) {
-  (void)head_dim;  // 128 (validated by the caller)
+namespace {
+hipError_t launch_decode(int kind, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                         const float* v_scale, const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                         int batch, int hq, int hkv, int page_size, int max_pages_per_seq, int64_t num_pages,
+                         int max_seqlen_kv, float scale, void* workspace, hipStream_t stream) {
   const int n_chunks = max(1, (max_seqlen_kv + kDecodeChunk - 1) / kDecodeChunk);
   const size_t slots = size_t(batch) * size_t(hq) * size_t(n_chunks);
   const size_t o_bytes = (slots * kD * sizeof(float) + 255) & ~size_t(255);
-  DecodeArgs a;
+  DecodeArgs a = {};
   a.q = static_cast<const uint16_t*>(q);
-  a.kc = static_cast<const uint16_t*>(k_cache);
-  a.vc = static_cast<const uint16_t*>(v_cache);
+  a.kc = k_cache;
+  a.vc = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.table = block_table; a.seq_lens = seq_lens;
   a.ws_o = static_cast<float*>(workspace);
   a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
@@ -282,14 +384,37 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
   while ((1 << shift) < page_size) ++shift;
   a.page_shift = shift; a.max_pages = max_pages_per_seq; a.max_len = max_seqlen_kv; a.n_chunks = n_chunks;
   a.num_pages = num_pages; a.scale = scale;
-  if (max_seqlen_kv > 0)
-    decode_paged_split_kernel<<<ATTN_DECODE_HEAD_MAJOR ? dim3(unsigned(hkv), unsigned(n_chunks), unsigned(batch))
-                                                       : dim3(unsigned(n_chunks), unsigned(hkv), unsigned(batch)),
-                                dim3(64), 0, stream>>>(a);
+  const dim3 grid = ATTN_DECODE_HEAD_MAJOR ? dim3(unsigned(hkv), unsigned(n_chunks), unsigned(batch))
+                                           : dim3(unsigned(n_chunks), unsigned(hkv), unsigned(batch));
+  if (max_seqlen_kv > 0) {
+    if (kind == kKvFp8) decode_paged_split_kernel<kKvFp8><<<grid, dim3(64), 0, stream>>>(a);
+    else if (kind == kKvInt8) decode_paged_split_kernel<kKvInt8><<<grid, dim3(64), 0, stream>>>(a);
+    else decode_paged_split_kernel<kKvBf16><<<grid, dim3(64), 0, stream>>>(a);
+  }
   decode_combine_kernel<<<dim3(unsigned(hq), unsigned(batch)), dim3(kD), 0, stream>>>(
       a.ws_o, a.ws_lse, seq_lens, static_cast<uint16_t*>(o), lse, hq, n_chunks, max_seqlen_kv,
       max_pages_per_seq * page_size);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, void* o, float* lse, int batch, int hq, int hkv,
+                               int head_dim, int page_size, int max_pages_per_seq, int64_t num_pages,
+                               int max_seqlen_kv, float scale, void* workspace, hipStream_t stream) {
+  (void)head_dim;  // 128 (validated by the caller)
+  return launch_decode(kKvBf16, q, k_cache, v_cache, nullptr, nullptr, block_table, seq_lens, o, lse, batch, hq, hkv,
+                       page_size, max_pages_per_seq, num_pages, max_seqlen_kv, scale, workspace, stream);
+}
+
+hipError_t launch_decode_paged_q8(int fp8, const void* q, const void* k_cache, const void* v_cache,
+                                  const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                  const int32_t* seq_lens, void* o, float* lse, int batch, int hq, int hkv,
+                                  int page_size, int max_pages_per_seq, int64_t num_pages, int max_seqlen_kv,
+                                  float scale, void* workspace, hipStream_t stream) {
+  return launch_decode(fp8 ? kKvFp8 : kKvInt8, q, k_cache, v_cache, k_scale, v_scale, block_table, seq_lens, o, lse,
+                       batch, hq, hkv, page_size, max_pages_per_seq, num_pages, max_seqlen_kv, scale, workspace,
+                       stream);
 }
 
 }  // namespace attn

@@ -25,7 +25,17 @@ namespace attn {
 namespace {
 
 constexpr int kIdxWaves = 4;            // waves per indexer workgroup
-constexpr int kIdxKeysPerWave = 256;    // tokens per wave (8 blocks of 32)
+#ifndef ATTN_IDX_KPW
+#define ATTN_IDX_KPW 256
+#endif
+#ifndef ATTN_IDX_PIPE
+#define ATTN_IDX_PIPE 2
+#endif
+#ifndef ATTN_IDX_NT
+#define ATTN_IDX_NT 0
+#endif
+constexpr int kIdxKeysPerWave = ATTN_IDX_KPW;   // tokens per wave (blocks of 32)
+constexpr int kIdxPipe = ATTN_IDX_PIPE;         // 32-token blocks of key rows in registers (kIdxPipe - 1 in flight)
 
 template <int HI, int DI>
 __global__ __launch_bounds__(64 * kIdxWaves, 2) void dsa_indexer_kernel(const uint16_t* __restrict__ q_idx,
@@ -65,7 +75,10 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void dsa_indexer_kernel(const ui
   auto load_block = [&](u32x4_t (&kb)[KS], int key0) {
     const uint16_t* kp = kbase + int64_t(min(key0 + col, L - 1)) * DI;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) kb[ks] = *reinterpret_cast<const u32x4_t*>(kp + 8 * ks);
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4_t* src = reinterpret_cast<const u32x4_t*>(kp + 8 * ks);
+      kb[ks] = ATTN_IDX_NT ? __builtin_nontemporal_load(src) : *src;   // read once: non-temporal
+    }
   };
   auto score_block = [&](const u32x4_t (&kb)[KS], int key0) {
     float part = 0.f;
@@ -82,16 +95,21 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void dsa_indexer_kernel(const ui
     if (hh == 0 && t < key_end) srow[t] = t < L ? part : -INFINITY;
   };
 
-  // Blocks of 32 tokens, the next block's key rows in flight while the current one is scored.
+  // Blocks of 32 tokens in a ring of kIdxPipe register buffers: the next kIdxPipe - 1 blocks' key rows are in
+  // flight while one is scored.
   const int nblk = (key_end - key_begin + 31) / 32;
-  u32x4_t k0[KS], k1[KS];
-  load_block(k0, key_begin);
-  for (int i = 0; i < nblk; i += 2) {
-    if (i + 1 < nblk) load_block(k1, key_begin + 32 * (i + 1));
-    score_block(k0, key_begin + 32 * i);
-    if (i + 1 >= nblk) break;
-    if (i + 2 < nblk) load_block(k0, key_begin + 32 * (i + 2));
-    score_block(k1, key_begin + 32 * (i + 1));
+  u32x4_t kb[kIdxPipe][KS];
+#pragma unroll
+  for (int p = 0; p + 1 < kIdxPipe; ++p)
+    if (p < nblk) load_block(kb[p], key_begin + 32 * p);
+  for (int i = 0; i < nblk; i += kIdxPipe) {
+#pragma unroll
+    for (int u = 0; u < kIdxPipe; ++u) {
+      const int blk = i + u;
+      if (blk >= nblk) break;
+      if (blk + kIdxPipe - 1 < nblk) load_block(kb[(u + kIdxPipe - 1) % kIdxPipe], key_begin + 32 * (blk + kIdxPipe - 1));
+      score_block(kb[u], key_begin + 32 * blk);
+    }
   }
 }
 

@@ -41,6 +41,14 @@ hipError_t launch_decode_paged(const void* q, const void* k_cache, const void* v
                                int head_dim, int page_size, int max_pages_per_seq, int64_t num_pages,
                                int max_seqlen_kv, float scale, void* workspace, hipStream_t stream);
 
+// Paged decode over 8-bit K/V caches (fp8 != 0: FP8 E4M3 codes, else int8) with per-(KV head, channel) fp32
+// scales [hkv, 128]; same workspace as launch_decode_paged.
+hipError_t launch_decode_paged_q8(int fp8, const void* q, const void* k_cache, const void* v_cache,
+                                  const float* k_scale, const float* v_scale, const int32_t* block_table,
+                                  const int32_t* seq_lens, void* o, float* lse, int batch, int hq, int hkv,
+                                  int page_size, int max_pages_per_seq, int64_t num_pages, int max_seqlen_kv,
+                                  float scale, void* workspace, hipStream_t stream);
+
 // MLA absorbed decode: split over tokens, then the log-sum-exp combine.
 int mla_num_splits(int batch, int n_heads, int max_seqlen_kv, int target_blocks);
 int mla_split_len(int batch, int n_heads, int max_seqlen_kv, int target_blocks);
