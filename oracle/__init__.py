@@ -26,4 +26,7 @@ from .attention import (  # noqa: F401
     int8_decode,
     dequantize_kv,
     decode_paged_q8,
+    local_global_visible,
+    attention_local_global,
+    attention_local_global_rows,
 )

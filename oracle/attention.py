@@ -12,6 +12,8 @@ Pages cited (by title, as they appear on the web):
   [V3]  "DeepSeek-V3 attention guide: einsum vs manual optimisation" (dksg.cn): the naive and the absorbed
         score einsums quoted from the model's inference code.
   [AP]  "7 anti-patterns of DeepSeek attention optimisation" (lpnh.cn): §4.2 GQA cache reorder.
+  [LC-SW] [LC] §4.1: hybrid sparse attention, a sliding window for the local neighbourhood plus a few global
+        tokens (a leading token such as CLS, periodic anchors at a global sampling rate).
   [LC-KV] [LC] §2.5, KV-cache compression: keys and values stored as 8-bit integers with a per-channel scale.
   [AP-F8] [AP] §3.3: FP8 E4M3, whose largest finite value is 448.
   [AN-LI] the "Lighting Indexer" section of [AN]: DeepSeek Sparse Attention scores every earlier token with
@@ -38,7 +40,10 @@ Readings taken where the pages are silent or garbled:
   * 8-bit KV caches ([LC-KV], [AP-F8]): a cached value is code * scale[kv_head, channel], the code being an int8
     (two's complement) or an OCP FP8 E4M3 byte (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is
     subnormal; no infinities, S.1111.111 is NaN) and the scale an fp32 per (KV head, channel) for K and for V;
-    attention is then exactly decode_paged on the dequantised caches.
+    attention is then exactly decode_paged on the dequantised caches;
+  * local + global mask ([LC-SW]): key j is visible to query i iff j <= i and (i - j < window, or j < n_lead, or
+    anchor_stride > 0 and j % anchor_stride == 0); window >= 1 (a query always sees itself); the global sampling
+    rate is 1 / anchor_stride, and j = 0 is an anchor whenever anchor_stride > 0.
 """
 import numpy as np
 
@@ -46,6 +51,7 @@ __all__ = [
     "bf16_bits_to_f64", "rope_inv_freq", "rope", "attention_prefill", "attention_prefill_rows", "gather_paged",
     "decode_paged", "mla_decode", "mla_naive", "kv_append_paged", "prefill_paged", "dsa_indexer_scores",
     "topk_indices", "mla_sparse_decode", "fp8_e4m3_decode", "int8_decode", "dequantize_kv", "decode_paged_q8",
+    "local_global_visible", "attention_local_global", "attention_local_global_rows",
 ]
 
 
@@ -370,3 +376,38 @@ def decode_paged_q8(q, k_codes, v_codes, k_scale, v_scale, kind, block_table, se
     """Paged decode over 8-bit K/V caches: decode_paged on the dequantised caches. kind: "fp8" or "int8"."""
     return decode_paged(q, dequantize_kv(k_codes, k_scale, kind), dequantize_kv(v_codes, v_scale, kind), block_table,
                         seq_lens, scale)
+
+
+def local_global_visible(rows, n_keys, window, n_lead, anchor_stride):
+    """Boolean [len(rows), n_keys]: key j visible to query i ([LC-SW] reading above)."""
+    i = np.asarray(rows, np.int64)[:, None]
+    j = np.arange(n_keys)[None, :]
+    glob = j < n_lead
+    if anchor_stride > 0:
+        glob = glob | (j % anchor_stride == 0)
+    return (j <= i) & ((i - j < window) | glob)
+
+
+def attention_local_global_rows(q, k, v, rows, window, n_lead, anchor_stride, scale):
+    """Causal attention with the local + global mask for the query positions `rows`, scores materialised.
+    q: [B, S, Hq, D]; k, v: [B, S, Hkv, D]. Returns (o [B, R, Hq, Dv], lse [B, Hq, R])."""
+    q = np.asarray(q, np.float64); k = np.asarray(k, np.float64); v = np.asarray(v, np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    bsz, s_len, hq, _ = q.shape
+    grp = hq // k.shape[2]
+    hidden = ~local_global_visible(rows, s_len, window, n_lead, anchor_stride)
+    o = np.zeros((bsz, rows.size, hq, v.shape[-1]), np.float64)
+    lse = np.zeros((bsz, hq, rows.size), np.float64)
+    for b in range(bsz):
+        for h in range(hq):
+            g = h // grp
+            sc = scale * (q[b, rows, h, :] @ k[b, :, g, :].T)        # [R, S] materialised
+            sc[hidden] = -np.inf
+            o[b, :, h, :], lse[b, h, :] = _softmax_rows_then_v(sc, v[b, :, g, :])
+    return o, lse
+
+
+def attention_local_global(q, k, v, window, n_lead, anchor_stride, scale):
+    """attention_local_global_rows over every query position. Returns (o [B, S, Hq, Dv], lse [B, Hq, S])."""
+    return attention_local_global_rows(q, k, v, np.arange(np.asarray(q).shape[1]), window, n_lead, anchor_stride,
+                                       scale)

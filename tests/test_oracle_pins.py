@@ -670,3 +670,52 @@ def test_q8_decode_scales_are_per_channel_and_linear():
         # V scale == output scaled per channel
         o5, _ = oracle.decode_paged_q8(q, kc, vc, ones, sv, kind, table, lens, 0.3)
         np.testing.assert_allclose(o5, o1 * sv[np.arange(Hq) // (Hq // Hkv)][None], atol=1e-13)
+
+
+# --------------------------------------------------------------------------------------- local + global mask ----
+
+def _lg_case(seed, B=1, S=40, Hq=4, Hkv=2, D=8):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((B, S, Hq, D)), rng.standard_normal((B, S, Hkv, D)), rng.standard_normal((B, S, Hkv, D))
+
+
+def test_local_global_reduces_to_causal():
+    q, k, v = _lg_case(90)
+    ref = oracle.attention_prefill(q, k, v, True, 0.4)
+    for w, g, p in [(40, 0, 0), (1000, 3, 7), (1, 40, 0), (1, 0, 1), (5, 0, 1)]:   # window >= S, all lead, stride 1
+        o, lse = oracle.attention_local_global(q, k, v, w, g, p, 0.4)
+        np.testing.assert_allclose(o, ref[0], atol=1e-13); np.testing.assert_allclose(lse, ref[1], atol=1e-13)
+
+
+def test_window_one_sees_only_itself():
+    q, k, v = _lg_case(91)
+    o, lse = oracle.attention_local_global(q, k, v, 1, 0, 0, 0.4)
+    grp = q.shape[2] // k.shape[2]
+    for h in range(q.shape[2]):
+        np.testing.assert_allclose(o[0, :, h], v[0, :, h // grp], atol=1e-14)
+        np.testing.assert_allclose(lse[0, h], 0.4 * np.einsum("sd,sd->s", q[0, :, h], k[0, :, h // grp]), atol=1e-13)
+
+
+def test_local_global_mask_brute_force():
+    """Explicit loops over (i, j) with the rule written out, softmax with exp and no max subtraction."""
+    q, k, v = _lg_case(92, S=23, Hq=2, Hkv=1, D=4)
+    W, G, P = 4, 2, 5
+    o, lse = oracle.attention_local_global(q, k, v, W, G, P, 0.5)
+    for i in range(23):
+        for h in range(2):
+            num, den = np.zeros(4), 0.0
+            for j in range(23):
+                if j <= i and (i - j < W or j < G or j % P == 0):
+                    e = math.exp(0.5 * float(q[0, i, h] @ k[0, j, 0]))
+                    num += e * v[0, j, 0]; den += e
+            np.testing.assert_allclose(o[0, i, h], num / den, atol=1e-12)
+            assert abs(lse[0, h, i] - math.log(den)) < 1e-12
+
+
+def test_local_global_visible_counts():
+    # the page's hybrid configuration: window 32 with global sampling rate 1/32 on a 512-token sequence
+    vis = oracle.local_global_visible(np.arange(512), 512, 32, 0, 32)
+    i = 511
+    assert vis[i].sum() == 32 + len([j for j in range(0, 512 - 32) if j % 32 == 0])      # window + 15 anchors
+    assert vis[i, 0] and vis[i, 32] and not vis[i, 33] and vis[i, 480] and vis[i, 511] and not vis[i, 479]
+    assert np.all(vis.sum(1) >= 1) and np.all(np.diag(vis))
