@@ -9,7 +9,8 @@ hot path over one batch: RoPE on Q, RoPE on K, then attn_prefill. `value` is the
 with the inputs already resident in HBM. Secondary objects on the same line (same method, HIP events on the
 launch stream): paged GQA decode (bf16, FP8 E4M3 and int8 caches) and MLA absorbed decode in GB/s of algorithmic
 bytes, the 131072-token prefill and the chunked prefill from a paged cache (four 2048-token chunks on 0 / 4096 /
-8192 / 14336 cached tokens; one step = append with RoPE on K, RoPE on Q, attend) in TFLOP/s, and DeepSeek Sparse
+8192 / 14336 cached tokens; one step = append with RoPE on K, RoPE on Q, attend) and the 131072-token prefill with a
+sliding window of 4096 plus anchors every 32 tokens in TFLOP/s of visible pairs, and DeepSeek Sparse
 Attention decode (lightning indexer over 32768 cached tokens, top-2048 selection, sparse MLA) in GB/s of
 algorithmic bytes.
 
@@ -114,7 +115,7 @@ def roofline_hbm(nbytes, ms, kernel, workload, timed=None):
 
 
 # --------------------------------------------------------------------------------------------------- prefill --
-def bench_prefill(torch, ta, w, steps, warmup, seed=0):
+def bench_prefill(torch, ta, w, steps, warmup, seed=0, local_global=False):
     log(f"[bench] {w.name}: generating inputs")
     inp = prefill_inputs(w, seed=seed)
     q, k, v = (dev_bf16(torch, inp[n]) for n in ("q", "k", "v"))
@@ -127,7 +128,10 @@ def bench_prefill(torch, ta, w, steps, warmup, seed=0):
         ta.attn_rope_apply(k, pos, w.theta)
         if timed:
             timer.start()
-        ta.attn_prefill(q, k, v, causal=True, softmax_scale=w.scale, o=o)
+        if local_global:
+            ta.attn_prefill_local_global(q, k, v, w.window, w.n_lead, w.anchor_stride, softmax_scale=w.scale, o=o)
+        else:
+            ta.attn_prefill(q, k, v, causal=True, softmax_scale=w.scale, o=o)
         if timed:
             timer.stop()
 
@@ -349,9 +353,9 @@ def main():
     # Warm-up long enough (about 0.1 s of work) for the GPU clock to settle before the timed steps.
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-secondary", action="store_true", help="only the primary prefill workload")
-    ap.add_argument("--workloads", default="prefill,decode,mla,long,chunked,dsa,decode_fp8,decode_int8",
-                    help="comma list of prefill (primary), decode, mla, long, chunked, dsa, decode_fp8, decode_int8; "
-                         "profiling runs select one")
+    ap.add_argument("--workloads", default="prefill,decode,mla,long,chunked,dsa,decode_fp8,decode_int8,swa",
+                    help="comma list of prefill (primary), decode, mla, long, chunked, dsa, decode_fp8, decode_int8, "
+                         "swa; profiling runs select one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration for traffic measurements)")
@@ -378,7 +382,7 @@ def main():
         return
 
     sel = set(args.workloads.split(","))
-    if sel - {"prefill", "decode", "mla", "long", "chunked", "dsa", "decode_fp8", "decode_int8"}:
+    if sel - {"prefill", "decode", "mla", "long", "chunked", "dsa", "decode_fp8", "decode_int8", "swa"}:
         print(f"unknown workloads {sel}", file=sys.stderr)
         sys.exit(2)
     if args.no_secondary:
@@ -450,6 +454,15 @@ def run_secondary(torch, ta, args, sel, line):
                                    "ctx_lens": list(wc.ctx_lens), "new_lens": list(wc.new_lens),
                                    "step": "kv_append_paged (rope k) + rope(q) + prefill_paged",
                                    "roofline": roofline_compute(wc.flops, kern_c, "prefill_bf16_kernel", wc.name)}
+    if "swa" in sel:
+        wsw = WORKLOADS["swa_prefill_s131072"]
+        wall_w, kern_w = bench_prefill(torch, ta, wsw, 5, 2, local_global=True)
+        line["local_global_prefill"] = {
+            "workload": wsw.name, "value": round(wsw.flops / (wall_w * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(wall_w, 3), "window": wsw.window, "n_lead": wsw.n_lead,
+            "anchor_stride": wsw.anchor_stride, "flops_per_step": wsw.flops,
+            "step": "rope(q) + rope(k) + prefill_local_global",
+            "roofline": roofline_compute(wsw.flops, kern_w, "prefill_bf16_kernel", wsw.name)}
     if "dsa" in sel:
         ws_ = WORKLOADS["dsa_decode_b32"]
         wall_s, ms = bench_dsa(torch, ta, ws_, max(20, args.steps), max(100, args.warmup))

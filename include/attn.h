@@ -3,6 +3,7 @@
  * Operations:
  *   attn_rope_apply       rotary position embedding, in place
  *   attn_prefill          causal (or full) grouped-query attention over a whole sequence
+ *   attn_prefill_local_global  causal prefill with a sliding window plus global (leading, periodic) tokens
  *   attn_decode_paged     one query token per sequence against a paged KV cache (split-KV + log-sum-exp combine)
  *   attn_decode_paged_q8  the same over 8-bit (FP8 E4M3 or int8) K/V caches with per-channel scales
  *   attn_mla_decode       multi-head latent attention decode in the absorbed form
@@ -92,6 +93,21 @@ int attn_rope_apply(void* x, int dtype, int64_t n_tokens, int n_heads, int head_
 int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int batch,
                  int seqlen, int n_heads_q, int n_heads_kv, int head_dim, int causal, float softmax_scale,
                  void* stream);
+
+/* Causal prefill with a local + global mask: key j is visible to query i iff j <= i and (i - j < window, or
+ * j < n_lead, or anchor_stride > 0 and j % anchor_stride == 0).
+ * ("DeepSeek 32K to 256K long context", tqpw.cn, section 4.1: a sliding window keeps the local neighbourhood and a
+ *  few global tokens, such as a leading CLS token and periodic anchors at a global sampling rate, keep long-range
+ *  links.) window >= S, or anchor_stride 1, gives plain causal attention; window 1 with no globals gives O = V.
+ *   q, k, v, o, lse, sizes and scale as attn_prefill (bf16 only, causal by definition).
+ *   window >= 1 (keys i-window+1 .. i), n_lead >= 0 leading global tokens, anchor_stride >= 0 (0: no anchors;
+ *   otherwise the global sampling rate is 1/anchor_stride and key 0 is an anchor).
+ * Work is proportional to window + globals per query, not to i. Unsupported: head_dim other than 64 or 128;
+ * anchor_stride * 64 * n_heads_kv * head_dim * 2 >= 2^31. INVALID_ARG as attn_prefill, and for window < 1 or a
+ * negative n_lead or anchor_stride. */
+int attn_prefill_local_global(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int seqlen,
+                              int n_heads_q, int n_heads_kv, int head_dim, int window, int n_lead, int anchor_stride,
+                              float softmax_scale, void* stream);
 
 /* Bytes of workspace attn_decode_paged needs for these sizes (0 if any size is non-positive). */
 size_t attn_decode_paged_workspace_size(int batch, int n_heads_q, int head_dim, int max_seqlen_kv);

@@ -7,6 +7,8 @@ context at head dim 128).
 from dataclasses import dataclass
 import math
 
+import numpy as np
+
 
 @dataclass(frozen=True)
 class Prefill:
@@ -98,6 +100,42 @@ class DSADecode:
     scale: float
 
 
+@dataclass(frozen=True)
+class LocalGlobalPrefill:
+    """Causal prefill with a local + global mask: key j visible to query i iff j <= i and (i - j < window, or
+    j < n_lead, or anchor_stride > 0 and j % anchor_stride == 0)."""
+    name: str
+    batch: int
+    seqlen: int
+    hq: int
+    hkv: int
+    head_dim: int
+    window: int
+    n_lead: int
+    anchor_stride: int
+    theta: float
+    scale: float
+    dtype: str = "bf16"
+
+    def visible_pairs(self, seqlen=None):
+        s = self.seqlen if seqlen is None else seqlen
+        i = np.arange(s, dtype=np.int64)
+        lo = i - self.window + 1                       # first key of the window
+        outside = np.maximum(lo, 0)                    # keys 0 .. lo-1 lie outside the window
+        lead = np.minimum(self.n_lead, outside)
+        anchors = np.zeros_like(i)
+        if self.anchor_stride > 0:
+            p = self.anchor_stride
+            first = -(-self.n_lead // p)                 # first anchor index at or past n_lead
+            anchors = np.maximum(0, (outside - 1) // p - first + 1) * (outside > 0)
+        return int((np.minimum(self.window, i + 1) + lead + anchors).sum())
+
+    @property
+    def flops(self):
+        """4 * D flop per visible (query, key) pair per query head and sequence."""
+        return 4 * self.batch * self.hq * self.head_dim * self.visible_pairs()
+
+
 WORKLOADS = {
     "mha_fp32_s256": Prefill("mha_fp32_s256", batch=1, seqlen=256, hq=4, hkv=4, head_dim=64, dtype="fp32",
                              theta=10000.0, scale=1.0 / math.sqrt(64)),
@@ -109,6 +147,9 @@ WORKLOADS = {
                                 scale=1.0 / math.sqrt(192)),
     "dsa_decode_b32": DSADecode("dsa_decode_b32", batch=32, heads=128, latent=512, rope=64, seqlen=32768,
                                 idx_heads=64, idx_dim=128, topk=2048, scale=1.0 / math.sqrt(192)),
+    "swa_prefill_s131072": LocalGlobalPrefill("swa_prefill_s131072", batch=1, seqlen=131072, hq=32, hkv=8,
+                                              head_dim=128, window=4096, n_lead=0, anchor_stride=32, theta=10000.0,
+                                              scale=1.0 / math.sqrt(128)),
     "chunked_prefill_b4": ChunkedPrefill("chunked_prefill_b4", hq=32, hkv=8, head_dim=128, page_size=64,
                                          ctx_lens=(0, 4096, 8192, 14336), new_lens=(2048, 2048, 2048, 2048),
                                          theta=10000.0, scale=1.0 / math.sqrt(128)),

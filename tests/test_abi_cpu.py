@@ -32,7 +32,8 @@ def lib():
 def test_header_declares_the_operations():
     names = declared_functions()
     for n in ("attn_rope_apply", "attn_prefill", "attn_decode_paged", "attn_mla_decode", "attn_kv_append_paged",
-              "attn_prefill_paged", "attn_dsa_indexer", "attn_topk", "attn_mla_sparse_decode", "attn_decode_paged_q8"):
+              "attn_prefill_paged", "attn_dsa_indexer", "attn_topk", "attn_mla_sparse_decode", "attn_decode_paged_q8",
+              "attn_prefill_local_global"):
         assert n in names
 
 
@@ -260,3 +261,18 @@ def test_decode_q8_validation(lib):
     assert f(*args(d=64)) == UNSUPPORTED
     assert f(*args(wsb=need - 1)) == WORKSPACE
     assert f(*args(b=0)) == OK
+
+
+def test_prefill_local_global_validation(lib):
+    f = lib.attn_prefill_local_global
+    args = lambda **kw: [kw.get(n, d) for n, d in [
+        ("q", FAKE), ("k", FAKE), ("v", FAKE), ("o", FAKE), ("lse", NULL), ("b", 1), ("s", 1000), ("hq", 32),
+        ("hkv", 8), ("d", 128), ("w", 128), ("g", 0), ("p", 32), ("scale", 0.088), ("stream", NULL)]]
+    assert f(*args(w=0)) == INVALID                   # a query must see at least itself
+    assert f(*args(g=-1)) == INVALID
+    assert f(*args(p=-2)) == INVALID
+    assert f(*args(hq=12, hkv=8)) == INVALID
+    assert f(*args(q=NULL)) == INVALID
+    assert f(*args(d=96)) == UNSUPPORTED
+    assert f(*args(p=1 << 20)) == UNSUPPORTED         # strided anchor tile beyond 32-bit offsets
+    assert f(*args(s=0, q=NULL)) == OK

@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     attn_mla_sparse_decode,
     attn_mla_sparse_decode_workspace_size,
     attn_prefill,
+    attn_prefill_local_global,
     attn_prefill_paged,
     attn_rope_apply,
     attn_topk,

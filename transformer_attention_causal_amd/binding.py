@@ -23,6 +23,7 @@ _P, _I, _I64, _D, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctype
 SIGNATURES = {
     "attn_rope_apply": (_I, [_P, _I, _I64, _I, _I, _P, _D, _I, _P]),
     "attn_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_prefill_local_global": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "attn_decode_paged_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _I, _F, _P, _SZ, _P]),
     "attn_decode_paged_q8": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _I, _F, _P, _SZ,
@@ -121,6 +122,29 @@ def attn_prefill(q, k, v, causal=True, softmax_scale=None, o=None, lse=None, ret
     _check("attn_prefill", lib.attn_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o", q.dtype), lse_p,
                                              _code(q.dtype), bsz, s_len, hq, hkv, d, 1 if causal else 0, scale,
                                              _stream(q, stream)))
+    return (o, lse) if return_lse else o
+
+
+def attn_prefill_local_global(q, k, v, window, n_lead=0, anchor_stride=0, softmax_scale=None, o=None, lse=None,
+                              return_lse=False, stream=None):
+    """Causal prefill with a local + global mask: q [B, S, Hq, D], k/v [B, S, Hkv, D] bf16 -> o [B, S, Hq, D]
+    (and lse [B, Hq, S]). Key j is visible to query i iff j <= i and (i - j < window or j < n_lead or
+    (anchor_stride > 0 and j % anchor_stride == 0))."""
+    lib = load_library()
+    bsz, s_len, hq, d = q.shape
+    hkv = k.shape[2]
+    if k.shape != (bsz, s_len, hkv, d) or v.shape != k.shape:
+        raise ValueError("q, k, v shapes do not match")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((bsz, hq, s_len), dtype=torch.float32, device=q.device)
+    lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
+    _check("attn_prefill_local_global", lib.attn_prefill_local_global(
+        _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
+        _dev(o, "o", torch.bfloat16), lse_p, bsz, s_len, hq, hkv, d, int(window), int(n_lead), int(anchor_stride),
+        scale, _stream(q, stream)))
     return (o, lse) if return_lse else o
 
 

@@ -59,6 +59,23 @@ ATTN_EXPORT int attn_prefill(const void* q, const void* k, const void* v, void* 
                                               causal ? 1 : 0, softmax_scale, s));
 }
 
+ATTN_EXPORT int attn_prefill_local_global(const void* q, const void* k, const void* v, void* o, float* lse,
+                                          int batch, int seqlen, int n_heads_q, int n_heads_kv, int head_dim,
+                                          int window, int n_lead, int anchor_stride, float softmax_scale,
+                                          void* stream) {
+  if (batch < 0 || seqlen < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0) return ATTN_ERR_INVALID_ARG;
+  if (n_heads_q % n_heads_kv != 0 || !valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (window < 1 || n_lead < 0 || anchor_stride < 0) return ATTN_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  // strided anchor tiles address 64 rows of stride anchor_stride within 32-bit offsets
+  if (int64_t(anchor_stride) * 64 * n_heads_kv * head_dim * 2 >= (int64_t(1) << 31)) return ATTN_ERR_UNSUPPORTED;
+  if (batch == 0 || seqlen == 0) return ATTN_OK;
+  if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
+  return hip_status(attn::launch_prefill_window(q, k, v, o, lse, batch, seqlen, n_heads_q, n_heads_kv, head_dim,
+                                                window, n_lead, anchor_stride, softmax_scale,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 ATTN_EXPORT size_t attn_decode_paged_workspace_size(int batch, int n_heads_q, int head_dim, int max_seqlen_kv) {
   return attn::decode_paged_workspace_bytes(batch, n_heads_q, head_dim, max_seqlen_kv);
 }

@@ -15,6 +15,11 @@ hipError_t launch_rope(void* x, int dtype, int64_t n_tokens, int n_heads, int he
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
                                int seqlen, int hq, int hkv, int head_dim, int causal, float scale,
                                hipStream_t stream);
+// Causal prefill with a local + global mask: key j visible to query i iff j <= i and (i - j < window or
+// j < n_lead or (anchor_stride > 0 and j % anchor_stride == 0)). bf16, head_dim 64 or 128.
+hipError_t launch_prefill_window(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                                 int seqlen, int hq, int hkv, int head_dim, int window, int n_lead, int anchor_stride,
+                                 float scale, hipStream_t stream);
 // Chunked / variable-length causal prefill from a paged cache (bf16, head_dim 64 or 128, page size a power of two
 // that is a multiple of 64).
 hipError_t launch_prefill_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,

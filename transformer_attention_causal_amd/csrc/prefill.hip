@@ -90,6 +90,9 @@ struct PrefillArgs {
   const int32_t* table;
   int page_shift, max_pages, total_new;
   int64_t num_pages;
+  // Local + global mask (the WIN kernel): key j is visible to query i iff j <= i and (i - j < window, or
+  // j < n_lead, or anchor_stride > 0 and j % anchor_stride == 0).
+  int window, n_lead, anchor_stride;
 };
 
 // LDS swizzle: 16-byte chunk c of tile row r is stored at chunk position c ^ swz_key(r). LDS has 64 four-byte
@@ -118,21 +121,24 @@ struct TileCopy {
   static_assert(ROWS * Tile<D>::kChunks % 64 == 0, "tile must split into 64-slot blocks");
   uint32_t off[kLoads];
 
-  __device__ __forceinline__ void init(int hkv, int g, int wave, int lane) {
+  // Tile row r is source row r * step (step > 1: a strided tile, e.g. every step-th key).
+  __device__ __forceinline__ void init(int hkv, int g, int wave, int lane, int step = 1) {
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int slot = (i * NW + wave) * 64 + lane;
       const int row = slot / Tile<D>::kChunks;
       const int lchunk = (slot % Tile<D>::kChunks) ^ swz_key<D>(row);
-      off[i] = uint32_t(((row * hkv + g) * D + lchunk * 8) * 2);
+      off[i] = uint32_t(((row * step * hkv + g) * D + lchunk * 8) * 2);
     }
   }
 
   // Copy `rows` tile rows starting at `base` (row 0 of the tile, head 0) into `dst`. The buffer resource spans
   // exactly those rows; the others read as zeros (measured: an out-of-range lane of a buffer load-to-LDS writes 0),
   // which are finite, so their masked scores and P = 0 stay exact.
-  __device__ __forceinline__ void issue(uint16_t* dst, const uint16_t* base, int rows, int hkv, int wave) const {
-    const buf_rsrc_t rs = make_buf_rsrc(base, uint32_t(max(0, min(ROWS, rows)) * hkv * D * 2));
+  __device__ __forceinline__ void issue(uint16_t* dst, const uint16_t* base, int rows, int hkv, int wave,
+                                        int step = 1) const {
+    const int nr = max(0, min(ROWS, rows));
+    const buf_rsrc_t rs = make_buf_rsrc(base, uint32_t(nr > 0 ? ((nr - 1) * step + 1) * hkv * D * 2 : 0));
 #pragma unroll
     for (int i = 0; i < kLoads; ++i)
       if (kBlocks % NW == 0 || i * NW + wave < kBlocks) load_lds16(rs, off[i], dst + (i * NW + wave) * 512);
@@ -221,8 +227,20 @@ __device__ bool pick_chunked_unit(const PrefillArgs& a, int span, int r, int& b_
   return false;                                  // unreachable for consistent inputs
 }
 
-template <int D, int QB, bool PAGED>
+// The WIN kernel (local + global mask, "DeepSeek 32K to 256K long context", tqpw.cn, section 4.1: a sliding window
+// for the local neighbourhood plus a few global tokens such as a leading token and periodic anchors) visits, per
+// workgroup, three disjoint kinds of key tiles, so the work is O(window + globals) per query instead of O(i):
+//   lead   contiguous tiles over keys j < n_lead that fall outside some query's window;
+//   anchor strided tiles over the anchors j = k * anchor_stride >= n_lead outside some query's window (each tile
+//          row is every anchor_stride-th key, copied with the same direct-to-LDS copy and a strided offset);
+//   window contiguous tiles over keys within window of the workgroup's queries.
+// Per query the three sets are disjoint (lead and anchor keys count only when outside the query's window), and
+// their union is exactly the visible set.
+constexpr int kPhaseWin = 0, kPhaseLead = 1, kPhaseAnchor = 2;
+
+template <int D, int QB, bool PAGED, bool WIN = false>
 __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void prefill_bf16_kernel(PrefillArgs a) {
+  static_assert(!(WIN && (PAGED || kSub != 1)), "the local + global mask is for contiguous prefill, 64-key tiles");
   constexpr int QW = 32 * QB;
   constexpr int KS = D / 16;   // k-steps of the QK^T contraction
   constexpr int DB = D / 32;   // 32-row blocks of O^T
@@ -339,7 +357,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   };
 
   // One kBN-key tile from LDS buffer BUF (a compile-time constant, so LDS addresses are base + immediate).
-  auto tile = [&](auto bufc, auto subc, int key0) {
+  auto tile = [&](auto bufc, auto subc, int key0, int kstep = 1, int phase = kPhaseWin, int nrows = kTileKeys) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr int SUB = decltype(subc)::value;
     const uint16_t* Kt = lds[BUF][0] + SUB * kBN * D;
@@ -362,8 +380,25 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
       }
     }
 
-    // ---- mask: only tiles crossing the diagonal or the ragged end
-    if ((a.causal && key0 + kBN - 1 > koff + qpos0) || key0 + kBN > T) {
+    // ---- mask. WIN: every tile, by the phase's rule; otherwise only tiles crossing the diagonal or the ragged end
+    if constexpr (WIN) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int qpos = qpos0 + 32 * qb + lq;
+#pragma unroll
+        for (int kb2 = 0; kb2 < kKB2; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rel = 32 * kb2 + 8 * (r >> 2) + 4 * lg + (r & 3);
+            const int key = key0 + kstep * rel;
+            bool vis = key <= qpos && key < T && rel < nrows;
+            if (phase == kPhaseWin) vis = vis && qpos - key < a.window;
+            else if (phase == kPhaseLead) vis = vis && key < a.n_lead && qpos - key >= a.window;
+            else vis = vis && qpos - key >= a.window;
+            if (!vis) sacc[qb][kb2][r] = -INFINITY;
+          }
+      }
+    } else if ((a.causal && key0 + kBN - 1 > koff + qpos0) || key0 + kBN > T) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int qpos = qpos0 + 32 * qb + lq;
@@ -391,13 +426,14 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
       // 2^kRescaleLog2; otherwise unnormalised P stays below that factor. O / l is unchanged.
       if (__any((mx - m[qb]) * c > kRescaleLog2)) {
         const float m_new = fmaxf(m[qb], mx);
-        const float alpha = fast_exp2((m[qb] - m_new) * c);
+        // (WIN: a query may have seen no visible key yet, m = m_new = -inf; its O and l are still 0)
+        const float alpha = (WIN && m_new == -INFINITY) ? 1.f : fast_exp2((m[qb] - m_new) * c);
         l[qb] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db) oacc[qb][db] *= alpha;
         m[qb] = m_new;
       }
-      const float mc = m[qb] * c;
+      const float mc = (WIN && m[qb] == -INFINITY) ? 0.f : m[qb] * c;   // WIN: P = exp2(-inf) = 0 until then
 #pragma unroll
       for (int kb2 = 0; kb2 < kKB2; ++kb2)
 #pragma unroll
@@ -438,6 +474,69 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   };
   static_assert(kSub == 1 || kSub == 2, "one or two sub-tiles per LDS tile");
 
+  if constexpr (WIN) {
+    // Tile list of this workgroup (uniform): lead tiles, anchor tiles, window tiles.
+    const int W = a.window, G = a.n_lead, P = a.anchor_stride;
+    const int qmin = wg_pos0, qmax = min(S, wg_pos0 + wg_span) - 1;
+    const int lead_end = min(G, qmax - W + 1);                      // keys [0, lead_end) may need the lead phase
+    const int n_lead = lead_end > 0 ? (lead_end + kTileKeys - 1) / kTileKeys : 0;
+    int k_lo = 0, n_anchor_keys = 0;
+    if (P > 0 && qmax - W >= 0) {
+      k_lo = (G + P - 1) / P;
+      n_anchor_keys = max(0, (qmax - W) / P - k_lo + 1);
+    }
+    const int n_anch = (n_anchor_keys + kTileKeys - 1) / kTileKeys;
+    const int w_first = max(0, qmin - W + 1) / kTileKeys, w_last = qmax / kTileKeys;
+    const int nlist = n_lead + n_anch + (w_last - w_first + 1);
+    TileCopy<D, kWaves, kTileKeys> cpa;                             // anchor tiles: every P-th key
+    cpa.init(a.hkv, g, wave, lane, max(P, 1));
+    // tile u -> (first key, key step, phase, rows)
+    auto desc = [&](int u, int& key0, int& step, int& phase, int& rows) {
+      if (u < n_lead) {
+        key0 = u * kTileKeys; step = 1; phase = kPhaseLead; rows = min(kTileKeys, T - key0);
+      } else if (u < n_lead + n_anch) {
+        const int k0 = k_lo + (u - n_lead) * kTileKeys;
+        key0 = k0 * P; step = P; phase = kPhaseAnchor; rows = min(kTileKeys, k_lo + n_anchor_keys - k0);
+      } else {
+        key0 = (w_first + u - n_lead - n_anch) * kTileKeys; step = 1; phase = kPhaseWin;
+        rows = min(kTileKeys, T - key0);
+      }
+    };
+    auto copy_u = [&](int buf, int u) {
+      int key0, step, phase, rows;
+      desc(u, key0, step, phase, rows);
+      const int64_t row0 = int64_t(b) * S + key0;
+      if (step == 1) {
+        cp.issue(lds[buf][0], a.k + row0 * a.hkv * D, rows, a.hkv, wave);
+        cp.issue(lds[buf][1], a.v + row0 * a.hkv * D, rows, a.hkv, wave);
+      } else {
+        cpa.issue(lds[buf][0], a.k + row0 * a.hkv * D, rows, a.hkv, wave, step);
+        cpa.issue(lds[buf][1], a.v + row0 * a.hkv * D, rows, a.hkv, wave, step);
+      }
+    };
+    // does this wave (queries qpos0 .. qw_max) see any key of tile u?
+    const int qw_max = min(S - 1, qpos0 + QW - 1);
+    auto run_u = [&](auto bufc, int u) {
+      int key0, step, phase, rows;
+      desc(u, key0, step, phase, rows);
+      bool need;
+      if (phase == kPhaseWin) need = key0 <= qw_max && key0 + kTileKeys - 1 >= qpos0 - W + 1;
+      else need = key0 <= qw_max - W;                              // some key of the tile outside some window
+      if (need && qpos0 < S) tile(bufc, std::integral_constant<int, 0>{}, key0, step, phase, rows);
+    };
+    copy_u(0, 0);
+    for (int u = 0; u < nlist; u += 2) {
+      wait_vmem();
+      __syncthreads();                                 // tile u visible to all; buffer 1 free
+      if (u + 1 < nlist) copy_u(1, u + 1);
+      run_u(std::integral_constant<int, 0>{}, u);
+      if (u + 1 >= nlist) break;
+      wait_vmem();
+      __syncthreads();                                 // tile u+1 visible to all; buffer 0 free
+      if (u + 2 < nlist) copy_u(0, u + 2);
+      run_u(std::integral_constant<int, 1>{}, u + 1);
+    }
+  } else {
   copy_tile(0, 0);
   // Two tiles per trip so each tile's LDS buffer is a compile-time constant.
   for (int t = 0; t < ntiles; t += 2) {
@@ -450,6 +549,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
     __syncthreads();                                   // tile t+1 visible to all; buffer 0 free
     if (t + 2 < ntiles) copy_tile(0, t + 2);
     if ((t + 1) * kTileKeys < kend_w) tiles(std::integral_constant<int, 1>{}, t + 1);
+  }
   }
 
   // ---- epilogue: O = O^T / l (lane holds query lq, dims 32*db + 8*(r/4) + 4*lg + r%4), lse = scale*m + ln l
@@ -567,6 +667,17 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   const dim3 grid(static_cast<unsigned>(int64_t(a.n_pblk) * batch * a.n_hgrp));
   if (head_dim == 128) prefill_bf16_kernel<128, 1, false><<<grid, dim3(kThreads), 0, stream>>>(a);
   else prefill_bf16_kernel<64, 1, false><<<grid, dim3(kThreads), 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_window(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                                 int seqlen, int hq, int hkv, int head_dim, int window, int n_lead, int anchor_stride,
+                                 float scale, hipStream_t stream) {
+  PrefillArgs a = prefill_args(q, k, v, o, lse, batch, seqlen, hq, hkv, 1, scale);
+  a.window = window; a.n_lead = n_lead; a.anchor_stride = anchor_stride;
+  const dim3 grid(static_cast<unsigned>(int64_t(a.n_pblk) * batch * a.n_hgrp));
+  if (head_dim == 128) prefill_bf16_kernel<128, 1, false, true><<<grid, dim3(kThreads), 0, stream>>>(a);
+  else prefill_bf16_kernel<64, 1, false, true><<<grid, dim3(kThreads), 0, stream>>>(a);
   return hipGetLastError();
 }
 
