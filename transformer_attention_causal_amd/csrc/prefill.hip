@@ -380,8 +380,19 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
       }
     }
 
-    // ---- mask. WIN: every tile, by the phase's rule; otherwise only tiles crossing the diagonal or the ragged end
+    // ---- mask. WIN: tiles not visible in full to every query of the wave, by the phase's rule; otherwise only
+    // tiles crossing the diagonal or the ragged end
+    bool win_full = false;
     if constexpr (WIN) {
+      const int key_max = key0 + kstep * (kBN - 1), qw_max = min(S - 1, qpos0 + QW - 1);
+      if (nrows == kBN && key_max <= qpos0 && key_max < T) {
+        if (phase == kPhaseWin) win_full = key0 >= qw_max - a.window + 1;
+        else if (phase == kPhaseLead) win_full = key_max < a.n_lead && key_max <= qpos0 - a.window;
+        else win_full = key_max <= qpos0 - a.window;
+      }
+    }
+    if constexpr (WIN) {
+      if (!win_full) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int qpos = qpos0 + 32 * qb + lq;
@@ -397,6 +408,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
             else vis = vis && qpos - key >= a.window;
             if (!vis) sacc[qb][kb2][r] = -INFINITY;
           }
+      }
       }
     } else if ((a.causal && key0 + kBN - 1 > koff + qpos0) || key0 + kBN > T) {
 #pragma unroll
