@@ -52,9 +52,9 @@ def test_status_strings(lib):
 
 
 def test_workspace_sizes(lib):
-    # decode: [B, Hq, ceil(L/512), D] fp32 partial outputs (256-byte aligned) + [B, Hq, chunks] fp32 lse
+    # decode: [B, Hq, ceil(L/1024), D] fp32 partial outputs (256-byte aligned) + [B, Hq, chunks] fp32 lse
     b, hq, d, lmax = 64, 32, 128, 32768
-    chunks = (lmax + 511) // 512
+    chunks = (lmax + 1023) // 1024
     o_bytes = (b * hq * chunks * d * 4 + 255) // 256 * 256
     assert lib.attn_decode_paged_workspace_size(b, hq, d, lmax) == o_bytes + b * hq * chunks * 4
     assert lib.attn_decode_paged_workspace_size(0, hq, d, lmax) == 0

@@ -8,7 +8,7 @@
 //
 // Decode is HBM-bound (about 4 flop per byte of K/V), so the design goal is to read each K/V byte once, with
 // wide loads and enough of them in flight:
-//   * Split kernel: one wave per (logical 512-key chunk, KV head, sequence). The wave serves all query heads of
+//   * Split kernel: one wave per (logical 1024-key chunk, KV head, sequence). The wave serves all query heads of
 //     its KV group at once, so every K/V byte is read once. Chunks at or past the sequence length exit at once.
 //   * Both products run on v_mfma_f32_16x16x32_bf16 with the group's query heads as the 16-wide N dimension
 //     (heads beyond the group size are zero columns). K fragments are loaded straight from global memory into
@@ -38,11 +38,9 @@ namespace {
 constexpr int kD = 128;
 static_assert(kDecodeChunk % 32 == 0 && kDecodeChunk / 16 <= 64, "a chunk's pages (>= 16 keys each) fit one wave");
 
-// Grid order: 1 = the KV heads of one chunk are consecutive workgroups (they read interleaved 256-byte pieces
-// of the same page slots at the same time); 0 = the chunks of one head are consecutive.
-#ifndef ATTN_DECODE_HEAD_MAJOR
-#define ATTN_DECODE_HEAD_MAJOR 0
-#endif
+// Grid order: head-major = the KV heads of one chunk are consecutive workgroups (they read interleaved 256-byte
+// pieces of the same page slots at the same time), chunk-major = the chunks of one head are consecutive. With
+// 1024-key chunks head-major measured faster for every kernel here, so the launch uses it.
 
 // Cache element kinds: 0 bf16, 1 FP8 E4M3 codes, 2 int8 codes (the 8-bit kinds carry per-channel scales).
 constexpr int kKvBf16 = 0, kKvFp8 = 1, kKvInt8 = 2;
@@ -58,6 +56,7 @@ struct DecodeArgs {
   float* ws_o;      // [batch, hq, n_chunks, D]
   float* ws_lse;    // [batch, hq, n_chunks]
   int hq, hkv, page_shift, max_pages, max_len, n_chunks;
+  int head_major;   // grid order: (hkv, n_chunks, batch) if set, else (n_chunks, hkv, batch)
   int64_t num_pages;
   float scale;
 };
@@ -95,11 +94,8 @@ __device__ __forceinline__ u32x4_t codes_to_bf16x8(uint32_t w0, uint32_t w1) {
 
 template <int KV>
 __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
-#if ATTN_DECODE_HEAD_MAJOR
-  const int g = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
-#else
-  const int chunk = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-#endif
+  const int g = a.head_major ? blockIdx.x : blockIdx.y, chunk = a.head_major ? blockIdx.y : blockIdx.x;
+  const int b = blockIdx.z;
   const int page_size = 1 << a.page_shift;
   const int L = clamp_len(a.seq_lens[b], a.max_len, a.max_pages * page_size);
   const int t_begin = chunk * kDecodeChunk;
@@ -133,7 +129,7 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
   float m = -INFINITY, l = 0.f;
   const int32_t* trow = a.table + int64_t(b) * a.max_pages;
   // The chunk's page numbers, read once: lane i holds the entry of the chunk's i-th page (a chunk spans at most
-  // 512/16 = 32 pages), fetched per 16 keys with a lane read instead of a dependent table load per iteration.
+  // 1024/16 = 64 pages), fetched per 16 keys with a lane read instead of a dependent table load per iteration.
   const int first_page = t_begin >> a.page_shift;
   const int last_page = (t_end - 1) >> a.page_shift;
   const int pg_lane = (lane <= last_page - first_page) ? trow[first_page + lane] : -1;
@@ -322,6 +318,211 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
   if (grp4 == 0) a.ws_lse[slot] = m * a.scale + logf(lt);
 }
 
+// ---- LDS-staged variant (bf16 caches). The register-loading kernel above reads, per load instruction, 64-byte
+// halves of 16 different rows; here each 32-key block of K and of V is copied global -> LDS by buffer loads with
+// the LDS bit, one instruction per 4 rows (1 KiB, whole 256-byte head slices), and the MFMA operands are read from
+// LDS: K fragments with ds_read_b128, V^T fragments with the transposing ds_read_b64_tr_b16 (the O^T layout is then
+// dims 16*db + 4*grp4 + r). 16-byte chunk c of tile row r is stored at c ^ swz(r) (the copy permutes its source
+// chunks): K key r & 15 keeps each b128 lane set on 16 distinct slots; V key 2*(r & 7) keeps each 32-lane
+// transposing read on 32 distinct 8-byte slots (measured bank model, see the prefill kernel).
+#ifndef ATTN_DECODE_LDS
+#define ATTN_DECODE_LDS 1
+#endif
+#ifndef ATTN_DECODE_NBUF
+#define ATTN_DECODE_NBUF 2
+#endif
+#ifndef ATTN_DECODE_COPY_AUX
+#define ATTN_DECODE_COPY_AUX 2                           // non-temporal: each cache byte is read once
+#endif
+constexpr int kDecNbuf = ATTN_DECODE_NBUF;               // 32-key LDS blocks per wave (kDecNbuf - 1 in flight)
+
+__device__ __forceinline__ int dec_swz_k(int row) { return row & 15; }
+__device__ __forceinline__ int dec_swz_v(int row) { return 2 * (row & 7); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+__global__ __launch_bounds__(64) void decode_paged_lds_kernel(DecodeArgs a) {
+  // One LDS array per buffer and tensor: distinct objects, so the compiler can see that a block's copies in
+  // flight do not alias the buffer being read, and keeps its waits at the block boundary.
+  __shared__ __attribute__((aligned(16))) uint16_t kl0[32 * kD], kl1[32 * kD], kl2[kDecNbuf > 2 ? 32 * kD : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t vl0[32 * kD], vl1[32 * kD], vl2[kDecNbuf > 2 ? 32 * kD : 8];
+  auto kbuf = [&](auto bufc) -> uint16_t* {
+    constexpr int B = decltype(bufc)::value;
+    if constexpr (B == 0) return kl0; else if constexpr (B == 1) return kl1; else return kl2;
+  };
+  auto vbuf = [&](auto bufc) -> uint16_t* {
+    constexpr int B = decltype(bufc)::value;
+    if constexpr (B == 0) return vl0; else if constexpr (B == 1) return vl1; else return vl2;
+  };
+  const int g = a.head_major ? blockIdx.x : blockIdx.y, chunk = a.head_major ? blockIdx.y : blockIdx.x;
+  const int b = blockIdx.z;
+  const int page_size = 1 << a.page_shift;
+  const int L = clamp_len(a.seq_lens[b], a.max_len, a.max_pages * page_size);
+  const int t_begin = chunk * kDecodeChunk;
+  if (t_begin >= L) return;
+  const int t_end = min(L, t_begin + kDecodeChunk);
+  const int lane = threadIdx.x, n = lane & 15, grp4 = lane >> 4;
+  const int G = a.hq / a.hkv;
+  const int h = g * G + n;
+  const bool hv = n < G;
+  const float c = a.scale * kLog2e;
+
+  // Q^T operand: lane holds head n, dims 8*(4*ks + grp4) .. +7 for k-step ks.
+  bf16x8_t qop[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4_t w = {0u, 0u, 0u, 0u};
+    if (hv) w = *reinterpret_cast<const u32x4_t*>(a.q + (int64_t(b) * a.hq + h) * kD + 8 * (4 * ks + grp4));
+    qop[ks] = as_bf16x8(w);
+  }
+  f32x4_t oacc[8];                                       // O^T: lane holds head n, dims 16*db + 4*grp4 + r
+#pragma unroll
+  for (int db = 0; db < 8; ++db) oacc[db] = f32x4_t{};
+  float m = -INFINITY, l = 0.f;
+  const int32_t* trow = a.table + int64_t(b) * a.max_pages;
+  const int first_page = t_begin >> a.page_shift;
+  const int last_page = (t_end - 1) >> a.page_shift;
+  const int pg_lane = (lane <= last_page - first_page) ? trow[first_page + lane] : -1;
+  const int64_t row_stride = int64_t(a.hkv) * kD;
+  const int64_t page_stride = int64_t(page_size) * row_stride;
+  const uint16_t* kcache = static_cast<const uint16_t*>(a.kc);
+  const uint16_t* vcache = static_cast<const uint16_t*>(a.vc);
+
+  // Copy instruction i of a block moves keys t0+4i .. t0+4i+3 (one page: pages hold >= 16 keys and t0 is a
+  // multiple of 32); keys at or past t_end and pages outside [0, num_pages) read as zeros (empty resource).
+  const int row_in = lane >> 4, pcs = lane & 15;
+  const uint32_t row_bytes = uint32_t(row_stride * 2);
+  auto copy_block = [&](auto bufc, int t0) {
+    uint16_t* kdst = kbuf(bufc);
+    uint16_t* vdst = vbuf(bufc);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key_first = t0 + 4 * i;
+      const int pg = __builtin_amdgcn_readlane(pg_lane, (min(key_first, t_end - 1) >> a.page_shift) - first_page);
+      const bool pv = pg >= 0 && pg < a.num_pages;
+      const int rows = pv ? max(0, min(4, t_end - key_first)) : 0;
+      const int64_t e0 = int64_t(max(pg, 0)) * page_stride + int64_t(key_first & (page_size - 1)) * row_stride +
+                         int64_t(g) * kD;
+      const buf_rsrc_t rk = make_buf_rsrc(kcache + e0, uint32_t(rows) * row_bytes);
+      const buf_rsrc_t rv = make_buf_rsrc(vcache + e0, uint32_t(rows) * row_bytes);
+      const int r = 4 * i + row_in;
+      raw_buffer_load_lds(rk, (lds_void_t*)(kdst + i * 512), 16, int(row_in * row_bytes + 16 * (pcs ^ dec_swz_k(r))),
+                          0, 0, ATTN_DECODE_COPY_AUX);
+      raw_buffer_load_lds(rv, (lds_void_t*)(vdst + i * 512), 16, int(row_in * row_bytes + 16 * (pcs ^ dec_swz_v(r))),
+                          0, 0, ATTN_DECODE_COPY_AUX);
+    }
+  };
+  // LDS read addresses (bytes): K row 16*tb + n, chunk 4*ks + grp4; V rows 4*grp4 + j (+16), dims 16*db + 4*(bl&3)
+  uint32_t kaddr[4], vaddr[8];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) kaddr[ks] = uint32_t(n * 256 + 16 * ((4 * ks + grp4) ^ dec_swz_k(n)));
+  {
+    const int vr = 4 * grp4 + (n >> 2), cq = n & 3;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      vaddr[db] = uint32_t(vr * 256 + 16 * ((2 * db + (cq >> 1)) ^ dec_swz_v(vr)) + 8 * (cq & 1));
+  }
+
+  // A block's operand fragments are read from LDS into registers before the next block's copies are issued: the
+  // compiler cannot tell the copies from these reads apart and would otherwise wait for the copies first.
+  u32x4_t kf[2][4], vf[8];
+  auto read_block = [&](auto bufc) {
+    const uint16_t* Kt = kbuf(bufc);
+    const uint16_t* Vt = vbuf(bufc);
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[tb][ks] = lds_read16(Kt, kaddr[ks] + tb * 16 * 256);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const u32x2_t lo = lds_read_tr16(Vt, vaddr[db]);
+      const u32x2_t hi = lds_read_tr16(Vt, vaddr[db] + 16 * 256);
+      vf[db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
+  auto block = [&](int t0) {
+    f32x4_t sacc[2] = {f32x4_t{}, f32x4_t{}};
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sacc[tb] = mfma16x16x32(as_bf16x8(kf[tb][ks]), qop[ks], sacc[tb]);
+    if (t0 + 32 > t_end) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (t0 + 16 * tb + 4 * grp4 + r >= t_end) sacc[tb][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sacc[tb][r]);
+    mx = fmaxf(mx, xor_lanes(mx, 16));
+    mx = fmaxf(mx, xor_lanes(mx, 32));
+    if (__any((mx - m) * c > kRescaleLog2)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = fast_exp2((m - m_new) * c);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) oacc[db] *= alpha;
+      m = m_new;
+    }
+    const float mc = m * c;
+#pragma unroll
+    for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(fmaf(sacc[tb][r], c, -mc));
+        sacc[tb][r] = p;
+        l += p;
+      }
+    const bf16x8_t pb = pack_bf16x8(sacc[0][0], sacc[0][1], sacc[0][2], sacc[0][3], sacc[1][0], sacc[1][1],
+                                    sacc[1][2], sacc[1][3]);
+#pragma unroll
+    for (int db = 0; db < 8; ++db) oacc[db] = mfma16x16x32(as_bf16x8(vf[db]), pb, oacc[db]);
+  };
+
+  // Ring of kDecNbuf blocks: at block u, wait for its copies, read its fragments, then issue the copies of block
+  // u + kDecNbuf - 1 into the buffer block u - 1 used, and compute.
+  constexpr int PRE = kDecNbuf - 1;
+  const int nblk = (t_end - t_begin + 31) / 32;
+  wait_vmem_n<0>();        // q and the page numbers are in: from here on only block copies are outstanding
+  copy_block(std::integral_constant<int, 0>{}, t_begin);
+  if (PRE >= 2 && 1 < nblk) copy_block(std::integral_constant<int, 1 % kDecNbuf>{}, t_begin + 32);
+  for (int u = 0; u < nblk; u += kDecNbuf) {
+#pragma unroll
+    for (int k = 0; k < kDecNbuf; ++k) {
+      const int uu = u + k;
+      if (uu >= nblk) break;
+      // copies of blocks uu+1 .. uu+PRE-1 may stay in flight (16 instructions per block)
+      if (PRE >= 2 && uu + 1 < nblk) wait_vmem_n<16>();
+      else wait_vmem_n<0>();
+      if (k == 0) read_block(std::integral_constant<int, 0>{});
+      else if (k == 1) read_block(std::integral_constant<int, 1 % kDecNbuf>{});
+      else read_block(std::integral_constant<int, 2 % kDecNbuf>{});
+      if (uu + PRE < nblk) {
+        const int nb = (k + PRE) % kDecNbuf;
+        if (nb == 0) copy_block(std::integral_constant<int, 0>{}, t_begin + 32 * (uu + PRE));
+        else if (nb == 1) copy_block(std::integral_constant<int, 1 % kDecNbuf>{}, t_begin + 32 * (uu + PRE));
+        else copy_block(std::integral_constant<int, 2 % kDecNbuf>{}, t_begin + 32 * (uu + PRE));
+      }
+      block(t_begin + 32 * uu);
+    }
+  }
+
+  float lt = l + xor_lanes(l, 16);
+  lt += xor_lanes(lt, 32);
+  if (!hv) return;
+  const int64_t slot = (int64_t(b) * a.hq + h) * a.n_chunks + chunk;
+  const float inv = 1.f / lt;
+  float* wo = a.ws_o + slot * kD + 4 * grp4;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) *reinterpret_cast<f32x4_t*>(wo + 16 * db) = oacc[db] * inv;
+  if (grp4 == 0) a.ws_lse[slot] = m * a.scale + logf(lt);
+}
+
 // Merge the chunks of one (sequence, query head): M = max lse_c, w_c = exp(lse_c - M),
 // O = sum_c w_c O_c / sum_c w_c, lse = M + ln sum_c w_c. A sequence of length 0 gets O = 0, lse = -inf.
 __global__ __launch_bounds__(kD) void decode_combine_kernel(const float* __restrict__ ws_o,
@@ -384,11 +585,13 @@ hipError_t launch_decode(int kind, const void* q, const void* k_cache, const voi
   while ((1 << shift) < page_size) ++shift;
   a.page_shift = shift; a.max_pages = max_pages_per_seq; a.max_len = max_seqlen_kv; a.n_chunks = n_chunks;
   a.num_pages = num_pages; a.scale = scale;
-  const dim3 grid = ATTN_DECODE_HEAD_MAJOR ? dim3(unsigned(hkv), unsigned(n_chunks), unsigned(batch))
-                                           : dim3(unsigned(n_chunks), unsigned(hkv), unsigned(batch));
+  a.head_major = 1;
+  const dim3 grid = a.head_major ? dim3(unsigned(hkv), unsigned(n_chunks), unsigned(batch))
+                                 : dim3(unsigned(n_chunks), unsigned(hkv), unsigned(batch));
   if (max_seqlen_kv > 0) {
     if (kind == kKvFp8) decode_paged_split_kernel<kKvFp8><<<grid, dim3(64), 0, stream>>>(a);
     else if (kind == kKvInt8) decode_paged_split_kernel<kKvInt8><<<grid, dim3(64), 0, stream>>>(a);
+    else if (ATTN_DECODE_LDS) decode_paged_lds_kernel<<<grid, dim3(64), 0, stream>>>(a);
     else decode_paged_split_kernel<kKvBf16><<<grid, dim3(64), 0, stream>>>(a);
   }
   decode_combine_kernel<<<dim3(unsigned(hq), unsigned(batch)), dim3(kD), 0, stream>>>(

@@ -37,7 +37,7 @@ hipError_t launch_prefill_fp32(const void* q, const void* k, const void* v, void
 
 // Paged decode: split-KV partials into the workspace, then the log-sum-exp combine.
 #ifndef ATTN_DECODE_CHUNK
-#define ATTN_DECODE_CHUNK 512
+#define ATTN_DECODE_CHUNK 1024
 #endif
 constexpr int kDecodeChunk = ATTN_DECODE_CHUNK;  // keys per split (a multiple of 32); boundaries are logical positions
 size_t decode_paged_workspace_bytes(int batch, int hq, int head_dim, int max_seqlen_kv);
