@@ -44,6 +44,7 @@ PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = {
     "prefill_bf16_kernel": "prefill.hip",
     "decode_paged_split_kernel": "decode.hip",
+    "decode_paged_lds_kernel": "decode.hip",
     "mla_split_kernel": "mla.hip",
     "dsa_indexer_kernel": "dsa.hip",
 }
@@ -419,8 +420,8 @@ def run_secondary(torch, ta, args, sel, line):
         ms, nbytes, tokens = bench_decode(torch, ta, wd, max(20, args.steps), max(100, args.warmup))
         line["paged_decode"] = {"workload": wd.name, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
                                 "ms": round(ms, 4), "bytes": nbytes, "tokens": tokens,
-                                "roofline": roofline_hbm(nbytes, ms, "decode_paged_split_kernel", wd.name,
-                                                         "decode_paged_split_kernel + decode_combine_kernel")}
+                                "roofline": roofline_hbm(nbytes, ms, "decode_paged_lds_kernel", wd.name,
+                                                         "decode_paged_lds_kernel + decode_combine_kernel")}
     for kv in ("fp8", "int8"):
         if f"decode_{kv}" not in sel:
             continue
