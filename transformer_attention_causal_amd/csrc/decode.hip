@@ -36,6 +36,16 @@ namespace attn {
 namespace {
 
 constexpr int kD = 128;
+// Build-time choices (measured): bf16 and 8-bit caches staged through LDS (1) or loaded through registers (0).
+#ifndef ATTN_DECODE_LDS
+#define ATTN_DECODE_LDS 1
+#endif
+#ifndef ATTN_DECODE_LDS8
+#define ATTN_DECODE_LDS8 1
+#endif
+#ifndef ATTN_DECODE_Q8_HEAD_MAJOR
+#define ATTN_DECODE_Q8_HEAD_MAJOR 1
+#endif
 static_assert(kDecodeChunk % 32 == 0 && kDecodeChunk / 16 <= 64, "a chunk's pages (>= 16 keys each) fit one wave");
 
 // Grid order: head-major = the KV heads of one chunk are consecutive workgroups (they read interleaved 256-byte
@@ -277,6 +287,65 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
       block(t0, kv, vv);
       if (t0 + 32 < t_end) load32(t0 + 32, kv, vv);
     }
+  } else if (ATTN_DECODE_LDS8) {
+    // 8-bit codes staged through LDS as in the bf16 kernel below: per 32-key block, 4 copy instructions per tensor
+    // (8 keys x one 128-byte head slice each, non-temporal), read back into the register formats of load32_q8.
+    // K chunk c of row r sits at c ^ ((r >> 1) & 3 | ((r >> 3) & 1) << 2) (conflict-free b128 reads); V rows are
+    // unswizzled (their b64 reads pair two rows of equal parity: a 2-way conflict whatever the swizzle).
+    __shared__ __attribute__((aligned(16))) uint8_t k8a[32 * kD], k8b[32 * kD], v8a[32 * kD], v8b[32 * kD];
+    const int row_in = lane >> 3, pcs = lane & 7;
+    const uint32_t row_bytes = uint32_t(row_stride);     // one byte per element
+    auto swz8 = [](int r) { return ((r >> 1) & 3) | (((r >> 3) & 1) << 2); };
+    auto copy8 = [&](uint8_t* kdst, uint8_t* vdst, int t0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key_first = t0 + 8 * i;
+        const int pg = __builtin_amdgcn_readlane(pg_lane, (min(key_first, t_end - 1) >> a.page_shift) - first_page);
+        const bool pv = pg >= 0 && pg < a.num_pages;
+        const int rows = pv ? max(0, min(8, t_end - key_first)) : 0;
+        const int64_t e0 = int64_t(max(pg, 0)) * page_stride + int64_t(key_first & (page_size - 1)) * row_stride +
+                           int64_t(g) * kD;
+        const buf_rsrc_t rk = make_buf_rsrc(kcache + e0, uint32_t(rows) * row_bytes);
+        const buf_rsrc_t rv = make_buf_rsrc(vcache + e0, uint32_t(rows) * row_bytes);
+        const int r = 8 * i + row_in;
+        raw_buffer_load_lds(rk, (lds_void_t*)(kdst + i * 1024), 16, int(row_in * row_bytes + 16 * (pcs ^ swz8(r))),
+                            0, 0, 2);
+        raw_buffer_load_lds(rv, (lds_void_t*)(vdst + i * 1024), 16, int(row_in * row_bytes + 16 * pcs), 0, 0, 2);
+      }
+    };
+    u32x4_t kv8[2][2];
+    u32x2_t vv8[8];
+    auto read8 = [&](const uint8_t* ks, const uint8_t* vs) {
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int hk = 0; hk < 2; ++hk) {
+          const int r = 16 * tb + n;
+          kv8[tb][hk] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+              (const __attribute__((address_space(3))) uint8_t*)ks + r * 128 + 16 * ((4 * hk + grp4) ^ swz8(r)));
+        }
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) {
+        const int r = 16 * (s2 >> 2) + 4 * grp4 + (s2 & 3);
+        vv8[s2] = *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>(
+            (const __attribute__((address_space(3))) uint8_t*)vs + r * 128 + 8 * n);
+      }
+    };
+    wait_vmem();              // q, scales and the page numbers are in: from here on only block copies are outstanding
+    copy8(k8a, v8a, t_begin);
+    for (int t0 = t_begin; t0 < t_end; t0 += 64) {
+      wait_vmem();
+      read8(k8a, v8a);                                   // block t0 into registers before the next copies
+      if (t0 + 32 < t_end) copy8(k8b, v8b, t0 + 32);
+      widen(kv8, vv8, kv, vv);
+      block(t0, kv, vv);
+      if (t0 + 32 >= t_end) break;
+      wait_vmem();
+      read8(k8b, v8b);
+      if (t0 + 64 < t_end) copy8(k8a, v8a, t0 + 64);
+      widen(kv8, vv8, kv, vv);
+      block(t0 + 32, kv, vv);
+    }
   } else {
     // 8-bit codes take half the registers: two blocks of codes in flight (ring of two), widened to bf16 operands
     // just before use.
@@ -325,9 +394,7 @@ __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {
 // dims 16*db + 4*grp4 + r). 16-byte chunk c of tile row r is stored at c ^ swz(r) (the copy permutes its source
 // chunks): K key r & 15 keeps each b128 lane set on 16 distinct slots; V key 2*(r & 7) keeps each 32-lane
 // transposing read on 32 distinct 8-byte slots (measured bank model, see the prefill kernel).
-#ifndef ATTN_DECODE_LDS
-#define ATTN_DECODE_LDS 1
-#endif
+
 #ifndef ATTN_DECODE_NBUF
 #define ATTN_DECODE_NBUF 2
 #endif
@@ -585,7 +652,7 @@ hipError_t launch_decode(int kind, const void* q, const void* k_cache, const voi
   while ((1 << shift) < page_size) ++shift;
   a.page_shift = shift; a.max_pages = max_pages_per_seq; a.max_len = max_seqlen_kv; a.n_chunks = n_chunks;
   a.num_pages = num_pages; a.scale = scale;
-  a.head_major = 1;
+  a.head_major = kind == kKvBf16 ? 1 : ATTN_DECODE_Q8_HEAD_MAJOR;
   const dim3 grid = a.head_major ? dim3(unsigned(hkv), unsigned(n_chunks), unsigned(batch))
                                  : dim3(unsigned(n_chunks), unsigned(hkv), unsigned(batch));
   if (max_seqlen_kv > 0) {
