@@ -103,8 +103,10 @@ __device__ __forceinline__ buf_rsrc_t make_buf_rsrc(const void* base, uint32_t b
 // 16 bytes per lane from `rsrc` at byte offset voff + soff into LDS: lane i's bytes land at lds_wave_base + 16*i,
 // where lds_wave_base and soff must be the same for the whole wave. Only voff is range-checked against the
 // resource size, so soff must keep the access inside the resource whenever voff is in range.
+// aux = 2: non-temporal (for data read once).
+template <int AUX = 0>
 __device__ __forceinline__ void load_lds16(buf_rsrc_t rsrc, uint32_t voff, void* lds_wave_base, uint32_t soff = 0) {
-  raw_buffer_load_lds(rsrc, (lds_void_t*)lds_wave_base, 16, static_cast<int>(voff), static_cast<int>(soff), 0, 0);
+  raw_buffer_load_lds(rsrc, (lds_void_t*)lds_wave_base, 16, static_cast<int>(voff), static_cast<int>(soff), 0, AUX);
 }
 
 // 4 bytes per lane: lane i's dword lands at lds_wave_base + 4*i (same addressing rules as load_lds16).
