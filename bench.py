@@ -4,7 +4,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
 
 Primary line: causal GQA prefill, bf16, B=2 Hq=32 Hkv=8 S=8192 D=128 (workload gqa_prefill_s8192). One step is the
-hot path over one batch: RoPE on Q, RoPE on K, then attn_prefill. `value` is the algorithmic attention flops
+hot path over one batch: the RoPE cos/sin table, RoPE on K, then attn_prefill_rope (attention with the rotation of
+Q fused into the kernel's load of Q). `value` is the algorithmic attention flops
 (QK^T and PV over the unmasked pairs, 2 flop per multiply-add) per second of wall time over K timed steps,
 with the inputs already resident in HBM. Secondary objects on the same line (same method, HIP events on the
 launch stream): paged GQA decode (bf16, FP8 E4M3 and int8 caches) and MLA absorbed decode in GB/s of algorithmic
@@ -124,15 +125,23 @@ def bench_prefill(torch, ta, w, steps, warmup, seed=0, local_global=False):
     o = torch.empty_like(q)
     timer = EventTimer(torch)
 
+    table = torch.empty((w.seqlen, w.head_dim // 2, 2), dtype=torch.float32, device="cuda")
+
     def step(timed):
-        ta.attn_rope_apply(q, pos, w.theta)
-        ta.attn_rope_apply(k, pos, w.theta)
-        if timed:
-            timer.start()
         if local_global:
+            ta.attn_rope_apply(q, pos, w.theta)
+            ta.attn_rope_apply(k, pos, w.theta)
+            if timed:
+                timer.start()
             ta.attn_prefill_local_global(q, k, v, w.window, w.n_lead, w.anchor_stride, softmax_scale=w.scale, o=o)
         else:
-            ta.attn_prefill(q, k, v, causal=True, softmax_scale=w.scale, o=o)
+            # RoPE(Q) fused into the prefill's load of Q: the step builds the cos/sin table, rotates K in place,
+            # and attends with q unrotated
+            ta.attn_rope_table(w.seqlen, w.head_dim, w.theta, table=table)
+            ta.attn_rope_apply(k, pos, w.theta)
+            if timed:
+                timer.start()
+            ta.attn_prefill_rope(q, k, v, table, softmax_scale=w.scale, o=o)
         if timed:
             timer.stop()
 
@@ -402,7 +411,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded iid N(0,1), bf16)",
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "hq": w.hq, "hkv": w.hkv,
                    "head_dim": w.head_dim, "causal": True, "rope_theta": w.theta,
-                   "step": "rope(q) + rope(k) + prefill", "flops_per_step": w.flops},
+                   "step": "rope_table + rope(k) + prefill_rope (rope(q) fused)", "flops_per_step": w.flops},
         "roofline": roofline_compute(w.flops, kern_ms, "prefill_bf16_kernel", w.name),
     }
     line["pct_bf16_peak_step"] = round(value / PEAK_BF16_TFLOPS, 4)

@@ -3,6 +3,8 @@
  * Operations:
  *   attn_rope_apply       rotary position embedding, in place
  *   attn_prefill          causal (or full) grouped-query attention over a whole sequence
+ *   attn_rope_table       (cos, sin) table of the rotary embedding by integer position
+ *   attn_prefill_rope     attn_prefill with the rotation of Q fused into the kernel's load of Q
  *   attn_prefill_local_global  causal prefill with a sliding window plus global (leading, periodic) tokens
  *   attn_decode_paged     one query token per sequence against a paged KV cache (split-KV + log-sum-exp combine)
  *   attn_decode_paged_q8  the same over 8-bit (FP8 E4M3 or int8) K/V caches with per-channel scales
@@ -68,8 +70,8 @@ typedef enum {
  *   positions  [n_tokens] int32 >= 0, the position of each token row.
  *   theta      RoPE base (10000 for standard RoPE; an NTK-scaled base for stretched contexts), finite, > 1.
  *   interleaved  1: pairs (2i, 2i+1) — the pairing the page prints; 0: pairs (i, i + head_dim/2).
- * For pair i of a token at position p the angle is p * theta^(-2i/head_dim), evaluated in fp64 and reduced to
- * [-pi, pi] before fp32 sin/cos; the rotated values are rounded to `dtype`.
+ * For pair i of a token at position p the angle is p * theta^(-2i/head_dim); the angle, its sine and its cosine
+ * are evaluated in fp64 and rounded to fp32, the rotation is fp32, and the results are rounded to `dtype`.
  * Errors: INVALID_ARG for NULL x/positions (with n_tokens > 0), odd or non-positive head_dim, n_heads <= 0,
  * theta <= 1 or non-finite; UNSUPPORTED for head_dim > 1024 or another dtype. */
 int attn_rope_apply(void* x, int dtype, int64_t n_tokens, int n_heads, int head_dim, const int32_t* positions,
@@ -93,6 +95,37 @@ int attn_rope_apply(void* x, int dtype, int64_t n_tokens, int n_heads, int head_
 int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int batch,
                  int seqlen, int n_heads_q, int n_heads_kv, int head_dim, int causal, float softmax_scale,
                  void* stream);
+
+/* The rotary embedding's (cos, sin) table by integer position.
+ * (DeepSeek 32K to 256K long context, tqpw.cn, section 2.5: cos and sin are precomputed per integer position and
+ *  looked up; section 2.1: pair i rotates by the angle position * theta^(-2i/d).)
+ *   table        [n_positions, head_dim/2] pairs of fp32 (cos, sin), written: entry (p, i) holds the cosine and
+ *                sine of p * theta^(-2i/head_dim), evaluated in fp64 and rounded to fp32 — exactly the values
+ *                attn_rope_apply uses, so a rotation read from this table matches attn_rope_apply bit for bit.
+ *   theta        RoPE base, finite, > 1.
+ * Errors: INVALID_ARG for NULL table (with n_positions > 0), n_positions < 0, odd or non-positive head_dim,
+ * bad theta; UNSUPPORTED for head_dim > 1024. */
+int attn_rope_table(void* table, int n_positions, int head_dim, double theta, void* stream);
+
+/* attn_prefill (bf16) with RoPE of the queries fused into the kernel: q is NOT rotated; each query is rotated
+ * as the kernel loads it, with the cos/sin of its position read from a table made by attn_rope_table, so the
+ * separate read and write of Q by attn_rope_apply disappear. Keys must be rotated already (attn_rope_apply): every
+ * workgroup of a KV head reads them.
+ * (Same passages as attn_rope_apply and attn_prefill.)
+ *   q, k, v, o, lse, batch .. softmax_scale   as attn_prefill with dtype ATTN_BF16.
+ *   q_positions  NULL (query i of each sequence is at position i) or [batch * seqlen] int32 device positions,
+ *                one per query row in q's row order. A position outside [0, rope_table_len) is clamped into it.
+ *   rope_table   [rope_table_len, head_dim/2] (cos, sin) fp32 from attn_rope_table with this head_dim, 16-byte
+ *                aligned; read only.
+ *   interleaved  pairing as attn_rope_apply (1: (2i, 2i+1); 0: (i, i + head_dim/2)).
+ * The output equals attn_rope_apply(q) followed by attn_prefill bit for bit (same table values, same fp32
+ * rotation arithmetic, same rounding); q itself is left unrotated.
+ * Supported: head_dim 64 or 128 (else UNSUPPORTED). INVALID_ARG: as attn_prefill, plus NULL or misaligned
+ * rope_table or rope_table_len <= 0 (with batch*seqlen > 0). */
+int attn_prefill_rope(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int seqlen,
+                      int n_heads_q, int n_heads_kv, int head_dim, int causal, float softmax_scale,
+                      const int32_t* q_positions, const void* rope_table, int rope_table_len, int interleaved,
+                      void* stream);
 
 /* Causal prefill with a local + global mask: key j is visible to query i iff j <= i and (i - j < window, or
  * j < n_lead, or anchor_stride > 0 and j % anchor_stride == 0).
@@ -172,7 +205,8 @@ size_t attn_mla_decode_workspace_size(int batch, int n_heads, int kv_lora_rank, 
  *   o_latent     [batch, n_heads, kv_lora_rank] bf16, written (0 for a sequence of length 0)
  *   lse          NULL or [batch, n_heads] fp32
  *   workspace    >= attn_mla_decode_workspace_size(batch, n_heads, kv_lora_rank, max_seqlen_kv) bytes.
- * Supported: kv_lora_rank 512, rope_dim 64, n_heads a multiple of 32 up to 128 (every wave owns 32 heads).
+ * Supported: kv_lora_rank 512, rope_dim 64, n_heads 32, 64, 96 or 128 (one wave per 16 heads, all heads of a
+ * sequence in one workgroup).
  * Otherwise UNSUPPORTED. INVALID_ARG as above. */
 int attn_mla_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
                     const int32_t* seq_lens, void* o_latent, float* lse, int batch, int n_heads, int kv_lora_rank,

@@ -33,7 +33,7 @@ def test_header_declares_the_operations():
     names = declared_functions()
     for n in ("attn_rope_apply", "attn_prefill", "attn_decode_paged", "attn_mla_decode", "attn_kv_append_paged",
               "attn_prefill_paged", "attn_dsa_indexer", "attn_topk", "attn_mla_sparse_decode", "attn_decode_paged_q8",
-              "attn_prefill_local_global"):
+              "attn_prefill_local_global", "attn_rope_table", "attn_prefill_rope"):
         assert n in names
 
 
@@ -95,6 +95,34 @@ def test_prefill_validation(lib):
     assert call(args(d=96)) == UNSUPPORTED
     assert call(args(dt=3)) == UNSUPPORTED
     assert call(args(q=NULL, k=NULL, v=NULL, o=NULL, s=0)) == OK     # empty: nothing launched
+
+
+def test_rope_table_validation(lib):
+    f = lib.attn_rope_table
+    assert f(FAKE, 16, 63, 10000.0, NULL) == INVALID          # odd head_dim
+    assert f(FAKE, 16, 0, 10000.0, NULL) == INVALID
+    assert f(FAKE, -1, 64, 10000.0, NULL) == INVALID          # negative count
+    assert f(FAKE, 16, 64, 0.5, NULL) == INVALID              # base must exceed 1
+    assert f(FAKE, 16, 64, float("inf"), NULL) == INVALID
+    assert f(NULL, 16, 64, 10000.0, NULL) == INVALID          # null table
+    assert f(FAKE, 16, 2048, 10000.0, NULL) == UNSUPPORTED    # head_dim > 1024
+    assert f(NULL, 0, 64, 10000.0, NULL) == OK                # nothing to do
+
+
+def test_prefill_rope_validation(lib):
+    f = lib.attn_prefill_rope
+    args = lambda **kw: dict(dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=NULL, b=1, s=16, hq=8, hkv=2, d=128, causal=1,
+                                  scale=0.088, pos=NULL, tab=FAKE, tlen=16, il=1), **kw)
+    call = lambda a: f(a["q"], a["k"], a["v"], a["o"], a["lse"], a["b"], a["s"], a["hq"], a["hkv"], a["d"],
+                       a["causal"], a["scale"], a["pos"], a["tab"], a["tlen"], a["il"], NULL)
+    assert call(args(hq=6, hkv=4)) == INVALID
+    assert call(args(scale=-1.0)) == INVALID
+    assert call(args(q=NULL)) == INVALID
+    assert call(args(tab=NULL)) == INVALID                     # table required
+    assert call(args(tlen=0)) == INVALID
+    assert call(args(tab=ctypes.c_void_p(0x1008))) == INVALID  # table must be 16-byte aligned
+    assert call(args(d=96)) == UNSUPPORTED
+    assert call(args(q=NULL, k=NULL, v=NULL, o=NULL, tab=NULL, b=0)) == OK
 
 
 def test_decode_validation(lib):

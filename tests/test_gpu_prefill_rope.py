@@ -1,0 +1,144 @@
+"""attn_rope_table and attn_prefill_rope on the GPU. The table is checked against the oracle's rotation of unit
+pairs (its cos and sin); the fused prefill against the unfused path (attn_rope_apply on Q, then attn_prefill) bit
+for bit — both pairings, explicit and implicit positions, clamped positions, several head layouts and the full
+S=8192 workload — and against the fp64 oracle within the bf16 tolerance."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from synth import WORKLOADS, prefill_inputs
+from gpu_util import require_gpu, say, dev, dev_bf16, host_bf16, bits_to_f32, check, check_bf16, BF16_MAX, BF16_MEAN
+
+pytestmark = pytest.mark.gpu
+
+
+def oracle_table(n_pos, d, theta, interleaved):
+    """(cos, sin) [n_pos, d/2] from the oracle's rotation of the unit pair (1, 0) at every position."""
+    x = np.zeros((n_pos, 1, d))
+    if interleaved:
+        x[..., 0::2] = 1.0
+    else:
+        x[..., : d // 2] = 1.0
+    r = oracle.rope(x, np.arange(n_pos), theta, interleaved=interleaved)[:, 0]
+    if interleaved:
+        return r[:, 0::2], r[:, 1::2]
+    return r[:, : d // 2], r[:, d // 2:]
+
+
+@pytest.mark.parametrize("d,theta,n_pos", [(128, 10000.0, 8192), (64, 10000.0, 300),
+                                           (128, 10000.0 * 4 ** (128 / 126), 131072)])
+def test_rope_table_matches_oracle(d, theta, n_pos):
+    ta = require_gpu()
+    say(f"rope table d={d} theta={theta} n={n_pos}")
+    t = ta.attn_rope_table(n_pos, d, theta).cpu().numpy().astype(np.float64)
+    for interleaved in (True, False):
+        c, s = oracle_table(n_pos, d, theta, interleaved)
+        # fp64 values rounded once to fp32: within one fp32 ulp of values of magnitude <= 1
+        check("cos", t[..., 0], c, 1.2e-7)
+        check("sin", t[..., 1], s, 1.2e-7)
+
+
+def unfused(ta, q_bits, k, v, pos, w, interleaved, causal=True):
+    q = dev_bf16(q_bits)
+    ta.attn_rope_apply(q, pos, w.theta, interleaved=interleaved)
+    return ta.attn_prefill(q, k, v, causal=causal, softmax_scale=w.scale, return_lse=True)
+
+
+SHAPES = [  # (batch, seqlen, hq, hkv, head_dim)
+    (2, 300, 32, 8, 128),   # heads mode, ragged tail
+    (1, 517, 16, 16, 64),   # positions mode, head_dim 64
+    (2, 1000, 12, 4, 128),  # groups of 3: positions mode
+    (1, 1, 8, 2, 128),      # a single token
+]
+
+
+@pytest.mark.parametrize("interleaved", [True, False])
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("explicit_pos", [True, False])
+def test_fused_equals_rotate_then_prefill(shape, interleaved, explicit_pos):
+    ta = require_gpu()
+    b, s_len, hq, hkv, d = shape
+    w = dataclasses.replace(WORKLOADS["gqa_prefill_s8192"], batch=b, seqlen=s_len, hq=hq, hkv=hkv, head_dim=d,
+                            scale=1.0 / np.sqrt(d))
+    say(f"fused rope prefill {shape} interleaved={interleaved} explicit_pos={explicit_pos}")
+    inp = prefill_inputs(w, seed=120 + s_len)
+    if explicit_pos:   # each sequence starts at its own offset
+        pos_h = (np.arange(s_len)[None, :] + 37 * np.arange(b)[:, None] + 5).astype(np.int32).reshape(-1)
+    else:
+        pos_h = np.tile(np.arange(s_len, dtype=np.int32), b)
+    pos = dev(pos_h)
+    k = dev_bf16(inp["k"])
+    ta.attn_rope_apply(k, pos, w.theta, interleaved=interleaved)
+    v = dev_bf16(inp["v"])
+    table = ta.attn_rope_table(int(pos_h.max()) + 1, d, w.theta)
+    o1, l1 = unfused(ta, inp["q"], k, v, pos, w, interleaved)
+    q = dev_bf16(inp["q"])
+    o2, l2 = ta.attn_prefill_rope(q, k, v, table, q_positions=pos if explicit_pos else None,
+                                  interleaved=interleaved, softmax_scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16(o1), host_bf16(o2))
+    assert np.array_equal(l1.cpu().numpy(), l2.cpu().numpy())
+    assert np.array_equal(host_bf16(q), inp["q"])             # q itself is not rotated
+
+
+def test_non_causal_and_oracle():
+    ta = require_gpu()
+    w = dataclasses.replace(WORKLOADS["gqa_prefill_s8192"], batch=2, seqlen=190, hq=8, hkv=2, head_dim=128,
+                            scale=1.0 / np.sqrt(128))
+    inp = prefill_inputs(w, seed=131)
+    pos = dev(inp["positions"])
+    k = dev_bf16(inp["k"])
+    ta.attn_rope_apply(k, pos, w.theta)
+    v = dev_bf16(inp["v"])
+    table = ta.attn_rope_table(w.seqlen, 128, w.theta)
+    for causal in (True, False):
+        o, lse = ta.attn_prefill_rope(dev_bf16(inp["q"]), k, v, table, causal=causal, softmax_scale=w.scale,
+                                      return_lse=True)
+        torch.cuda.synchronize()
+        p = inp["positions"].reshape(w.batch, w.seqlen)
+        qr = oracle.rope(bits_to_f32(inp["q"]), p, w.theta)
+        kr = oracle.rope(bits_to_f32(inp["k"]), p, w.theta)
+        o_ref, lse_ref = oracle.attention_prefill(qr, kr, bits_to_f32(inp["v"]).astype(np.float64), causal, w.scale)
+        check_bf16(f"o causal={causal}", host_bf16(o), o_ref)
+        check("lse", lse.cpu().numpy(), lse_ref, BF16_MAX, BF16_MEAN)
+
+
+def test_positions_are_clamped_into_the_table():
+    """Positions past the table (or negative) read its last (or first) row: the same output as positions clamped
+    on the host."""
+    ta = require_gpu()
+    w = dataclasses.replace(WORKLOADS["gqa_prefill_s8192"], batch=1, seqlen=200, hq=8, hkv=2, head_dim=128,
+                            scale=1.0 / np.sqrt(128))
+    inp = prefill_inputs(w, seed=132)
+    k = dev_bf16(inp["k"])
+    v = dev_bf16(inp["v"])
+    n_tab = 150
+    table = ta.attn_rope_table(n_tab, 128, w.theta)
+    raw = np.arange(200, dtype=np.int32) - 20                 # -20 .. 179
+    o1 = ta.attn_prefill_rope(dev_bf16(inp["q"]), k, v, table, q_positions=dev(raw), softmax_scale=w.scale)
+    o2 = ta.attn_prefill_rope(dev_bf16(inp["q"]), k, v, table, q_positions=dev(np.clip(raw, 0, n_tab - 1)),
+                              softmax_scale=w.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bf16(o1), host_bf16(o2))
+
+
+def test_full_size_fused_equals_unfused():
+    """The S=8192 workload in the bench's launch configuration: fused and unfused outputs agree bit for bit
+    (the unfused path is checked against the oracle on sampled rows at this size elsewhere)."""
+    ta = require_gpu()
+    w = WORKLOADS["gqa_prefill_s8192"]
+    say(f"fused rope prefill full size S={w.seqlen}")
+    inp = prefill_inputs(w, seed=0)
+    pos = dev(inp["positions"])
+    k = dev_bf16(inp["k"])
+    ta.attn_rope_apply(k, pos, w.theta)
+    v = dev_bf16(inp["v"])
+    table = ta.attn_rope_table(w.seqlen, w.head_dim, w.theta)
+    o1, l1 = unfused(ta, inp["q"], k, v, pos, w, True)
+    o2, l2 = ta.attn_prefill_rope(dev_bf16(inp["q"]), k, v, table, softmax_scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(l1, l2)

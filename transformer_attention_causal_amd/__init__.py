@@ -19,7 +19,9 @@ from .binding import (  # noqa: F401
     attn_prefill,
     attn_prefill_local_global,
     attn_prefill_paged,
+    attn_prefill_rope,
     attn_rope_apply,
+    attn_rope_table,
     attn_topk,
     load_library,
 )

@@ -23,6 +23,8 @@ _P, _I, _I64, _D, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctype
 SIGNATURES = {
     "attn_rope_apply": (_I, [_P, _I, _I64, _I, _I, _P, _D, _I, _P]),
     "attn_prefill": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
+    "attn_rope_table": (_I, [_P, _I, _I, _D, _P]),
+    "attn_prefill_rope": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _I, _P]),
     "attn_prefill_local_global": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "attn_decode_paged_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _I, _F, _P, _SZ, _P]),
@@ -122,6 +124,46 @@ def attn_prefill(q, k, v, causal=True, softmax_scale=None, o=None, lse=None, ret
     _check("attn_prefill", lib.attn_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o", q.dtype), lse_p,
                                              _code(q.dtype), bsz, s_len, hq, hkv, d, 1 if causal else 0, scale,
                                              _stream(q, stream)))
+    return (o, lse) if return_lse else o
+
+
+def attn_rope_table(n_positions, head_dim, theta, device=None, table=None, stream=None):
+    """(cos, sin) fp32 table [n_positions, head_dim/2, 2] of the rotation by integer position (the values
+    attn_rope_apply uses)."""
+    lib = load_library()
+    if table is None:
+        table = torch.empty((n_positions, head_dim // 2, 2), dtype=torch.float32,
+                            device=device if device is not None else "cuda")
+    _check("attn_rope_table", lib.attn_rope_table(_dev(table, "table", torch.float32) if table.numel() else None,
+                                                   int(n_positions), int(head_dim), float(theta),
+                                                   _stream(table, stream)))
+    return table
+
+
+def attn_prefill_rope(q, k, v, rope_table, q_positions=None, interleaved=True, causal=True, softmax_scale=None,
+                      o=None, lse=None, return_lse=False, stream=None):
+    """attn_prefill (bf16) with q UNROTATED: each query is rotated as the kernel loads it, by the cos/sin of its
+    position (q_positions int32 [B*S], or 0..S-1 per sequence when None) from rope_table [n_pos, D/2, 2] fp32.
+    k must be rotated already. Returns o [B, S, Hq, D] (and lse [B, Hq, S])."""
+    lib = load_library()
+    bsz, s_len, hq, d = q.shape
+    hkv = k.shape[2]
+    if k.shape != (bsz, s_len, hkv, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, S, Hkv, D]")
+    if rope_table.dim() != 3 or rope_table.shape[1:] != (d // 2, 2):
+        raise ValueError("rope_table must be [n_positions, head_dim/2, 2]")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((bsz, hq, s_len), dtype=torch.float32, device=q.device)
+    lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
+    pos_p = _dev(q_positions, "q_positions", torch.int32) if q_positions is not None else None
+    _check("attn_prefill_rope", lib.attn_prefill_rope(
+        _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
+        _dev(o, "o", torch.bfloat16), lse_p, bsz, s_len, hq, hkv, d, 1 if causal else 0, scale, pos_p,
+        _dev(rope_table, "rope_table", torch.float32), rope_table.shape[0], 1 if interleaved else 0,
+        _stream(q, stream)))
     return (o, lse) if return_lse else o
 
 

@@ -59,6 +59,30 @@ ATTN_EXPORT int attn_prefill(const void* q, const void* k, const void* v, void* 
                                               causal ? 1 : 0, softmax_scale, s));
 }
 
+ATTN_EXPORT int attn_rope_table(void* table, int n_positions, int head_dim, double theta, void* stream) {
+  if (n_positions < 0 || head_dim <= 0 || (head_dim & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(theta) || theta <= 1.0) return ATTN_ERR_INVALID_ARG;
+  if (head_dim > 1024) return ATTN_ERR_UNSUPPORTED;
+  if (n_positions == 0) return ATTN_OK;
+  if (!table) return ATTN_ERR_INVALID_ARG;
+  return hip_status(attn::launch_rope_table(table, n_positions, head_dim, theta, static_cast<hipStream_t>(stream)));
+}
+
+ATTN_EXPORT int attn_prefill_rope(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
+                                  int seqlen, int n_heads_q, int n_heads_kv, int head_dim, int causal,
+                                  float softmax_scale, const int32_t* q_positions, const void* rope_table,
+                                  int rope_table_len, int interleaved, void* stream) {
+  if (batch < 0 || seqlen < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0) return ATTN_ERR_INVALID_ARG;
+  if (n_heads_q % n_heads_kv != 0 || !valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (int64_t(batch) * seqlen == 0) return ATTN_OK;
+  if (!q || !k || !v || !o || !rope_table || rope_table_len <= 0) return ATTN_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(rope_table) % 16 != 0) return ATTN_ERR_INVALID_ARG;
+  return hip_status(attn::launch_prefill_bf16(q, k, v, o, lse, batch, seqlen, n_heads_q, n_heads_kv, head_dim,
+                                              causal ? 1 : 0, softmax_scale, static_cast<hipStream_t>(stream),
+                                              rope_table, rope_table_len, q_positions, interleaved ? 1 : 0));
+}
+
 ATTN_EXPORT int attn_prefill_local_global(const void* q, const void* k, const void* v, void* o, float* lse,
                                           int batch, int seqlen, int n_heads_q, int n_heads_kv, int head_dim,
                                           int window, int n_lead, int anchor_stride, float softmax_scale,

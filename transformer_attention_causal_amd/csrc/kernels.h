@@ -12,9 +12,15 @@ hipError_t launch_rope(void* x, int dtype, int64_t n_tokens, int n_heads, int he
                        double theta, int interleaved, hipStream_t stream);
 
 // Prefill. bf16: MFMA path; fp32: VALU path. head_dim 64 or 128.
+// rope_table != NULL: Q is rotated as it is loaded ([rope_len, head_dim/2] (cos, sin) fp32 by position; query
+// positions from q_positions [batch*seqlen], or 0..seqlen-1 when NULL; clamped into [0, rope_len)).
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
                                int seqlen, int hq, int hkv, int head_dim, int causal, float scale,
-                               hipStream_t stream);
+                               hipStream_t stream, const void* rope_table = nullptr, int rope_len = 0,
+                               const int32_t* q_positions = nullptr, int rope_interleaved = 0);
+// table[p][i] = (cos, sin) of p * theta^(-2i/head_dim), p < n_positions, in fp64 rounded to fp32 (the values the
+// rope kernel uses).
+hipError_t launch_rope_table(void* table, int n_positions, int head_dim, double theta, hipStream_t stream);
 // Causal prefill with a local + global mask: key j visible to query i iff j <= i and (i - j < window or
 // j < n_lead or (anchor_stride > 0 and j % anchor_stride == 0)). bf16, head_dim 64 or 128.
 hipError_t launch_prefill_window(const void* q, const void* k, const void* v, void* o, float* lse, int batch,

@@ -93,6 +93,84 @@ struct PrefillArgs {
   // Local + global mask (the WIN kernel): key j is visible to query i iff j <= i and (i - j < window, or
   // j < n_lead, or anchor_stride > 0 and j % anchor_stride == 0).
   int window, n_lead, anchor_stride;
+  // RoPE of Q fused into its load: rope_cs is a [rope_len, D/2] table of (cos, sin) fp32 by integer position, and
+  // the position of query row r is q_pos[r] (NULL: its position in the sequence, koff + i), clamped into
+  // [0, rope_len). No rotation when rope_cs is NULL.
+  const float2* rope_cs;
+  const int32_t* q_pos;
+  int rope_len, rope_inter;
+};
+
+// RoPE of the resident Q^T operands (DeepSeek 32K to 256K long context, tqpw.cn, section 2.1: pair i rotated by
+// the angle position * theta^(-2i/d); section 2.5: cos and sin read from a table indexed by integer positions).
+// The rope kernel's table values and arithmetic (fp32 FMA, bf16 rounding to nearest even), so a query rotated here
+// is bit-identical to one rotated in place by the rope kernel first. A lane holds dims 16*ks + 8*lg + s: a
+// half-split pair (i, i + D/2) lies in k-steps ks and ks + KS/2 of the same lane, an interleaved pair (2i, 2i+1)
+// in slots s and s + 1 of one register. The table rows are loaded together with Q (load) and applied after the
+// first tile copy is issued (apply), so their latency overlaps that copy.
+template <int D, int QB>
+struct RopeQ {
+  static constexpr int KS = D / 16;
+  f32x4_t t[QB][2 * KS];   // the lane's (cos, sin) pairs, in the order apply() consumes them
+
+  __device__ __forceinline__ void load(const PrefillArgs& a, int64_t qrow0, int qpos0, int koff, int S, int lq,
+                                       int lg) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qi = min(qpos0 + 32 * qb + lq, S - 1);
+      int p = a.q_pos ? a.q_pos[qrow0 + qi] : koff + qi;
+      p = min(max(p, 0), a.rope_len - 1);
+      const float* cs = reinterpret_cast<const float*>(a.rope_cs + int64_t(p) * (D / 2));
+      if (a.rope_inter) {          // pairs 8*ks + 4*lg + j, j = 0..3
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int u = 0; u < 2; ++u) t[qb][2 * ks + u] = *reinterpret_cast<const f32x4_t*>(cs + 16 * ks + 8 * lg + 4 * u);
+      } else {                     // pairs 16*ks + 8*lg + s, s = 0..7, ks < KS/2
+#pragma unroll
+        for (int ks = 0; ks < KS / 2; ++ks)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) t[qb][4 * ks + u] = *reinterpret_cast<const f32x4_t*>(cs + 32 * ks + 16 * lg + 4 * u);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void apply(bf16x8_t (&qop)[QB][KS], int inter) const {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (inter) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          u32x4_t w = __builtin_bit_cast(u32x4_t, qop[qb][ks]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4_t& tv = t[qb][2 * ks + (j >> 1)];
+            const float c = tv[2 * (j & 1)], sn = tv[2 * (j & 1) + 1];
+            const float x0 = bf16lo_to_f32(w[j]), x1 = bf16hi_to_f32(w[j]);
+            w[j] = pack_bf16x2(fmaf(x0, c, -x1 * sn), fmaf(x0, sn, x1 * c));
+          }
+          qop[qb][ks] = as_bf16x8(w);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < KS / 2; ++ks) {
+          u32x4_t wa = __builtin_bit_cast(u32x4_t, qop[qb][ks]);
+          u32x4_t wb = __builtin_bit_cast(u32x4_t, qop[qb][ks + KS / 2]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const f32x4_t& tv = t[qb][4 * ks + j];              // pairs 2j and 2j + 1
+            const float c0 = tv[0], s0 = tv[1], c1 = tv[2], s1 = tv[3];
+            const float a0 = bf16lo_to_f32(wa[j]), a1 = bf16hi_to_f32(wa[j]);
+            const float b0 = bf16lo_to_f32(wb[j]), b1 = bf16hi_to_f32(wb[j]);
+            wa[j] = pack_bf16x2(fmaf(a0, c0, -b0 * s0), fmaf(a1, c1, -b1 * s1));
+            wb[j] = pack_bf16x2(fmaf(a0, s0, b0 * c0), fmaf(a1, s1, b1 * c1));
+          }
+          qop[qb][ks] = as_bf16x8(wa);
+          qop[qb][ks + KS / 2] = as_bf16x8(wb);
+        }
+      }
+    }
+  }
 };
 
 // LDS swizzle: 16-byte chunk c of tile row r is stored at chunk position c ^ swz_key(r). LDS has 64 four-byte
@@ -305,6 +383,9 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
       qop[qb][ks] = as_bf16x8(w);
     }
   }
+  RopeQ<D, QB> rq;
+  const bool rope = !PAGED && !WIN && a.rope_cs != nullptr;   // uniform; only the plain kernel takes the table
+  if (rope) rq.load(a, qrow0, qpos0, koff, S, lq, lg);
 
   f32x16_t oacc[QB][DB];
   float m[QB], l[QB];
@@ -537,6 +618,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
       if (need && qpos0 < S) tile(bufc, std::integral_constant<int, 0>{}, key0, step, phase, rows);
     };
     copy_u(0, 0);
+    if (rope) rq.apply(qop, a.rope_inter);
     for (int u = 0; u < nlist; u += 2) {
       wait_vmem();
       __syncthreads();                                 // tile u visible to all; buffer 1 free
@@ -550,6 +632,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
     }
   } else {
   copy_tile(0, 0);
+  if (rope) rq.apply(qop, a.rope_inter);
   // Two tiles per trip so each tile's LDS buffer is a compile-time constant.
   for (int t = 0; t < ntiles; t += 2) {
     wait_vmem();
@@ -674,8 +757,11 @@ PrefillArgs prefill_args(const void* q, const void* k, const void* v, void* o, f
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int batch,
                                int seqlen, int hq, int hkv, int head_dim, int causal, float scale,
-                               hipStream_t stream) {
-  const PrefillArgs a = prefill_args(q, k, v, o, lse, batch, seqlen, hq, hkv, causal, scale);
+                               hipStream_t stream, const void* rope_table, int rope_len, const int32_t* q_positions,
+                               int rope_interleaved) {
+  PrefillArgs a = prefill_args(q, k, v, o, lse, batch, seqlen, hq, hkv, causal, scale);
+  a.rope_cs = static_cast<const float2*>(rope_table); a.rope_len = rope_len; a.q_pos = q_positions;
+  a.rope_inter = rope_interleaved;
   const dim3 grid(static_cast<unsigned>(int64_t(a.n_pblk) * batch * a.n_hgrp));
   if (head_dim == 128) prefill_bf16_kernel<128, 1, false><<<grid, dim3(kThreads), 0, stream>>>(a);
   else prefill_bf16_kernel<64, 1, false><<<grid, dim3(kThreads), 0, stream>>>(a);

@@ -145,6 +145,20 @@ __global__ __launch_bounds__(kRopeThreads) void rope_pair_kernel(T* __restrict__
   }
 }
 
+// Table of (cos, sin) by integer position for every pair: the same fp64 expressions as build_table.
+__global__ __launch_bounds__(kRopeThreads) void rope_table_kernel(float2* __restrict__ table, int n_positions,
+                                                                 int head_dim, double theta) {
+  const int half = head_dim / 2;
+  const int64_t e = int64_t(blockIdx.x) * kRopeThreads + threadIdx.x;
+  if (e >= int64_t(n_positions) * half) return;
+  const int p = int(e / half), i = int(e % half);
+  const double inv_freq = pow(theta, -2.0 * double(i) / double(head_dim));
+  const double ang = double(p) * inv_freq;
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  table[e] = make_float2(float(cs), float(sn));
+}
+
 template <typename T>
 hipError_t launch_typed(T* x, int64_t n_tokens, int n_heads, int head_dim, const int32_t* positions, double theta,
                         int interleaved, hipStream_t stream) {
@@ -279,6 +293,14 @@ hipError_t launch_rope(void* x, int dtype, int64_t n_tokens, int n_heads, int he
   if (dtype == 0)
     return launch_typed(static_cast<uint16_t*>(x), n_tokens, n_heads, head_dim, positions, theta, interleaved, stream);
   return launch_typed(static_cast<float*>(x), n_tokens, n_heads, head_dim, positions, theta, interleaved, stream);
+}
+
+hipError_t launch_rope_table(void* table, int n_positions, int head_dim, double theta, hipStream_t stream) {
+  const int64_t n = int64_t(n_positions) * (head_dim / 2);
+  if (n == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((n + kRopeThreads - 1) / kRopeThreads)), block(kRopeThreads);
+  rope_table_kernel<<<grid, block, 0, stream>>>(static_cast<float2*>(table), n_positions, head_dim, theta);
+  return hipGetLastError();
 }
 
 }  // namespace attn
