@@ -114,6 +114,11 @@ __device__ __forceinline__ void load_lds4(buf_rsrc_t rsrc, uint32_t voff, void* 
   raw_buffer_load_lds(rsrc, (lds_void_t*)lds_wave_base, 4, static_cast<int>(voff), static_cast<int>(soff), 0, 0);
 }
 
+// One dword per lane from `rsrc` at byte offset voffset + soffset into a VGPR (counted by vmcnt like the copies;
+// offsets past the resource read 0).
+__device__ int raw_buffer_load_i32(buf_rsrc_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.i32");
+
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // ---------------------------------------------------------------------------------------- cross-lane --

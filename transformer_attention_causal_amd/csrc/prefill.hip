@@ -417,11 +417,20 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   // Row 0 of the K or V tile at key0 and its valid row count. Paged: tiles never straddle pages (page size a
   // multiple of the tile); a page number outside [0, num_pages), or a tile past the table's max_pages entries,
   // gives no rows (zeros, no memory access).
-  auto tile_src = [&](const uint16_t* kv, int key0, int& rows) -> const uint16_t* {
+  // Paged: the block-table entry of a tile is read one tile ahead of its copy, by a vector load that the loop's
+  // wait for the tile copies also covers, so no table-load latency sits between a barrier and the next copy
+  // (measured: a scalar load there cost about 6% of the chunked prefill). Entries past max_pages read as 0 and
+  // are replaced by -1 (no page) at use.
+  buf_rsrc_t trs = {0, 0, 0, 0};
+  if constexpr (PAGED) trs = make_buf_rsrc(a.table + int64_t(b) * a.max_pages, uint32_t(a.max_pages) * 4u);
+  auto page_load = [&](int t) -> int {                 // raw table entry of tile t (in flight until the next wait)
+    return PAGED ? raw_buffer_load_i32(trs, ((t * kTileKeys) >> a.page_shift) * 4, 0, 0) : 0;
+  };
+  auto tile_src = [&](const uint16_t* kv, int key0, int& rows, int page_raw) -> const uint16_t* {
     rows = max(0, min(kTileKeys, T - key0));
     if constexpr (PAGED) {
       const int pi = key0 >> a.page_shift;
-      const int page = pi < a.max_pages ? a.table[int64_t(b) * a.max_pages + pi] : -1;
+      const int page = pi < a.max_pages ? __builtin_amdgcn_readfirstlane(page_raw) : -1;
       if (page < 0 || page >= a.num_pages) rows = 0;
       const int64_t slot0 = (int64_t(max(page, 0)) << a.page_shift) + (key0 & ((1 << a.page_shift) - 1));
       return kv + slot0 * a.hkv * D;
@@ -429,11 +438,11 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
       return kv + (int64_t(b) * S + min(key0, T - 1)) * a.hkv * D;
     }
   };
-  auto copy_tile = [&](int buf, int t) {
+  auto copy_tile = [&](int buf, int t, int page_raw) {
     int rows;
-    const uint16_t* kb = tile_src(a.k, t * kTileKeys, rows);
+    const uint16_t* kb = tile_src(a.k, t * kTileKeys, rows, page_raw);
     cp.issue(lds[buf][0], kb, rows, a.hkv, wave);
-    const uint16_t* vb = tile_src(a.v, t * kTileKeys, rows);
+    const uint16_t* vb = tile_src(a.v, t * kTileKeys, rows, page_raw);
     cp.issue(lds[buf][1], vb, rows, a.hkv, wave);
   };
 
@@ -631,18 +640,28 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
       run_u(std::integral_constant<int, 1>{}, u + 1);
     }
   } else {
-  copy_tile(0, 0);
+  int pg = page_load(0);
+  copy_tile(0, 0, pg);
+  pg = page_load(1);                                   // table entry of the next tile to copy
   if (rope) rq.apply(qop, a.rope_inter);
   // Two tiles per trip so each tile's LDS buffer is a compile-time constant.
   for (int t = 0; t < ntiles; t += 2) {
     wait_vmem();
     __syncthreads();                                   // tile t visible to all; buffer 1 free
-    if (t + 1 < ntiles) copy_tile(1, t + 1);
+    if (t + 1 < ntiles) {
+      const int cur = pg;
+      pg = page_load(t + 2);
+      copy_tile(1, t + 1, cur);
+    }
     if (t * kTileKeys < kend_w) tiles(std::integral_constant<int, 0>{}, t);
     if (t + 1 >= ntiles) break;
     wait_vmem();
     __syncthreads();                                   // tile t+1 visible to all; buffer 0 free
-    if (t + 2 < ntiles) copy_tile(0, t + 2);
+    if (t + 2 < ntiles) {
+      const int cur = pg;
+      pg = page_load(t + 3);
+      copy_tile(0, t + 2, cur);
+    }
     if ((t + 1) * kTileKeys < kend_w) tiles(std::integral_constant<int, 1>{}, t + 1);
   }
   }
