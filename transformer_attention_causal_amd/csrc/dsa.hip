@@ -29,7 +29,11 @@ namespace {
 
 constexpr int kIdxWaves = 4;            // waves per indexer workgroup
 #ifndef ATTN_IDX_KPW
-#define ATTN_IDX_KPW 256
+#define ATTN_IDX_KPW 1024
+#endif
+// LDS buffers per wave in the staged path (2: one block's copy in flight while one is scored; 3: two).
+#ifndef ATTN_IDX_NBUF
+#define ATTN_IDX_NBUF 2
 #endif
 #ifndef ATTN_IDX_PIPE
 #define ATTN_IDX_PIPE 2
@@ -113,7 +117,14 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void dsa_indexer_kernel(const ui
     constexpr int NCH = DI / 8;                // 16-byte chunks per row
     constexpr int RPI = 1024 / RB;             // rows per copy instruction
     constexpr int NI = 32 / RPI;               // copy instructions per block
-    __shared__ __attribute__((aligned(16))) uint16_t kl0[kIdxWaves][32 * DI], kl1[kIdxWaves][32 * DI];
+    constexpr int NB = ATTN_IDX_NBUF;
+    static_assert(NB == 2 || NB == 3, "two or three buffers");
+    __shared__ __attribute__((aligned(16))) uint16_t kl0[kIdxWaves][32 * DI], kl1[kIdxWaves][32 * DI],
+        kl2[kIdxWaves][NB > 2 ? 32 * DI : 8];
+    auto buf = [&](auto bc) -> uint16_t* {
+      constexpr int B = decltype(bc)::value;
+      if constexpr (B == 0) return kl0[wave]; else if constexpr (B == 1) return kl1[wave]; else return kl2[wave];
+    };
     auto swz = [](int r) { return (NCH == 16 ? r : r >> 1) & (NCH - 1); };
     const uint16_t* kseq = k_idx + int64_t(b) * max_len * DI;
     const int crow = lane / NCH, cslot = lane % NCH;
@@ -133,26 +144,32 @@ __global__ __launch_bounds__(64 * kIdxWaves, 2) void dsa_indexer_kernel(const ui
       for (int ks = 0; ks < KS; ++ks) kb[ks] = lds_read16(src, koff[ks]);
     };
     wait_vmem();                               // query and weights are in: only block copies are outstanding now
-    copy_block(kl0[wave], key_begin);
+    constexpr int PRE = NB - 1;                // blocks in flight while one is scored
+    copy_block(buf(std::integral_constant<int, 0>{}), key_begin);
+    if (PRE >= 2 && 1 < nblk) copy_block(buf(std::integral_constant<int, 1>{}), key_begin + 32);
     u32x4_t kb[KS];
-    for (int i = 0; i < nblk; i += 2) {
-      if (i + 1 < nblk) {
-        copy_block(kl1[wave], key_begin + 32 * (i + 1));
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");   // block i landed; block i+1 in flight
-      } else {
-        wait_vmem();
+    for (int u = 0; u < nblk; u += NB) {
+#pragma unroll
+      for (int k = 0; k < NB; ++k) {
+        const int i = u + k;
+        if (i >= nblk) break;
+        // issue block i + PRE into the buffer read at step i - 1, then wait for block i (the PRE blocks after it
+        // may stay in flight)
+        const int nfly = min(PRE, nblk - 1 - i);
+        if (nfly == PRE) {
+          const int nb = (k + PRE) % NB;         // resolves at compile time once the loop is unrolled
+          uint16_t* dst = nb == 0 ? buf(std::integral_constant<int, 0>{})
+                        : nb == 1 ? buf(std::integral_constant<int, 1>{}) : buf(std::integral_constant<int, 2>{});
+          copy_block(dst, key_begin + 32 * (i + PRE));
+        }
+        if (nfly >= 2) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NI) : "memory");
+        else if (nfly == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
+        else wait_vmem();
+        const uint16_t* src = k == 0 ? buf(std::integral_constant<int, 0>{})
+                            : k == 1 ? buf(std::integral_constant<int, 1>{}) : buf(std::integral_constant<int, 2>{});
+        read_block(src, kb);
+        score_block(kb, key_begin + 32 * i);
       }
-      read_block(kl0[wave], kb);
-      score_block(kb, key_begin + 32 * i);
-      if (i + 1 >= nblk) break;
-      if (i + 2 < nblk) {
-        copy_block(kl0[wave], key_begin + 32 * (i + 2));
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NI) : "memory");
-      } else {
-        wait_vmem();
-      }
-      read_block(kl1[wave], kb);
-      score_block(kb, key_begin + 32 * (i + 1));
     }
     return;
   }
