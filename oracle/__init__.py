@@ -28,5 +28,6 @@ from .attention import (  # noqa: F401
     decode_paged_q8,
     local_global_visible,
     attention_local_global,
+    mla_decode_q8,
     attention_local_global_rows,
 )

@@ -41,6 +41,9 @@ Readings taken where the pages are silent or garbled:
     (two's complement) or an OCP FP8 E4M3 byte (sign, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is
     subnormal; no infinities, S.1111.111 is NaN) and the scale an fp32 per (KV head, channel) for K and for V;
     attention is then exactly decode_paged on the dequantised caches;
+  * 8-bit MLA latent cache (the same passages, for the shared latent cache): c_kv and k_pe are stored as codes with
+    one fp32 scale per latent channel (c_scale [C]) and per rope channel (pe_scale [R]), shared by every head and
+    token; attention is exactly mla_decode on the dequantised caches;
   * local + global mask ([LC-SW]): key j is visible to query i iff j <= i and (i - j < window, or j < n_lead, or
     anchor_stride > 0 and j % anchor_stride == 0); window >= 1 (a query always sees itself); the global sampling
     rate is 1 / anchor_stride, and j = 0 is an anchor whenever anchor_stride > 0.
@@ -51,7 +54,7 @@ __all__ = [
     "bf16_bits_to_f64", "rope_inv_freq", "rope", "attention_prefill", "attention_prefill_rows", "gather_paged",
     "decode_paged", "mla_decode", "mla_naive", "kv_append_paged", "prefill_paged", "dsa_indexer_scores",
     "topk_indices", "mla_sparse_decode", "fp8_e4m3_decode", "int8_decode", "dequantize_kv", "decode_paged_q8",
-    "local_global_visible", "attention_local_global", "attention_local_global_rows",
+    "local_global_visible", "attention_local_global", "attention_local_global_rows", "mla_decode_q8",
 ]
 
 
@@ -376,6 +379,15 @@ def decode_paged_q8(q, k_codes, v_codes, k_scale, v_scale, kind, block_table, se
     """Paged decode over 8-bit K/V caches: decode_paged on the dequantised caches. kind: "fp8" or "int8"."""
     return decode_paged(q, dequantize_kv(k_codes, k_scale, kind), dequantize_kv(v_codes, v_scale, kind), block_table,
                         seq_lens, scale)
+
+
+def mla_decode_q8(q_lat, q_pe, c_codes, pe_codes, c_scale, pe_scale, kind, seq_lens, scale):
+    """Absorbed MLA decode over an 8-bit latent cache: mla_decode on c_kv = code * c_scale[channel] and
+    k_pe = code * pe_scale[channel] ([LC-KV], [AP-F8] applied to the latent cache). kind: "fp8" or "int8"."""
+    dec = fp8_e4m3_decode if kind == "fp8" else int8_decode
+    c_kv = dec(c_codes) * np.asarray(c_scale, np.float64)
+    k_pe = dec(pe_codes) * np.asarray(pe_scale, np.float64)
+    return mla_decode(q_lat, q_pe, c_kv, k_pe, seq_lens, scale)
 
 
 def local_global_visible(rows, n_keys, window, n_lead, anchor_stride):

@@ -159,16 +159,32 @@ def paged_decode_inputs(w: PagedDecode, seed=0, batch=None, seq_lens=None, page_
     return out
 
 
-def mla_inputs(w: MLADecode, seed=0, batch=None, seqlen=None, seq_lens=None):
-    """q_lat [B, H, C], q_pe [B, H, R], c_kv [B, T, C], k_pe [B, T, R] (bf16 bits), seq_lens [B] int32."""
+def mla_scales(seed, w, kind):
+    """Per-channel fp32 scales of an 8-bit latent cache of N(0,1) values: 4 / code_max times a seeded factor in
+    [0.75, 1.25], as (c_scale [C], pe_scale [R])."""
+    top = 448.0 if kind == "fp8" else 127.0
+    f = _rng(seed, "mla.scale").uniform(0.75, 1.25, size=w.latent + w.rope)
+    s = (4.0 / top * f).astype(np.float32)
+    return s[: w.latent].copy(), s[w.latent:].copy()
+
+
+def mla_inputs(w: MLADecode, seed=0, batch=None, seqlen=None, seq_lens=None, kv="bf16"):
+    """q_lat [B, H, C], q_pe [B, H, R], c_kv [B, T, C], k_pe [B, T, R] (bf16 bits), seq_lens [B] int32.
+    kv "fp8" / "int8": c_kv and k_pe hold 8-bit codes of the same draws divided by per-channel scales c_scale [C]
+    and pe_scale [R] (also returned, with kv)."""
     b = w.batch if batch is None else batch
     t = w.seqlen if seqlen is None else seqlen
     q_lat = normal(seed, "mla.q_lat", (b, w.heads, w.latent), "bf16")
     q_pe = normal(seed, "mla.q_pe", (b, w.heads, w.rope), "bf16")
-    c_kv = normal(seed, "mla.c_kv", (b, t, w.latent), "bf16")
-    k_pe = normal(seed, "mla.k_pe", (b, t, w.rope), "bf16")
     lens = np.full(b, t, dtype=np.int32) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
-    return dict(q_lat=q_lat, q_pe=q_pe, c_kv=c_kv, k_pe=k_pe, seq_lens=lens)
+    if kv == "bf16":
+        c_kv = normal(seed, "mla.c_kv", (b, t, w.latent), "bf16")
+        k_pe = normal(seed, "mla.k_pe", (b, t, w.rope), "bf16")
+        return dict(q_lat=q_lat, q_pe=q_pe, c_kv=c_kv, k_pe=k_pe, seq_lens=lens)
+    cs, ps = mla_scales(seed, w, kv)
+    c_kv = normal(seed, "mla.c_kv", (b, t, w.latent), None, q8=(cs, kv))
+    k_pe = normal(seed, "mla.k_pe", (b, t, w.rope), None, q8=(ps, kv))
+    return dict(q_lat=q_lat, q_pe=q_pe, c_kv=c_kv, k_pe=k_pe, seq_lens=lens, c_scale=cs, pe_scale=ps, kv=kv)
 
 
 def chunked_prefill_inputs(w, seed=0, ctx_lens=None, new_lens=None, page_size=None, hq=None, hkv=None,

@@ -672,6 +672,42 @@ def test_q8_decode_scales_are_per_channel_and_linear():
         np.testing.assert_allclose(o5, o1 * sv[np.arange(Hq) // (Hq // Hkv)][None], atol=1e-13)
 
 
+def test_mla_q8_single_token_and_constant_value_closed_forms():
+    """One token: the output is its dequantised latent row (softmax over one key is 1), per channel. Identical
+    latent rows: the output is that row whatever the scores. FP8 0x38 = 1, 0x40 = 2, 0xC4 = -3; int8 codes are the
+    integers; distinct per-channel scales catch a misplaced or transposed scale."""
+    C, R, H = 6, 2, 3
+    rng = np.random.default_rng(71)
+    q_lat = rng.standard_normal((1, H, C)); q_pe = rng.standard_normal((1, H, R))
+    cs = np.array([0.5, 0.25, 2.0, 1.5, 0.75, 3.0]); ps = np.array([0.1, 0.2])
+    row8 = np.array([0x38, 0x40, 0xC4, 0x38, 0x40, 0xC4], np.uint8)          # 1, 2, -3, 1, 2, -3
+    row_i = np.array([1, 2, -3, 1, 2, -3], np.int8).view(np.uint8)
+    want = np.array([1, 2, -3, 1, 2, -3]) * cs
+    pe = rng.integers(0, 0x70, (1, 5, R)).astype(np.uint8)                     # finite codes (FP8 and int8)
+    for kind, row in (("fp8", row8), ("int8", row_i)):
+        o, _ = oracle.mla_decode_q8(q_lat, q_pe, row[None, None], pe[:, :1], cs, ps, kind, [1], 0.2)
+        np.testing.assert_allclose(o[0], np.broadcast_to(want, (H, C)), rtol=0, atol=1e-15)
+        o, _ = oracle.mla_decode_q8(q_lat, q_pe, np.repeat(row[None, None], 5, axis=1), pe, cs, ps, kind, [5], 0.2)
+        np.testing.assert_allclose(o[0], np.broadcast_to(want, (H, C)), rtol=0, atol=1e-13)
+
+
+def test_mla_q8_rope_scale_sits_on_the_scores():
+    """Two tokens, zero latent query: the scores are scale * q_pe . (code * pe_scale), so the weights are a
+    two-way softmax written out by hand."""
+    C, R = 4, 2
+    q_lat = np.zeros((1, 1, C)); q_pe = np.array([[[1.5, -0.5]]])
+    cs = np.ones(C); ps = np.array([0.7, 0.3])
+    c = np.array([[[0x38, 0x38, 0x38, 0x38], [0x40, 0xC4, 0x38, 0x40]]], np.uint8)   # rows (1,1,1,1), (2,-3,1,2)
+    pe = np.array([[[0x40, 0x38], [0xC4, 0x40]]], np.uint8)                             # (2, 1), (-3, 2)
+    o, lse = oracle.mla_decode_q8(q_lat, q_pe, c, pe, cs, ps, "fp8", [2], 0.5)
+    s0 = 0.5 * (1.5 * 2 * 0.7 - 0.5 * 1 * 0.3)
+    s1 = 0.5 * (1.5 * -3 * 0.7 - 0.5 * 2 * 0.3)
+    w0, w1 = np.exp(s0), np.exp(s1)
+    want = (w0 * np.array([1, 1, 1, 1]) + w1 * np.array([2, -3, 1, 2])) / (w0 + w1)
+    np.testing.assert_allclose(o[0, 0], want, rtol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], np.log(w0 + w1), rtol=1e-14)
+
+
 # --------------------------------------------------------------------------------------- local + global mask ----
 
 def _lg_case(seed, B=1, S=40, Hq=4, Hkv=2, D=8):
