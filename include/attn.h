@@ -9,6 +9,7 @@
  *   attn_decode_paged     one query token per sequence against a paged KV cache (split-KV + log-sum-exp combine)
  *   attn_decode_paged_q8  the same over 8-bit (FP8 E4M3 or int8) K/V caches with per-channel scales
  *   attn_mla_decode       multi-head latent attention decode in the absorbed form
+ *   attn_mla_decode_q8    the same over an 8-bit (FP8 E4M3 or int8) latent cache with per-channel scales
  *   attn_kv_append_paged  write new tokens' keys (rotated) and values into a paged KV cache
  *   attn_prefill_paged    chunked / variable-length causal prefill of new tokens against a paged KV cache
  *   attn_dsa_indexer      DeepSeek Sparse Attention: lightning-indexer relevance score of every cached token
@@ -212,6 +213,28 @@ int attn_mla_decode(const void* q_latent, const void* q_pe, const void* c_kv, co
                     const int32_t* seq_lens, void* o_latent, float* lse, int batch, int n_heads, int kv_lora_rank,
                     int rope_dim, int max_seqlen_kv, float softmax_scale, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* MLA decode (as attn_mla_decode) over an 8-bit latent cache: c_kv and k_pe hold 8-bit codes with one fp32 scale
+ * per channel, shared by every token and head.
+ * ("DeepSeek 32K to 256K long context", tqpw.cn, section 2.5: cached keys and values stored as 8-bit integers with
+ *  a per-channel scale; "7 anti-patterns of DeepSeek attention optimisation", lpnh.cn, section 3.3: FP8 E4M3,
+ *  largest finite value 448; "DeepSeek-V3 attention guide", dksg.cn: the absorbed scores over the shared latent
+ *  cache kv_cache and rope cache pe_cache, served in FP8 as well as BF16.)
+ *   c_kv       [batch, max_seqlen_kv, kv_lora_rank] uint8 codes; value = decode(code) * c_scale[channel]
+ *   k_pe       [batch, max_seqlen_kv, rope_dim] uint8 codes;     value = decode(code) * pe_scale[channel]
+ *   c_scale    [kv_lora_rank] fp32, pe_scale [rope_dim] fp32
+ *   kv_kind    ATTN_KV_FP8_E4M3 (OCP E4M3: bias 7, subnormals, no infinities, S.1111.111 is NaN) or ATTN_KV_INT8
+ *              (two's complement)
+ *   q_latent, q_pe, seq_lens, o_latent, lse, workspace: as attn_mla_decode (same workspace size).
+ * The result is the exact attention over the dequantised cache. Codes widen exactly to bf16 for the MFMA; the key
+ * scales are folded into the query (one bf16 rounding of q * scale per element), the value scales multiply the
+ * output channels in fp32. All of q_latent, q_pe, c_kv, k_pe and both scale arrays must be 16-byte aligned.
+ * Errors: as attn_mla_decode, plus INVALID_ARG for a NULL or misaligned scale or tensor, UNSUPPORTED for another
+ * kv_kind. */
+int attn_mla_decode_q8(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
+                       const float* c_scale, const float* pe_scale, int kv_kind, const int32_t* seq_lens,
+                       void* o_latent, float* lse, int batch, int n_heads, int kv_lora_rank, int rope_dim,
+                       int max_seqlen_kv, float softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Append new tokens to a paged KV cache, rotating the keys.
  * (Attention notes, makinaruto.github.io, "Page Attention": logical token t of a sequence lives in physical page

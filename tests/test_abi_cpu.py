@@ -33,7 +33,7 @@ def test_header_declares_the_operations():
     names = declared_functions()
     for n in ("attn_rope_apply", "attn_prefill", "attn_decode_paged", "attn_mla_decode", "attn_kv_append_paged",
               "attn_prefill_paged", "attn_dsa_indexer", "attn_topk", "attn_mla_sparse_decode", "attn_decode_paged_q8",
-              "attn_prefill_local_global", "attn_rope_table", "attn_prefill_rope"):
+              "attn_prefill_local_global", "attn_rope_table", "attn_prefill_rope", "attn_mla_decode_q8"):
         assert n in names
 
 
@@ -173,6 +173,28 @@ def test_mla_validation(lib):
     assert call(h=256) == UNSUPPORTED
     assert call(wsb=ws_need - 4) == WORKSPACE
     assert call(b=0) == OK
+
+
+def test_mla_q8_validation(lib):
+    f = lib.attn_mla_decode_q8
+    WS = ctypes.c_size_t(1 << 40)
+    args = lambda **kw: dict(dict(ql=FAKE, qp=FAKE, ckv=FAKE, kpe=FAKE, cs=FAKE, ps=FAKE, kind=1, sl=FAKE, o=FAKE,
+                                  b=2, h=128, c=512, r=64, t=100, scale=0.07, ws=FAKE), **kw)
+    call = lambda **kw: (lambda a: f(a["ql"], a["qp"], a["ckv"], a["kpe"], a["cs"], a["ps"], a["kind"], a["sl"],
+                                     a["o"], NULL, a["b"], a["h"], a["c"], a["r"], a["t"], a["scale"], a["ws"], WS,
+                                     NULL))(args(**kw))
+    assert call(kind=0) == UNSUPPORTED                  # bf16 has its own entry point
+    assert call(kind=3) == UNSUPPORTED
+    assert call(cs=NULL) == INVALID
+    assert call(ps=NULL) == INVALID
+    assert call(cs=ctypes.c_void_p(0x1004)) == INVALID  # scales must be 16-byte aligned
+    assert call(ckv=ctypes.c_void_p(0x1008)) == INVALID
+    assert call(h=48) == UNSUPPORTED
+    assert call(c=256) == UNSUPPORTED
+    assert call(scale=0.0) == INVALID
+    assert call(t=-1) == INVALID
+    assert call(ws=NULL) == WORKSPACE
+    assert call(b=0, ql=NULL, qp=NULL, ckv=NULL, kpe=NULL, cs=NULL, ps=NULL, sl=NULL, o=NULL) == OK
 
 
 def test_binding_refuses_without_library(tmp_path):

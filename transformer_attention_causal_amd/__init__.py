@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     attn_dsa_indexer,
     attn_kv_append_paged,
     attn_mla_decode,
+    attn_mla_decode_q8,
     attn_mla_decode_workspace_size,
     attn_mla_sparse_decode,
     attn_mla_sparse_decode_workspace_size,

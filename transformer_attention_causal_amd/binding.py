@@ -32,6 +32,7 @@ SIGNATURES = {
                                   _P]),
     "attn_mla_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "attn_mla_decode": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
+    "attn_mla_decode_q8": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "attn_kv_append_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _D, _I, _P]),
     "attn_prefill_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I64, _F, _P]),
     "attn_dsa_indexer": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
@@ -245,6 +246,33 @@ def attn_mla_decode(q_latent, q_pe, c_kv, k_pe, seq_lens, softmax_scale, o=None,
         _dev(seq_lens, "seq_lens", torch.int32), _dev(o, "o_latent", torch.bfloat16), lse_p, bsz, nh, c, r, t,
         float(softmax_scale), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(q_latent, stream)))
+    return (o, lse) if return_lse else o
+
+
+def attn_mla_decode_q8(q_latent, q_pe, c_kv, k_pe, c_scale, pe_scale, kv_kind, seq_lens, softmax_scale, o=None,
+                       lse=None, workspace=None, return_lse=False, stream=None):
+    """MLA decode over an 8-bit latent cache: c_kv [B, T, C] and k_pe [B, T, R] uint8 codes of kv_kind ("fp8" or
+    "int8") with per-channel fp32 scales c_scale [C], pe_scale [R]; q_latent [B, H, C],
+    q_pe [B, H, R] bf16; seq_lens [B] int32. Returns o_latent [B, H, C] bf16 (and lse [B, H] fp32)."""
+    lib = load_library()
+    bsz, nh, c = q_latent.shape
+    r = q_pe.shape[-1]
+    t = c_kv.shape[1]
+    kind = {"fp8": ATTN_KV_FP8_E4M3, "int8": ATTN_KV_INT8}[kv_kind]
+    if o is None:
+        o = torch.empty_like(q_latent)
+    if lse is None and return_lse:
+        lse = torch.empty((bsz, nh), dtype=torch.float32, device=q_latent.device)
+    need = attn_mla_decode_workspace_size(bsz, nh, c, max(1, t))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_latent.device)
+    lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
+    _check("attn_mla_decode_q8", lib.attn_mla_decode_q8(
+        _dev(q_latent, "q_latent", torch.bfloat16), _dev(q_pe, "q_pe", torch.bfloat16),
+        _dev(c_kv, "c_kv", torch.uint8), _dev(k_pe, "k_pe", torch.uint8), _dev(c_scale, "c_scale", torch.float32),
+        _dev(pe_scale, "pe_scale", torch.float32), int(kind), _dev(seq_lens, "seq_lens", torch.int32),
+        _dev(o, "o_latent", torch.bfloat16), lse_p, bsz, nh, c, r, t, float(softmax_scale),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(), _stream(q_latent, stream)))
     return (o, lse) if return_lse else o
 
 

@@ -175,6 +175,29 @@ ATTN_EXPORT int attn_mla_decode(const void* q_latent, const void* q_pe, const vo
                                             static_cast<hipStream_t>(stream)));
 }
 
+ATTN_EXPORT int attn_mla_decode_q8(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
+                                   const float* c_scale, const float* pe_scale, int kv_kind, const int32_t* seq_lens,
+                                   void* o_latent, float* lse, int batch, int n_heads, int kv_lora_rank, int rope_dim,
+                                   int max_seqlen_kv, float softmax_scale, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (batch < 0 || n_heads <= 0 || kv_lora_rank <= 0 || rope_dim <= 0 || max_seqlen_kv < 0) return ATTN_ERR_INVALID_ARG;
+  if (!valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (kv_kind != ATTN_KV_FP8_E4M3 && kv_kind != ATTN_KV_INT8) return ATTN_ERR_UNSUPPORTED;
+  if (kv_lora_rank != 512 || rope_dim != 64 || n_heads % 32 != 0 || n_heads > 128) return ATTN_ERR_UNSUPPORTED;
+  if (batch == 0) return ATTN_OK;
+  if (!q_latent || !q_pe || !seq_lens || !o_latent || !c_scale || !pe_scale) return ATTN_ERR_INVALID_ARG;
+  if (max_seqlen_kv > 0 && (!c_kv || !k_pe)) return ATTN_ERR_INVALID_ARG;
+  const uintptr_t align = reinterpret_cast<uintptr_t>(q_latent) | reinterpret_cast<uintptr_t>(q_pe) |
+                          reinterpret_cast<uintptr_t>(c_kv) | reinterpret_cast<uintptr_t>(k_pe) |
+                          reinterpret_cast<uintptr_t>(c_scale) | reinterpret_cast<uintptr_t>(pe_scale);
+  if (align % 16 != 0) return ATTN_ERR_INVALID_ARG;
+  const size_t need = attn::mla_decode_workspace_bytes(batch, n_heads, kv_lora_rank, max(1, max_seqlen_kv));
+  if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+  return hip_status(attn::launch_mla_decode_q8(q_latent, q_pe, c_kv, k_pe, c_scale, pe_scale, kv_kind, seq_lens,
+                                               o_latent, lse, batch, n_heads, max_seqlen_kv, softmax_scale,
+                                               workspace, static_cast<hipStream_t>(stream)));
+}
+
 ATTN_EXPORT int attn_kv_append_paged(const void* k_new, const void* v_new, const int32_t* cu_new,
                                      const int32_t* cache_lens, void* k_cache, void* v_cache,
                                      const int32_t* block_table, int batch, int total_new, int n_heads_kv,

@@ -52,8 +52,6 @@ static_assert(kDecodeChunk % 32 == 0 && kDecodeChunk / 16 <= 64, "a chunk's page
 // pieces of the same page slots at the same time), chunk-major = the chunks of one head are consecutive. With
 // 1024-key chunks head-major measured faster for every kernel here, so the launch uses it.
 
-// Cache element kinds: 0 bf16, 1 FP8 E4M3 codes, 2 int8 codes (the 8-bit kinds carry per-channel scales).
-constexpr int kKvBf16 = 0, kKvFp8 = 1, kKvInt8 = 2;
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -82,25 +80,6 @@ __device__ __forceinline__ bf16x8_t transpose_pick(const u32x4_t* vv, int j) {
   return as_bf16x8(w);
 }
 
-// Two 8-bit codes (bytes 0-1, or 2-3 when hi) of `w` as two bf16 (exact).
-template <int KV>
-__device__ __forceinline__ uint32_t codes_to_bf16x2(uint32_t w, bool hi) {
-  if constexpr (KV == kKvFp8) {
-    return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
-                                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
-  } else {
-    const uint32_t u = w ^ 0x80808080u;               // biased bytes: code + 128
-    const int sh = hi ? 16 : 0;
-    return pack_bf16x2(float((u >> sh) & 255u) - 128.f, float((u >> (sh + 8)) & 255u) - 128.f);
-  }
-}
-
-// Eight 8-bit codes (two dwords) as eight bf16 (four dwords), in order.
-template <int KV>
-__device__ __forceinline__ u32x4_t codes_to_bf16x8(uint32_t w0, uint32_t w1) {
-  return u32x4_t{codes_to_bf16x2<KV>(w0, false), codes_to_bf16x2<KV>(w0, true), codes_to_bf16x2<KV>(w1, false),
-                 codes_to_bf16x2<KV>(w1, true)};
-}
 
 template <int KV>
 __global__ __launch_bounds__(64) void decode_paged_split_kernel(DecodeArgs a) {

@@ -57,6 +57,31 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// ------------------------------------------------------------------------------------- 8-bit cache codes --
+// Cache element kinds: 0 bf16, 1 FP8 E4M3 codes, 2 int8 codes (the 8-bit kinds carry per-channel scales). Every
+// E4M3 and int8 value is exact in bf16, so codes become bf16 MFMA operands by exact conversion.
+constexpr int kKvBf16 = 0, kKvFp8 = 1, kKvInt8 = 2;
+
+// Two 8-bit codes (bytes 0-1, or 2-3 when hi) of `w` as two bf16 (exact).
+template <int KV>
+__device__ __forceinline__ uint32_t codes_to_bf16x2(uint32_t w, bool hi) {
+  if constexpr (KV == kKvFp8) {
+    return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
+                                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+  } else {
+    const uint32_t u = w ^ 0x80808080u;               // biased bytes: code + 128
+    const int sh = hi ? 16 : 0;
+    return pack_bf16x2(float((u >> sh) & 255u) - 128.f, float((u >> (sh + 8)) & 255u) - 128.f);
+  }
+}
+
+// Eight 8-bit codes (two dwords) as eight bf16 (four dwords), in order.
+template <int KV>
+__device__ __forceinline__ u32x4_t codes_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return u32x4_t{codes_to_bf16x2<KV>(w0, false), codes_to_bf16x2<KV>(w0, true), codes_to_bf16x2<KV>(w1, false),
+                 codes_to_bf16x2<KV>(w1, true)};
+}
+
 // ------------------------------------------------------------------------------------------------- LDS --
 // LDS reads. The base pointer is __restrict__ so that, once inlined, each read carries alias-scope
 // metadata; without it the compiler treats every LDS read as possibly aliasing an in-flight direct-to-LDS

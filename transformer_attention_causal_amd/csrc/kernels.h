@@ -68,6 +68,13 @@ size_t mla_sparse_workspace_bytes(int batch, int n_heads, int kv_lora_rank, int 
 hipError_t launch_mla_decode(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
                              const int32_t* seq_lens, void* o_latent, float* lse, int batch, int n_heads,
                              int max_seqlen_kv, float scale, void* workspace, hipStream_t stream);
+// MLA decode over an 8-bit latent cache: c_kv [batch, max_len, 512] and k_pe [batch, max_len, 64] codes of `kind`
+// (1 FP8 E4M3, 2 int8) with per-channel scales c_scale [512], pe_scale [64] (16-byte aligned); workspace as
+// mla_decode_workspace_bytes.
+hipError_t launch_mla_decode_q8(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
+                                const float* c_scale, const float* pe_scale, int kind, const int32_t* seq_lens,
+                                void* o_latent, float* lse, int batch, int n_heads, int max_seqlen_kv, float scale,
+                                void* workspace, hipStream_t stream);
 
 // Sparse MLA decode over a [batch, topk] list of token indices per sequence (same workspace layout as the dense
 // form with topk in place of max_seqlen_kv).

@@ -68,7 +68,24 @@ struct MlaArgs {
   float scale;
   const int32_t* idx;   // sparse form: [batch, topk] token indices (entries outside [0, L) are ignored)
   int topk;
+  const float* c_scale;   // 8-bit latent cache: [kC] and [kR] per-channel scales
+  const float* pe_scale;
 };
+
+// 8-bit latent cache (the KV template argument): a tile's codes (64 latent rows of 512 bytes, then 64 rope rows of
+// 64 bytes, in token order) are copied into a staging buffer, then widened by all waves into the bf16 tile above,
+// which the unchanged product code reads. Each copy instruction moves 1 KiB of contiguous codes.
+constexpr int kStageBytes = kRows * (kC + kR);
+constexpr int kStagePeOff = kRows * kC;
+constexpr int kCopies8 = kStageBytes / 1024;        // 36 at 64-token tiles
+
+__device__ __forceinline__ void mla_copy_one8(uint8_t* stage, const buf_rsrc_t& rc, const buf_rsrc_t& rp, int i,
+                                              int lane) {
+  if (i < kStagePeOff / 1024)
+    load_lds16<ATTN_MLA_COPY_AUX>(rc, uint32_t(1024 * i + 16 * lane), stage + 1024 * i);
+  else
+    load_lds16<ATTN_MLA_COPY_AUX>(rp, uint32_t(1024 * (i - kStagePeOff / 1024) + 16 * lane), stage + 1024 * i);
+}
 
 // One tile copy: tokens t_tile .. t_tile + kRows - 1 of sequence b. Copy instruction i < kRows moves latent row
 // i (1024 contiguous bytes), the others 8 rope rows each (1024 contiguous bytes). Tokens at or past t_end come from
@@ -86,6 +103,16 @@ __device__ __forceinline__ MlaCopy mla_copy_setup(const MlaArgs& a, int b, int t
   cp.rc = make_buf_rsrc(a.c_kv + tok0 * kC, uint32_t(cp.rows * kC * 2));
   cp.rp = make_buf_rsrc(a.k_pe + tok0 * kR, uint32_t(cp.rows * kR * 2));
   return cp;
+}
+
+// 8-bit resources over the codes of tokens t_tile .. min(t_tile + kRows, t_end) - 1 of sequence b (a tile past the
+// end gets empty resources: its copies read zeros).
+__device__ __forceinline__ void mla_rsrc8(const MlaArgs& a, int b, int t_tile, int t_end, buf_rsrc_t& rc,
+                                          buf_rsrc_t& rp) {
+  const int rows = max(0, min(kRows, t_end - t_tile));
+  const int64_t tok0 = int64_t(b) * a.max_len + min(t_tile, max(t_end - 1, 0));
+  rc = make_buf_rsrc(reinterpret_cast<const uint8_t*>(a.c_kv) + tok0 * kC, uint32_t(rows * kC));
+  rp = make_buf_rsrc(reinterpret_cast<const uint8_t*>(a.k_pe) + tok0 * kR, uint32_t(rows * kR));
 }
 
 // Sparse form. The token list of a tile (64 entries) is staged in LDS by one 4-byte-per-lane load-to-LDS; slot
@@ -152,13 +179,18 @@ constexpr int kPipe = ATTN_MLA_PIPE;
 // NW waves per workgroup (16 heads each). Each wave issues kCopies / NW copy instructions per tile, spread over
 // its score MFMAs (one every NW), so the copy of tile t+1 overlaps tile t's work instead of stalling every wave
 // on a burst of vector-memory issues right after the barrier.
-template <int NW, bool SPARSE>
+template <int NW, bool SPARSE, int KV = kKvBf16>
 __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
+  static_assert(!(SPARSE && KV != kKvBf16), "the sparse form reads a bf16 cache");
   // LDS fragments in flight (the sparse form keeps two: its token-list handling needs the registers)
   constexpr int kP = SPARSE ? 2 : kPipe;
   static_assert(kCopies % NW == 0, "copy instructions must split evenly over the waves");
   constexpr int NC = kCopies / NW;
-  __shared__ __attribute__((aligned(16))) char lds[2][kTileBytes];
+  // bf16 tiles: two (double-buffered copies) for a bf16 cache; one for an 8-bit cache, whose copies go to the two
+  // staging buffers instead
+  __shared__ __attribute__((aligned(16))) char lds[KV ? 1 : 2][kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t stage[KV ? 2 : 1][KV ? kStageBytes : 16];
+  constexpr int NC8 = (kCopies8 + NW - 1) / NW;      // 8-bit copy instructions per wave per tile
   __shared__ int32_t lds_idx[SPARSE ? 4 : 1][64];     // sparse: token lists of tiles t .. t+3 (slot t & 3)
   const int split = blockIdx.x, b = blockIdx.y;
   // Wave index in a scalar register, with its range [0, NW) visible to the compiler (resolves at compile time
@@ -183,6 +215,15 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
     const uint16_t* p = d < kC ? a.q_lat + (int64_t(b) * a.heads + h) * kC + d
                                : a.q_pe + (int64_t(b) * a.heads + h) * kR + (d - kC);
     qop[ks] = as_bf16x8(*reinterpret_cast<const u32x4_t*>(p));
+    if constexpr (KV != kKvBf16) {
+      // a key channel's scale folds into the query: q . (code * s) = (q * s) . code (one bf16 rounding)
+      const float* sc = d < kC ? a.c_scale + d : a.pe_scale + (d - kC);
+      const u32x4_t w = __builtin_bit_cast(u32x4_t, qop[ks]);
+      const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(sc), s1 = *reinterpret_cast<const f32x4_t*>(sc + 4);
+      qop[ks] = pack_bf16x8(bf16lo_to_f32(w[0]) * s0[0], bf16hi_to_f32(w[0]) * s0[1], bf16lo_to_f32(w[1]) * s0[2],
+                            bf16hi_to_f32(w[1]) * s0[3], bf16lo_to_f32(w[2]) * s1[0], bf16hi_to_f32(w[2]) * s1[1],
+                            bf16lo_to_f32(w[3]) * s1[2], bf16hi_to_f32(w[3]) * s1[3]);
+    }
   }
   // O^T: 32 blocks of 16 latent dims; lane holds head n, dims 16*db + 4*g4 + r
   f32x4_t oacc[kC / 16];
@@ -222,6 +263,12 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
       for (int k = 0; k < NC; ++k)
         mla_copy_one_sparse(lds[0], cps, wave + k * NW, lane, lds_idx[0], L, t_end - t_begin, oob);
     }
+  } else if constexpr (KV != kKvBf16) {
+    buf_rsrc_t rc, rp;
+    mla_rsrc8(a, b, t_begin, t_end, rc, rp);
+#pragma unroll
+    for (int k = 0; k < NC8; ++k)
+      if (wave + k * NW < kCopies8) mla_copy_one8(stage[0], rc, rp, wave + k * NW, lane);
   } else {
     const MlaCopy cp0 = mla_copy_setup(a, b, t_begin, t_end);
 #pragma unroll
@@ -238,8 +285,34 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
       stage_idx(t + 2);                                // lands with this iteration's copies
     }
     const MlaCopy cpn = SPARSE ? cps : mla_copy_setup(a, b, t_begin + (t + 1) * kRows, t_end);
-    char* nbuf = lds[(t + 1) & 1];
-    const uint16_t* T = reinterpret_cast<const uint16_t*>(lds[t & 1]);
+    char* nbuf = lds[(t + 1) & 1 & (KV ? 0 : 1)];
+    const uint16_t* T = reinterpret_cast<const uint16_t*>(lds[t & 1 & (KV ? 0 : 1)]);
+    buf_rsrc_t rc8, rp8;                               // 8-bit: resources of tile t+1
+    if constexpr (KV != kKvBf16) {
+      mla_rsrc8(a, b, t_begin + (t + 1) * kRows, t_end, rc8, rp8);
+      // widen staged tile t into the bf16 tile: 8 codes per chunk, 9 chunks per thread (latent rows at the
+      // padded stride, rope rows with their XOR key)
+      const uint8_t* st = stage[t & 1];
+      char* tile = lds[0];
+#pragma unroll
+      for (int u = 0; u < (kStageBytes / 8) / (64 * NW) + 1; ++u) {
+        const int q = threadIdx.x + u * 64 * NW;
+        if (q >= kStageBytes / 8) break;
+        const u32x2_t w = *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>(
+            (const __attribute__((address_space(3))) uint8_t*)st + 8 * q);
+        uint32_t off;
+        if (q < kStagePeOff / 8) {
+          const int r = q / (kC / 8), c8 = q % (kC / 8);
+          off = uint32_t(r * kCkvStride + 16 * c8);
+        } else {
+          const int qq = q - kStagePeOff / 8, r = qq / (kR / 8), c8 = qq % (kR / 8);
+          off = uint32_t(kPeOff + r * kR * 2 + 16 * (c8 ^ ((r >> 1) & 7)));
+        }
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>((__attribute__((address_space(3))) char*)tile +
+                                                                      off) = codes_to_bf16x8<KV>(w[0], w[1]);
+      }
+      __syncthreads();                                 // bf16 tile t ready; stage (t+1)&1 free for the next copy
+    }
     const int tok0 = t_begin + t * kRows;
 
     // S^T = Kc Q^T: 16-token blocks tb; lane holds head n, tokens 16*tb + 4*g4 + r. The K fragments are
@@ -266,11 +339,14 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
       sacc[j % TB] = mfma16x16x32(cur, qop[j / TB], sacc[j % TB]);
       MLA_SGB(0x008, 1);
       if (j + kP < NQ) MLA_SGB(0x100, 1);
-      if (j % NW == 0 && j / NW < NC) {                // next tile's copy, one instruction every NW MFMAs
+      if (j % NW == 0 && j / NW < (KV ? NC8 : NC)) {   // next tile's copy, one instruction every NW MFMAs
         if constexpr (SPARSE) {
           if (t + 1 < ntiles)
             mla_copy_one_sparse(nbuf, cpn, wave + (j / NW) * NW, lane, lds_idx[(t + 1) & 3], L,
                                 t_end - t_begin - (t + 1) * kRows, oob);
+        } else if constexpr (KV != kKvBf16) {
+          if (t + 1 < ntiles && wave + (j / NW) * NW < kCopies8)
+            mla_copy_one8(stage[(t + 1) & 1], rc8, rp8, wave + (j / NW) * NW, lane);
         } else {
           mla_copy_one(nbuf, cpn, wave + (j / NW) * NW, lane);
         }
@@ -357,7 +433,8 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
   float* wo = a.ws_o + slot * kC + 4 * g4;
 #pragma unroll
   for (int db = 0; db < kC / 16; ++db) {
-    const f32x4_t v = {oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv};
+    f32x4_t v = {oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv};
+    if constexpr (KV != kKvBf16) v *= *reinterpret_cast<const f32x4_t*>(a.c_scale + 16 * db + 4 * g4);   // code * s
     *reinterpret_cast<f32x4_t*>(wo + 16 * db) = v;
   }
   if (g4 == 0) a.ws_lse[slot] = (SPARSE && lt == 0.f) ? -INFINITY : m * a.scale + logf(lt);
@@ -463,6 +540,44 @@ hipError_t launch_mla_decode(const void* q_latent, const void* q_pe, const void*
       case 4: mla_split_kernel<4, false><<<grid, block, 0, stream>>>(a); break;
       case 6: mla_split_kernel<6, false><<<grid, block, 0, stream>>>(a); break;
       default: mla_split_kernel<8, false><<<grid, block, 0, stream>>>(a); break;
+    }
+  }
+  mla_combine_kernel<<<dim3(unsigned(n_heads), unsigned(batch)), dim3(kC / 2), 0, stream>>>(
+      a.ws_o, a.ws_lse, seq_lens, static_cast<uint16_t*>(o_latent), lse, n_heads, a.n_split, a.split_len,
+      max_seqlen_kv, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_decode_q8(const void* q_latent, const void* q_pe, const void* c_kv, const void* k_pe,
+                                const float* c_scale, const float* pe_scale, int kind, const int32_t* seq_lens,
+                                void* o_latent, float* lse, int batch, int n_heads, int max_seqlen_kv, float scale,
+                                void* workspace, hipStream_t stream) {
+  MlaArgs a = {};
+  a.q_lat = static_cast<const uint16_t*>(q_latent);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.c_kv = static_cast<const uint16_t*>(c_kv);        // 8-bit codes, read as bytes
+  a.k_pe = static_cast<const uint16_t*>(k_pe);
+  a.c_scale = c_scale; a.pe_scale = pe_scale;
+  a.seq_lens = seq_lens;
+  a.heads = n_heads; a.max_len = max_seqlen_kv; a.scale = scale;
+  a.n_split = mla_num_splits(batch, n_heads, max_seqlen_kv, kTargetBlocks);
+  a.split_len = mla_split_len(batch, n_heads, max_seqlen_kv, kTargetBlocks);
+  const size_t slots = size_t(batch) * size_t(n_heads) * size_t(a.n_split);
+  const size_t o_bytes = (slots * kC * sizeof(float) + 255) & ~size_t(255);
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes);
+  if (max_seqlen_kv > 0) {
+    const dim3 grid(unsigned(a.n_split), unsigned(batch)), block(64 * (n_heads / kHeadsPerWave));
+    const bool fp8 = kind == kKvFp8;
+    switch (n_heads / kHeadsPerWave) {
+      case 2: fp8 ? mla_split_kernel<2, false, kKvFp8><<<grid, block, 0, stream>>>(a)
+                  : mla_split_kernel<2, false, kKvInt8><<<grid, block, 0, stream>>>(a); break;
+      case 4: fp8 ? mla_split_kernel<4, false, kKvFp8><<<grid, block, 0, stream>>>(a)
+                  : mla_split_kernel<4, false, kKvInt8><<<grid, block, 0, stream>>>(a); break;
+      case 6: fp8 ? mla_split_kernel<6, false, kKvFp8><<<grid, block, 0, stream>>>(a)
+                  : mla_split_kernel<6, false, kKvInt8><<<grid, block, 0, stream>>>(a); break;
+      default: fp8 ? mla_split_kernel<8, false, kKvFp8><<<grid, block, 0, stream>>>(a)
+                   : mla_split_kernel<8, false, kKvInt8><<<grid, block, 0, stream>>>(a); break;
     }
   }
   mla_combine_kernel<<<dim3(unsigned(n_heads), unsigned(batch)), dim3(kC / 2), 0, stream>>>(
