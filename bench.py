@@ -207,19 +207,26 @@ def bench_decode(torch, ta, w, steps, warmup, seed=0, kv="bf16"):
     return ms, nbytes, int(inp["seq_lens"].sum())
 
 
-def mla_bytes(w):
-    return (w.batch * w.seqlen * (w.latent + w.rope) * 2 + w.batch * w.heads * (w.latent + w.rope) * 2
-            + w.batch * w.heads * w.latent * 2 + w.batch * 4)
+def mla_bytes(w, elem=2):
+    """Algorithmic bytes of one MLA decode: every cached latent and rope element once (2 bytes, or 1 for an 8-bit
+    cache plus its per-channel scales), the queries, the output and the lengths."""
+    scales = (w.latent + w.rope) * 4 if elem == 1 else 0
+    return (w.batch * w.seqlen * (w.latent + w.rope) * elem + w.batch * w.heads * (w.latent + w.rope) * 2
+            + w.batch * w.heads * w.latent * 2 + w.batch * 4 + scales)
 
 
 def mla_flops(w):
     return w.batch * w.heads * w.seqlen * (2 * (w.latent + w.rope) + 2 * w.latent)
 
 
-def bench_mla(torch, ta, w, steps, warmup, seed=0):
-    log(f"[bench] {w.name}: generating inputs")
-    inp = mla_inputs(w, seed=seed)
-    ql, qp, ckv, kpe = (dev_bf16(torch, inp[n]) for n in ("q_lat", "q_pe", "c_kv", "k_pe"))
+def bench_mla(torch, ta, w, steps, warmup, seed=0, kv="bf16"):
+    log(f"[bench] {w.name} ({kv} cache): generating inputs")
+    inp = mla_inputs(w, seed=seed, kv=kv)
+    ql, qp = (dev_bf16(torch, inp[n]) for n in ("q_lat", "q_pe"))
+    if kv == "bf16":
+        ckv, kpe = (dev_bf16(torch, inp[n]) for n in ("c_kv", "k_pe"))
+    else:
+        ckv, kpe, cs, ps = (torch.from_numpy(inp[n]).cuda() for n in ("c_kv", "k_pe", "c_scale", "pe_scale"))
     lens = torch.from_numpy(inp["seq_lens"]).cuda()
     o = torch.empty_like(ql)
     ws = torch.empty(ta.attn_mla_decode_workspace_size(w.batch, w.heads, w.latent, w.seqlen), dtype=torch.uint8,
@@ -228,7 +235,10 @@ def bench_mla(torch, ta, w, steps, warmup, seed=0):
     for i in range(warmup + steps):
         if i >= warmup:
             timer.start()
-        ta.attn_mla_decode(ql, qp, ckv, kpe, lens, w.scale, o=o, workspace=ws)
+        if kv == "bf16":
+            ta.attn_mla_decode(ql, qp, ckv, kpe, lens, w.scale, o=o, workspace=ws)
+        else:
+            ta.attn_mla_decode_q8(ql, qp, ckv, kpe, cs, ps, kv, lens, w.scale, o=o, workspace=ws)
         if i >= warmup:
             timer.stop()
     torch.cuda.synchronize()
@@ -363,7 +373,7 @@ def main():
     # Warm-up long enough (about 0.1 s of work) for the GPU clock to settle before the timed steps.
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-secondary", action="store_true", help="only the primary prefill workload")
-    ap.add_argument("--workloads", default="prefill,decode,mla,long,chunked,dsa,decode_fp8,decode_int8,swa",
+    ap.add_argument("--workloads", default="prefill,decode,mla,long,chunked,dsa,decode_fp8,decode_int8,swa,mla_fp8,mla_int8",
                     help="comma list of prefill (primary), decode, mla, long, chunked, dsa, decode_fp8, decode_int8, "
                          "swa; profiling runs select one")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -392,7 +402,8 @@ def main():
         return
 
     sel = set(args.workloads.split(","))
-    if sel - {"prefill", "decode", "mla", "long", "chunked", "dsa", "decode_fp8", "decode_int8", "swa"}:
+    if sel - {"prefill", "decode", "mla", "long", "chunked", "dsa", "decode_fp8", "decode_int8", "swa", "mla_fp8",
+              "mla_int8"}:
         print(f"unknown workloads {sel}", file=sys.stderr)
         sys.exit(2)
     if args.no_secondary:
@@ -450,6 +461,17 @@ def run_secondary(torch, ta, args, sel, line):
                               "tflops": round(mla_flops(wm) / (ms * 1e-3) / 1e12, 1),
                               "roofline": roofline_hbm(nbytes, ms, "mla_split_kernel", wm.name,
                                                        "mla_split_kernel + mla_combine_kernel")}
+    for kv in ("fp8", "int8"):
+        if f"mla_{kv}" in sel:
+            wm = WORKLOADS["mla_decode_b32"]
+            ms = bench_mla(torch, ta, wm, max(20, args.steps), max(300, args.warmup), kv=kv)
+            nbytes = mla_bytes(wm, elem=1)
+            line[f"mla_decode_{kv}"] = {
+                "workload": f"{wm.name} ({kv} latent cache)", "value": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                "unit": "GB/s", "ms": round(ms, 4), "bytes": nbytes,
+                "tflops": round(mla_flops(wm) / (ms * 1e-3) / 1e12, 1),
+                "roofline": roofline_hbm(nbytes, ms, "mla_split_kernel", f"{wm.name}_{kv}",
+                                         "mla_split_kernel + mla_combine_kernel")}
     if "long" in sel:
         wl = WORKLOADS["gqa_prefill_s131072"]
         wall_l, kern_l = bench_prefill(torch, ta, wl, 2, 1)

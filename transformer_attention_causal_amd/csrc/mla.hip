@@ -79,12 +79,17 @@ constexpr int kStageBytes = kRows * (kC + kR);
 constexpr int kStagePeOff = kRows * kC;
 constexpr int kCopies8 = kStageBytes / 1024;        // 36 at 64-token tiles
 
+// The per-lane offset is formed at the copy (opaque to the compiler): precomputed for every copy of a tile it would
+// hold one register per instruction across the loop. Offsets stay in the range-checked voffset, so rows past the
+// resource read zeros.
 __device__ __forceinline__ void mla_copy_one8(uint8_t* stage, const buf_rsrc_t& rc, const buf_rsrc_t& rp, int i,
                                               int lane) {
+  uint32_t vo = uint32_t(16 * lane);
+  asm volatile("" : "+v"(vo));
   if (i < kStagePeOff / 1024)
-    load_lds16<ATTN_MLA_COPY_AUX>(rc, uint32_t(1024 * i + 16 * lane), stage + 1024 * i);
+    load_lds16<ATTN_MLA_COPY_AUX>(rc, vo + uint32_t(1024 * i), stage + 1024 * i);
   else
-    load_lds16<ATTN_MLA_COPY_AUX>(rp, uint32_t(1024 * (i - kStagePeOff / 1024) + 16 * lane), stage + 1024 * i);
+    load_lds16<ATTN_MLA_COPY_AUX>(rp, vo + uint32_t(1024 * (i - kStagePeOff / 1024)), stage + 1024 * i);
 }
 
 // One tile copy: tokens t_tile .. t_tile + kRows - 1 of sequence b. Copy instruction i < kRows moves latent row
@@ -180,7 +185,7 @@ constexpr int kPipe = ATTN_MLA_PIPE;
 // its score MFMAs (one every NW), so the copy of tile t+1 overlaps tile t's work instead of stalling every wave
 // on a burst of vector-memory issues right after the barrier.
 template <int NW, bool SPARSE, int KV = kKvBf16>
-__global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
+__global__ __launch_bounds__(64 * NW) void mla_split_kernel(MlaArgs a) {
   static_assert(!(SPARSE && KV != kKvBf16), "the sparse form reads a bf16 cache");
   // LDS fragments in flight (the sparse form keeps two: its token-list handling needs the registers)
   constexpr int kP = SPARSE ? 2 : kPipe;
@@ -290,27 +295,28 @@ __global__ __launch_bounds__(512) void mla_split_kernel(MlaArgs a) {
     buf_rsrc_t rc8, rp8;                               // 8-bit: resources of tile t+1
     if constexpr (KV != kKvBf16) {
       mla_rsrc8(a, b, t_begin + (t + 1) * kRows, t_end, rc8, rp8);
-      // widen staged tile t into the bf16 tile: 8 codes per chunk, 9 chunks per thread (latent rows at the
-      // padded stride, rope rows with their XOR key)
+      // widen staged tile t into the bf16 tile, 8 codes (one 8-byte chunk) at a time. Thread tid takes latent
+      // chunks tid + 64*NW*u: row tid/64 + NW*u, chunk tid%64 (the padded row stride), and rope chunks likewise
+      // (row tid/8 + 8*NW*u, chunk tid%8, whose XOR key ((row >> 1) & 7) does not depend on u), so every address
+      // is a per-thread base plus an immediate.
       const uint8_t* st = stage[t & 1];
       char* tile = lds[0];
-#pragma unroll
-      for (int u = 0; u < (kStageBytes / 8) / (64 * NW) + 1; ++u) {
-        const int q = threadIdx.x + u * 64 * NW;
-        if (q >= kStageBytes / 8) break;
+      const int tid = threadIdx.x;
+      auto widen8 = [&](uint32_t rd, uint32_t wr) {
         const u32x2_t w = *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>(
-            (const __attribute__((address_space(3))) uint8_t*)st + 8 * q);
-        uint32_t off;
-        if (q < kStagePeOff / 8) {
-          const int r = q / (kC / 8), c8 = q % (kC / 8);
-          off = uint32_t(r * kCkvStride + 16 * c8);
-        } else {
-          const int qq = q - kStagePeOff / 8, r = qq / (kR / 8), c8 = qq % (kR / 8);
-          off = uint32_t(kPeOff + r * kR * 2 + 16 * (c8 ^ ((r >> 1) & 7)));
-        }
+            (const __attribute__((address_space(3))) uint8_t*)st + rd);
         *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>((__attribute__((address_space(3))) char*)tile +
-                                                                      off) = codes_to_bf16x8<KV>(w[0], w[1]);
-      }
+                                                                      wr) = codes_to_bf16x8<KV>(w[0], w[1]);
+      };
+      const uint32_t rd_c = uint32_t(8 * tid), wr_c = uint32_t((tid / 64) * kCkvStride + 16 * (tid % 64));
+#pragma unroll 4
+      for (int u = 0; u < (kStagePeOff / 8 + 64 * NW - 1) / (64 * NW); ++u)
+        if (tid + 64 * NW * u < kStagePeOff / 8) widen8(rd_c + 512 * NW * u, wr_c + NW * kCkvStride * u);
+      const uint32_t rd_p = uint32_t(kStagePeOff + 8 * tid);
+      const uint32_t wr_p = uint32_t(kPeOff + (tid / 8) * kR * 2 + 16 * ((tid % 8) ^ ((tid / 16) & 7)));
+#pragma unroll
+      for (int u = 0; u < (kRows * kR / 8 + 64 * NW - 1) / (64 * NW); ++u)
+        if (tid + 64 * NW * u < kRows * kR / 8) widen8(rd_p + 512 * NW * u, wr_p + 8 * NW * kR * 2 * u);
       __syncthreads();                                 // bf16 tile t ready; stage (t+1)&1 free for the next copy
     }
     const int tok0 = t_begin + t * kRows;
