@@ -19,6 +19,9 @@
 //   * Pages are looked up once per 16 keys (page size is a power of two >= 16, so 16 aligned keys share a page).
 //   * Partial (O / l, lse) per chunk goes to the workspace; the combine kernel merges a sequence's chunks.
 // Split boundaries are logical key positions, so the result does not depend on physical page placement.
+// The default build stages K and V blocks through LDS with whole-row copies (the LDS-staged kernel below for bf16
+// caches, the ATTN_DECODE_LDS8 path for 8-bit ones) and reads the same operand layouts from there; loading the
+// operands straight into registers, as described above, is the measured-slower alternative kept for comparison.
 //
 // 8-bit caches ("7 anti-patterns of DeepSeek attention optimisation", lpnh.cn, section 3.3: FP8 E4M3, largest
 // value 448; "DeepSeek 32K to 256K long context", tqpw.cn, section 2.5: int8 K/V with per-channel scales): the

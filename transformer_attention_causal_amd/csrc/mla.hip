@@ -10,8 +10,9 @@
 // a single-KV-head attention with 128 query rows: the same structure as the prefill kernel with heads in place
 // of query positions.
 //   * One workgroup = (token split, sequence), 8 waves x 16 heads. Token tiles of 64 rows x 576 are copied
-//     straight into LDS (global_load_lds, 16 bytes per lane), double-buffered, one barrier per tile; rows are
-//     unpadded and their 16-byte chunks XOR-swizzled by (row & 7) so both read patterns are conflict-free.
+//     straight into LDS (buffer loads with the LDS bit, non-temporal, one latent row or eight rope rows per
+//     instruction, spread over the score MFMAs), double-buffered, one barrier per tile. Latent rows are padded
+//     to 1056 bytes and rope rows XOR-swizzled (layout below), so both read patterns are conflict-free.
 //   * S^T = Kc Q^T on v_mfma_f32_16x16x32_bf16 (K fragments from LDS, the 576-wide query of the wave's 16 heads
 //     resident in registers). Each lane then holds one head, so the online-softmax statistics and the output
 //     rescale are per-lane scalars plus two exchanges across the four 16-lane groups.
@@ -22,7 +23,12 @@
 //     part): the same kernel over a list of token indices per sequence. The splits cut the list; each copy
 //     instruction of a latent row takes its token from the list (a lane read of the tile's index vector into the
 //     scalar offset), the rope rows take theirs per lane; list entries outside [0, L) are masked like the tail.
-// HBM-bound in principle (about 240 flop per byte) but close to the MFMA ridge, so both matter.
+//   * 8-bit latent cache (FP8 E4M3 or int8 codes with per-channel scales; DeepSeek 32K to 256K long context,
+//     tqpw.cn, section 2.5; 7 anti-patterns of DeepSeek attention optimisation, lpnh.cn, section 3.3): codes are
+//     staged in LDS, widened exactly into the bf16 tile by all waves between two barriers, and the product code
+//     above runs unchanged; key scales fold into the query, value scales multiply the output channels.
+// HBM-bound in principle (about 240 flop per byte) but close to the MFMA ridge, so both matter; measured, the
+// LDS fragment reads (three in flight per wave) are what bound it.
 #include "device.h"
 #include "kernels.h"
 

@@ -23,6 +23,9 @@
 //     ds_read_b64_tr_b16 from the row-major V tile. P never leaves registers.
 //   * exp is exp2 with scale*log2(e) folded into one FMA. Tiles fully above the diagonal are skipped; only tiles
 //     that cross the diagonal or the ragged end are masked. Heaviest query blocks are launched first.
+//   * Optionally Q is rotated as it is loaded (RoPE fused into the prefill, from a cos/sin table by position), so
+//     the separate rotation pass over Q disappears; keys are rotated beforehand, since every workgroup of a KV
+//     head reads them.
 // fp32 path (correctness workload, head_dim 64/128): plain VALU, K/V tiles of 32 keys in LDS, fp32 throughout.
 #include <type_traits>
 

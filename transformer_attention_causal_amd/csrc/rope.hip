@@ -9,6 +9,8 @@
 // cos in fp64 (full range reduction), rounded to fp32. Every head of a token reuses the same table row, so the
 // fp64 work is d/2 angles per token, not per element. The rotation itself is fp32 FMA on 16-byte vectors,
 // rounded back to the storage type (bf16: nearest even). HBM-bound: one read and one write of x.
+// rope_table_kernel writes the same cos/sin values for every position of a range, for the prefill kernel's fused
+// rotation of Q.
 #include "device.h"
 #include "kernels.h"
 
