@@ -25,6 +25,7 @@ head): a reported baseline, not a target.
 """
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -56,11 +57,15 @@ def log(*a):
 
 
 def source_digest(fname):
+    """Digest of a kernel source and device.h with comments and blank space removed: the counters stay valid for
+    an edit that only touches comments, and any change to the code itself invalidates them."""
     p = os.path.join(ROOT, "transformer_attention_causal_amd", "csrc", fname)
     h = hashlib.sha256()
     for f in (p, os.path.join(ROOT, "transformer_attention_causal_amd", "csrc", "device.h")):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update(re.sub(r"\s+", " ", text).strip().encode())
     return h.hexdigest()[:16]
 
 
