@@ -121,8 +121,8 @@ int attn_rope_table(void* table, int n_positions, int head_dim, double theta, vo
  *   interleaved  pairing as attn_rope_apply (1: (2i, 2i+1); 0: (i, i + head_dim/2)).
  * The output equals attn_rope_apply(q) followed by attn_prefill bit for bit (same table values, same fp32
  * rotation arithmetic, same rounding); q itself is left unrotated.
- * Supported: head_dim 64 or 128 (else UNSUPPORTED). INVALID_ARG: as attn_prefill, plus NULL or misaligned
- * rope_table or rope_table_len <= 0 (with batch*seqlen > 0). */
+ * Supported: head_dim 64 or 128, and a table under 4 GiB (else UNSUPPORTED). INVALID_ARG: as attn_prefill, plus
+ * NULL or misaligned rope_table or rope_table_len <= 0 (with batch*seqlen > 0). */
 int attn_prefill_rope(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int seqlen,
                       int n_heads_q, int n_heads_kv, int head_dim, int causal, float softmax_scale,
                       const int32_t* q_positions, const void* rope_table, int rope_table_len, int interleaved,

@@ -78,6 +78,7 @@ ATTN_EXPORT int attn_prefill_rope(const void* q, const void* k, const void* v, v
   if (int64_t(batch) * seqlen == 0) return ATTN_OK;
   if (!q || !k || !v || !o || !rope_table || rope_table_len <= 0) return ATTN_ERR_INVALID_ARG;
   if (reinterpret_cast<uintptr_t>(rope_table) % 16 != 0) return ATTN_ERR_INVALID_ARG;
+  if (int64_t(rope_table_len) * head_dim * 4 >= (int64_t(1) << 32)) return ATTN_ERR_UNSUPPORTED;   // 32-bit offsets
   return hip_status(attn::launch_prefill_bf16(q, k, v, o, lse, batch, seqlen, n_heads_q, n_heads_kv, head_dim,
                                               causal ? 1 : 0, softmax_scale, static_cast<hipStream_t>(stream),
                                               rope_table, rope_table_len, q_positions, interleaved ? 1 : 0));
