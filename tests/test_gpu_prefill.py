@@ -59,6 +59,11 @@ SMALL = [  # (batch, seqlen, hq, hkv, head_dim, causal)
     (1, 1, 8, 2, 128, True),       # a single token
     (1, 64, 4, 1, 64, True),       # exactly one tile
     (1, 513, 4, 4, 128, False),    # MHA, full attention, ragged
+    # more workgroups than the device holds at once (256 compute units, one each): two or three rounds
+    (3, 2000, 32, 8, 128, True),   # 504 units
+    (4, 1600, 32, 8, 64, True),    # 544 units, head_dim 64
+    (1, 2000, 80, 80, 64, True),   # positions mode, 480 units over 80 head groups
+    (3, 1200, 32, 8, 128, False),  # no causal mask, 312 units
 ]
 
 
