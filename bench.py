@@ -262,14 +262,16 @@ def bench_chunked(torch, ta, w, steps, warmup, seed=0):
     table, cu, ctx, pos = (torch.from_numpy(inp[n]).cuda() for n in ("block_table", "cu_new", "ctx_lens",
                                                                      "positions"))
     o = torch.empty_like(q)
+    n_pos = int(inp["positions"].max()) + 1
+    rope_tab = torch.empty((n_pos, q.shape[-1] // 2, 2), dtype=torch.float32, device="cuda")
     timer = EventTimer(torch)
 
     def step(timed):
+        ta.attn_rope_table(n_pos, q.shape[-1], w.theta, table=rope_tab)
         ta.attn_kv_append_paged(kn, vn, cu, ctx, kc, vc, table, w.theta)
-        ta.attn_rope_apply(q, pos, w.theta)
         if timed:
             timer.start()
-        ta.attn_prefill_paged(q, kc, vc, table, cu, ctx, inp["max_new"], softmax_scale=w.scale, o=o)
+        ta.attn_prefill_paged_rope(q, kc, vc, table, cu, ctx, inp["max_new"], rope_tab, softmax_scale=w.scale, o=o)
         if timed:
             timer.stop()
 
@@ -283,7 +285,7 @@ def bench_chunked(torch, ta, w, steps, warmup, seed=0):
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     kern_ms = timer.mean_ms()
-    del q, kn, vn, kc, vc, o
+    del q, kn, vn, kc, vc, o, rope_tab
     torch.cuda.empty_cache()
     return wall_ms, kern_ms
 
@@ -514,7 +516,7 @@ def run_secondary(torch, ta, args, sel, line):
         line["chunked_prefill"] = {"workload": wc.name, "value": round(wc.flops / (wall_c * 1e-3) / 1e12, 2),
                                    "unit": "TFLOP/s", "ms_per_step": round(wall_c, 4),
                                    "ctx_lens": list(wc.ctx_lens), "new_lens": list(wc.new_lens),
-                                   "step": "kv_append_paged (rope k) + rope(q) + prefill_paged",
+                                   "step": "rope_table + kv_append_paged (rope k) + prefill_paged_rope (rope(q) fused)",
                                    "roofline": roofline_compute(wc.flops, kern_c, "prefill_bf16_kernel", wc.name)}
     if "swa" in sel:
         wsw = WORKLOADS["swa_prefill_s131072"]

@@ -12,6 +12,7 @@
  *   attn_mla_decode_q8    the same over an 8-bit (FP8 E4M3 or int8) latent cache with per-channel scales
  *   attn_kv_append_paged  write new tokens' keys (rotated) and values into a paged KV cache
  *   attn_prefill_paged    chunked / variable-length causal prefill of new tokens against a paged KV cache
+ *   attn_prefill_paged_rope  the same with RoPE of the queries fused into their load
  *   attn_dsa_indexer      DeepSeek Sparse Attention: lightning-indexer relevance score of every cached token
  *   attn_topk             the indices of the top-k scores of each sequence
  *   attn_mla_sparse_decode  absorbed MLA decode over a list of selected tokens per sequence
@@ -278,6 +279,24 @@ int attn_prefill_paged(const void* q, const void* k_cache, const void* v_cache, 
                        const int32_t* cu_new, const int32_t* cache_lens, void* o, float* lse, int batch, int total_new,
                        int max_new, int n_heads_q, int n_heads_kv, int head_dim, int page_size, int max_pages_per_seq,
                        int64_t num_pages, float softmax_scale, void* stream);
+
+/* attn_prefill_paged with q UNROTATED: each query is rotated as the kernel loads it, by the cos/sin of its position
+ * from a table made by attn_rope_table, so the separate rotation pass over q is not needed. (Long-context page,
+ * "DeepSeek 32K to 256K long context", tqpw.cn: section 2.1 for the rotation of pairs by position times frequency,
+ * section 2.5 for the cos/sin cache indexed by integer position.) The result equals attn_rope_apply of q at the same
+ * positions followed by attn_prefill_paged, bit for bit.
+ *   q_positions  NULL (query i of sequence b is at its absolute position cache_lens[b] + i) or [total_new] int32
+ *                device positions, one per row of q. A position outside [0, rope_table_len) is clamped into it.
+ *   rope_table   [rope_table_len, head_dim/2] (cos, sin) fp32 from attn_rope_table with this head_dim, 16-byte
+ *                aligned, rope_table_len * head_dim * 4 < 2^32.
+ *   interleaved  pairing as attn_rope_apply (1: (2i, 2i+1); 0: (i, i + head_dim/2)).
+ * Other arguments, layouts and errors as attn_prefill_paged; also ATTN_ERR_INVALID_ARG for a NULL or misaligned
+ * rope_table or rope_table_len <= 0 (with work to do). */
+int attn_prefill_paged_rope(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                            const int32_t* cu_new, const int32_t* cache_lens, void* o, float* lse, int batch,
+                            int total_new, int max_new, int n_heads_q, int n_heads_kv, int head_dim, int page_size,
+                            int max_pages_per_seq, int64_t num_pages, float softmax_scale, const int32_t* q_positions,
+                            const void* rope_table, int rope_table_len, int interleaved, void* stream);
 
 /* DeepSeek Sparse Attention, step 1: lightning-indexer scores for one query token per sequence.
  * (Attention notes, makinaruto.github.io, "Lighting Indexer": each earlier token s is scored by the sum over the

@@ -33,7 +33,8 @@ def test_header_declares_the_operations():
     names = declared_functions()
     for n in ("attn_rope_apply", "attn_prefill", "attn_decode_paged", "attn_mla_decode", "attn_kv_append_paged",
               "attn_prefill_paged", "attn_dsa_indexer", "attn_topk", "attn_mla_sparse_decode", "attn_decode_paged_q8",
-              "attn_prefill_local_global", "attn_rope_table", "attn_prefill_rope", "attn_mla_decode_q8"):
+              "attn_prefill_local_global", "attn_rope_table", "attn_prefill_rope", "attn_mla_decode_q8",
+              "attn_prefill_paged_rope"):
         assert n in names
 
 
@@ -123,6 +124,25 @@ def test_prefill_rope_validation(lib):
     assert call(args(tab=ctypes.c_void_p(0x1008))) == INVALID  # table must be 16-byte aligned
     assert call(args(d=96)) == UNSUPPORTED
     assert call(args(q=NULL, k=NULL, v=NULL, o=NULL, tab=NULL, b=0)) == OK
+
+
+def test_prefill_paged_rope_validation(lib):
+    f = lib.attn_prefill_paged_rope
+    args = lambda **kw: dict(dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cu=FAKE, cl=FAKE, o=FAKE, lse=NULL, b=2, tot=100,
+                                  mx=60, hq=8, hkv=2, d=128, page=64, mp=4, np_=8, scale=0.088, pos=NULL, tab=FAKE,
+                                  tlen=300, il=1), **kw)
+    call = lambda a: f(a["q"], a["kc"], a["vc"], a["bt"], a["cu"], a["cl"], a["o"], a["lse"], a["b"], a["tot"],
+                       a["mx"], a["hq"], a["hkv"], a["d"], a["page"], a["mp"], a["np_"], a["scale"], a["pos"],
+                       a["tab"], a["tlen"], a["il"], NULL)
+    assert call(args(hq=6, hkv=4)) == INVALID
+    assert call(args(mx=101)) == INVALID                       # max_new > total_new
+    assert call(args(bt=NULL)) == INVALID
+    assert call(args(tab=NULL)) == INVALID                     # table required
+    assert call(args(tlen=0)) == INVALID
+    assert call(args(tab=ctypes.c_void_p(0x1008))) == INVALID  # table must be 16-byte aligned
+    assert call(args(page=48)) == UNSUPPORTED
+    assert call(args(d=96)) == UNSUPPORTED
+    assert call(args(q=NULL, kc=NULL, vc=NULL, bt=NULL, cu=NULL, cl=NULL, o=NULL, tab=NULL, tot=0, mx=0)) == OK
 
 
 def test_decode_validation(lib):

@@ -248,3 +248,35 @@ def _one_row(q, k, v, w):
     vp = np.concatenate([v, np.zeros((pad,) + v.shape[1:])]).reshape(-1, w.page_size, *v.shape[1:])
     o, lse = oracle.prefill_paged(q[None], kp, vp, table, np.array([0, 1]), np.array([L - 1]), w.scale)
     return o[0], lse[:, 0]
+
+
+@pytest.mark.parametrize("interleaved", [True, False])
+@pytest.mark.parametrize("explicit_pos", [True, False])
+@pytest.mark.parametrize("ctx,new,hq,hkv,d", [((0, 4096, 8192, 14336), (2048,) * 4, 32, 8, 128),
+                                              ((3, 0, 190, 64), (100, 65, 1, 63), 32, 8, 128),
+                                              ((70, 500), (90, 150), 16, 16, 64)])
+def test_fused_rope_equals_rotate_then_attend(ctx, new, hq, hkv, d, interleaved, explicit_pos):
+    """attn_prefill_paged_rope on unrotated q gives attn_rope_apply(q) then attn_prefill_paged bit for bit, with
+    the default positions (cache_lens[b] + i) or the same positions passed explicitly; q itself is not rotated."""
+    ta = require_gpu()
+    w = WORKLOADS["chunked_prefill_b4"]
+    say(f"chunked fused rope ctx={ctx} new={new} hq={hq} hkv={hkv} d={d} interleaved={interleaved}")
+    inp = chunked_prefill_inputs(w, seed=50, ctx_lens=ctx, new_lens=new, hq=hq, hkv=hkv, head_dim=d)
+    kc, vc = dev_bf16(inp["k_cache"]), dev_bf16(inp["v_cache"])
+    table, cu, cl = dev(inp["block_table"]), dev(inp["cu_new"]), dev(inp["ctx_lens"])
+    ta.attn_kv_append_paged(dev_bf16(inp["k_new"]), dev_bf16(inp["v_new"]), cu, cl, kc, vc, table, w.theta,
+                            interleaved=interleaved)
+    pos = dev(inp["positions"])
+    q1 = dev_bf16(inp["q"])
+    ta.attn_rope_apply(q1, pos, w.theta, interleaved=interleaved)
+    o1, l1 = ta.attn_prefill_paged(q1, kc, vc, table, cu, cl, inp["max_new"], softmax_scale=w.scale,
+                                   return_lse=True)
+    rope_tab = ta.attn_rope_table(int(inp["positions"].max()) + 1, d, w.theta)
+    q2 = dev_bf16(inp["q"])
+    o2, l2 = ta.attn_prefill_paged_rope(q2, kc, vc, table, cu, cl, inp["max_new"], rope_tab,
+                                        q_positions=pos if explicit_pos else None, interleaved=interleaved,
+                                        softmax_scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(l1, l2)
+    assert np.array_equal(host_bf16(q2), inp["q"])

@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     attn_prefill,
     attn_prefill_local_global,
     attn_prefill_paged,
+    attn_prefill_paged_rope,
     attn_prefill_rope,
     attn_rope_apply,
     attn_rope_table,

@@ -35,6 +35,8 @@ SIGNATURES = {
     "attn_mla_decode_q8": (_I, [_P, _P, _P, _P, _P, _P, _I, _P, _P, _P, _I, _I, _I, _I, _I, _F, _P, _SZ, _P]),
     "attn_kv_append_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _D, _I, _P]),
     "attn_prefill_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I64, _F, _P]),
+    "attn_prefill_paged_rope": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I64, _F, _P,
+                                     _P, _I, _I, _P]),
     "attn_dsa_indexer": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _P]),
     "attn_topk": (_I, [_P, _P, _P, _I, _I, _I, _P]),
     "attn_mla_sparse_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
@@ -314,6 +316,33 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_new, cache_lens, max
         _dev(block_table, "block_table", torch.int32), _dev(cu_new, "cu_new", torch.int32),
         _dev(cache_lens, "cache_lens", torch.int32), _dev(o, "o", torch.bfloat16), lse_p, cu_new.numel() - 1, total,
         int(max_new), hq, hkv, d, page, block_table.shape[1], num_pages, scale, _stream(q, stream)))
+    return (o, lse) if return_lse else o
+
+
+def attn_prefill_paged_rope(q, k_cache, v_cache, block_table, cu_new, cache_lens, max_new, rope_table,
+                            q_positions=None, interleaved=True, softmax_scale=None, o=None, lse=None,
+                            return_lse=False, stream=None):
+    """attn_prefill_paged with q UNROTATED: each query is rotated as the kernel loads it, by the cos/sin of its
+    position (q_positions int32 [total_new], or cache_lens[b] + i when None) from rope_table [n_pos, D/2, 2] fp32."""
+    lib = load_library()
+    total, hq, d = q.shape
+    num_pages, page, hkv, _ = k_cache.shape
+    if rope_table.dim() != 3 or rope_table.shape[1:] != (d // 2, 2):
+        raise ValueError("rope_table must be [n_positions, head_dim/2, 2]")
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((hq, total), dtype=torch.float32, device=q.device)
+    lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
+    pos_p = _dev(q_positions, "q_positions", torch.int32) if q_positions is not None else None
+    _check("attn_prefill_paged_rope", lib.attn_prefill_paged_rope(
+        _dev(q, "q", torch.bfloat16), _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+        _dev(block_table, "block_table", torch.int32), _dev(cu_new, "cu_new", torch.int32),
+        _dev(cache_lens, "cache_lens", torch.int32), _dev(o, "o", torch.bfloat16), lse_p, cu_new.numel() - 1, total,
+        int(max_new), hq, hkv, d, page, block_table.shape[1], num_pages, scale, pos_p,
+        _dev(rope_table, "rope_table", torch.float32), rope_table.shape[0], 1 if interleaved else 0,
+        _stream(q, stream)))
     return (o, lse) if return_lse else o
 
 

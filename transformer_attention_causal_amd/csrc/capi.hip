@@ -240,6 +240,31 @@ ATTN_EXPORT int attn_prefill_paged(const void* q, const void* k_cache, const voi
                                                static_cast<hipStream_t>(stream)));
 }
 
+ATTN_EXPORT int attn_prefill_paged_rope(const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_table, const int32_t* cu_new, const int32_t* cache_lens,
+                                        void* o, float* lse, int batch, int total_new, int max_new, int n_heads_q,
+                                        int n_heads_kv, int head_dim, int page_size, int max_pages_per_seq,
+                                        int64_t num_pages, float softmax_scale, const int32_t* q_positions,
+                                        const void* rope_table, int rope_table_len, int interleaved, void* stream) {
+  if (batch < 0 || total_new < 0 || max_new < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (n_heads_q % n_heads_kv != 0 || !valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
+  if (page_size <= 0 || max_pages_per_seq < 0 || num_pages < 0 || max_new > total_new) return ATTN_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return ATTN_ERR_UNSUPPORTED;
+  if (!is_pow2(page_size) || page_size < 64) return ATTN_ERR_UNSUPPORTED;
+  if (batch == 0 || total_new == 0 || max_new == 0) return ATTN_OK;
+  if (!q || !k_cache || !v_cache || !block_table || !cu_new || !cache_lens || !o) return ATTN_ERR_INVALID_ARG;
+  if (max_pages_per_seq <= 0 || num_pages <= 0) return ATTN_ERR_INVALID_ARG;
+  if (!rope_table || rope_table_len <= 0) return ATTN_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(rope_table) % 16 != 0) return ATTN_ERR_INVALID_ARG;
+  if (int64_t(rope_table_len) * head_dim * 4 >= (int64_t(1) << 32)) return ATTN_ERR_UNSUPPORTED;   // 32-bit offsets
+  return hip_status(attn::launch_prefill_paged(q, k_cache, v_cache, block_table, cu_new, cache_lens, o, lse, batch,
+                                               total_new, max_new, n_heads_q, n_heads_kv, head_dim, page_size,
+                                               max_pages_per_seq, num_pages, softmax_scale,
+                                               static_cast<hipStream_t>(stream), rope_table, rope_table_len,
+                                               q_positions, interleaved ? 1 : 0));
+}
+
 ATTN_EXPORT int attn_dsa_indexer(const void* q_idx, const float* w_idx, const void* k_idx, const int32_t* seq_lens,
                                  float* scores, int batch, int n_heads_idx, int idx_dim, int max_seqlen_kv,
                                  void* stream) {

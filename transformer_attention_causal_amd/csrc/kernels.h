@@ -31,7 +31,9 @@ hipError_t launch_prefill_window(const void* q, const void* k, const void* v, vo
 hipError_t launch_prefill_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
                                 const int32_t* cu_new, const int32_t* ctx_lens, void* o, float* lse, int batch,
                                 int total_new, int max_new, int hq, int hkv, int head_dim, int page_size,
-                                int max_pages_per_seq, int64_t num_pages, float scale, hipStream_t stream);
+                                int max_pages_per_seq, int64_t num_pages, float scale, hipStream_t stream,
+                                const void* rope_table = nullptr, int rope_len = 0,
+                                const int32_t* q_positions = nullptr, int rope_interleaved = 0);
 // Append new K (rotated at its absolute positions) and V rows to a paged cache (bf16).
 hipError_t launch_kv_append_paged(const void* k_new, const void* v_new, const int32_t* cu_new,
                                   const int32_t* ctx_lens, void* k_cache, void* v_cache, const int32_t* block_table,

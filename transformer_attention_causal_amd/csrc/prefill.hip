@@ -387,8 +387,11 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
     }
   }
   RopeQ<D, QB> rq;
-  const bool rope = !PAGED && !WIN && a.rope_cs != nullptr;   // uniform; only the plain kernel takes the table
+  const bool rope = !WIN && a.rope_cs != nullptr;     // uniform; the local + global kernel takes no table
   if (rope) rq.load(a, qrow0, qpos0, koff, S, lq, lg);
+  // paged: rotated at once, so the table rows are dead before the tile loop's registers come alive (rotating after
+  // the first copy, as the plain kernel does, spills there)
+  if (PAGED && rope) rq.apply(qop, a.rope_inter);
 
   f32x16_t oacc[QB][DB];
   float m[QB], l[QB];
@@ -646,7 +649,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   int pg = page_load(0);
   copy_tile(0, 0, pg);
   pg = page_load(1);                                   // table entry of the next tile to copy
-  if (rope) rq.apply(qop, a.rope_inter);
+  if (!PAGED && rope) rq.apply(qop, a.rope_inter);
   // Two tiles per trip so each tile's LDS buffer is a compile-time constant.
   for (int t = 0; t < ntiles; t += 2) {
     wait_vmem();
@@ -804,9 +807,13 @@ hipError_t launch_prefill_window(const void* q, const void* k, const void* v, vo
 hipError_t launch_prefill_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
                                 const int32_t* cu_new, const int32_t* ctx_lens, void* o, float* lse, int batch,
                                 int total_new, int max_new, int hq, int hkv, int head_dim, int page_size,
-                                int max_pages_per_seq, int64_t num_pages, float scale, hipStream_t stream) {
+                                int max_pages_per_seq, int64_t num_pages, float scale, hipStream_t stream,
+                                const void* rope_table, int rope_len, const int32_t* q_positions,
+                                int rope_interleaved) {
   if (max_new <= 0 || total_new <= 0) return hipSuccess;
   PrefillArgs a = prefill_args(q, k_cache, v_cache, o, lse, batch, max_new, hq, hkv, 1, scale);
+  a.rope_cs = static_cast<const float2*>(rope_table); a.rope_len = rope_len; a.q_pos = q_positions;
+  a.rope_inter = rope_interleaved;
   a.cu_new = cu_new; a.ctx_lens = ctx_lens; a.table = block_table;
   int shift = 0;
   while ((1 << shift) < page_size) ++shift;
