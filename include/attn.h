@@ -315,10 +315,10 @@ int attn_dsa_indexer(const void* q_idx, const float* w_idx, const void* k_idx, c
 /* DeepSeek Sparse Attention, step 2: the top-k tokens of each sequence by score ("only the most relevant tokens",
  * Attention notes, "Lighting Indexer").
  *   scores    [batch, max_seqlen_kv] fp32 (e.g. from attn_dsa_indexer); only the first seq_lens[b] of row b are
- *             read. NaN is ordered above +inf.
+ *             read. A NaN score (of either sign) ranks below every number, -inf included, and all NaNs tie.
  *   indices   [batch, topk] int32, written: the min(topk, seq_lens[b]) selected token indices in ascending order,
  *             then -1. Selected = the topk largest scores; at equal scores the lower index wins, so the result is
- *             unique. A sequence with at most topk tokens keeps all of them.
+ *             unique (-0 and +0 are equal). A sequence with at most topk tokens keeps all of them.
  * INVALID_ARG for topk <= 0. */
 int attn_topk(const float* scores, const int32_t* seq_lens, int32_t* indices, int batch, int max_seqlen_kv, int topk,
               void* stream);

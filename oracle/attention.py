@@ -317,15 +317,21 @@ def dsa_indexer_scores(q_idx, w, k_idx, seq_lens):
 
 def topk_indices(scores, seq_lens, k):
     """Indices of the k largest scores among the first seq_lens[b] of each row ([AN-LI]: keep the most relevant
-    tokens). Ties at the cut go to the lower index. All min(k, L) selected indices are returned in ascending order,
-    the rest of the k slots hold -1. Returns int32 [B, k].
+    tokens). Ties at the cut go to the lower index. A NaN score (either sign) counts as less relevant than every
+    number, -inf included, and NaNs tie among themselves (the page is silent; a NaN carries no relevance).
+    All min(k, L) selected indices are returned in ascending order, the rest of the k slots hold -1.
+    Returns int32 [B, k].
     """
     scores = np.asarray(scores)
     out = np.full((scores.shape[0], k), -1, np.int32)
     for b in range(scores.shape[0]):
         n = int(seq_lens[b])
         idx = np.arange(n)
-        order = np.lexsort((idx, -scores[b, :n].astype(np.float64)))   # by descending score, then by index
+        with np.errstate(invalid="ignore"):                 # signalling NaNs convert quietly
+            sc = scores[b, :n].astype(np.float64)
+        nan = np.isnan(sc)
+        # numbers before NaNs, then by descending score, then by index (lexsort sorts by its last key first)
+        order = np.lexsort((idx, -np.where(nan, 0.0, sc), nan))
         sel = np.sort(order[: min(k, n)])
         out[b, : sel.size] = sel
     return out

@@ -95,6 +95,34 @@ def test_topk_ties_signed_zeros_and_infinities():
         np.testing.assert_array_equal(got, ref, err_msg=f"k={k}")
 
 
+def test_topk_nan_scores_rank_below_every_number():
+    """NaN scores of either sign (several payloads) among numbers and infinities: every NaN ranks below -inf and
+    NaNs tie among themselves (lower index first), index-exact against the oracle's selection on the same scores."""
+    ta = require_gpu()
+    rng = np.random.default_rng(64)
+    t = 3000
+    lens = [t, t, t, 40]
+    sc = rng.standard_normal((4, t)).astype(np.float32)
+    nan_bits = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF], np.uint32)   # +qNaN, -qNaN, sNaN, -NaN
+    for b in range(3):
+        pos = rng.choice(t, 200, replace=False)
+        sc[b, pos] = nan_bits[rng.integers(0, 4, 200)].view(np.float32)
+    sc[1, rng.choice(t, 50, replace=False)] = -np.inf
+    sc[1, rng.choice(t, 50, replace=False)] = np.inf
+    sc[2, :] = nan_bits[rng.integers(0, 4, t)].view(np.float32)                     # mostly NaN ...
+    sc[2, rng.choice(t, 10, replace=False)] = -np.inf                                # ... a few -inf
+    sc[3, :] = nan_bits[0].view(np.float32)
+    sc[3, 7] = -np.inf
+    for k in (1, 5, 100, 2799, 2800, 2801, 2990, 2999):
+        say(f"topk NaN k={k}")
+        got = run_topk(ta, sc, lens, k)
+        ref = oracle.topk_indices(sc, lens, k)
+        np.testing.assert_array_equal(got, ref, err_msg=f"k={k}")
+    # no NaN is selected while numbers remain unselected
+    got = run_topk(ta, sc, lens, 2800)
+    assert not np.isnan(sc[0, got[0]]).any()
+
+
 def test_topk_long_rows_in_rounds():
     """Rows longer than one register-resident round (32768 scores), with ties spread across rounds."""
     ta = require_gpu()

@@ -565,6 +565,18 @@ def test_topk_ties_and_short_rows():
     np.testing.assert_array_equal(got[1], [-1, -1, -1, -1])
 
 
+def test_topk_nan_ranks_below_every_number():
+    """Reading: a NaN score is less relevant than any number, -inf included; NaNs tie (lower index first)."""
+    nan, inf = np.nan, np.inf
+    x = np.array([[nan, -inf, 2.0, -nan, inf, nan, -1.0]])
+    np.testing.assert_array_equal(oracle.topk_indices(x, [7], 2), [[2, 4]])
+    np.testing.assert_array_equal(oracle.topk_indices(x, [7], 4), [[1, 2, 4, 6]])          # -inf before any NaN
+    np.testing.assert_array_equal(oracle.topk_indices(x, [7], 5), [[0, 1, 2, 4, 6]])       # first NaN by index
+    np.testing.assert_array_equal(oracle.topk_indices(x, [7], 6), [[0, 1, 2, 3, 4, 6]])
+    y = np.full((1, 5), nan)
+    np.testing.assert_array_equal(oracle.topk_indices(y, [5], 2), [[0, 1]])                 # all NaN: lowest indices
+
+
 def _mla_case(seed, B=2, H=3, C=16, R=4, T=12):
     rng = np.random.default_rng(seed)
     return (rng.standard_normal((B, H, C)), rng.standard_normal((B, H, R)), rng.standard_normal((B, T, C)),

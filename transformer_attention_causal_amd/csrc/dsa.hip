@@ -201,10 +201,12 @@ constexpr int kTopkRound = kTopkThreads * kTopkPer;   // 32768 scores per round 
 constexpr int kHistCopies = 16;
 constexpr int kHistStride = 257;
 
-// Order-preserving key: a larger float gives a larger unsigned key (-0 is taken as +0).
+// Order-preserving key: a larger float gives a larger unsigned key (-0 is taken as +0). Every NaN maps to key 0,
+// below -inf's key 0x007fffff: a NaN score is the least relevant, and NaNs tie (the lower index wins).
 __device__ __forceinline__ uint32_t order_key(float f) {
   const uint32_t u = __float_as_uint(f == 0.f ? 0.f : f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return f != f ? 0u : k;
 }
 
 // Number of set bits of `m` below this lane.
