@@ -208,35 +208,34 @@ def test_max_new_smaller_than_a_sequence_leaves_its_tail_unwritten():
 
 def test_full_size_sampled():
     """The bench workload (4 sequences x 2048 new tokens on 0 / 4096 / 8192 / 14336 cached ones) in the bench's
-    launch configuration, checked on sampled query rows computed one by one by the oracle."""
+    launch configuration. The oracle appends the new tokens to its own copy of the caches (keys rotated at their
+    absolute positions); every appended key and value of all four sequences is compared with it, every other slot
+    must be untouched, and sampled query rows are computed one by one against the oracle's caches."""
     ta = require_gpu()
     w = WORKLOADS["chunked_prefill_b4"]
     inp = chunked_prefill_inputs(w, seed=0)
     say(f"chunked full size ctx={w.ctx_lens} new={w.new_lens}")
     kc, vc, o, lse = run_gpu(ta, w, inp)
+    say("  oracle append")
+    kc_ref, vc_ref = oracle.kv_append_paged(bits_to_f32(inp["k_cache"]), bits_to_f32(inp["v_cache"]),
+                                            inp["block_table"], inp["ctx_lens"], bits_to_f32(inp["k_new"]),
+                                            bits_to_f32(inp["v_new"]), inp["cu_new"], w.theta)
+    check_cache(inp, kc, vc, kc_ref)
     # sampled rows: first, last and three seeded others of each sequence; all heads
     rows = []
     for b in range(w.batch):
         r0, r1 = int(inp["cu_new"][b]), int(inp["cu_new"][b + 1])
         rows += [r0 + int(i) for i in sampled_rows(r1 - r0, 5, seed=b)]
-    ps = w.page_size
+    say(f"  oracle on {len(rows)} rows")
     q_all = oracle.rope(bits_to_f32(inp["q"][rows]), inp["positions"][rows], w.theta)
     for j, r in enumerate(rows):
         b = int(np.searchsorted(inp["cu_new"], r, side="right") - 1)
         L = int(inp["positions"][r]) + 1
-        k = bits_to_f32(oracle.gather_paged(kc, inp["block_table"][b], L))          # the GPU-written cache
-        v = bits_to_f32(oracle.gather_paged(vc, inp["block_table"][b], L))
+        k = oracle.gather_paged(kc_ref, inp["block_table"][b], L)
+        v = oracle.gather_paged(vc_ref, inp["block_table"][b], L)
         o_ref, lse_ref = _one_row(q_all[j], k, v, w)
         check_bf16(f"o row {r}", o[r], o_ref)
         check(f"lse row {r}", lse[:, r], lse_ref, BF16_MAX)
-    # the appended keys of one sequence, all rows: rotation at the absolute positions
-    b = 3
-    r0, r1 = int(inp["cu_new"][b]), int(inp["cu_new"][b + 1])
-    k_ref = oracle.rope(bits_to_f32(inp["k_new"][r0:r1]), inp["positions"][r0:r1], w.theta)
-    pos = inp["positions"][r0:r1]
-    pg = inp["block_table"][b, pos // ps]
-    check("appended keys", bits_to_f32(kc[pg, pos % ps]), k_ref, BF16_MAX, BF16_MEAN)
-    assert np.array_equal(vc[pg, pos % ps], inp["v_new"][r0:r1])
 
 
 def _one_row(q, k, v, w):
@@ -280,3 +279,33 @@ def test_fused_rope_equals_rotate_then_attend(ctx, new, hq, hkv, d, interleaved,
     assert torch.equal(o1, o2)
     assert torch.equal(l1, l2)
     assert np.array_equal(host_bf16(q2), inp["q"])
+
+
+def test_fused_rope_at_other_positions_and_clamped():
+    """Explicit query positions that differ from cache_lens[b] + i (shifted per sequence, permuted within it, some
+    negative, some past the table) give the same bits as attn_rope_apply at the positions clamped into the table
+    followed by attn_prefill_paged: the kernel rotates by the positions it is given, clamped into [0, rows)."""
+    ta = require_gpu()
+    w = WORKLOADS["chunked_prefill_b4"]
+    inp = chunked_prefill_inputs(w, seed=51, ctx_lens=(3, 0, 190, 64), new_lens=(100, 65, 1, 63))
+    say("chunked fused rope at shifted / permuted / clamped positions")
+    kc, vc = dev_bf16(inp["k_cache"]), dev_bf16(inp["v_cache"])
+    table, cu, cl = dev(inp["block_table"]), dev(inp["cu_new"]), dev(inp["ctx_lens"])
+    ta.attn_kv_append_paged(dev_bf16(inp["k_new"]), dev_bf16(inp["v_new"]), cu, cl, kc, vc, table, w.theta)
+    rng = np.random.default_rng(52)
+    pos = inp["positions"].astype(np.int64).copy()
+    for b, shift in enumerate((37, -20, 1000, 5)):
+        r0, r1 = int(inp["cu_new"][b]), int(inp["cu_new"][b + 1])
+        pos[r0:r1] = rng.permutation(pos[r0:r1]) + shift
+    pos = pos.astype(np.int32)
+    n_tab = 200
+    assert pos.min() < 0 and pos.max() >= n_tab
+    rope_tab = ta.attn_rope_table(n_tab, w.head_dim, w.theta)
+    q1 = dev_bf16(inp["q"])
+    ta.attn_rope_apply(q1, dev(np.clip(pos, 0, n_tab - 1)), w.theta)
+    o1, l1 = ta.attn_prefill_paged(q1, kc, vc, table, cu, cl, inp["max_new"], softmax_scale=w.scale, return_lse=True)
+    o2, l2 = ta.attn_prefill_paged_rope(dev_bf16(inp["q"]), kc, vc, table, cu, cl, inp["max_new"], rope_tab,
+                                        q_positions=dev(pos), softmax_scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(l1, l2)

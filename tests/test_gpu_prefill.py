@@ -50,6 +50,32 @@ def test_mha_fp32_s256_full():
     check("lse", lse, lse_ref, FP32_MAX)
 
 
+FP32_CASES = [  # (batch, seqlen, hq, hkv, head_dim, causal)
+    (1, 300, 8, 2, 128, True),     # head_dim 128, 4 query heads per KV head, ragged tail
+    (2, 513, 4, 4, 64, False),     # no causal mask, ragged
+    (1, 300, 8, 2, 64, False),     # GQA without the mask
+    (1, 513, 6, 3, 128, True),     # 2 query heads per KV head, ragged
+    (1, 1, 4, 2, 128, True),       # a single token
+    (1, 64, 8, 1, 128, False),     # one KV head for all query heads, exactly two 32-key tiles
+]
+
+
+@pytest.mark.parametrize("case", FP32_CASES, ids=lambda c: "b{}_s{}_hq{}_hkv{}_d{}_{}".format(*c[:5], "causal" if c[5] else "full"))
+def test_fp32_prefill_small(case):
+    """The fp32 path against the oracle at the fp32 bound (max abs <= 1e-5) beyond the 256-token MHA workload."""
+    ta = require_gpu()
+    b, s, hq, hkv, d, causal = case
+    w = dataclasses.replace(WORKLOADS["mha_fp32_s256"], batch=b, seqlen=s, hq=hq, hkv=hkv, head_dim=d,
+                            scale=scale_for(d), causal=causal)
+    say(f"prefill fp32 {case}")
+    inp = prefill_inputs(w, seed=12)
+    o, lse = run_gpu(ta, w, inp, causal=causal)
+    q, k, v = oracle_inputs(w, inp)
+    o_ref, lse_ref = oracle.attention_prefill(q, k, v, causal, w.scale)
+    check("o", o, o_ref, FP32_MAX)
+    check("lse", lse, lse_ref, FP32_MAX)
+
+
 SMALL = [  # (batch, seqlen, hq, hkv, head_dim, causal)
     (2, 300, 8, 2, 128, True),     # 4 query heads per KV head: heads mode; ragged tail
     (1, 200, 4, 4, 64, True),      # MHA: positions mode, head_dim 64

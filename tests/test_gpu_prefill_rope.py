@@ -142,3 +142,45 @@ def test_full_size_fused_equals_unfused():
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
     assert torch.equal(l1, l2)
+
+
+@pytest.mark.timeout(900)
+def test_full_size_fused_all_rows_against_oracle():
+    """The benchmark step at full size (the RoPE table, RoPE(K) in place, attention with RoPE(Q) fused: B=2,
+    Hq=32, Hkv=8, S=8192, D=128) against the oracle on EVERY query row of both sequences and all heads. The oracle
+    materialises each (sequence, head)'s 8192 x 8192 scores in fp64; errors are accumulated over all outputs."""
+    ta = require_gpu()
+    w = WORKLOADS["gqa_prefill_s8192"]
+    say(f"fused rope prefill full size S={w.seqlen}, all rows against the oracle")
+    inp = prefill_inputs(w, seed=0)
+    pos = dev(inp["positions"])
+    k = dev_bf16(inp["k"])
+    table = ta.attn_rope_table(w.seqlen, w.head_dim, w.theta)
+    ta.attn_rope_apply(k, pos, w.theta)
+    o, lse = ta.attn_prefill_rope(dev_bf16(inp["q"]), k, dev_bf16(inp["v"]), table, softmax_scale=w.scale,
+                                  return_lse=True)
+    torch.cuda.synchronize()
+    o = bits_to_f32(host_bf16(o)).astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    p = inp["positions"].reshape(w.batch, w.seqlen)
+    qr = oracle.rope(bits_to_f32(inp["q"]), p, w.theta)
+    kr = oracle.rope(bits_to_f32(inp["k"]), p, w.theta)
+    v = bits_to_f32(inp["v"]).astype(np.float64)
+    grp = w.hq // w.hkv
+    o_max = o_sum = l_max = l_sum = 0.0
+    for b in range(w.batch):
+        for h in range(w.hq):
+            g = h // grp
+            o_ref, l_ref = oracle.attention_prefill(qr[b:b + 1, :, h:h + 1], kr[b:b + 1, :, g:g + 1],
+                                                    v[b:b + 1, :, g:g + 1], True, w.scale)
+            eo = np.abs(o[b, :, h] - o_ref[0, :, 0])
+            el = np.abs(lse[b, h] - l_ref[0, 0])
+            assert np.all(np.isfinite(eo)) and np.all(np.isfinite(el)), (b, h)
+            o_max, o_sum = max(o_max, float(eo.max())), o_sum + float(eo.sum())
+            l_max, l_sum = max(l_max, float(el.max())), l_sum + float(el.sum())
+        say(f"  sequence {b}: max abs err o {o_max:.3e}, lse {l_max:.3e}")
+    o_mean = o_sum / o.size
+    l_mean = l_sum / lse.size
+    say(f"  o: max {o_max:.3e} mean {o_mean:.3e}; lse: max {l_max:.3e} mean {l_mean:.3e}; n={o.size}")
+    assert o_max <= BF16_MAX and o_mean <= BF16_MEAN
+    assert l_max <= BF16_MAX and l_mean <= BF16_MEAN

@@ -91,6 +91,12 @@ def _dev(t, name, dtype=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _shape(t, shape, name):
+    """Raise unless tensor t has exactly this shape (the kernels index every buffer by the sizes passed)."""
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _code(dtype):
     if dtype == torch.bfloat16:
         return ATTN_BF16
@@ -123,6 +129,9 @@ def attn_prefill(q, k, v, causal=True, softmax_scale=None, o=None, lse=None, ret
         o = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((bsz, hq, s_len), dtype=torch.float32, device=q.device)
+    _shape(o, q.shape, "o")
+    if lse is not None:
+        _shape(lse, (bsz, hq, s_len), "lse")
     lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
     _check("attn_prefill", lib.attn_prefill(_dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(o, "o", q.dtype), lse_p,
                                              _code(q.dtype), bsz, s_len, hq, hkv, d, 1 if causal else 0, scale,
@@ -160,6 +169,11 @@ def attn_prefill_rope(q, k, v, rope_table, q_positions=None, interleaved=True, c
         o = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((bsz, hq, s_len), dtype=torch.float32, device=q.device)
+    _shape(o, q.shape, "o")
+    if lse is not None:
+        _shape(lse, (bsz, hq, s_len), "lse")
+    if q_positions is not None and q_positions.numel() != bsz * s_len:
+        raise ValueError("q_positions must have one entry per query row (B*S)")
     lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
     pos_p = _dev(q_positions, "q_positions", torch.int32) if q_positions is not None else None
     _check("attn_prefill_rope", lib.attn_prefill_rope(
@@ -185,6 +199,9 @@ def attn_prefill_local_global(q, k, v, window, n_lead=0, anchor_stride=0, softma
         o = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((bsz, hq, s_len), dtype=torch.float32, device=q.device)
+    _shape(o, q.shape, "o")
+    if lse is not None:
+        _shape(lse, (bsz, hq, s_len), "lse")
     lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
     _check("attn_prefill_local_global", lib.attn_prefill_local_global(
         _dev(q, "q", torch.bfloat16), _dev(k, "k", torch.bfloat16), _dev(v, "v", torch.bfloat16),
@@ -212,6 +229,13 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seqlen_kv,
     need = attn_decode_paged_workspace_size(bsz, hq, d, max(1, int(max_seqlen_kv)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if k_cache.dim() != 4 or k_cache.shape[3] != d or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must both be [num_pages, page, Hkv, D] with q's D")
+    if block_table.dim() != 2 or block_table.shape[0] != bsz or tuple(seq_lens.shape) != (bsz,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    _shape(o, q.shape, "o")
+    if lse is not None:
+        _shape(lse, (bsz, hq), "lse")
     lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
     _check("attn_decode_paged", lib.attn_decode_paged(
         _dev(q, "q", torch.bfloat16), _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
@@ -241,6 +265,13 @@ def attn_mla_decode(q_latent, q_pe, c_kv, k_pe, seq_lens, softmax_scale, o=None,
     need = attn_mla_decode_workspace_size(bsz, nh, c, max(1, t))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_latent.device)
+    if q_pe.shape[:2] != (bsz, nh) or c_kv.shape[0] != bsz or c_kv.shape[2] != c or k_pe.shape != (bsz, t, r):
+        raise ValueError("q_pe [B, H, R], c_kv [B, T, C] and k_pe [B, T, R] must agree with q_latent [B, H, C]")
+    if tuple(seq_lens.shape) != (bsz,):
+        raise ValueError("seq_lens must be [B]")
+    _shape(o, q_latent.shape, "o")
+    if lse is not None:
+        _shape(lse, (bsz, nh), "lse")
     lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
     _check("attn_mla_decode", lib.attn_mla_decode(
         _dev(q_latent, "q_latent", torch.bfloat16), _dev(q_pe, "q_pe", torch.bfloat16),
@@ -268,6 +299,15 @@ def attn_mla_decode_q8(q_latent, q_pe, c_kv, k_pe, c_scale, pe_scale, kv_kind, s
     need = attn_mla_decode_workspace_size(bsz, nh, c, max(1, t))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_latent.device)
+    if q_pe.shape[:2] != (bsz, nh) or c_kv.shape[0] != bsz or c_kv.shape[2] != c or k_pe.shape != (bsz, t, r):
+        raise ValueError("q_pe [B, H, R], c_kv [B, T, C] and k_pe [B, T, R] must agree with q_latent [B, H, C]")
+    if tuple(seq_lens.shape) != (bsz,):
+        raise ValueError("seq_lens must be [B]")
+    _shape(c_scale, (c,), "c_scale")
+    _shape(pe_scale, (r,), "pe_scale")
+    _shape(o, q_latent.shape, "o")
+    if lse is not None:
+        _shape(lse, (bsz, nh), "lse")
     lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
     _check("attn_mla_decode_q8", lib.attn_mla_decode_q8(
         _dev(q_latent, "q_latent", torch.bfloat16), _dev(q_pe, "q_pe", torch.bfloat16),
@@ -297,6 +337,18 @@ def attn_kv_append_paged(k_new, v_new, cu_new, cache_lens, k_cache, v_cache, blo
     return k_cache, v_cache
 
 
+def _check_paged_prefill(q, k_cache, v_cache, block_table, cu_new, cache_lens, o, lse):
+    total, hq, d = q.shape
+    if k_cache.dim() != 4 or k_cache.shape[3] != d or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must both be [num_pages, page, Hkv, D] with q's D")
+    bsz = cu_new.numel() - 1
+    if bsz < 0 or tuple(cache_lens.shape) != (bsz,) or block_table.dim() != 2 or block_table.shape[0] != bsz:
+        raise ValueError("cu_new [B+1], cache_lens [B] and block_table [B, max_pages] must agree")
+    _shape(o, q.shape, "o")
+    if lse is not None:
+        _shape(lse, (hq, total), "lse")
+
+
 def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_new, cache_lens, max_new, softmax_scale=None, o=None,
                        lse=None, return_lse=False, stream=None):
     """q [total_new, Hq, D] bf16 (rotated at absolute positions) against the paged caches that already hold each
@@ -310,6 +362,7 @@ def attn_prefill_paged(q, k_cache, v_cache, block_table, cu_new, cache_lens, max
         o = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((hq, total), dtype=torch.float32, device=q.device)
+    _check_paged_prefill(q, k_cache, v_cache, block_table, cu_new, cache_lens, o, lse)
     lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
     _check("attn_prefill_paged", lib.attn_prefill_paged(
         _dev(q, "q", torch.bfloat16), _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
@@ -334,6 +387,9 @@ def attn_prefill_paged_rope(q, k_cache, v_cache, block_table, cu_new, cache_lens
         o = torch.empty_like(q)
     if lse is None and return_lse:
         lse = torch.empty((hq, total), dtype=torch.float32, device=q.device)
+    _check_paged_prefill(q, k_cache, v_cache, block_table, cu_new, cache_lens, o, lse)
+    if q_positions is not None and q_positions.numel() != total:
+        raise ValueError("q_positions must have one entry per new token (total_new)")
     lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
     pos_p = _dev(q_positions, "q_positions", torch.int32) if q_positions is not None else None
     _check("attn_prefill_paged_rope", lib.attn_prefill_paged_rope(
@@ -356,6 +412,8 @@ def attn_dsa_indexer(q_idx, w_idx, k_idx, seq_lens, scores=None, stream=None):
         raise ValueError("shape mismatch between q_idx, w_idx and k_idx")
     if scores is None:
         scores = torch.empty((bsz, t), dtype=torch.float32, device=q_idx.device)
+    _shape(scores, (bsz, t), "scores")
+    _shape(seq_lens, (bsz,), "seq_lens")
     _check("attn_dsa_indexer", lib.attn_dsa_indexer(
         _dev(q_idx, "q_idx", torch.bfloat16), _dev(w_idx, "w_idx", torch.float32), _dev(k_idx, "k_idx", torch.bfloat16),
         _dev(seq_lens, "seq_lens", torch.int32), _dev(scores, "scores", torch.float32), bsz, hi, di, t,
@@ -370,6 +428,8 @@ def attn_topk(scores, seq_lens, topk, indices=None, stream=None):
     bsz, t = scores.shape
     if indices is None:
         indices = torch.empty((bsz, topk), dtype=torch.int32, device=scores.device)
+    _shape(indices, (bsz, topk), "indices")
+    _shape(seq_lens, (bsz,), "seq_lens")
     _check("attn_topk", lib.attn_topk(_dev(scores, "scores", torch.float32), _dev(seq_lens, "seq_lens", torch.int32),
                                       _dev(indices, "indices", torch.int32), bsz, t, int(topk),
                                       _stream(scores, stream)))
@@ -395,6 +455,13 @@ def attn_mla_sparse_decode(q_latent, q_pe, c_kv, k_pe, seq_lens, indices, softma
     need = attn_mla_sparse_decode_workspace_size(bsz, nh, c, topk)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q_latent.device)
+    if q_pe.shape[:2] != (bsz, nh) or c_kv.shape[0] != bsz or c_kv.shape[2] != c or k_pe.shape != (bsz, t, r):
+        raise ValueError("q_pe [B, H, R], c_kv [B, T, C] and k_pe [B, T, R] must agree with q_latent [B, H, C]")
+    if tuple(seq_lens.shape) != (bsz,) or indices.dim() != 2 or indices.shape[0] != bsz:
+        raise ValueError("seq_lens must be [B] and indices [B, topk]")
+    _shape(o, q_latent.shape, "o")
+    if lse is not None:
+        _shape(lse, (bsz, nh), "lse")
     lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
     _check("attn_mla_sparse_decode", lib.attn_mla_sparse_decode(
         _dev(q_latent, "q_latent", torch.bfloat16), _dev(q_pe, "q_pe", torch.bfloat16),
@@ -421,6 +488,15 @@ def attn_decode_paged_q8(q, k_cache, v_cache, k_scale, v_scale, kv_kind, block_t
     need = attn_decode_paged_workspace_size(bsz, hq, d, max(1, int(max_seqlen_kv)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if k_cache.dim() != 4 or k_cache.shape[3] != d or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must both be [num_pages, page, Hkv, D] with q's D")
+    if block_table.dim() != 2 or block_table.shape[0] != bsz or tuple(seq_lens.shape) != (bsz,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    _shape(k_scale, (hkv, d), "k_scale")
+    _shape(v_scale, (hkv, d), "v_scale")
+    _shape(o, q.shape, "o")
+    if lse is not None:
+        _shape(lse, (bsz, hq), "lse")
     lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
     _check("attn_decode_paged_q8", lib.attn_decode_paged_q8(
         _dev(q, "q", torch.bfloat16), _dev(k_cache, "k_cache", torch.uint8), _dev(v_cache, "v_cache", torch.uint8),
