@@ -163,7 +163,9 @@ def test_decode_validation(lib):
     assert call(sl=NULL) == INVALID
     assert call(bt=NULL) == INVALID
     assert call(npages=0) == INVALID
-    assert call(d=64) == UNSUPPORTED
+    assert call(d=96) == UNSUPPORTED
+    assert call(d=64, ws=NULL) == WORKSPACE              # head_dim 64 is supported: validation reaches the workspace
+    assert call(d=64, b=0) == OK
     assert call(hq=64, hkv=2) == UNSUPPORTED             # group of 32 query heads > 16
     assert call(ps=48) == UNSUPPORTED                    # not a power of two
     assert call(ps=8) == UNSUPPORTED
@@ -328,7 +330,8 @@ def test_decode_q8_validation(lib):
     assert f(*args(scale=0.0)) == INVALID
     assert f(*args(kind=0)) == UNSUPPORTED            # bf16 caches go through attn_decode_paged
     assert f(*args(kind=3)) == UNSUPPORTED
-    assert f(*args(d=64)) == UNSUPPORTED
+    assert f(*args(d=96)) == UNSUPPORTED
+    assert f(*args(d=64, ws=NULL)) == WORKSPACE       # head_dim 64 is supported: validation reaches the workspace
     assert f(*args(wsb=need - 1)) == WORKSPACE
     assert f(*args(b=0)) == OK
 

@@ -32,11 +32,14 @@ def run_oracle(w, inp):
 LENS = [1, 17, 64, 65, 600, 1300, 511, 512, 513, 1024]
 
 
-@pytest.mark.parametrize("hq,hkv,page", [(32, 8, 64), (32, 8, 16), (32, 2, 128), (8, 8, 32), (12, 4, 64)])
-def test_decode_small(hq, hkv, page):
+@pytest.mark.parametrize("hq,hkv,page,d", [(32, 8, 64, 128), (32, 8, 16, 128), (32, 2, 128, 128), (8, 8, 32, 128),
+                                         (12, 4, 64, 128), (32, 8, 64, 64), (32, 8, 16, 64), (16, 1, 128, 64),
+                                         (12, 4, 32, 64)])
+def test_decode_small(hq, hkv, page, d):
     ta = require_gpu()
-    w = dataclasses.replace(WORKLOADS["paged_decode_b64"], hq=hq, hkv=hkv, page_size=page)
-    say(f"decode hq={hq} hkv={hkv} page={page} lens={LENS}")
+    w = dataclasses.replace(WORKLOADS["paged_decode_b64"], hq=hq, hkv=hkv, page_size=page, head_dim=d,
+                            scale=1.0 / np.sqrt(d))
+    say(f"decode hq={hq} hkv={hkv} page={page} d={d} lens={LENS}")
     inp = paged_decode_inputs(w, seed=21, seq_lens=LENS, max_len=2048)
     o, lse = run_gpu(ta, w, inp)
     o_ref, lse_ref = run_oracle(w, inp)
@@ -63,9 +66,11 @@ def relayout(inp, seed, poison_spare=True, bad_unused=True):
     return out
 
 
-def test_physical_placement_and_poison_are_invisible():
+@pytest.mark.parametrize("d", [128, 64])
+def test_physical_placement_and_poison_are_invisible(d):
     ta = require_gpu()
-    w = WORKLOADS["paged_decode_b64"]
+    w = dataclasses.replace(WORKLOADS["paged_decode_b64"], head_dim=d, scale=1.0 / np.sqrt(d))
+    say(f"decode placement / poison d={d}")
     inp = paged_decode_inputs(w, seed=22, seq_lens=[3, 70, 999, 1500, 64, 1], max_len=1600)
     o1, l1 = run_gpu(ta, w, inp)
     for seed in (1, 2):
@@ -73,9 +78,10 @@ def test_physical_placement_and_poison_are_invisible():
         assert np.array_equal(o1, o2) and np.array_equal(l1, l2), seed
 
 
-def test_slots_past_the_length_are_invisible():
+@pytest.mark.parametrize("d", [128, 64])
+def test_slots_past_the_length_are_invisible(d):
     ta = require_gpu()
-    w = WORKLOADS["paged_decode_b64"]
+    w = dataclasses.replace(WORKLOADS["paged_decode_b64"], head_dim=d, scale=1.0 / np.sqrt(d))
     inp = paged_decode_inputs(w, seed=23, seq_lens=[5, 130, 1001], max_len=1024)
     o1, l1 = run_gpu(ta, w, inp)
     ps = w.page_size
@@ -87,9 +93,10 @@ def test_slots_past_the_length_are_invisible():
     assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
-def test_length_one_is_v0_and_length_zero_is_empty():
+@pytest.mark.parametrize("d", [128, 64])
+def test_length_one_is_v0_and_length_zero_is_empty(d):
     ta = require_gpu()
-    w = WORKLOADS["paged_decode_b64"]
+    w = dataclasses.replace(WORKLOADS["paged_decode_b64"], head_dim=d, scale=1.0 / np.sqrt(d))
     inp = paged_decode_inputs(w, seed=24, seq_lens=[1, 0, 1], max_len=64)
     o, lse = run_gpu(ta, w, inp)
     grp = w.hq // w.hkv

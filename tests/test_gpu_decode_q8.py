@@ -34,11 +34,14 @@ def run_oracle(w, inp):
 
 
 @pytest.mark.parametrize("kind", ["fp8", "int8"])
-@pytest.mark.parametrize("hq,hkv,page", [(32, 8, 64), (32, 8, 16), (32, 2, 128), (8, 8, 32), (12, 4, 64)])
-def test_q8_decode_small(kind, hq, hkv, page):
+@pytest.mark.parametrize("hq,hkv,page,d", [(32, 8, 64, 128), (32, 8, 16, 128), (32, 2, 128, 128), (8, 8, 32, 128),
+                                         (12, 4, 64, 128), (32, 8, 64, 64), (32, 8, 16, 64), (16, 1, 128, 64),
+                                         (12, 4, 32, 64)])
+def test_q8_decode_small(kind, hq, hkv, page, d):
     ta = require_gpu()
-    w = dataclasses.replace(WORKLOADS["paged_decode_b64"], hq=hq, hkv=hkv, page_size=page)
-    say(f"q8 decode {kind} hq={hq} hkv={hkv} page={page} lens={LENS}")
+    w = dataclasses.replace(WORKLOADS["paged_decode_b64"], hq=hq, hkv=hkv, page_size=page, head_dim=d,
+                            scale=1.0 / np.sqrt(d))
+    say(f"q8 decode {kind} hq={hq} hkv={hkv} page={page} d={d} lens={LENS}")
     inp = paged_decode_inputs(w, seed=81, seq_lens=LENS, max_len=2048, kv=kind)
     o, lse = run_gpu(ta, w, inp)
     o_ref, lse_ref = run_oracle(w, inp)
@@ -47,9 +50,11 @@ def test_q8_decode_small(kind, hq, hkv, page):
 
 
 @pytest.mark.parametrize("kind", ["fp8", "int8"])
-def test_q8_placement_and_poison_are_invisible(kind):
+@pytest.mark.parametrize("d", [128, 64])
+def test_q8_placement_and_poison_are_invisible(kind, d):
     ta = require_gpu()
-    w = WORKLOADS["paged_decode_b64"]
+    w = dataclasses.replace(WORKLOADS["paged_decode_b64"], head_dim=d, scale=1.0 / np.sqrt(d))
+    say(f"q8 decode placement / poison {kind} d={d}")
     inp = paged_decode_inputs(w, seed=82, seq_lens=[3, 70, 999, 1500, 64, 1], max_len=1600, kv=kind)
     o1, l1 = run_gpu(ta, w, inp)
     ps = w.page_size

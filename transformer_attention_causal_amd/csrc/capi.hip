@@ -113,7 +113,7 @@ ATTN_EXPORT int attn_decode_paged(const void* q, const void* k_cache, const void
   if (batch < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0 || max_seqlen_kv < 0) return ATTN_ERR_INVALID_ARG;
   if (n_heads_q % n_heads_kv != 0 || !valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
   if (page_size <= 0 || max_pages_per_seq < 0) return ATTN_ERR_INVALID_ARG;
-  if (head_dim != 128 || n_heads_q / n_heads_kv > 16) return ATTN_ERR_UNSUPPORTED;
+  if ((head_dim != 128 && head_dim != 64) || n_heads_q / n_heads_kv > 16) return ATTN_ERR_UNSUPPORTED;
   if (!is_pow2(page_size) || page_size < 16 || page_size > 1024) return ATTN_ERR_UNSUPPORTED;
   if (batch == 0) return ATTN_OK;
   if (!q || !seq_lens || !o) return ATTN_ERR_INVALID_ARG;
@@ -137,7 +137,7 @@ ATTN_EXPORT int attn_decode_paged_q8(const void* q, const void* k_cache, const v
   if (n_heads_q % n_heads_kv != 0 || !valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
   if (page_size <= 0 || max_pages_per_seq < 0) return ATTN_ERR_INVALID_ARG;
   if (kv_kind != ATTN_KV_FP8_E4M3 && kv_kind != ATTN_KV_INT8) return ATTN_ERR_UNSUPPORTED;
-  if (head_dim != 128 || n_heads_q / n_heads_kv > 16) return ATTN_ERR_UNSUPPORTED;
+  if ((head_dim != 128 && head_dim != 64) || n_heads_q / n_heads_kv > 16) return ATTN_ERR_UNSUPPORTED;
   if (!is_pow2(page_size) || page_size < 16 || page_size > 1024) return ATTN_ERR_UNSUPPORTED;
   if (batch == 0) return ATTN_OK;
   if (!q || !seq_lens || !o || !k_scale || !v_scale) return ATTN_ERR_INVALID_ARG;
@@ -151,7 +151,7 @@ ATTN_EXPORT int attn_decode_paged_q8(const void* q, const void* k_cache, const v
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   return hip_status(attn::launch_decode_paged_q8(kv_kind == ATTN_KV_FP8_E4M3 ? 1 : 0, q, k_cache, v_cache, k_scale,
                                                  v_scale, block_table, seq_lens, o, lse, batch, n_heads_q, n_heads_kv,
-                                                 page_size, max_pages_per_seq, num_pages, max_seqlen_kv, softmax_scale,
+                                                 head_dim, page_size, max_pages_per_seq, num_pages, max_seqlen_kv, softmax_scale,
                                                  workspace, static_cast<hipStream_t>(stream)));
 }
 
