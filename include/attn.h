@@ -7,6 +7,7 @@
  *   attn_prefill_rope     attn_prefill with the rotation of Q fused into the kernel's load of Q
  *   attn_prefill_local_global  causal prefill with a sliding window plus global (leading, periodic) tokens
  *   attn_decode_paged     one query token per sequence against a paged KV cache (split-KV + log-sum-exp combine)
+ *   attn_decode_paged_noalloc  attn_decode_paged with library-owned static scratch instead of a workspace
  *   attn_decode_paged_q8  the same over 8-bit (FP8 E4M3 or int8) K/V caches with per-channel scales
  *   attn_mla_decode       multi-head latent attention decode in the absorbed form
  *   attn_mla_decode_q8    the same over an 8-bit (FP8 E4M3 or int8) latent cache with per-channel scales
@@ -27,7 +28,8 @@
  *   - Pointers named as tensors are DEVICE pointers; `stream` is a hipStream_t passed as void* (NULL = the
  *     default stream). Every call only enqueues work on `stream` and returns; it never synchronises, never
  *     allocates or frees device memory, never changes the current device, and keeps no state between calls,
- *     so calls are re-entrant and thread-safe. The caller owns every buffer, including the workspace.
+ *     so calls are re-entrant and thread-safe. The caller owns every buffer, including the workspace. The one
+ *     exception is attn_decode_paged_noalloc, whose scratch is the library's own (see there).
  *   - Layouts are row-major with the last dimension contiguous. "bf16" is IEEE bfloat16 (results rounded to
  *     nearest even); arithmetic inside the kernels is fp32.
  *   - All validation happens on the host before anything is enqueued: on any error nothing is launched and the
@@ -172,6 +174,30 @@ int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache, c
                       const int32_t* seq_lens, void* o, float* lse, int batch, int n_heads_q, int n_heads_kv,
                       int head_dim, int page_size, int max_pages_per_seq, int64_t num_pages, int max_seqlen_kv,
                       float softmax_scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Size of the static device scratch behind attn_decode_paged_noalloc (64 MiB per GPU): the largest workspace,
+ * as attn_decode_paged_workspace_size reports it, that the no-allocation entry point can serve. */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)64 << 20)
+
+/* attn_decode_paged without a workspace argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. The split partials go to a static device
+ * array of ATTN_DECODE_SCRATCH_BYTES owned by the library, one copy per GPU, which exists from the moment the
+ * library's code is loaded on that GPU until the process ends. The first call on a device looks up that device's
+ * copy (hipGetSymbolAddress with the device current); later calls reuse the address. The call itself allocates
+ * and frees nothing.
+ *   All arguments as attn_decode_paged, without workspace; `stream` must belong to the current device.
+ * Errors: as attn_decode_paged, plus ATTN_ERR_WORKSPACE when attn_decode_paged_workspace_size(batch, n_heads_q,
+ * head_dim, max_seqlen_kv) exceeds ATTN_DECODE_SCRATCH_BYTES (at head_dim 128 and 64 sequences x 32 query heads,
+ * max_seqlen_kv up to 64512 fits), ATTN_ERR_UNSUPPORTED for a device ordinal of 64 or more, and ATTN_ERR_HIP when
+ * the device's scratch address cannot be obtained.
+ * Every call on one GPU shares that GPU's scratch, which keeps the last call's contents: calls whose executions
+ * overlap on one GPU (different streams, or host threads that do not order their streams) race and give wrong
+ * results. Calls on one stream are ordered and safe. Nothing in the scratch needs to start at zero: every partial
+ * a call reads is written earlier by the same call. Results are bitwise those of attn_decode_paged. */
+int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                              const int32_t* seq_lens, void* o, float* lse, int batch, int n_heads_q, int n_heads_kv,
+                              int head_dim, int page_size, int max_pages_per_seq, int64_t num_pages,
+                              int max_seqlen_kv, float softmax_scale, void* stream);
 
 /* Paged decode over 8-bit K/V caches: attn_decode_paged where each cached value is code * scale[kv_head][channel].
  * ("DeepSeek 32K to 256K long context", tqpw.cn, section 2.5: K and V kept as int8 with per-channel scales;

@@ -174,6 +174,33 @@ def test_decode_validation(lib):
     assert call(b=0) == OK
 
 
+def test_decode_noalloc_validation(lib):
+    """The no-allocation decode validates exactly as attn_decode_paged, and refuses a request whose workspace would
+    exceed the static scratch (64 MiB), all before any HIP call."""
+    f = lib.attn_decode_paged_noalloc
+    scratch = 64 << 20
+
+    def call(**kw):
+        a = dict(q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, sl=FAKE, o=FAKE, lse=NULL, b=2, hq=8, hkv=2, d=128, ps=64,
+                 maxp=2, npages=4, maxlen=100, scale=0.088)
+        a.update(kw)
+        return f(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["o"], a["lse"], a["b"], a["hq"], a["hkv"], a["d"],
+                 a["ps"], a["maxp"], a["npages"], a["maxlen"], a["scale"], NULL)
+    assert call(hq=6, hkv=4) == INVALID
+    assert call(maxlen=-1) == INVALID
+    assert call(scale=-1.0) == INVALID
+    assert call(q=NULL) == INVALID
+    assert call(bt=NULL) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(ps=48) == UNSUPPORTED
+    assert call(b=0) == OK
+    # 64 sequences x 32 heads x D=128: 64512 cached tokens fit the scratch, one more chunk does not
+    assert lib.attn_decode_paged_workspace_size(64, 32, 128, 64512) <= scratch
+    assert lib.attn_decode_paged_workspace_size(64, 32, 128, 64513) > scratch
+    assert call(b=64, hq=32, hkv=8, maxp=1100, npages=70000, maxlen=64513) == WORKSPACE
+    assert call(b=64, hq=32, hkv=8, maxp=1100, npages=70000, maxlen=1 << 30) == WORKSPACE
+
+
 def test_mla_validation(lib):
     f = lib.attn_mla_decode
     ws_need = lib.attn_mla_decode_workspace_size(2, 128, 512, 64)

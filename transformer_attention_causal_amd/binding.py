@@ -28,6 +28,7 @@ SIGNATURES = {
     "attn_prefill_local_global": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P]),
     "attn_decode_paged_workspace_size": (_SZ, [_I, _I, _I, _I]),
     "attn_decode_paged": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _I, _F, _P, _SZ, _P]),
+    "attn_decode_paged_noalloc": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _I, _F, _P]),
     "attn_decode_paged_q8": (_I, [_P, _P, _P, _P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I64, _I, _F, _P, _SZ,
                                   _P]),
     "attn_mla_decode_workspace_size": (_SZ, [_I, _I, _I, _I]),
@@ -243,6 +244,37 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, max_seqlen_kv,
         _dev(o, "o", torch.bfloat16), lse_p, bsz, hq, hkv, d, page, block_table.shape[1], num_pages,
         int(max_seqlen_kv), scale, _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(q, stream)))
+    return (o, lse) if return_lse else o
+
+
+DECODE_SCRATCH_BYTES = 64 << 20     # ATTN_DECODE_SCRATCH_BYTES
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, max_seqlen_kv, softmax_scale=None, o=None,
+                              lse=None, return_lse=False, stream=None):
+    """attn_decode_paged with the library's static per-GPU scratch instead of a workspace (no device allocation in
+    the call; pass o and lse to allocate nothing here either). Calls that overlap on one GPU race on the scratch."""
+    lib = load_library()
+    bsz, hq, d = q.shape
+    num_pages, page, hkv, _ = k_cache.shape
+    scale = 1.0 / math.sqrt(d) if softmax_scale is None else float(softmax_scale)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and return_lse:
+        lse = torch.empty((bsz, hq), dtype=torch.float32, device=q.device)
+    if k_cache.dim() != 4 or k_cache.shape[3] != d or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must both be [num_pages, page, Hkv, D] with q's D")
+    if block_table.dim() != 2 or block_table.shape[0] != bsz or tuple(seq_lens.shape) != (bsz,):
+        raise ValueError("block_table must be [B, max_pages] and seq_lens [B]")
+    _shape(o, q.shape, "o")
+    if lse is not None:
+        _shape(lse, (bsz, hq), "lse")
+    lse_p = _dev(lse, "lse", torch.float32) if lse is not None else None
+    _check("attn_decode_paged_noalloc", lib.attn_decode_paged_noalloc(
+        _dev(q, "q", torch.bfloat16), _dev(k_cache, "k_cache", torch.bfloat16), _dev(v_cache, "v_cache", torch.bfloat16),
+        _dev(block_table, "block_table", torch.int32), _dev(seq_lens, "seq_lens", torch.int32),
+        _dev(o, "o", torch.bfloat16), lse_p, bsz, hq, hkv, d, page, block_table.shape[1], num_pages,
+        int(max_seqlen_kv), scale, _stream(q, stream)))
     return (o, lse) if return_lse else o
 
 

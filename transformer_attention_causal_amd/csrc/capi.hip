@@ -2,9 +2,12 @@
 //
 // Each entry point validates its arguments on the host BEFORE touching the HIP runtime, so an invalid call
 // returns its status without any device work (and without needing a GPU), then enqueues the kernels on the
-// caller's stream. No allocation, no synchronisation, no state kept between calls.
+// caller's stream. No allocation, no synchronisation, no state kept between calls, except for
+// attn_decode_paged_noalloc's per-device scratch address, looked up once per device.
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/attn.h"
 #include "kernels.h"
@@ -105,20 +108,89 @@ ATTN_EXPORT size_t attn_decode_paged_workspace_size(int batch, int n_heads_q, in
   return attn::decode_paged_workspace_bytes(batch, n_heads_q, head_dim, max_seqlen_kv);
 }
 
-ATTN_EXPORT int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                                  const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
-                                  int batch, int n_heads_q, int n_heads_kv, int head_dim, int page_size,
-                                  int max_pages_per_seq, int64_t num_pages, int max_seqlen_kv,
-                                  float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+// Static scratch of attn_decode_paged_noalloc: the split partials of one call. Each GPU the library runs on holds
+// its own copy at its own address for the life of the process. In host code `scratch` names a host-side stand-in,
+// not device memory, so it is never passed to a kernel or a copy: the device address of the current GPU's copy
+// comes from hipGetSymbolAddress, looked up once per device and kept in scratch_addr.
+static __device__ __align__(256) uint8_t scratch[ATTN_DECODE_SCRATCH_BYTES];
+
+namespace {
+// Checks of attn_decode_paged other than the workspace. Returns ATTN_OK with *nothing_to_do set for batch 0.
+int check_decode_paged(const void* q, const void* k_cache, const void* v_cache, const int32_t* block_table,
+                       const int32_t* seq_lens, void* o, int batch, int n_heads_q, int n_heads_kv, int head_dim,
+                       int page_size, int max_pages_per_seq, int64_t num_pages, int max_seqlen_kv,
+                       float softmax_scale, bool* nothing_to_do) {
+  *nothing_to_do = false;
   if (batch < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0 || max_seqlen_kv < 0) return ATTN_ERR_INVALID_ARG;
   if (n_heads_q % n_heads_kv != 0 || !valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
   if (page_size <= 0 || max_pages_per_seq < 0) return ATTN_ERR_INVALID_ARG;
   if ((head_dim != 128 && head_dim != 64) || n_heads_q / n_heads_kv > 16) return ATTN_ERR_UNSUPPORTED;
   if (!is_pow2(page_size) || page_size < 16 || page_size > 1024) return ATTN_ERR_UNSUPPORTED;
-  if (batch == 0) return ATTN_OK;
+  if (batch == 0) {
+    *nothing_to_do = true;
+    return ATTN_OK;
+  }
   if (!q || !seq_lens || !o) return ATTN_ERR_INVALID_ARG;
   if (max_seqlen_kv > 0 && (!k_cache || !v_cache || !block_table || num_pages <= 0 || max_pages_per_seq <= 0))
     return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_addr[kMaxDevices];
+std::mutex scratch_mutex;
+
+// Device address of the current device's scratch (looked up on the first call for that device).
+int current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ATTN_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return ATTN_ERR_UNSUPPORTED;
+  void* p = scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    p = scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return ATTN_ERR_HIP;
+      scratch_addr[dev].store(addr, std::memory_order_release);
+      p = addr;
+    }
+  }
+  *out = p;
+  return ATTN_OK;
+}
+}  // namespace
+
+ATTN_EXPORT int attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                          const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                                          int batch, int n_heads_q, int n_heads_kv, int head_dim, int page_size,
+                                          int max_pages_per_seq, int64_t num_pages, int max_seqlen_kv,
+                                          float softmax_scale, void* stream) {
+  bool done = false;
+  const int st = check_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, batch, n_heads_q, n_heads_kv,
+                                    head_dim, page_size, max_pages_per_seq, num_pages, max_seqlen_kv,
+                                    softmax_scale, &done);
+  if (st != ATTN_OK || done) return st;
+  const size_t need = attn::decode_paged_workspace_bytes(batch, n_heads_q, head_dim, max(1, max_seqlen_kv));
+  if (need > ATTN_DECODE_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int sst = current_scratch(&ws);
+  if (sst != ATTN_OK) return sst;
+  return hip_status(attn::launch_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, batch, n_heads_q,
+                                              n_heads_kv, head_dim, page_size, max_pages_per_seq, num_pages,
+                                              max_seqlen_kv, softmax_scale, ws, static_cast<hipStream_t>(stream)));
+}
+
+ATTN_EXPORT int attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                                  int batch, int n_heads_q, int n_heads_kv, int head_dim, int page_size,
+                                  int max_pages_per_seq, int64_t num_pages, int max_seqlen_kv,
+                                  float softmax_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  bool done = false;
+  const int st = check_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, batch, n_heads_q, n_heads_kv,
+                                    head_dim, page_size, max_pages_per_seq, num_pages, max_seqlen_kv,
+                                    softmax_scale, &done);
+  if (st != ATTN_OK || done) return st;
   const size_t need = attn::decode_paged_workspace_bytes(batch, n_heads_q, head_dim, max(1, max_seqlen_kv));
   if (!workspace || workspace_bytes < need) return ATTN_ERR_WORKSPACE;
   return hip_status(attn::launch_decode_paged(q, k_cache, v_cache, block_table, seq_lens, o, lse, batch, n_heads_q,
