@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Benchmark of the exact-attention hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-secondary] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--prewarm SECONDS] [--no-secondary] [--no-cpu-baseline]
+                    [--no-cpu-configs] [--workloads LIST]
 
 Primary line: causal GQA prefill, bf16, B=2 Hq=32 Hkv=8 S=8192 D=128 (workload gqa_prefill_s8192). One step is the
 hot path over one batch: the RoPE cos/sin table, RoPE on K, then attn_prefill_rope (attention with the rotation of
@@ -20,8 +21,13 @@ launch duration (HIP events on the stream the kernel runs on), against MI355X's 
 2.5 PFLOP/s, HBM 8 TB/s). `traffic` is the counter-measured HBM bytes per launch from the committed rocprofv3
 summary (profiles/traffic.json) when it was taken on the current kernel source, else null.
 
+Before its `warmup` steps the primary workload runs untimed steps for `--prewarm` seconds (0.5 by default) so the
+GPU clock has settled; the timed region is the same K steps (reported as `prewarm`).
+
 `cpu_baseline` times the fp64 CPU oracle on a bounded sample of the primary workload (seeded query rows, every
-head): a reported baseline, not a target.
+head): a reported baseline, not a target. `cpu_baseline_configs` times the oracle on every configuration the parity
+tests run in full (fp32 MHA, paged decode, MLA decode) and on the 131072-token prefill's 256 sampled rows, with the
+CPU model and BLAS thread count.
 """
 import argparse
 import hashlib
@@ -45,7 +51,7 @@ PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = {
     "prefill_bf16_kernel": "prefill.hip",
-    "decode_paged_split_kernel": "decode.hip",
+    "decode_paged_q8_kernel": "decode.hip",
     "decode_paged_lds_kernel": "decode.hip",
     "mla_split_kernel": "mla.hip",
     "dsa_indexer_kernel": "dsa.hip",
@@ -122,7 +128,7 @@ def roofline_hbm(nbytes, ms, kernel, workload, timed=None):
 
 
 # --------------------------------------------------------------------------------------------------- prefill --
-def bench_prefill(torch, ta, w, steps, warmup, seed=0, local_global=False):
+def bench_prefill(torch, ta, w, steps, warmup, seed=0, local_global=False, prewarm_s=0.0):
     log(f"[bench] {w.name}: generating inputs")
     inp = prefill_inputs(w, seed=seed)
     q, k, v = (dev_bf16(torch, inp[n]) for n in ("q", "k", "v"))
@@ -150,6 +156,15 @@ def bench_prefill(torch, ta, w, steps, warmup, seed=0, local_global=False):
         if timed:
             timer.stop()
 
+    # Clock-settle pre-warm, independent of `warmup`: untimed steps until prewarm_s seconds of wall time have
+    # passed (the GPU clock takes about 0.1 s of load to settle; shorter warm-ups under-report by 5-25%).
+    pw_steps, t_pw = 0, time.perf_counter()
+    while time.perf_counter() - t_pw < prewarm_s:
+        for _ in range(8):
+            step(False)
+        pw_steps += 8
+        torch.cuda.synchronize()
+    prewarm = {"seconds": round(time.perf_counter() - t_pw, 3), "steps": pw_steps}
     for _ in range(warmup):
         step(False)
     torch.cuda.synchronize()
@@ -162,6 +177,8 @@ def bench_prefill(torch, ta, w, steps, warmup, seed=0, local_global=False):
     kern_ms = timer.mean_ms()
     del q, k, v, o
     torch.cuda.empty_cache()
+    if prewarm_s > 0:
+        return wall_ms, kern_ms, prewarm
     return wall_ms, kern_ms
 
 
@@ -394,7 +411,87 @@ def cpu_baseline(w, n_rows=4096, seed=0):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows.size} seeded query rows x {w.hq} heads x {w.batch} sequences of {w.name} "
                       f"(fp64 numpy, scores materialised, {dt:.1f} s)",
-            "affinity_cpus": len(os.sched_getaffinity(0))}
+            "wall_s": round(dt, 3), "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_info()["model"]}
+
+
+def cpu_info():
+    """CPU model, cores the process may run on, and numpy's BLAS thread count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:
+        threads = 1
+    return {"model": model, "affinity_cpus": len(os.sched_getaffinity(0)), "blas_threads": int(threads)}
+
+
+def cpu_oracle_configs():
+    """The fp64 oracle timed on each configuration as the parity tests run it: the fp32 MHA workload, the paged
+    decode and the MLA decode in full, and the 131072-token prefill on its 256 seeded rows (every head). Input
+    generation is not timed. Reports wall time, implied fp64 GFLOP/s of the algorithmic flops, and GB/s of the
+    algorithmic bytes for the decode workloads. A reported baseline, not a target."""
+    import oracle
+
+    def f32(b):
+        return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+    out = {"cpu": cpu_info()}
+    # fp32 MHA, full
+    w = WORKLOADS["mha_fp32_s256"]
+    inp = prefill_inputs(w, seed=0)
+    t0 = time.perf_counter()
+    pos = inp["positions"].reshape(w.batch, w.seqlen)
+    oracle.attention_prefill(oracle.rope(inp["q"], pos, w.theta), oracle.rope(inp["k"], pos, w.theta),
+                             inp["v"].astype(np.float64), True, w.scale)
+    dt = time.perf_counter() - t0
+    out[w.name] = {"sample": "full", "wall_s": round(dt, 3), "gflops": round(w.flops / dt / 1e9, 2)}
+    # paged decode, full
+    wd = WORKLOADS["paged_decode_b64"]
+    inp = paged_decode_inputs(wd, seed=0)
+    kc, vc = f32(inp["k_cache"]), f32(inp["v_cache"])
+    t0 = time.perf_counter()
+    qr = oracle.rope(f32(inp["q"])[:, None], inp["positions"][:, None], wd.theta)[:, 0]
+    oracle.decode_paged(qr, kc, vc, inp["block_table"], inp["seq_lens"], wd.scale)
+    dt = time.perf_counter() - t0
+    tokens = int(inp["seq_lens"].astype(np.int64).sum())
+    out[wd.name] = {"sample": "full", "wall_s": round(dt, 3),
+                    "gflops": round(4 * wd.hq * wd.head_dim * tokens / dt / 1e9, 2),
+                    "GB/s": round(decode_bytes(wd, inp) / dt / 1e9, 3)}
+    del inp, kc, vc
+    # MLA decode, full
+    wm = WORKLOADS["mla_decode_b32"]
+    m = mla_inputs(wm, seed=0)
+    ql, qp, ckv, kpe = (f32(m[n]) for n in ("q_lat", "q_pe", "c_kv", "k_pe"))
+    t0 = time.perf_counter()
+    oracle.mla_decode(ql, qp, ckv, kpe, m["seq_lens"], wm.scale)
+    dt = time.perf_counter() - t0
+    out[wm.name] = {"sample": "full", "wall_s": round(dt, 3), "gflops": round(mla_flops(wm) / dt / 1e9, 2),
+                    "GB/s": round(mla_bytes(wm) / dt / 1e9, 3)}
+    del m, ql, qp, ckv, kpe
+    # 131072-token prefill on its 256 sampled rows
+    wl = WORKLOADS["gqa_prefill_s131072"]
+    inp = prefill_inputs(wl, seed=0)
+    rows = sampled_rows(wl.seqlen, wl.sampled_rows, seed=0)
+    t0 = time.perf_counter()
+    pos = np.broadcast_to(np.arange(wl.seqlen), (wl.batch, wl.seqlen))
+    k = oracle.rope(f32(inp["k"]), pos, wl.theta)
+    v = f32(inp["v"]).astype(np.float64)
+    q = np.zeros((wl.batch, wl.seqlen, wl.hq, wl.head_dim))
+    q[:, rows] = oracle.rope(f32(inp["q"][:, rows]), np.broadcast_to(rows, (wl.batch, rows.size)), wl.theta)
+    oracle.attention_prefill_rows(q, k, v, rows, True, wl.scale)
+    dt = time.perf_counter() - t0
+    flops = 4 * wl.batch * wl.hq * wl.head_dim * int((rows + 1).sum())
+    out[wl.name] = {"sample": f"{rows.size} seeded query rows x {wl.hq} heads", "wall_s": round(dt, 3),
+                    "gflops": round(flops / dt / 1e9, 2)}
+    return out
 
 
 # ------------------------------------------------------------------------------------------------------ main --
@@ -408,7 +505,11 @@ def main():
     ap.add_argument("--workloads", default="prefill,decode,mla,long,chunked,dsa,decode_fp8,decode_int8,swa,mla_fp8,mla_int8",
                     help="comma list of prefill (primary), decode, mla, long, chunked, dsa, decode_fp8, decode_int8, "
                          "swa; profiling runs select one")
+    ap.add_argument("--prewarm", type=float, default=0.5,
+                    help="seconds of untimed primary steps before the warm-up steps (GPU clock settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-configs", action="store_true",
+                    help="skip the per-configuration oracle timings (keep only the bounded primary sample)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration for traffic measurements)")
     args = ap.parse_args()
@@ -446,7 +547,7 @@ def main():
         run_secondary(torch, ta, args, sel, line)
         print(json.dumps(line))
         return
-    wall_ms, kern_ms = bench_prefill(torch, ta, w, args.steps, args.warmup)
+    wall_ms, kern_ms, prewarm = bench_prefill(torch, ta, w, args.steps, args.warmup, prewarm_s=args.prewarm)
     value = w.flops / (wall_ms * 1e-3) / 1e12
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -458,11 +559,14 @@ def main():
         "roofline": roofline_compute(w.flops, kern_ms, "prefill_bf16_kernel", w.name),
     }
     line["pct_bf16_peak_step"] = round(value / PEAK_BF16_TFLOPS, 4)
+    line["prewarm"] = prewarm          # untimed clock-settle steps run before the `warmup` steps
 
     run_secondary(torch, ta, args, sel, line)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (fp64 oracle sample)")
         line["cpu_baseline"] = cpu_baseline(w)
+        if not args.no_cpu_configs:
+            line["cpu_baseline_configs"] = cpu_oracle_configs()
     print(json.dumps(line))
 
 
@@ -482,8 +586,8 @@ def run_secondary(torch, ta, args, sel, line):
         line[f"paged_decode_{kv}"] = {
             "workload": wd.name, "kv_cache": kv, "value": round(nbytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
             "ms": round(ms, 4), "bytes": nbytes, "tokens": tokens,
-            "roofline": roofline_hbm(nbytes, ms, "decode_paged_split_kernel", f"{wd.name}_{kv}",
-                                     "decode_paged_split_kernel + decode_combine_kernel")}
+            "roofline": roofline_hbm(nbytes, ms, "decode_paged_q8_kernel", f"{wd.name}_{kv}",
+                                     "decode_paged_q8_kernel + decode_combine_kernel")}
     if "mla" in sel:
         wm = WORKLOADS["mla_decode_b32"]
         ms = bench_mla(torch, ta, wm, max(20, args.steps), max(300, args.warmup))

@@ -8,7 +8,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "attn.h")
-LIB = os.path.join(ROOT, "transformer_attention_causal_amd", "libattn.so")
+# ATTN_LIB selects another build of the library (e.g. the host-ASan build of the validation code)
+LIB = os.environ.get("ATTN_LIB") or os.path.join(ROOT, "transformer_attention_causal_amd", "libattn.so")
 
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 NULL = None
