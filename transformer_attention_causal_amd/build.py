@@ -27,6 +27,10 @@ HIPCC_FLAGS = [
     "-Wno-unused-result", "-I", os.path.join(ROOT, "include"),
 ]
 
+# Per-source flags. decode.hip: MFMA accumulators in ordinary VGPRs (the multi-head 8-bit kernel otherwise splits
+# its registers over VGPRs and AGPRs, drops to one wave per SIMD, and moves accumulators between the two files).
+SOURCE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 
 def hipcc():
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -37,7 +41,7 @@ def hipcc():
 
 def _compile(src, verbose, extra):
     obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                     if "is not a recognized feature for this target" not in line)

@@ -53,15 +53,200 @@ struct DecodeArgs {
   const int32_t* seq_lens;
   float* ws_o;      // [batch, hq, n_chunks, D]
   float* ws_lse;    // [batch, hq, n_chunks]
-  int hq, hkv, page_shift, max_pages, max_len, n_chunks;
+  int hq, hkv, page_shift, max_pages, max_len, n_chunks, batch;
+  int n_hg;                // KV-head groups (one per wave): hkv / heads per wave
   int64_t num_pages;
   float scale;
 };
 
 __device__ __forceinline__ int clamp_len(int L, int max_len, int cap) { return max(0, min(L, min(max_len, cap))); }
 
+#ifndef ATTN_DECODE_AUX
+#define ATTN_DECODE_AUX 2
+#endif
+#ifndef ATTN_DECODE_XCD_GROUP
+#define ATTN_DECODE_XCD_GROUP 0
+#endif
+// Workgroup -> (KV head g, chunk, sequence b). Default: grid (hkv, n_chunks, batch), head fastest. XCD-grouped: a 1-D
+// grid where consecutive workgroups go to consecutive XCDs (eight), and the hkv heads of one chunk are the
+// consecutive workgroups of one XCD, so each cache row is read whole into one L2.
+__device__ __forceinline__ bool decode_unit(const DecodeArgs& a, int& g, int& chunk, int& b) {
+  if constexpr (ATTN_DECODE_XCD_GROUP) {
+    const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
+    g = j % a.n_hg;
+    const int unit = (j / a.n_hg) * 8 + xcd;
+    if (unit >= a.batch * a.n_chunks) return false;
+    b = unit / a.n_chunks; chunk = unit % a.n_chunks;
+  } else {
+    g = blockIdx.x; chunk = blockIdx.y; b = blockIdx.z;
+  }
+  return true;
+}
+
+// LDS address `byte_off` bytes into a __shared__ buffer, formed in the LDS address space (a cast of the buffer
+// itself, then the offset), so the copy's destination stays a known object the compiler can tell from the others.
+template <class T>
+__device__ __forceinline__ lds_void_t* lds_at(T* buf, int byte_off) {
+  return (lds_void_t*)((__attribute__((address_space(3))) char*)buf + byte_off);
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* buf) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)buf));
+}
+
+// Fragment reads of one block written out in inline assembly, each group ending with its own lgkmcnt(0) wait (the
+// outputs are complete when the statement ends). The compiler's wait insertion cannot tell LDS reads at the head
+// of the ring loop from the copies in flight there and would drain every copy before them; reads it does not
+// see need no such wait, and the ring's own vmcnt wait orders them after their block's copies.
+// bf16 block, K: kf[tb][ks] at ka[ks] + tb * 32 * D (16 rows of 2D bytes).
+template <int D>
+__device__ __forceinline__ void bf16_k_reads(const uint32_t (&ka)[D / 32], u32x4_t (&kf)[2][D / 32]) {
+  if constexpr (D == 128) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\tds_read_b128 %3, %11\n\t"
+        "ds_read_b128 %4, %8 offset:%12\n\tds_read_b128 %5, %9 offset:%12\n\t"
+        "ds_read_b128 %6, %10 offset:%12\n\tds_read_b128 %7, %11 offset:%12\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(kf[0][0]), "=&v"(kf[0][1]), "=&v"(kf[0][2]), "=&v"(kf[0][3]), "=&v"(kf[1][0]), "=&v"(kf[1][1]),
+          "=&v"(kf[1][2]), "=&v"(kf[1][3])
+        : "v"(ka[0]), "v"(ka[1]), "v"(ka[2]), "v"(ka[3]), "n"(32 * D)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %4 offset:%6\n\tds_read_b128 %3, %5 offset:%6\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(kf[0][0]), "=&v"(kf[0][1]), "=&v"(kf[1][0]), "=&v"(kf[1][1])
+        : "v"(ka[0]), "v"(ka[1]), "n"(32 * D)
+        : "memory");
+  }
+}
+// bf16 block, V^T: vf[db] = transposing reads at va[db] (keys 0-15) and va[db] + 32 * D (keys 16-31).
+template <int D>
+__device__ __forceinline__ void bf16_v_reads(const uint32_t (&va)[D / 16], u32x4_t (&vf)[D / 16]) {
+  u32x2_t lo[D / 16], hi[D / 16];
+  if constexpr (D == 128) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %16\n\tds_read_b64_tr_b16 %1, %17\n\tds_read_b64_tr_b16 %2, %18\n\t"
+        "ds_read_b64_tr_b16 %3, %19\n\tds_read_b64_tr_b16 %4, %20\n\tds_read_b64_tr_b16 %5, %21\n\t"
+        "ds_read_b64_tr_b16 %6, %22\n\tds_read_b64_tr_b16 %7, %23\n\t"
+        "ds_read_b64_tr_b16 %8, %16 offset:%24\n\tds_read_b64_tr_b16 %9, %17 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %10, %18 offset:%24\n\tds_read_b64_tr_b16 %11, %19 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %12, %20 offset:%24\n\tds_read_b64_tr_b16 %13, %21 offset:%24\n\t"
+        "ds_read_b64_tr_b16 %14, %22 offset:%24\n\tds_read_b64_tr_b16 %15, %23 offset:%24\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(lo[4]), "=&v"(lo[5]), "=&v"(lo[6]),
+          "=&v"(lo[7]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]), "=&v"(hi[3]), "=&v"(hi[4]), "=&v"(hi[5]),
+          "=&v"(hi[6]), "=&v"(hi[7])
+        : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "v"(va[4]), "v"(va[5]), "v"(va[6]), "v"(va[7]),
+          "n"(32 * D)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\tds_read_b64_tr_b16 %2, %10\n\t"
+        "ds_read_b64_tr_b16 %3, %11\n\tds_read_b64_tr_b16 %4, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %9 offset:%12\n\tds_read_b64_tr_b16 %6, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%12\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3]), "=&v"(hi[0]), "=&v"(hi[1]), "=&v"(hi[2]),
+          "=&v"(hi[3])
+        : "v"(va[0]), "v"(va[1]), "v"(va[2]), "v"(va[3]), "n"(32 * D)
+        : "memory");
+  }
+#pragma unroll
+  for (int db = 0; db < D / 16; ++db) vf[db] = u32x4_t{lo[db][0], lo[db][1], hi[db][0], hi[db][1]};
+}
+// 8-bit block of one head (rows of RL bytes): K pieces kv8[tb][hk] at ka[hk] + tb * 16 * RL; V rows vv8[s] at
+// va + (16 * (s / 4) + s % 4) * RL.
+template <int D, int RL>
+__device__ __forceinline__ void q8_reads(const uint32_t (&ka)[D / 64], uint32_t va, u32x4_t (&kv8)[2][D / 64],
+                                         u32x2_t (&vv8)[8]) {
+  if constexpr (D == 128) {
+    asm volatile(
+        "ds_read_b128 %0, %12\n\tds_read_b128 %1, %12 offset:%15\n\t"
+        "ds_read_b128 %2, %13\n\tds_read_b128 %3, %13 offset:%15\n\t"
+        "ds_read_b64 %4, %14\n\tds_read_b64 %5, %14 offset:%16\n\t"
+        "ds_read_b64 %6, %14 offset:%17\n\tds_read_b64 %7, %14 offset:%18\n\t"
+        "ds_read_b64 %8, %14 offset:%15\n\tds_read_b64 %9, %14 offset:%19\n\t"
+        "ds_read_b64 %10, %14 offset:%20\n\tds_read_b64 %11, %14 offset:%21\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kv8[0][0]), "=&v"(kv8[1][0]), "=&v"(kv8[0][1]), "=&v"(kv8[1][1]), "=&v"(vv8[0]), "=&v"(vv8[1]),
+          "=&v"(vv8[2]), "=&v"(vv8[3]), "=&v"(vv8[4]), "=&v"(vv8[5]), "=&v"(vv8[6]), "=&v"(vv8[7])
+        : "v"(ka[0]), "v"(ka[1]), "v"(va), "n"(16 * RL), "n"(RL), "n"(2 * RL), "n"(3 * RL), "n"(17 * RL),
+          "n"(18 * RL), "n"(19 * RL)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %10\n\tds_read_b128 %1, %10 offset:%12\n\t"
+        "ds_read_b64 %2, %11\n\tds_read_b64 %3, %11 offset:%13\n\t"
+        "ds_read_b64 %4, %11 offset:%14\n\tds_read_b64 %5, %11 offset:%15\n\t"
+        "ds_read_b64 %6, %11 offset:%12\n\tds_read_b64 %7, %11 offset:%16\n\t"
+        "ds_read_b64 %8, %11 offset:%17\n\tds_read_b64 %9, %11 offset:%18\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(kv8[0][0]), "=&v"(kv8[1][0]), "=&v"(vv8[0]), "=&v"(vv8[1]), "=&v"(vv8[2]), "=&v"(vv8[3]),
+          "=&v"(vv8[4]), "=&v"(vv8[5]), "=&v"(vv8[6]), "=&v"(vv8[7])
+        : "v"(ka[0]), "v"(va), "n"(16 * RL), "n"(RL), "n"(2 * RL), "n"(3 * RL), "n"(17 * RL), "n"(18 * RL), "n"(19 * RL)
+        : "memory");
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmem_n() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// Copy ring over the 32-key blocks of a chunk, NB buffers deep: while block u is read and computed, the copies of
+// blocks u+1 .. u+NB-2 are in flight (NB-1 blocks are issued before the first is used). Every block index gets its
+// copies, also past the chunk end (they have no rows: zeros, no memory access), so the number of copy
+// instructions issued after block u is always (NB-2) * kPerBlock and one immediate vmcnt wait covers it.
+// copy(buffer, t0) issues kPerBlock copies; read(buffer) takes the block's fragments from LDS into registers
+// before the buffer of the previous block is refilled; compute(buffer, t0) does the block's products.
+template <int NB, int kPerBlock, int I = 0, class Copy, class Read, class Compute>
+__device__ __forceinline__ bool ring_stage(int t, int t_end, Copy& copy, Read& read, Compute& compute) {
+  if constexpr (I == NB) {
+    return true;
+  } else {
+    if (t >= t_end) return false;
+    wait_vmem_n<(NB - 2) * kPerBlock>();
+    read(std::integral_constant<int, I>{});
+    __builtin_amdgcn_sched_barrier(0);                 // the reads are issued before the buffer refill
+    copy(std::integral_constant<int, (I + NB - 1) % NB>{}, t + 32 * (NB - 1));
+    compute(std::integral_constant<int, I>{}, t);
+    return ring_stage<NB, kPerBlock, I + 1>(t + 32, t_end, copy, read, compute);
+  }
+}
+template <int NB, int kPerBlock, int I = 0, class Copy>
+__device__ __forceinline__ void ring_prologue(int t_begin, Copy& copy) {
+  if constexpr (I < NB - 1) {
+    copy(std::integral_constant<int, I>{}, t_begin + 32 * I);
+    ring_prologue<NB, kPerBlock, I + 1>(t_begin, copy);
+  }
+}
+template <int NB, int kPerBlock, class Copy, class Read, class Compute>
+__device__ __forceinline__ void block_ring(int t_begin, int t_end, Copy& copy, Read& read, Compute& compute) {
+  static_assert(NB >= 2 && (NB - 2) * kPerBlock <= 63, "ring depth within the vmcnt range");
+  ring_prologue<NB, kPerBlock>(t_begin, copy);
+  for (int t0 = t_begin; ring_stage<NB, kPerBlock>(t0, t_end, copy, read, compute); t0 += 32 * NB) {
+  }
+  wait_vmem_n<0>();        // the trailing empty copies have landed before the wave ends
+}
+
+// LDS buffer i of a ring (compile-time index): separate objects, so the compiler can tell a buffer being read
+// from the ones with copies in flight. Unused buffers are not allocated.
+#define ATTN_RING_BUFFERS(T, name, n)                                                                              \
+  __shared__ __attribute__((aligned(16))) T name##0[n], name##1[n], name##2[n], name##3[n], name##4[n], name##5[n]; \
+  auto name = [&](auto i) -> T* {                                                                                  \
+    constexpr int k = decltype(i)::value;                                                                          \
+    static_assert(k < 6, "at most six ring buffers");                                                              \
+    if constexpr (k == 0) return name##0;                                                                          \
+    else if constexpr (k == 1) return name##1;                                                                     \
+    else if constexpr (k == 2) return name##2;                                                                     \
+    else if constexpr (k == 3) return name##3;                                                                     \
+    else if constexpr (k == 4) return name##4;                                                                     \
+    else return name##5;                                                                                           \
+  };
+
+#ifndef ATTN_DECODE_RING_BF16
+#define ATTN_DECODE_RING_BF16 2
+#endif
+#ifndef ATTN_DECODE_RING_Q8
+#define ATTN_DECODE_RING_Q8 2
+#endif
 
 // Element j (0..7) of each of the 8 rows in vv, packed in row order: the A operand for dimension offset j.
 __device__ __forceinline__ bf16x8_t transpose_pick(const u32x4_t* vv, int j) {
@@ -159,9 +344,11 @@ __global__ __launch_bounds__(64) void decode_paged_lds_kernel(DecodeArgs a) {
   constexpr int kDb = D / 16;                // 16-dim row blocks of O^T
   // One LDS array per buffer and tensor: distinct objects, so the compiler can see that a block's copies in
   // flight do not alias the buffer being read, and keeps its waits at the block boundary.
-  __shared__ __attribute__((aligned(16))) uint16_t kl0[32 * D], kl1[32 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vl0[32 * D], vl1[32 * D];
-  const int g = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
+  constexpr int NB = ATTN_DECODE_RING_BF16;
+  ATTN_RING_BUFFERS(uint16_t, kl, 32 * D)
+  ATTN_RING_BUFFERS(uint16_t, vl, 32 * D)
+  int g, chunk, b;
+  if (!decode_unit(a, g, chunk, b)) return;
   Chunk ck;
   if (!load_chunk(a, b, chunk, ck)) return;
   const int t_begin = ck.t_begin, t_end = ck.t_end;
@@ -205,10 +392,10 @@ __global__ __launch_bounds__(64) void decode_paged_lds_kernel(DecodeArgs a) {
       const buf_rsrc_t rk = make_buf_rsrc(kcache + e0, uint32_t(rows) * row_bytes);
       const buf_rsrc_t rv = make_buf_rsrc(vcache + e0, uint32_t(rows) * row_bytes);
       const int r = kRowsPerCopy * i + row_in;
-      raw_buffer_load_lds(rk, (lds_void_t*)(kdst + i * 512), 16, int(row_in * row_bytes + 16 * (pcs ^ dec_swz_k<D>(r))),
-                          0, 0, 2);
-      raw_buffer_load_lds(rv, (lds_void_t*)(vdst + i * 512), 16, int(row_in * row_bytes + 16 * (pcs ^ dec_swz_v<D>(r))),
-                          0, 0, 2);
+      raw_buffer_load_lds(rk, lds_at(kdst, 1024 * i), 16, int(row_in * row_bytes + 16 * (pcs ^ dec_swz_k<D>(r))),
+                          0, 0, ATTN_DECODE_AUX);
+      raw_buffer_load_lds(rv, lds_at(vdst, 1024 * i), 16, int(row_in * row_bytes + 16 * (pcs ^ dec_swz_v<D>(r))),
+                          0, 0, ATTN_DECODE_AUX);
     }
   };
   // LDS read addresses (bytes): K row 16*tb + n, chunk 4*ks + grp4; V rows 4*grp4 + j (+16), dims 16*db + 4*(n&3)
@@ -226,16 +413,14 @@ __global__ __launch_bounds__(64) void decode_paged_lds_kernel(DecodeArgs a) {
   // compiler cannot tell the copies from these reads apart and would otherwise wait for the copies first.
   u32x4_t kf[2][kKs], vf[kDb];
   auto read_block = [&](const uint16_t* Kt, const uint16_t* Vt) {
+    const uint32_t kb = lds_addr(Kt), vb = lds_addr(Vt);
+    uint32_t ka[kKs], va[kDb];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+    for (int ks = 0; ks < kKs; ++ks) ka[ks] = kb + kaddr[ks];
 #pragma unroll
-      for (int ks = 0; ks < kKs; ++ks) kf[tb][ks] = lds_read16(Kt, kaddr[ks] + tb * 16 * 2 * D);
-#pragma unroll
-    for (int db = 0; db < kDb; ++db) {
-      const u32x2_t lo = lds_read_tr16(Vt, vaddr[db]);
-      const u32x2_t hi = lds_read_tr16(Vt, vaddr[db] + 16 * 2 * D);
-      vf[db] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-    }
+    for (int db = 0; db < kDb; ++db) va[db] = vb + vaddr[db];
+    bf16_k_reads<D>(ka, kf);
+    bf16_v_reads<D>(va, vf);
   };
   auto block = [&](int t0) {
     f32x4_t sacc[2] = {f32x4_t{}, f32x4_t{}};
@@ -248,21 +433,11 @@ __global__ __launch_bounds__(64) void decode_paged_lds_kernel(DecodeArgs a) {
     for (int db = 0; db < kDb; ++db) oacc[db] = mfma16x16x32(as_bf16x8(vf[db]), pb, oacc[db]);
   };
 
-  // Ring of two blocks: at block u, wait for its copies, read its fragments, issue the copies of block u + 1 into
-  // the other buffer, and compute.
   wait_vmem_n<0>();        // q and the page numbers are in: from here on only block copies are outstanding
-  copy_block(kl0, vl0, t_begin);
-  for (int t0 = t_begin; t0 < t_end; t0 += 64) {
-    wait_vmem_n<0>();
-    read_block(kl0, vl0);
-    if (t0 + 32 < t_end) copy_block(kl1, vl1, t0 + 32);
-    block(t0);
-    if (t0 + 32 >= t_end) break;
-    wait_vmem_n<0>();
-    read_block(kl1, vl1);
-    if (t0 + 64 < t_end) copy_block(kl0, vl0, t0 + 64);
-    block(t0 + 32);
-  }
+  auto copy_i = [&](auto i, int t0) { copy_block(kl(i), vl(i), t0); };
+  auto read_i = [&](auto i) { read_block(kl(i), vl(i)); };
+  auto compute_i = [&](auto, int t0) { block(t0); };
+  block_ring<NB, 2 * kCopies>(t_begin, t_end, copy_i, read_i, compute_i);
 
   float lt = l + xor_lanes(l, 16);
   lt += xor_lanes(lt, 32);
@@ -288,44 +463,64 @@ __device__ __forceinline__ int dec_swz8(int r) {
   return D == 128 ? (((r >> 1) & 3) | (((r >> 3) & 1) << 2)) : ((r >> 2) & 3);
 }
 
-template <int KV, int D>
+// K chunk swizzle of the 8-bit rows: one head per wave keeps the 128- or 64-byte rows above; rows of 256 bytes or
+// more (several heads) take chunk c of row r at c ^ (r & 15), conflict-free by the same count as the bf16 rows.
+template <int D, int HPW>
+__device__ __forceinline__ int q8_swz(int r) {
+  if constexpr (HPW == 1) return dec_swz8<D>(r);
+  else return r & 15;
+}
+
+template <int KV, int D, int HPW>
 __global__ __launch_bounds__(64) void decode_paged_q8_kernel(DecodeArgs a) {
   static_assert(D == 128 || D == 64, "head dim");
-  constexpr int kCh = D / 16;                // 16-byte chunks per row of codes
+  constexpr int RL = HPW * D;                // bytes of one key's codes for the wave's HPW heads (one LDS row)
+  static_assert(HPW == 1 || RL >= 256, "several heads per wave take rows of at least 256 bytes");
+  constexpr int kCh = RL / 16;               // 16-byte chunks per row
   constexpr int kRowsPerCopy = 64 / kCh;     // rows per 1 KiB copy instruction
   constexpr int kCopies = 32 / kRowsPerCopy; // copy instructions per tensor per block
   constexpr int kKs = D / 32;                // k-steps of S^T = K Q^T
-  constexpr int kHk = D / 64;                // 16-byte K pieces per lane and key
-  __shared__ __attribute__((aligned(16))) uint8_t k8a[32 * D], k8b[32 * D], v8a[32 * D], v8b[32 * D];
-  const int g = blockIdx.x, chunk = blockIdx.y, b = blockIdx.z;
+  constexpr int kHk = D / 64;                // 16-byte K pieces per lane, key and head
+  constexpr int NB = ATTN_DECODE_RING_Q8;
+  ATTN_RING_BUFFERS(uint8_t, k8, 32 * RL)
+  ATTN_RING_BUFFERS(uint8_t, v8, 32 * RL)
+  int gw, chunk, b;
+  if (!decode_unit(a, gw, chunk, b)) return;
+  const int g0 = gw * HPW;                   // the wave's first KV head
   Chunk ck;
   if (!load_chunk(a, b, chunk, ck)) return;
   const int t_begin = ck.t_begin, t_end = ck.t_end;
   const int lane = threadIdx.x, n = lane & 15, grp4 = lane >> 4;
   const int G = a.hq / a.hkv;
-  const int h = g * G + n;
   const bool hv = n < G;
   const float c = a.scale * kLog2e;
   const int page_size = 1 << a.page_shift;
 
-  // Q^T operand: lane holds head n, dims kdim(ks) .. +7 for k-step ks, times the K scale.
+  // Q^T operand per head: lane holds query head n of KV head g0 + e, dims kdim(ks) .. +7 for k-step ks, times the
+  // K scale.
   auto kdim = [&](int ks) { return 64 * (ks >> 1) + 16 * grp4 + 8 * (ks & 1); };
-  bf16x8_t qop[kKs];
+  bf16x8_t qop[HPW][kKs];
 #pragma unroll
-  for (int ks = 0; ks < kKs; ++ks) {
-    u32x4_t w = {0u, 0u, 0u, 0u};
-    if (hv) w = *reinterpret_cast<const u32x4_t*>(a.q + (int64_t(b) * a.hq + h) * D + kdim(ks));
-    const float* ks_p = a.k_scale + g * D + kdim(ks);
-    w = u32x4_t{pack_bf16x2(bf16lo_to_f32(w[0]) * ks_p[0], bf16hi_to_f32(w[0]) * ks_p[1]),
-                pack_bf16x2(bf16lo_to_f32(w[1]) * ks_p[2], bf16hi_to_f32(w[1]) * ks_p[3]),
-                pack_bf16x2(bf16lo_to_f32(w[2]) * ks_p[4], bf16hi_to_f32(w[2]) * ks_p[5]),
-                pack_bf16x2(bf16lo_to_f32(w[3]) * ks_p[6], bf16hi_to_f32(w[3]) * ks_p[7])};
-    qop[ks] = as_bf16x8(w);
+  for (int e = 0; e < HPW; ++e)
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) {
+      u32x4_t w = {0u, 0u, 0u, 0u};
+      if (hv) w = *reinterpret_cast<const u32x4_t*>(a.q + (int64_t(b) * a.hq + (g0 + e) * G + n) * D + kdim(ks));
+      const float* ks_p = a.k_scale + (g0 + e) * D + kdim(ks);
+      w = u32x4_t{pack_bf16x2(bf16lo_to_f32(w[0]) * ks_p[0], bf16hi_to_f32(w[0]) * ks_p[1]),
+                  pack_bf16x2(bf16lo_to_f32(w[1]) * ks_p[2], bf16hi_to_f32(w[1]) * ks_p[3]),
+                  pack_bf16x2(bf16lo_to_f32(w[2]) * ks_p[4], bf16hi_to_f32(w[2]) * ks_p[5]),
+                  pack_bf16x2(bf16lo_to_f32(w[3]) * ks_p[6], bf16hi_to_f32(w[3]) * ks_p[7])};
+      qop[e][ks] = as_bf16x8(w);
+    }
+  f32x4_t oacc[HPW][8];                                  // O^T: lane holds head n, dims 8*(4*grp4 + r) + j
+  float m[HPW], l[HPW];
+#pragma unroll
+  for (int e = 0; e < HPW; ++e) {
+    m[e] = -INFINITY; l[e] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) oacc[e][j] = f32x4_t{};
   }
-  f32x4_t oacc[8];                                       // O^T: lane holds head n, dims 8*(4*grp4 + r) + j
-#pragma unroll
-  for (int j = 0; j < 8; ++j) oacc[j] = f32x4_t{};
-  float m = -INFINITY, l = 0.f;
   const int64_t row_stride = int64_t(a.hkv) * D;       // bytes between consecutive slots of a page
   const int64_t page_stride = int64_t(page_size) * row_stride;
   const uint8_t* kcache = static_cast<const uint8_t*>(a.kc);
@@ -341,85 +536,87 @@ __global__ __launch_bounds__(64) void decode_paged_q8_kernel(DecodeArgs a) {
       const bool pv = pg >= 0 && pg < a.num_pages;
       const int rows = pv ? max(0, min(kRowsPerCopy, t_end - key_first)) : 0;
       const int64_t e0 = int64_t(max(pg, 0)) * page_stride + int64_t(key_first & (page_size - 1)) * row_stride +
-                         int64_t(g) * D;
+                         int64_t(g0) * D;
       const buf_rsrc_t rk = make_buf_rsrc(kcache + e0, uint32_t(rows) * row_bytes);
       const buf_rsrc_t rv = make_buf_rsrc(vcache + e0, uint32_t(rows) * row_bytes);
       const int r = kRowsPerCopy * i + row_in;
-      raw_buffer_load_lds(rk, (lds_void_t*)(kdst + i * 1024), 16, int(row_in * row_bytes + 16 * (pcs ^ dec_swz8<D>(r))),
-                          0, 0, 2);
-      raw_buffer_load_lds(rv, (lds_void_t*)(vdst + i * 1024), 16, int(row_in * row_bytes + 16 * pcs), 0, 0, 2);
+      raw_buffer_load_lds(rk, lds_at(kdst, 1024 * i), 16, int(row_in * row_bytes + 16 * (pcs ^ q8_swz<D, HPW>(r))),
+                          0, 0, ATTN_DECODE_AUX);
+      raw_buffer_load_lds(rv, lds_at(vdst, 1024 * i), 16, int(row_in * row_bytes + 16 * pcs), 0, 0, ATTN_DECODE_AUX);
     }
   };
-  // K of key 16*tb + n as 16-byte pieces (dims 64*hk + 16*grp4 ..), V rows of keys 16*(s/4) + 4*grp4 + s%4 as
-  // 8 bytes (dims 8*n' .. 8*n' + 7, n' = n mod D/8).
-  u32x4_t kv8[2][kHk];
-  u32x2_t vv8[8];
-  auto read8 = [&](const uint8_t* ks, const uint8_t* vs) {
+  // Head e's K of key 16*tb + n as 16-byte pieces (dims 64*hk + 16*grp4 ..), its V rows of keys
+  // 16*(s/4) + 4*grp4 + s%4 as 8 bytes (dims 8*n' .. 8*n' + 7, n' = n mod D/8). The swizzle of row 16*tb + n is
+  // that of row n, so tb is an immediate offset.
+  uint32_t ko[HPW][kHk], vo[HPW];
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
+  for (int e = 0; e < HPW; ++e) {
 #pragma unroll
-      for (int hk = 0; hk < kHk; ++hk) {
-        const int r = 16 * tb + n;
-        kv8[tb][hk] = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
-            (const __attribute__((address_space(3))) uint8_t*)ks + r * D + 16 * ((4 * hk + grp4) ^ dec_swz8<D>(r)));
-      }
+    for (int hk = 0; hk < kHk; ++hk)
+      ko[e][hk] = uint32_t(n * RL + 16 * ((e * (D / 16) + 4 * hk + grp4) ^ q8_swz<D, HPW>(n)));
+    vo[e] = uint32_t(4 * grp4 * RL + e * D + 8 * (n % (D / 8)));
+  }
+  // The fragments are read head by head inside the block step (inline-assembly reads, invisible to the compiler's
+  // wait insertion): the copies issued just before target another buffer.
+  auto block = [&](auto bufc, int t0) {
+    const uint32_t kb = lds_addr(k8(bufc)), vb = lds_addr(v8(bufc));
 #pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) {
-      const int r = 16 * (s2 >> 2) + 4 * grp4 + (s2 & 3);
-      vv8[s2] = *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>(
-          (const __attribute__((address_space(3))) uint8_t*)vs + r * D + 8 * (n % (D / 8)));
+    for (int e = 0; e < HPW; ++e) {
+      u32x4_t kv8[2][kHk];
+      u32x2_t vv8[8];
+      uint32_t ka[kHk];
+#pragma unroll
+      for (int hk = 0; hk < kHk; ++hk) ka[hk] = kb + ko[e][hk];
+      q8_reads<D, RL>(ka, vb + vo[e], kv8, vv8);
+      u32x4_t kv[2][kKs], vv[8];
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks)
+          kv[tb][ks] = codes_to_bf16x8<KV>(kv8[tb][ks >> 1][2 * (ks & 1)], kv8[tb][ks >> 1][2 * (ks & 1) + 1]);
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2) vv[s2] = codes_to_bf16x8<KV>(vv8[s2][0], vv8[s2][1]);
+      f32x4_t sacc[2] = {f32x4_t{}, f32x4_t{}};
+#pragma unroll
+      for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) sacc[tb] = mfma16x16x32(as_bf16x8(kv[tb][ks]), qop[e][ks], sacc[tb]);
+      const bf16x8_t pb = softmax_block<8>(sacc, oacc[e], m[e], l[e], t0, t_end, grp4, c);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) oacc[e][j] = mfma16x16x32(transpose_pick(vv, j), pb, oacc[e][j]);
+      __builtin_amdgcn_sched_barrier(0);             // one head's fragments live at a time
     }
-  };
-  auto block = [&](int t0) {
-    u32x4_t kv[2][kKs], vv[8];
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int ks = 0; ks < kKs; ++ks)
-        kv[tb][ks] = codes_to_bf16x8<KV>(kv8[tb][ks >> 1][2 * (ks & 1)], kv8[tb][ks >> 1][2 * (ks & 1) + 1]);
-#pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) vv[s2] = codes_to_bf16x8<KV>(vv8[s2][0], vv8[s2][1]);
-    f32x4_t sacc[2] = {f32x4_t{}, f32x4_t{}};
-#pragma unroll
-    for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-      for (int ks = 0; ks < kKs; ++ks) sacc[tb] = mfma16x16x32(as_bf16x8(kv[tb][ks]), qop[ks], sacc[tb]);
-    const bf16x8_t pb = softmax_block<8>(sacc, oacc, m, l, t0, t_end, grp4, c);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) oacc[j] = mfma16x16x32(transpose_pick(vv, j), pb, oacc[j]);
   };
 
   wait_vmem_n<0>();        // q, scales and the page numbers are in: from here on only block copies are outstanding
-  copy8(k8a, v8a, t_begin);
-  for (int t0 = t_begin; t0 < t_end; t0 += 64) {
-    wait_vmem_n<0>();
-    read8(k8a, v8a);                                   // block t0 into registers before the next copies
-    if (t0 + 32 < t_end) copy8(k8b, v8b, t0 + 32);
-    block(t0);
-    if (t0 + 32 >= t_end) break;
-    wait_vmem_n<0>();
-    read8(k8b, v8b);
-    if (t0 + 64 < t_end) copy8(k8a, v8a, t0 + 64);
-    block(t0 + 32);
-  }
+  auto copy_i = [&](auto i, int t0) { copy8(k8(i), v8(i), t0); };
+  auto read_i = [&](auto) {};
+  block_ring<NB, 2 * kCopies>(t_begin, t_end, copy_i, read_i, block);
 
-  // partial result: O / l and lse for this chunk (lane holds head n, dims 8*(4*grp4 + r) + j)
-  float lt = l + xor_lanes(l, 16);
-  lt += xor_lanes(lt, 32);
-  if (!hv || 4 * grp4 >= D / 8) return;
-  const int64_t slot = (int64_t(b) * a.hq + h) * a.n_chunks + chunk;
-  const float inv = 1.f / lt;
-  float* wo = a.ws_o + slot * D;
+  // partial results: O / l and lse for this chunk (lane holds head n, dims 8*(4*grp4 + r) + j)
+  float lt[HPW];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int d0 = 8 * (4 * grp4 + r);
-    const f32x4_t* vs = reinterpret_cast<const f32x4_t*>(a.v_scale + g * D + d0);     // per-channel V scale
-    const f32x4_t lo = f32x4_t{oacc[0][r], oacc[1][r], oacc[2][r], oacc[3][r]} * inv * vs[0];
-    const f32x4_t hi = f32x4_t{oacc[4][r], oacc[5][r], oacc[6][r], oacc[7][r]} * inv * vs[1];
-    *reinterpret_cast<f32x4_t*>(wo + d0) = lo;
-    *reinterpret_cast<f32x4_t*>(wo + d0 + 4) = hi;
+  for (int e = 0; e < HPW; ++e) {
+    lt[e] = l[e] + xor_lanes(l[e], 16);
+    lt[e] += xor_lanes(lt[e], 32);
   }
-  if (grp4 == 0) a.ws_lse[slot] = m * a.scale + logf(lt);
+  if (!hv || 4 * grp4 >= D / 8) return;
+#pragma unroll
+  for (int e = 0; e < HPW; ++e) {
+    const int64_t slot = (int64_t(b) * a.hq + (g0 + e) * G + n) * a.n_chunks + chunk;
+    const float inv = 1.f / lt[e];
+    float* wo = a.ws_o + slot * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int d0 = 8 * (4 * grp4 + r);
+      const f32x4_t* vs = reinterpret_cast<const f32x4_t*>(a.v_scale + (g0 + e) * D + d0);   // per-channel V scale
+      const f32x4_t lo = f32x4_t{oacc[e][0][r], oacc[e][1][r], oacc[e][2][r], oacc[e][3][r]} * inv * vs[0];
+      const f32x4_t hi = f32x4_t{oacc[e][4][r], oacc[e][5][r], oacc[e][6][r], oacc[e][7][r]} * inv * vs[1];
+      *reinterpret_cast<f32x4_t*>(wo + d0) = lo;
+      *reinterpret_cast<f32x4_t*>(wo + d0 + 4) = hi;
+    }
+    if (grp4 == 0) a.ws_lse[slot] = m[e] * a.scale + logf(lt[e]);
+  }
 }
 
 // Merge the chunks of one (sequence, query head): M = max lse_c, w_c = exp(lse_c - M),
@@ -464,11 +661,36 @@ size_t decode_paged_workspace_bytes(int batch, int hq, int head_dim, int max_seq
 }
 
 namespace {
+#ifndef ATTN_DECODE_Q8_HPW
+#define ATTN_DECODE_Q8_HPW 2
+#endif
+template <class Kernel>
+void launch_grid(Kernel kernel, DecodeArgs a, int hpw, hipStream_t stream) {
+  a.n_hg = a.hkv / hpw;
+  const unsigned n_units = unsigned(a.batch) * unsigned(a.n_chunks);
+  const dim3 grid = ATTN_DECODE_XCD_GROUP ? dim3{((n_units + 7u) / 8u) * 8u * unsigned(a.n_hg), 1u, 1u}
+                                          : dim3{unsigned(a.n_hg), unsigned(a.n_chunks), unsigned(a.batch)};
+  kernel<<<grid, dim3(64), 0, stream>>>(a);   // head-major: the head groups of one chunk are consecutive
+}
+
+// FP8 caches: a wave takes several KV heads when that makes its rows at least 256 bytes. Measured on the 64-sequence
+// workload: FP8 at head dim 128 streams 4.95 TB/s with one head per wave (128-byte rows) and 5.10 with two; at head
+// dim 64, 2.94 with one and 3.59 with four. Int8 stays at one head per wave: its code conversion takes more
+// instructions, and with the fewer waves per CU of the multi-head kernel it ran slower (3.45 vs 4.77 TB/s at 128).
+template <int KV, int D>
+void launch_q8(const DecodeArgs& a, hipStream_t stream) {
+  constexpr int H = KV == kKvInt8 ? 1 : D == 128 ? ATTN_DECODE_Q8_HPW : 4;
+  if constexpr (H > 1) {
+    if (a.hkv % H == 0) return launch_grid(decode_paged_q8_kernel<KV, D, H>, a, H, stream);
+  }
+  launch_grid(decode_paged_q8_kernel<KV, D, 1>, a, 1, stream);
+}
+
 template <int D>
-void launch_split(int kind, const DecodeArgs& a, dim3 grid, hipStream_t stream) {
-  if (kind == kKvFp8) decode_paged_q8_kernel<kKvFp8, D><<<grid, dim3(64), 0, stream>>>(a);
-  else if (kind == kKvInt8) decode_paged_q8_kernel<kKvInt8, D><<<grid, dim3(64), 0, stream>>>(a);
-  else decode_paged_lds_kernel<D><<<grid, dim3(64), 0, stream>>>(a);
+void launch_split(int kind, const DecodeArgs& a, hipStream_t stream) {
+  if (kind == kKvFp8) launch_q8<kKvFp8, D>(a, stream);
+  else if (kind == kKvInt8) launch_q8<kKvInt8, D>(a, stream);
+  else launch_grid(decode_paged_lds_kernel<D>, a, 1, stream);
 }
 
 hipError_t launch_decode(int kind, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
@@ -492,10 +714,10 @@ hipError_t launch_decode(int kind, const void* q, const void* k_cache, const voi
   while ((1 << shift) < page_size) ++shift;
   a.page_shift = shift; a.max_pages = max_pages_per_seq; a.max_len = max_seqlen_kv; a.n_chunks = n_chunks;
   a.num_pages = num_pages; a.scale = scale;
-  const dim3 grid{unsigned(hkv), unsigned(n_chunks), unsigned(batch)};     // head-major
+  a.batch = batch;
   if (max_seqlen_kv > 0) {
-    if (head_dim == 64) launch_split<64>(kind, a, grid, stream);
-    else launch_split<128>(kind, a, grid, stream);
+    if (head_dim == 64) launch_split<64>(kind, a, stream);
+    else launch_split<128>(kind, a, stream);
   }
   decode_combine_kernel<<<dim3(unsigned(hq), unsigned(batch)), dim3(unsigned(head_dim)), 0, stream>>>(
       a.ws_o, a.ws_lse, seq_lens, static_cast<uint16_t*>(o), lse, hq, head_dim, n_chunks, max_seqlen_kv,

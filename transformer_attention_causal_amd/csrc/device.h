@@ -94,6 +94,16 @@ __device__ __forceinline__ u32x4_t lds_read16(const uint16_t* __restrict__ lds_b
   return *(const __attribute__((address_space(3))) u32x4_t*)((const __attribute__((address_space(3))) char*)lds_base +
                                                                 byte_off);
 }
+__device__ __forceinline__ u32x4_t lds_read16(const uint8_t* __restrict__ lds_base, uint32_t byte_off) {
+  return *(const __attribute__((address_space(3))) u32x4_t*)((const __attribute__((address_space(3))) char*)lds_base +
+                                                                byte_off);
+}
+
+// 8-byte LDS read.
+__device__ __forceinline__ u32x2_t lds_read8(const uint8_t* __restrict__ lds_base, uint32_t byte_off) {
+  return *(const __attribute__((address_space(3))) u32x2_t*)((const __attribute__((address_space(3))) char*)lds_base +
+                                                                byte_off);
+}
 
 // Transposing 8-byte LDS read (see the layout note at the top of this file).
 __device__ __forceinline__ u32x2_t lds_read_tr16(const uint16_t* __restrict__ lds_base, uint32_t byte_off) {

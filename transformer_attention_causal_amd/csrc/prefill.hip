@@ -62,6 +62,16 @@ static_assert(kBN == 32 || kBN == 64, "tile of 32 or 64 keys");
 #ifndef ATTN_PREFILL_QB
 #define ATTN_PREFILL_QB 1
 #endif
+// Software-pipelining depth of the LDS fragment reads in the tile products (fragments read ahead of the MFMA that
+// uses them): K fragments for S^T, pairs of V^T fragment reads for O^T. Measured on the 8192-token GQA prefill:
+// the compiler's own order keeps one K and one V^T fragment in flight (0.975 ms); 3 and 2 give 0.951 ms; deeper
+// runs out of the 168 registers that three waves per SIMD allow.
+#ifndef ATTN_PREFILL_VPRE
+#define ATTN_PREFILL_VPRE 2
+#endif
+#ifndef ATTN_PREFILL_KPRE
+#define ATTN_PREFILL_KPRE 3
+#endif
 #ifndef ATTN_PREFILL_MIN_WAVES_PER_SIMD
 #define ATTN_PREFILL_MIN_WAVES_PER_SIMD 3
 #endif
@@ -475,6 +485,16 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
         for (int qb = 0; qb < QB; ++qb) sacc[qb][kb2] = mfma32x32x16(ka, qop[qb][ks], sacc[qb][kb2]);
       }
     }
+#if ATTN_PREFILL_KPRE > 0
+    // K fragment reads run ATTN_PREFILL_KPRE fragments ahead of the products that use them
+#pragma unroll
+    for (int i = 0; i < ATTN_PREFILL_KPRE; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < KS * kKB2; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      if (i + ATTN_PREFILL_KPRE < KS * kKB2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#endif
 
     // ---- mask. WIN: tiles not visible in full to every query of the wave, by the phase's rule; otherwise only
     // tiles crossing the diagonal or the ragged end
@@ -572,6 +592,16 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
         for (int qb = 0; qb < QB; ++qb) oacc[qb][db] = mfma32x32x16(va, pb[qb][kb], oacc[qb][db]);
       }
     }
+#if ATTN_PREFILL_VPRE > 0
+    // V^T fragment reads (two each) run ATTN_PREFILL_VPRE fragments ahead of the products that use them
+#pragma unroll
+    for (int i = 0; i < ATTN_PREFILL_VPRE; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int i = 0; i < kKB * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      if (i + ATTN_PREFILL_VPRE < kKB * DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+#endif
   };
 
   // All sub-tiles of one LDS tile (compile-time buffer and sub-tile indices, so LDS addresses are immediates);
