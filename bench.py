@@ -177,9 +177,7 @@ def bench_prefill(torch, ta, w, steps, warmup, seed=0, local_global=False, prewa
     kern_ms = timer.mean_ms()
     del q, k, v, o
     torch.cuda.empty_cache()
-    if prewarm_s > 0:
-        return wall_ms, kern_ms, prewarm
-    return wall_ms, kern_ms
+    return wall_ms, kern_ms, prewarm
 
 
 # ---------------------------------------------------------------------------------------------- paged decode --
@@ -610,7 +608,7 @@ def run_secondary(torch, ta, args, sel, line):
                                          "mla_split_kernel + mla_combine_kernel")}
     if "long" in sel:
         wl = WORKLOADS["gqa_prefill_s131072"]
-        wall_l, kern_l = bench_prefill(torch, ta, wl, 2, 1)
+        wall_l, kern_l, _ = bench_prefill(torch, ta, wl, 2, 1)
         line["long_prefill"] = {"workload": wl.name, "value": round(wl.flops / (wall_l * 1e-3) / 1e12, 2),
                                 "unit": "TFLOP/s", "ms_per_step": round(wall_l, 3),
                                 "roofline": roofline_compute(wl.flops, kern_l, "prefill_bf16_kernel", wl.name)}
@@ -624,7 +622,7 @@ def run_secondary(torch, ta, args, sel, line):
                                    "roofline": roofline_compute(wc.flops, kern_c, "prefill_bf16_kernel", wc.name)}
     if "swa" in sel:
         wsw = WORKLOADS["swa_prefill_s131072"]
-        wall_w, kern_w = bench_prefill(torch, ta, wsw, 5, 2, local_global=True)
+        wall_w, kern_w, _ = bench_prefill(torch, ta, wsw, 5, 2, local_global=True)
         line["local_global_prefill"] = {
             "workload": wsw.name, "value": round(wsw.flops / (wall_w * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
             "ms_per_step": round(wall_w, 3), "window": wsw.window, "n_lead": wsw.n_lead,
