@@ -34,9 +34,12 @@ def run_oracle(w, inp):
 
 
 @pytest.mark.parametrize("kind", ["fp8", "int8"])
+# FP8 waves take two KV heads at head dim 128 (four at 64) when the KV head count divides, one otherwise; int8
+# always one. The cases cover both forms at both head dims: odd KV head counts (12/3, 5/5 at 128) and a count that
+# 4 does not divide (8/2 at 64) fall back to one head per wave.
 @pytest.mark.parametrize("hq,hkv,page,d", [(32, 8, 64, 128), (32, 8, 16, 128), (32, 2, 128, 128), (8, 8, 32, 128),
-                                         (12, 4, 64, 128), (32, 8, 64, 64), (32, 8, 16, 64), (16, 1, 128, 64),
-                                         (12, 4, 32, 64)])
+                                         (12, 4, 64, 128), (12, 3, 64, 128), (5, 5, 16, 128), (32, 8, 64, 64),
+                                         (32, 8, 16, 64), (16, 1, 128, 64), (12, 4, 32, 64), (8, 2, 64, 64)])
 def test_q8_decode_small(kind, hq, hkv, page, d):
     ta = require_gpu()
     w = dataclasses.replace(WORKLOADS["paged_decode_b64"], hq=hq, hkv=hkv, page_size=page, head_dim=d,
