@@ -78,8 +78,8 @@ typedef enum {
  * are evaluated in fp64 and rounded to fp32, the rotation is fp32, and the results are rounded to `dtype`.
  * Errors: INVALID_ARG for NULL x/positions (with n_tokens > 0), odd or non-positive head_dim, n_heads <= 0,
  * theta <= 1 or non-finite; UNSUPPORTED for head_dim > 1024 or another dtype. */
-int attn_rope_apply(void* x, int dtype, int64_t n_tokens, int n_heads, int head_dim, const int32_t* positions,
-                    double theta, int interleaved, void* stream);
+int attn_rope_apply(void* x, attn_dtype_t dtype, int64_t n_tokens, int n_heads, int head_dim,
+                    const int32_t* positions, double theta, int interleaved, void* stream);
 
 /* Prefill attention: every query position of a batch of sequences attends to the keys of its own sequence.
  * (Attention notes, makinaruto.github.io: "FlashAttention" — intermediates stay on chip, one read and one write
@@ -96,7 +96,7 @@ int attn_rope_apply(void* x, int dtype, int64_t n_tokens, int n_heads, int head_
  * Supported: dtype ATTN_BF16 (bf16 MFMA, fp32 accumulation) or ATTN_FP32 (fp32 throughout), head_dim 64 or
  * 128; anything else is UNSUPPORTED. INVALID_ARG: NULL q/k/v/o (with batch*seqlen > 0), n_heads_q % n_heads_kv
  * != 0, non-positive head counts, bad scale. */
-int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int batch,
+int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, attn_dtype_t dtype, int batch,
                  int seqlen, int n_heads_q, int n_heads_kv, int head_dim, int causal, float softmax_scale,
                  void* stream);
 

@@ -33,7 +33,7 @@ ATTN_EXPORT const char* attn_status_string(int status) {
   }
 }
 
-ATTN_EXPORT int attn_rope_apply(void* x, int dtype, int64_t n_tokens, int n_heads, int head_dim,
+ATTN_EXPORT int attn_rope_apply(void* x, attn_dtype_t dtype, int64_t n_tokens, int n_heads, int head_dim,
                                 const int32_t* positions, double theta, int interleaved, void* stream) {
   if (n_tokens < 0 || n_heads <= 0 || head_dim <= 0 || (head_dim & 1)) return ATTN_ERR_INVALID_ARG;
   if (!std::isfinite(theta) || theta <= 1.0) return ATTN_ERR_INVALID_ARG;
@@ -45,8 +45,8 @@ ATTN_EXPORT int attn_rope_apply(void* x, int dtype, int64_t n_tokens, int n_head
                                       static_cast<hipStream_t>(stream)));
 }
 
-ATTN_EXPORT int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, int dtype, int batch,
-                             int seqlen, int n_heads_q, int n_heads_kv, int head_dim, int causal,
+ATTN_EXPORT int attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse, attn_dtype_t dtype,
+                             int batch, int seqlen, int n_heads_q, int n_heads_kv, int head_dim, int causal,
                              float softmax_scale, void* stream) {
   if (batch < 0 || seqlen < 0 || n_heads_q <= 0 || n_heads_kv <= 0 || head_dim <= 0) return ATTN_ERR_INVALID_ARG;
   if (n_heads_q % n_heads_kv != 0 || !valid_scale(softmax_scale)) return ATTN_ERR_INVALID_ARG;
