@@ -79,7 +79,10 @@ def test_q8_placement_and_poison_are_invisible(kind, d):
 
 def test_q8_with_unit_scales_matches_bf16_decode():
     """FP8 codes are exact in bf16: with unit scales the 8-bit kernel and the bf16 kernel on the decoded cache agree
-    within the bf16 tolerance (their contraction orders differ)."""
+    to the rounding of their bf16 outputs. Unit scales make the cached values (and outputs) as large as the codes
+    (up to 448), so the bound is relative: two roundings to bf16 of nearly the same value differ by at most one
+    unit in the last place, 2^-7 of the value (2^-6 allowed); the kernels' split sizes and contraction orders
+    differ, so the fp32 results themselves differ slightly. The lse agrees to fp32 summation order (1e-4 relative)."""
     ta = require_gpu()
     w = WORKLOADS["paged_decode_b64"]
     inp = paged_decode_inputs(w, seed=83, seq_lens=[700, 2048, 5], max_len=2048, kv="fp8")
@@ -93,8 +96,15 @@ def test_q8_with_unit_scales_matches_bf16_decode():
     ob, lb = ta.attn_decode_paged(q, dev_bf16(kb), dev_bf16(vb), dev(inp["block_table"]), dev(inp["seq_lens"]),
                                   inp["max_len"], softmax_scale=w.scale, return_lse=True)
     torch.cuda.synchronize()
-    check("q8 vs bf16", bits_to_f32(o8), bits_to_f32(host_bf16(ob)), BF16_MAX, BF16_MEAN)
-    check("lse", l8, lb.cpu().numpy(), BF16_MAX, BF16_MEAN)
+    a, b = bits_to_f32(o8).astype(np.float64), bits_to_f32(host_bf16(ob)).astype(np.float64)
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(b))
+    rel = np.abs(a - b) / np.maximum(np.maximum(np.abs(a), np.abs(b)), 1e-3)
+    say(f"  q8 vs bf16: max relative difference {rel.max():.3e} (max |o| {np.abs(b).max():.1f})")
+    assert rel.max() <= 2.0 ** -6, rel.max()
+    la, lb_ = l8.astype(np.float64), lb.cpu().numpy().astype(np.float64)
+    lrel = np.abs(la - lb_) / np.maximum(np.abs(lb_), 1.0)
+    say(f"  lse: max relative difference {lrel.max():.3e}")
+    assert lrel.max() <= 1e-4, lrel.max()
 
 
 def compact(inp, seqs):
