@@ -8,12 +8,14 @@
 //
 // Decode is HBM-bound (about 4 flop per byte of K/V), so the design goal is to read each K/V byte once, with
 // whole-line copies and enough of them in flight:
-//   * Split kernels: one wave per (logical key chunk, KV head, sequence), launched head-major (the KV heads of one
-//     chunk are consecutive workgroups: they read interleaved head slices of the same page slots at the same time).
-//     The wave serves all query heads of its KV group at once, so every K/V byte is read once. Chunks at or past
-//     the sequence length exit at once.
+//   * Split kernels: one wave per (logical key chunk, KV-head group, sequence), launched head-major (the head
+//     groups of one chunk are consecutive workgroups: they read interleaved head slices of the same page slots at
+//     the same time). The wave serves all query heads of its KV heads at once, so every K/V byte is read once.
+//     Chunks at or past the sequence length exit at once. The chunk size is chosen per launch (2048 keys for bf16
+//     caches when a chunk's pages fit one wave, else 1024).
 //   * K and V blocks are copied global -> LDS with buffer loads carrying the LDS bit (whole head slices,
-//     non-temporal: every cache byte is read once), two blocks in a ring, and the MFMA operands are read from LDS.
+//     non-temporal: every cache byte is read once), in a ring of blocks (two by default), and the MFMA operands
+//     are read from LDS by inline-assembly reads (see block_ring).
 //   * Both products run on v_mfma_f32_16x16x32_bf16 with the group's query heads as the 16-wide N dimension
 //     (heads beyond the group size are zero columns). S^T = K Q^T gives each lane one head and 8 keys; those 8
 //     keys are the contraction slots of its P^T operand, so P^T feeds O^T = V^T P^T from registers.
@@ -31,6 +33,7 @@
 // V scale multiplies the output channels at the end. For the K reads the contraction order over the head dims is
 // permuted (k-steps 2i and 2i+1 of lane group g take dims 64i + 16g .. +15) so a lane reads 16 contiguous bytes;
 // V rows are read 8 bytes per lane and an 8x8 register transpose (byte permutes) turns them into eight A operands.
+// With FP8 codes a wave takes two KV heads at head dim 128 (four at 64), so each copied row piece is 256 bytes.
 //
 // Head dims 128 and 64 are template instances of the same kernels.
 #include <type_traits>
@@ -71,27 +74,16 @@ struct DecodeArgs {
 
 __device__ __forceinline__ int clamp_len(int L, int max_len, int cap) { return max(0, min(L, min(max_len, cap))); }
 
-#ifndef ATTN_DECODE_AUX
-#define ATTN_DECODE_AUX 2
-#endif
-#ifndef ATTN_DECODE_XCD_GROUP
-#define ATTN_DECODE_XCD_GROUP 0
-#endif
-// Workgroup -> (KV head g, chunk, sequence b). Default: grid (hkv, n_chunks, batch), head fastest. XCD-grouped: a 1-D
-// grid where consecutive workgroups go to consecutive XCDs (eight), and the hkv heads of one chunk are the
-// consecutive workgroups of one XCD, so each cache row is read whole into one L2.
-__device__ __forceinline__ bool decode_unit(const DecodeArgs& a, int& g, int& chunk, int& b) {
-  if constexpr (ATTN_DECODE_XCD_GROUP) {
-    const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
-    g = j % a.n_hg;
-    const int unit = (j / a.n_hg) * 8 + xcd;
-    if (unit >= a.batch * a.n_chunks) return false;
-    b = unit / a.n_chunks; chunk = unit % a.n_chunks;
-  } else {
-    g = blockIdx.x; chunk = blockIdx.y; b = blockIdx.z;
-  }
-  return true;
+// Workgroup -> (KV-head group g, chunk, sequence b): grid (head groups, n_chunks, batch), head groups fastest, so
+// the head groups of one chunk are consecutive workgroups and read interleaved slices of the same page slots.
+// (Measured: all head groups of a chunk on one XCD instead, a 1-D grid over XCD-strided workgroups, ran 6% slower
+// for bf16 and 3% faster for FP8.)
+__device__ __forceinline__ void decode_unit(int& g, int& chunk, int& b) {
+  g = blockIdx.x; chunk = blockIdx.y; b = blockIdx.z;
 }
+
+// Copy cache policy: non-temporal, every cache byte is read once (measured: cached copies 7% slower).
+constexpr int kCopyAux = 2;
 
 // LDS address `byte_off` bytes into a __shared__ buffer, formed in the LDS address space (a cast of the buffer
 // itself, then the offset), so the copy's destination stays a known object the compiler can tell from the others.
@@ -358,7 +350,7 @@ __global__ __launch_bounds__(64) void decode_paged_lds_kernel(DecodeArgs a) {
   ATTN_RING_BUFFERS(uint16_t, kl, 32 * D)
   ATTN_RING_BUFFERS(uint16_t, vl, 32 * D)
   int g, chunk, b;
-  if (!decode_unit(a, g, chunk, b)) return;
+  decode_unit(g, chunk, b);
   Chunk ck;
   if (!load_chunk(a, b, chunk, ck)) return;
   const int t_begin = ck.t_begin, t_end = ck.t_end;
@@ -403,9 +395,9 @@ __global__ __launch_bounds__(64) void decode_paged_lds_kernel(DecodeArgs a) {
       const buf_rsrc_t rv = make_buf_rsrc(vcache + e0, uint32_t(rows) * row_bytes);
       const int r = kRowsPerCopy * i + row_in;
       raw_buffer_load_lds(rk, lds_at(kdst, 1024 * i), 16, int(row_in * row_bytes + 16 * (pcs ^ dec_swz_k<D>(r))),
-                          0, 0, ATTN_DECODE_AUX);
+                          0, 0, kCopyAux);
       raw_buffer_load_lds(rv, lds_at(vdst, 1024 * i), 16, int(row_in * row_bytes + 16 * (pcs ^ dec_swz_v<D>(r))),
-                          0, 0, ATTN_DECODE_AUX);
+                          0, 0, kCopyAux);
     }
   };
   // LDS read addresses (bytes): K row 16*tb + n, chunk 4*ks + grp4; V rows 4*grp4 + j (+16), dims 16*db + 4*(n&3)
@@ -495,7 +487,7 @@ __global__ __launch_bounds__(64) void decode_paged_q8_kernel(DecodeArgs a) {
   ATTN_RING_BUFFERS(uint8_t, k8, 32 * RL)
   ATTN_RING_BUFFERS(uint8_t, v8, 32 * RL)
   int gw, chunk, b;
-  if (!decode_unit(a, gw, chunk, b)) return;
+  decode_unit(gw, chunk, b);
   const int g0 = gw * HPW;                   // the wave's first KV head
   Chunk ck;
   if (!load_chunk(a, b, chunk, ck)) return;
@@ -551,8 +543,8 @@ __global__ __launch_bounds__(64) void decode_paged_q8_kernel(DecodeArgs a) {
       const buf_rsrc_t rv = make_buf_rsrc(vcache + e0, uint32_t(rows) * row_bytes);
       const int r = kRowsPerCopy * i + row_in;
       raw_buffer_load_lds(rk, lds_at(kdst, 1024 * i), 16, int(row_in * row_bytes + 16 * (pcs ^ q8_swz<D, HPW>(r))),
-                          0, 0, ATTN_DECODE_AUX);
-      raw_buffer_load_lds(rv, lds_at(vdst, 1024 * i), 16, int(row_in * row_bytes + 16 * pcs), 0, 0, ATTN_DECODE_AUX);
+                          0, 0, kCopyAux);
+      raw_buffer_load_lds(rv, lds_at(vdst, 1024 * i), 16, int(row_in * row_bytes + 16 * pcs), 0, 0, kCopyAux);
     }
   };
   // Head e's K of key 16*tb + n as 16-byte pieces (dims 64*hk + 16*grp4 ..), its V rows of keys
@@ -677,10 +669,8 @@ namespace {
 template <class Kernel>
 void launch_grid(Kernel kernel, DecodeArgs a, int hpw, hipStream_t stream) {
   a.n_hg = a.hkv / hpw;
-  const unsigned n_units = unsigned(a.batch) * unsigned(a.n_chunks);
-  const dim3 grid = ATTN_DECODE_XCD_GROUP ? dim3{((n_units + 7u) / 8u) * 8u * unsigned(a.n_hg), 1u, 1u}
-                                          : dim3{unsigned(a.n_hg), unsigned(a.n_chunks), unsigned(a.batch)};
-  kernel<<<grid, dim3(64), 0, stream>>>(a);   // head-major: the head groups of one chunk are consecutive
+  const dim3 grid{unsigned(a.n_hg), unsigned(a.n_chunks), unsigned(a.batch)};   // head-major
+  kernel<<<grid, dim3(64), 0, stream>>>(a);
 }
 
 // FP8 caches: a wave takes several KV heads when that makes its rows at least 256 bytes. Measured on the 64-sequence
