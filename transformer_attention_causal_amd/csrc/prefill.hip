@@ -130,7 +130,7 @@ struct RopeQ {
                                        int lg) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const int qi = min(qpos0 + 32 * qb + lq, S - 1);
+      const int qi = max(0, min(qpos0 + 32 * qb + lq, S - 1));
       int p = a.q_pos ? a.q_pos[qrow0 + qi] : koff + qi;
       p = min(max(p, 0), a.rope_len - 1);
       const float* cs = reinterpret_cast<const float*>(a.rope_cs + int64_t(p) * (D / 2));
@@ -266,6 +266,9 @@ __device__ bool pick_chunked_unit(const PrefillArgs& a, int span, int r, int& b_
     S = min(a.cu_new[b + 1] - a.cu_new[b], a.seqlen);
     ctx = max(0, a.ctx_lens[b]);
   };
+  // Units are shifted back by sh = the excess of nb whole spans over S, rounded down to 32 queries (see the
+  // kernel), so unit p ends at key ctx + (p+1)*span - sh, the last at ctx + S.
+  auto shift = [&](int S) { return ((((S + span - 1) / span) * span - S) / 32) * 32; };
   // number of units with kend > X
   auto count_above = [&](int X) {
     int c = 0;
@@ -274,7 +277,8 @@ __device__ bool pick_chunked_unit(const PrefillArgs& a, int span, int r, int& b_
       seq(b, S, ctx);
       if (S > 0 && ctx + S > X) {
         const int nb = (S + span - 1) / span;
-        c += X < ctx ? nb : max(1, nb - (X - ctx) / span);
+        const int y = X - ctx + shift(S);
+        c += y < 0 ? nb : max(1, nb - y / span);
       }
     }
     return wave_sum_i(c);
@@ -301,8 +305,9 @@ __device__ bool pick_chunked_unit(const PrefillArgs& a, int span, int r, int& b_
     if (b < a.batch) {
       int S, ctx;
       seq(b, S, ctx);
-      has = S > 0 && ctx < K && K <= ctx + S && (K == ctx + S || (K - ctx) % span == 0);
-      p = (K - ctx + span - 1) / span - 1;
+      const int y = K - ctx + shift(S);
+      has = S > 0 && ctx < K && K <= ctx + S && (K == ctx + S || y % span == 0);
+      p = K == ctx + S ? (S + span - 1) / span - 1 : y / span - 1;
     }
     uint64_t mask = __ballot(has);
     const int cnt = __popcll(mask);
@@ -377,9 +382,18 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   } else {
     S = a.seqlen; koff = 0; T = S; qrow0 = int64_t(b) * S;
   }
+  if constexpr (!WIN) {
+    // The units of a sequence are shifted back so that the one that is partly outside the queries is its first,
+    // the cheapest, rather than its last, the dearest (whole 32-query blocks: a wave's queries are either all at
+    // positions >= 0 or all before 0). Each wave keeps its own key range, so the results are unchanged.
+    const int sh = ((((S + wg_span - 1) / wg_span) * wg_span - S) / QW) * QW;
+    wg_pos0 -= sh;
+    qpos0 -= sh;
+  }
   if (wg_pos0 >= S) return;                            // uniform: a block past this sequence's queries
   const int kend_wg = a.causal ? min(T, koff + wg_pos0 + wg_span) : T;
-  const int kend_w = a.causal ? min(T, koff + qpos0 + QW) : T;
+  // a wave whose queries all lie before position 0 has none and computes no tile
+  const int kend_w = qpos0 + QW <= 0 ? 0 : a.causal ? min(T, koff + qpos0 + QW) : T;
   const int ntiles = (kend_wg + kTileKeys - 1) / kTileKeys;
   const float c = a.scale * kLog2e;
 
@@ -388,11 +402,11 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qpos = qpos0 + 32 * qb + lq;
-    const uint16_t* qp = a.q + ((qrow0 + min(qpos, S - 1)) * a.hq + h) * D + 8 * lg;
+    const uint16_t* qp = a.q + ((qrow0 + max(0, min(qpos, S - 1))) * a.hq + h) * D + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4_t w = {0u, 0u, 0u, 0u};
-      if (qpos < S) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
+      if (qpos >= 0 && qpos < S) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
       qop[qb][ks] = as_bf16x8(w);
     }
   }
@@ -707,7 +721,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   for (int qb = 0; qb < QB; ++qb) {
     const int qpos = qpos0 + 32 * qb + lq;
     const float lt = sum_xor32(l[qb]);
-    if (qpos >= S) continue;
+    if (qpos < 0 || qpos >= S) continue;
     const float inv = 1.f / lt;
     uint16_t* op = a.o + ((qrow0 + qpos) * a.hq + h) * D + 4 * lg;
 #pragma unroll
