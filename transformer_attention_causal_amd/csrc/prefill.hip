@@ -8,7 +8,9 @@
 // bf16 path, one workgroup = 12 waves (one per CU, three per SIMD: registers capped at 168 per lane):
 //   * Work unit: 3 blocks of 32 query positions x 4 query heads of one KV group ("heads mode", when the group
 //     size is a multiple of 4: each K/V tile in LDS feeds 384 query rows), or 12 consecutive 32-position blocks of
-//     one query head ("positions mode", any other group size). Each wave owns 32 queries of one head.
+//     one query head ("positions mode", any other group size). Each wave owns 32 queries of one head. The chunked
+//     prefill from a paged cache uses 6 blocks x 2 heads in heads mode. Units are dealt heaviest first, in a snake
+//     order over the shader engines (snake_id).
 //   * K and V tiles of 64 keys x D are copied straight from global memory into LDS (buffer loads with the LDS
 //     bit, 16 bytes per lane, no register staging), double-buffered, one barrier per tile. LDS rows are unpadded;
 //     their 16-byte chunks are XOR-swizzled by a key of the row index (swz_key) that makes both LDS read patterns
@@ -45,8 +47,15 @@ constexpr int kWaves = ATTN_PREFILL_WAVES;
 #define ATTN_PREFILL_HEADS 4
 #endif
 constexpr int kHeads = ATTN_PREFILL_HEADS;
-constexpr int kPosBlocks = kWaves / kHeads;   // 32-position blocks per workgroup in heads mode
 static_assert(kWaves % kHeads == 0, "waves split into heads x position blocks");
+// The chunked prefill from a paged cache takes 2 heads x 6 position blocks: its units differ in cost by orders of
+// magnitude, and the taller units balance better over the shader engines (measured 2% faster on four 2048-token
+// chunks; the plain prefill is the same speed either way).
+#ifndef ATTN_PREFILL_HEADS_PAGED
+#define ATTN_PREFILL_HEADS_PAGED 2
+#endif
+constexpr int kHeadsPaged = ATTN_PREFILL_HEADS_PAGED;
+static_assert(kWaves % kHeadsPaged == 0, "waves split into heads x position blocks");
 constexpr int kThreads = 64 * kWaves;
 // Keys per compute tile (32 or 64).
 #ifndef ATTN_PREFILL_BN
@@ -92,7 +101,8 @@ struct PrefillArgs {
   int batch, seqlen, hq, hkv;
   float scale;
   int causal;
-  int heads_mode;    // 1: kHeads heads x kPosBlocks*32 positions per workgroup; 0: 1 head x kWaves*32 positions
+  int heads_mode;    // 1: H heads x (kWaves/H)*32 positions per workgroup (H = kHeads, or kHeadsPaged for the
+                     // chunked kernel); 0: 1 head x kWaves*32 positions
   int n_pblk;        // position blocks per (batch, head group)
   int n_hgrp;        // head groups: hq/4 in heads mode, hq in positions mode
   // Chunked prefill from a paged cache (the PAGED kernel): the queries of sequence b are rows cu_new[b] ..
@@ -125,14 +135,23 @@ template <int D, int QB>
 struct RopeQ {
   static constexpr int KS = D / 16;
   f32x4_t t[QB][2 * KS];   // the lane's (cos, sin) pairs, in the order apply() consumes them
+  int pos[QB];             // table row of each query
 
-  __device__ __forceinline__ void load(const PrefillArgs& a, int64_t qrow0, int qpos0, int koff, int S, int lq,
-                                       int lg) {
+  // Positions first (an explicit position list is read before the Q loads are issued, so waiting for it does not
+  // wait for them), then the table rows.
+  __device__ __forceinline__ void positions(const PrefillArgs& a, int64_t qrow0, int qpos0, int koff, int S,
+                                            int lq) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int qi = max(0, min(qpos0 + 32 * qb + lq, S - 1));
-      int p = a.q_pos ? a.q_pos[qrow0 + qi] : koff + qi;
-      p = min(max(p, 0), a.rope_len - 1);
+      pos[qb] = a.q_pos ? a.q_pos[qrow0 + qi] : koff + qi;
+    }
+  }
+
+  __device__ __forceinline__ void load(const PrefillArgs& a, int lg) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int p = min(max(pos[qb], 0), a.rope_len - 1);
       const float* cs = reinterpret_cast<const float*>(a.rope_cs + int64_t(p) * (D / 2));
       if (a.rope_inter) {          // pairs 8*ks + 4*lg + j, j = 0..3
 #pragma unroll
@@ -225,14 +244,24 @@ struct TileCopy {
 
   // Copy `rows` tile rows starting at `base` (row 0 of the tile, head 0) into `dst`. The buffer resource spans
   // exactly those rows; the others read as zeros (measured: an out-of-range lane of a buffer load-to-LDS writes 0),
-  // which are finite, so their masked scores and P = 0 stay exact.
+  // which are finite, so their masked scores and P = 0 stay exact. Every wave issues kLoads instructions: when
+  // the blocks do not split evenly, a wave's surplus instruction reads out of range into the 1 KiB `spare` LDS
+  // block (zeros, no memory access), so the copies are never skipped by a branch and the compiler counts the
+  // loads in flight exactly (with a skipped copy possible it waited for every load before the first use of
+  // registers loaded ahead of the copy).
   __device__ __forceinline__ void issue(uint16_t* dst, const uint16_t* base, int rows, int hkv, int wave,
-                                        int step = 1) const {
+                                        uint16_t* spare, int step = 1) const {
     const int nr = max(0, min(ROWS, rows));
     const buf_rsrc_t rs = make_buf_rsrc(base, uint32_t(nr > 0 ? ((nr - 1) * step + 1) * hkv * D * 2 : 0));
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-      if (kBlocks % NW == 0 || i * NW + wave < kBlocks) load_lds16(rs, off[i], dst + (i * NW + wave) * 512);
+    for (int i = 0; i < kLoads; ++i) {
+      if (kBlocks % NW == 0) {
+        load_lds16(rs, off[i], dst + (i * NW + wave) * 512);
+      } else {
+        const bool ok = i * NW + wave < kBlocks;       // wave-uniform
+        load_lds16(rs, ok ? off[i] : 0x80000000u, ok ? dst + (i * NW + wave) * 512 : spare);
+      }
+    }
   }
 };
 
@@ -249,11 +278,6 @@ constexpr int kTileKeys = kSub * kBN;
 // sequences. Rank r picks the unit with the r-th largest kend (ties: lower b first), so the heaviest units start
 // first and the light ones fill the tail. Every wave computes the same answer from wave-wide reductions over the
 // batch (64 sequences per step); no synchronisation, no workspace.
-__device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
 __device__ __forceinline__ int wave_max_i(int v) {
 #pragma unroll
   for (int o = 32; o; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
@@ -262,13 +286,33 @@ __device__ __forceinline__ int wave_max_i(int v) {
 
 __device__ bool pick_chunked_unit(const PrefillArgs& a, int span, int r, int& b_out, int& p_out) {
   const int lane = threadIdx.x & 63;
-  auto seq = [&](int b, int& S, int& ctx) {
-    S = min(a.cu_new[b + 1] - a.cu_new[b], a.seqlen);
-    ctx = max(0, a.ctx_lens[b]);
+  // Up to 64 sequences: lane b reads sequence b's sizes once, and the search below runs on registers (reading
+  // them again on every step put about 15 dependent memory round trips before each workgroup's first tile).
+  const bool cached = a.batch <= 64;
+  int S_l = 0, ctx_l = 0;
+  if (cached && lane < a.batch) {
+    S_l = min(a.cu_new[lane + 1] - a.cu_new[lane], a.seqlen);
+    ctx_l = max(0, a.ctx_lens[lane]);
+  }
+  auto seq = [&](int b, int& S, int& ctx) {   // b = lane + 64 * k
+    if (cached) {
+      S = S_l; ctx = ctx_l;
+    } else {
+      S = min(a.cu_new[b + 1] - a.cu_new[b], a.seqlen);
+      ctx = max(0, a.ctx_lens[b]);
+    }
   };
   // Units are shifted back by sh = the excess of nb whole spans over S, rounded down to 32 queries (see the
   // kernel), so unit p ends at key ctx + (p+1)*span - sh, the last at ctx + S.
   auto shift = [&](int S) { return ((((S + span - 1) / span) * span - S) / 32) * 32; };
+  // Wave-wide sum of per-lane counts below 2^nbits, bit by bit with ballots: scalar population counts instead of
+  // a chain of cross-lane shuffles through LDS (the search below takes about 16 sums).
+  const int nbits = 32 - __clz(max(1, ((a.batch + 63) / 64) * ((a.seqlen + span - 1) / span)));
+  auto wave_count = [&](int c) {
+    int total = 0;
+    for (int j = 0; j < nbits; ++j) total += __popcll(__ballot((c >> j) & 1)) << j;
+    return total;
+  };
   // number of units with kend > X
   auto count_above = [&](int X) {
     int c = 0;
@@ -281,7 +325,7 @@ __device__ bool pick_chunked_unit(const PrefillArgs& a, int span, int r, int& b_
         c += y < 0 ? nb : max(1, nb - y / span);
       }
     }
-    return wave_sum_i(c);
+    return wave_count(c);
   };
   int hi = 0;
   for (int b = lane; b < a.batch; b += 64) {
@@ -334,13 +378,29 @@ __device__ bool pick_chunked_unit(const PrefillArgs& a, int span, int r, int& b_
 // their union is exactly the visible set.
 constexpr int kPhaseWin = 0, kPhaseLead = 1, kPhaseAnchor = 2;
 
+// Work units go to workgroup ids heaviest first, with the n_hgrp head groups of a unit on consecutive ids. The
+// hardware deals a launch's workgroups to its 32 shader engines (8 compute units each) round-robin, workgroup i to
+// engine i mod 32 (measured), so an engine runs every 32nd unit of that order and the engines that take the first
+// unit of each group of 32 would always hold its heaviest one. Odd groups of 32 ids take their units in reverse
+// order (whole units; a head group stays on the same engine), which evens out the engines' totals: the chunked
+// prefill's last engine finished 3% earlier in a replay of measured unit times. Outputs do not depend on the order.
+__device__ __forceinline__ int snake_id(int id, int n, int n_hgrp) {
+  const int g = id >> 5;
+  if (n_hgrp <= 0 || 32 % n_hgrp != 0 || (g & 1) == 0 || 32 * g + 32 > n) return id;
+  const int r = id & 31, per = 32 / n_hgrp;            // units per group of 32 ids
+  return 32 * g + (per - 1 - r / n_hgrp) * n_hgrp + r % n_hgrp;
+}
+
 template <int D, int QB, bool PAGED, bool WIN = false>
 __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void prefill_bf16_kernel(PrefillArgs a) {
   static_assert(!(WIN && (PAGED || kSub != 1)), "the local + global mask is for contiguous prefill, 64-key tiles");
+  constexpr int kH = PAGED ? kHeadsPaged : kHeads;     // heads per workgroup in heads mode
+  constexpr int kPB = kWaves / kH;                     // 32-position blocks per workgroup in heads mode
   constexpr int QW = 32 * QB;
   constexpr int KS = D / 16;   // k-steps of the QK^T contraction
   constexpr int DB = D / 32;   // 32-row blocks of O^T
   __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTileKeys * D];   // [buffer][K, V]
+  __shared__ __attribute__((aligned(16))) uint16_t lds_spare[512];             // target of surplus copies
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar register)
   const int lane = threadIdx.x & 63;
@@ -348,11 +408,11 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   // ---- work unit (heaviest position blocks first; consecutive ids share a position block)
   // (chunked prefill: heaviest units first by the device-side ranking above; head groups innermost, so the
   // blocks of one unit land on consecutive XCDs and each XCD keeps to a fixed set of KV heads)
-  const int id = blockIdx.x;
+  const int id = snake_id(blockIdx.x, gridDim.x, a.n_hgrp);
   int pblk, b, hgrp;
   if constexpr (PAGED) {
     hgrp = id % a.n_hgrp;
-    const int span = a.heads_mode ? kPosBlocks * QW : kWaves * QW;
+    const int span = a.heads_mode ? kPB * QW : kWaves * QW;
     int bb, pp;
     if (!pick_chunked_unit(a, span, id / a.n_hgrp, bb, pp)) return;
     // one scalar for both (measured: keeps the D=128 kernel within its register budget, no spills)
@@ -367,8 +427,8 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   const int grp = a.hq / a.hkv;
   int h, qpos0, wg_pos0, wg_span;
   if (a.heads_mode) {
-    h = hgrp * kHeads + wave % kHeads; wg_pos0 = pblk * kPosBlocks * QW; qpos0 = wg_pos0 + (wave / kHeads) * QW;
-    wg_span = kPosBlocks * QW;
+    h = hgrp * kH + wave % kH; wg_pos0 = pblk * kPB * QW; qpos0 = wg_pos0 + (wave / kH) * QW;
+    wg_span = kPB * QW;
   } else {
     h = hgrp; wg_pos0 = pblk * kWaves * QW; qpos0 = wg_pos0 + wave * QW; wg_span = kWaves * QW;
   }
@@ -397,22 +457,40 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   const int ntiles = (kend_wg + kTileKeys - 1) / kTileKeys;
   const float c = a.scale * kLog2e;
 
+  // Paged: the block-table entry of a tile is read one tile ahead of its copy, by a vector load that the loop's
+  // wait for the tile copies also covers, so no table-load latency sits between a barrier and the next copy
+  // (measured: a scalar load there cost about 6% of the chunked prefill). Entries past max_pages read as 0 and
+  // are replaced by -1 (no page) at use.
+  buf_rsrc_t trs = {0, 0, 0, 0};
+  if constexpr (PAGED) trs = make_buf_rsrc(a.table + int64_t(b) * a.max_pages, uint32_t(a.max_pages) * 4u);
+  auto page_load = [&](int t) -> int {                 // raw table entry of tile t (in flight until the next wait)
+    return PAGED ? raw_buffer_load_i32(trs, ((t * kTileKeys) >> a.page_shift) * 4, 0, 0) : 0;
+  };
+  // (the first entry is read before the Q loads, so no table-load latency sits before the first copy either)
+  const int pg0 = page_load(0);
+  RopeQ<D, QB> rq;
+  const bool rope = !WIN && a.rope_cs != nullptr;     // uniform; the local + global kernel takes no table
+  if (rope) rq.positions(a, qrow0, qpos0, koff, S, lq);
+
   // ---- Q^T operands, resident for the whole kernel: lane holds query (qpos0 + 32*qb + lq), dims 16*ks + 8*lg ..
   bf16x8_t qop[QB][KS];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int qpos = qpos0 + 32 * qb + lq;
     const uint16_t* qp = a.q + ((qrow0 + max(0, min(qpos, S - 1))) * a.hq + h) * D + 8 * lg;
+    // Loaded unconditionally from the clamped row (loads under a lane mask made the compiler wait for the first of
+    // them before issuing the rest). A lane past the last query then holds row S-1's query, sees the same keys
+    // (all of them) and so takes the same online-softmax decisions as row S-1's lane in the same wave: the other
+    // lanes' results are unchanged, and its own are never stored. Lanes before position 0 fill whole waves, which
+    // compute no tile. The local + global mask depends on the position itself, so there such lanes hold zeros.
+    const bool qin = qpos >= 0 && qpos < S;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      u32x4_t w = {0u, 0u, 0u, 0u};
-      if (qpos >= 0 && qpos < S) w = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
-      qop[qb][ks] = as_bf16x8(w);
+      const u32x4_t w = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
+      qop[qb][ks] = as_bf16x8(!WIN || qin ? w : u32x4_t{0u, 0u, 0u, 0u});
     }
   }
-  RopeQ<D, QB> rq;
-  const bool rope = !WIN && a.rope_cs != nullptr;     // uniform; the local + global kernel takes no table
-  if (rope) rq.load(a, qrow0, qpos0, koff, S, lq, lg);
+  if (rope) rq.load(a, lg);
   // paged: rotated at once, so the table rows are dead before the tile loop's registers come alive (rotating after
   // the first copy, as the plain kernel does, spills there)
   if (PAGED && rope) rq.apply(qop, a.rope_inter);
@@ -447,15 +525,6 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   // Row 0 of the K or V tile at key0 and its valid row count. Paged: tiles never straddle pages (page size a
   // multiple of the tile); a page number outside [0, num_pages), or a tile past the table's max_pages entries,
   // gives no rows (zeros, no memory access).
-  // Paged: the block-table entry of a tile is read one tile ahead of its copy, by a vector load that the loop's
-  // wait for the tile copies also covers, so no table-load latency sits between a barrier and the next copy
-  // (measured: a scalar load there cost about 6% of the chunked prefill). Entries past max_pages read as 0 and
-  // are replaced by -1 (no page) at use.
-  buf_rsrc_t trs = {0, 0, 0, 0};
-  if constexpr (PAGED) trs = make_buf_rsrc(a.table + int64_t(b) * a.max_pages, uint32_t(a.max_pages) * 4u);
-  auto page_load = [&](int t) -> int {                 // raw table entry of tile t (in flight until the next wait)
-    return PAGED ? raw_buffer_load_i32(trs, ((t * kTileKeys) >> a.page_shift) * 4, 0, 0) : 0;
-  };
   auto tile_src = [&](const uint16_t* kv, int key0, int& rows, int page_raw) -> const uint16_t* {
     rows = max(0, min(kTileKeys, T - key0));
     if constexpr (PAGED) {
@@ -471,9 +540,9 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   auto copy_tile = [&](int buf, int t, int page_raw) {
     int rows;
     const uint16_t* kb = tile_src(a.k, t * kTileKeys, rows, page_raw);
-    cp.issue(lds[buf][0], kb, rows, a.hkv, wave);
+    cp.issue(lds[buf][0], kb, rows, a.hkv, wave, lds_spare);
     const uint16_t* vb = tile_src(a.v, t * kTileKeys, rows, page_raw);
-    cp.issue(lds[buf][1], vb, rows, a.hkv, wave);
+    cp.issue(lds[buf][1], vb, rows, a.hkv, wave, lds_spare);
   };
 
   // One kBN-key tile from LDS buffer BUF (a compile-time constant, so LDS addresses are base + immediate).
@@ -659,11 +728,11 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
       desc(u, key0, step, phase, rows);
       const int64_t row0 = int64_t(b) * S + key0;
       if (step == 1) {
-        cp.issue(lds[buf][0], a.k + row0 * a.hkv * D, rows, a.hkv, wave);
-        cp.issue(lds[buf][1], a.v + row0 * a.hkv * D, rows, a.hkv, wave);
+        cp.issue(lds[buf][0], a.k + row0 * a.hkv * D, rows, a.hkv, wave, lds_spare);
+        cp.issue(lds[buf][1], a.v + row0 * a.hkv * D, rows, a.hkv, wave, lds_spare);
       } else {
-        cpa.issue(lds[buf][0], a.k + row0 * a.hkv * D, rows, a.hkv, wave, step);
-        cpa.issue(lds[buf][1], a.v + row0 * a.hkv * D, rows, a.hkv, wave, step);
+        cpa.issue(lds[buf][0], a.k + row0 * a.hkv * D, rows, a.hkv, wave, lds_spare, step);
+        cpa.issue(lds[buf][1], a.v + row0 * a.hkv * D, rows, a.hkv, wave, lds_spare, step);
       }
     };
     // does this wave (queries qpos0 .. qw_max) see any key of tile u?
@@ -690,7 +759,7 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
       run_u(std::integral_constant<int, 1>{}, u + 1);
     }
   } else {
-  int pg = page_load(0);
+  int pg = pg0;
   copy_tile(0, 0, pg);
   pg = page_load(1);                                   // table entry of the next tile to copy
   if (!PAGED && rope) rq.apply(qop, a.rope_inter);
@@ -810,16 +879,16 @@ __global__ __launch_bounds__(kF32Queries * (D / 16)) void prefill_fp32_kernel(co
 namespace {
 // Shared launch geometry: n_pblk position blocks (heaviest first) x batch x head groups.
 PrefillArgs prefill_args(const void* q, const void* k, const void* v, void* o, float* lse, int batch, int max_q,
-                         int hq, int hkv, int causal, float scale) {
+                         int hq, int hkv, int causal, float scale, int heads = kHeads) {
   PrefillArgs a = {};
   a.q = static_cast<const uint16_t*>(q); a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v); a.o = static_cast<uint16_t*>(o); a.lse = lse;
   a.batch = batch; a.seqlen = max_q; a.hq = hq; a.hkv = hkv; a.scale = scale; a.causal = causal;
   const int grp = hq / hkv;
-  a.heads_mode = (grp % kHeads == 0) ? 1 : 0;
-  const int span = a.heads_mode ? kPosBlocks * 32 : kWaves * 32;
+  a.heads_mode = (grp % heads == 0) ? 1 : 0;
+  const int span = a.heads_mode ? (kWaves / heads) * 32 : kWaves * 32;
   a.n_pblk = (max_q + span - 1) / span;
-  a.n_hgrp = a.heads_mode ? hq / kHeads : hq;
+  a.n_hgrp = a.heads_mode ? hq / heads : hq;
   return a;
 }
 }  // namespace
@@ -855,7 +924,7 @@ hipError_t launch_prefill_paged(const void* q, const void* k_cache, const void* 
                                 const void* rope_table, int rope_len, const int32_t* q_positions,
                                 int rope_interleaved) {
   if (max_new <= 0 || total_new <= 0) return hipSuccess;
-  PrefillArgs a = prefill_args(q, k_cache, v_cache, o, lse, batch, max_new, hq, hkv, 1, scale);
+  PrefillArgs a = prefill_args(q, k_cache, v_cache, o, lse, batch, max_new, hq, hkv, 1, scale, kHeadsPaged);
   a.rope_cs = static_cast<const float2*>(rope_table); a.rope_len = rope_len; a.q_pos = q_positions;
   a.rope_inter = rope_interleaved;
   a.cu_new = cu_new; a.ctx_lens = ctx_lens; a.table = block_table;
