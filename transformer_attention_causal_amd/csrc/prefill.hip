@@ -399,7 +399,11 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   constexpr int QW = 32 * QB;
   constexpr int KS = D / 16;   // k-steps of the QK^T contraction
   constexpr int DB = D / 32;   // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTileKeys * D];   // [buffer][K, V]
+  // [buffer][K, V]; buffers 0 and 1 hold the tiles, and after the last tile the whole array stages the output rows
+  // (kWaves * QW rows of D, hence a third buffer when that is larger than two; the chunked kernel stores directly)
+  constexpr int kStageBuf = (kWaves * QW + 2 * kTileKeys - 1) / (2 * kTileKeys);
+  constexpr int kNBuf = !PAGED && kStageBuf > 2 ? kStageBuf : 2;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kNBuf][2][kTileKeys * D];
   __shared__ __attribute__((aligned(16))) uint16_t lds_spare[512];             // target of surplus copies
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (scalar register)
@@ -785,14 +789,54 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
   }
   }
 
-  // ---- epilogue: O = O^T / l (lane holds query lq, dims 32*db + 8*(r/4) + 4*lg + r%4), lse = scale*m + ln l
+  // ---- epilogue: O = O^T / l (lane holds query lq, dims 32*db + 8*(r/4) + 4*lg + r%4), lse = scale*m + ln l.
+  if constexpr (PAGED) {
+    // (the chunked kernel stores straight from the accumulators: staging through LDS made it spill registers in
+    // its tile loop, and its longer work units spend under 1% of their time here)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qpos = qpos0 + 32 * qb + lq;
+      const float lt = sum_xor32(l[qb]);
+      if (qpos < 0 || qpos >= S) continue;
+      const float inv = 1.f / lt;
+      uint16_t* op = a.o + ((qrow0 + qpos) * a.hq + h) * D + 4 * lg;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const f32x16_t& x = oacc[qb][db];
+          const u32x2_t w = {pack_bf16x2(x[4 * rq] * inv, x[4 * rq + 1] * inv),
+                             pack_bf16x2(x[4 * rq + 2] * inv, x[4 * rq + 3] * inv)};
+          *reinterpret_cast<u32x2_t*>(op + 32 * db + 8 * rq) = w;
+        }
+      if (a.lse && lg == 0) a.lse[int64_t(h) * a.total_new + qrow0 + qpos] = m[qb] * a.scale + logf(lt);
+    }
+    return;
+  }
+  // O goes through LDS so that each store instruction writes whole rows (a row of D bf16 per query and head is
+  // contiguous in o; written straight from the accumulator layout, every instruction writes 16-byte pieces of 32
+  // rows, and that epilogue took about 2% of the S=8192 prefill). Staging row r of this wave holds query
+  // qpos0 + r; its 16-byte chunk c sits at chunk c ^ key(r), and the two 8-byte halves swap when (r / 16) is odd,
+  // so the accumulator-order writes (32 rows at one chunk per instruction half) and the row-order reads are
+  // conflict-free.
+  constexpr int RB2 = D * 2;                           // bytes per staging row
+  constexpr int RPI = 1024 / RB2;                      // rows per 1 KiB store instruction
+  auto stg_key = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  uint16_t* stg = &lds[0][0][0] + wave * QW * D;       // this wave's staging rows (the tile buffers are done)
+  __syncthreads();                                     // every wave has finished reading the last tile
+  // The lane index passes through an empty asm statement, so the staging addresses are formed here: shared with
+  // the loop's lane-fixed addresses they kept registers alive across the tile loop, which then lost its read
+  // pipelining.
+  int ln = lane;
+  asm volatile("" : "+v"(ln));
+  const int slq = ln & 31, slg = ln >> 5;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int qpos = qpos0 + 32 * qb + lq;
+    const int qpos = qpos0 + 32 * qb + slq;
     const float lt = sum_xor32(l[qb]);
-    if (qpos < 0 || qpos >= S) continue;
     const float inv = 1.f / lt;
-    uint16_t* op = a.o + ((qrow0 + qpos) * a.hq + h) * D + 4 * lg;
+    const int r = 32 * qb + slq;
+    const int half = slg ^ ((r >> 4) & 1);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -800,12 +844,21 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
         const f32x16_t& x = oacc[qb][db];
         const u32x2_t w = {pack_bf16x2(x[4 * rq] * inv, x[4 * rq + 1] * inv),
                            pack_bf16x2(x[4 * rq + 2] * inv, x[4 * rq + 3] * inv)};
-        *reinterpret_cast<u32x2_t*>(op + 32 * db + 8 * rq) = w;
+        const int c = 4 * db + rq;                     // logical 16-byte chunk (dims 8c .. 8c+7)
+        *reinterpret_cast<u32x2_t*>(stg + r * D + 8 * (c ^ stg_key(r)) + 4 * half) = w;
       }
-    if (a.lse && lg == 0) {
-      const int64_t li = PAGED ? int64_t(h) * a.total_new + qrow0 + qpos : (int64_t(b) * a.hq + h) * S + qpos;
-      a.lse[li] = m[qb] * a.scale + logf(lt);
-    }
+    if (a.lse && slg == 0 && qpos >= 0 && qpos < S)
+      a.lse[(int64_t(b) * a.hq + h) * S + qpos] = m[qb] * a.scale + logf(lt);
+  }
+  // (the wave reads back only its own rows: its LDS writes are complete at the reads' wait, no barrier needed)
+#pragma unroll
+  for (int it = 0; it < QW / RPI; ++it) {
+    const int r = it * RPI + ln / (RB2 / 16), c = ln % (RB2 / 16);
+    u32x4_t w = *reinterpret_cast<const u32x4_t*>(stg + r * D + 8 * (c ^ stg_key(r)));
+    if ((r >> 4) & 1) w = u32x4_t{w[2], w[3], w[0], w[1]};
+    const int qpos = qpos0 + r;
+    if (qpos >= 0 && qpos < S)
+      *reinterpret_cast<u32x4_t*>(a.o + ((qrow0 + qpos) * a.hq + h) * D + 8 * c) = w;
   }
 }
 
