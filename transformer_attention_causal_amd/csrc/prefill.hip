@@ -81,6 +81,11 @@ static_assert(kBN == 32 || kBN == 64, "tile of 32 or 64 keys");
 #ifndef ATTN_PREFILL_KPRE
 #define ATTN_PREFILL_KPRE 3
 #endif
+// The chunked kernel keeps two K fragments in flight: its tile loop holds a few more registers (the next block-table
+// entry), and with three the compiler fell back to one.
+#ifndef ATTN_PREFILL_KPRE_PAGED
+#define ATTN_PREFILL_KPRE_PAGED 2
+#endif
 #ifndef ATTN_PREFILL_MIN_WAVES_PER_SIMD
 #define ATTN_PREFILL_MIN_WAVES_PER_SIMD 3
 #endif
@@ -572,16 +577,17 @@ __global__ __launch_bounds__(kThreads, ATTN_PREFILL_MIN_WAVES_PER_SIMD) void pre
         for (int qb = 0; qb < QB; ++qb) sacc[qb][kb2] = mfma32x32x16(ka, qop[qb][ks], sacc[qb][kb2]);
       }
     }
-#if ATTN_PREFILL_KPRE > 0
-    // K fragment reads run ATTN_PREFILL_KPRE fragments ahead of the products that use them
+    // K fragment reads run kKPre fragments ahead of the products that use them
+    constexpr int kKPre = PAGED ? ATTN_PREFILL_KPRE_PAGED : ATTN_PREFILL_KPRE;
+    if constexpr (kKPre > 0) {
 #pragma unroll
-    for (int i = 0; i < ATTN_PREFILL_KPRE; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < kKPre; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
-    for (int i = 0; i < KS * kKB2; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
-      if (i + ATTN_PREFILL_KPRE < KS * kKB2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      for (int i = 0; i < KS * kKB2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+        if (i + kKPre < KS * kKB2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
     }
-#endif
 
     // ---- mask. WIN: tiles not visible in full to every query of the wave, by the phase's rule; otherwise only
     // tiles crossing the diagonal or the ragged end
