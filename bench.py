@@ -54,6 +54,7 @@ KERNEL_SOURCES = {
     "decode_paged_q8_kernel": "decode.hip",
     "decode_paged_lds_kernel": "decode.hip",
     "mla_split_kernel": "mla.hip",
+    "mla_split_fp8mma_kernel": "mla.hip",
     "dsa_indexer_kernel": "dsa.hip",
 }
 
@@ -600,12 +601,12 @@ def run_secondary(torch, ta, args, sel, line):
             wm = WORKLOADS["mla_decode_b32"]
             ms = bench_mla(torch, ta, wm, max(20, args.steps), max(300, args.warmup), kv=kv)
             nbytes = mla_bytes(wm, elem=1)
+            kern = "mla_split_fp8mma_kernel" if kv == "fp8" else "mla_split_kernel"
             line[f"mla_decode_{kv}"] = {
                 "workload": f"{wm.name} ({kv} latent cache)", "value": round(nbytes / (ms * 1e-3) / 1e9, 1),
                 "unit": "GB/s", "ms": round(ms, 4), "bytes": nbytes,
                 "tflops": round(mla_flops(wm) / (ms * 1e-3) / 1e12, 1),
-                "roofline": roofline_hbm(nbytes, ms, "mla_split_kernel", f"{wm.name}_{kv}",
-                                         "mla_split_kernel + mla_combine_kernel")}
+                "roofline": roofline_hbm(nbytes, ms, kern, f"{wm.name}_{kv}", f"{kern} + mla_combine_kernel")}
     if "long" in sel:
         wl = WORKLOADS["gqa_prefill_s131072"]
         wall_l, kern_l, _ = bench_prefill(torch, ta, wl, 2, 1)

@@ -60,8 +60,12 @@ def test_mla_q8_length_zero_and_poison_past_the_length(kind):
 
 
 def test_mla_fp8_unit_scales_match_bf16_kernel_on_decoded_cache():
-    """FP8 codes are exact in bf16: with unit scales the 8-bit kernel and the bf16 kernel on the decoded cache
-    agree within the bf16 tolerance (the query is not rounded again when the scale is 1)."""
+    """FP8 codes are exact in bf16: with unit scales the 8-bit kernel and the bf16 kernel on the decoded cache compute
+    the same attention. Unit scales make the latent values, and so the outputs, as large as the codes (up to 448),
+    so the bound is relative to each head's output scale (its largest |o|): the FP8 kernel carries the query and
+    the probabilities as two E4M3 terms (about the 8 significant bits of bf16) and rounds in other places than the
+    bf16 kernel, and two such results agree to a few units of bf16 rounding of that scale (2^-6 allowed; mean
+    2^-9). The lse agrees to 1e-4 relative."""
     ta = require_gpu()
     w = WORKLOADS["mla_decode_b32"]
     inp = mla_inputs(w, seed=43, batch=2, seqlen=700, seq_lens=[700, 333], kv="fp8")
@@ -72,8 +76,17 @@ def test_mla_fp8_unit_scales_match_bf16_kernel_on_decoded_cache():
     ob, lb = ta.attn_mla_decode(dev_bf16(inp["q_lat"]), dev_bf16(inp["q_pe"]), dev_bf16(to_bits(inp["c_kv"])),
                                 dev_bf16(to_bits(inp["k_pe"])), dev(inp["seq_lens"]), w.scale, return_lse=True)
     torch.cuda.synchronize()
-    check("q8 vs bf16", bits_to_f32(o8), bits_to_f32(host_bf16(ob)), BF16_MAX, BF16_MEAN)
-    check("lse", l8, lb.cpu().numpy(), BF16_MAX, BF16_MEAN)
+    a, b = bits_to_f32(o8).astype(np.float64), bits_to_f32(host_bf16(ob)).astype(np.float64)
+    assert np.all(np.isfinite(a)) and np.all(np.isfinite(b))
+    scale = np.maximum(np.abs(b).max(axis=-1, keepdims=True), 1e-3)      # per (sequence, head)
+    rel = np.abs(a - b) / scale
+    say(f"  q8 vs bf16: max {rel.max():.3e}, mean {rel.mean():.3e} of each head's output scale "
+        f"(max |o| {np.abs(b).max():.1f})")
+    assert rel.max() <= 2.0 ** -6 and rel.mean() <= 2.0 ** -9, (rel.max(), rel.mean())
+    la, lb_ = l8.astype(np.float64), lb.cpu().numpy().astype(np.float64)
+    lrel = np.abs(la - lb_) / np.maximum(np.abs(lb_), 1.0)
+    say(f"  lse: max relative difference {lrel.max():.3e}")
+    assert lrel.max() <= 1e-4, lrel.max()
 
 
 def test_mla_q8_is_deterministic():

@@ -57,6 +57,29 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// v_mfma_scale_f32_16x16x128_f8f6f4 with both operands FP8 E4M3 (OCP: 0x38 is 1.0) and unit scales:
+// D[16x16] += A[16x128] * B[128x16]. Lane l holds row l%16 of A (32 codes) and column l%16 of B (32 codes), and
+// the K index of each of those 32 bytes is the same function of (l / 16, byte) for A and B, so a kernel may assign
+// K positions to (lane group, byte) as it likes as long as both operands follow it. D as for the 16x16x32 form.
+// (Measured on gfx950 with small integers, which the products and sums keep exact.)
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4_t mfma16x16x128_fp8(i32x8_t a, i32x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// FP8 E4M3 (OCP) conversions, round to nearest even: two fp32 into word `hi` of `old`, and the two codes of word
+// `hi` of `w` back to fp32 (exact).
+__device__ __forceinline__ uint32_t f32x2_to_fp8(uint32_t old, float a, float b, bool hi) {
+  typedef short s16x2_t __attribute__((ext_vector_type(2)));
+  const s16x2_t o = __builtin_bit_cast(s16x2_t, old);
+  return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, 1.0f, true)
+                                         : __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(o, a, b, 1.0f, false));
+}
+__device__ __forceinline__ f32x2_t fp8x2_to_f32(uint32_t w, bool hi) {
+  return hi ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true)
+            : __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+}
+
 // ------------------------------------------------------------------------------------- 8-bit cache codes --
 // Cache element kinds: 0 bf16, 1 FP8 E4M3 codes, 2 int8 codes (the 8-bit kinds carry per-channel scales). Every
 // E4M3 and int8 value is exact in bf16, so codes become bf16 MFMA operands by exact conversion.
@@ -103,6 +126,15 @@ __device__ __forceinline__ u32x4_t lds_read16(const uint8_t* __restrict__ lds_ba
 __device__ __forceinline__ u32x2_t lds_read8(const uint8_t* __restrict__ lds_base, uint32_t byte_off) {
   return *(const __attribute__((address_space(3))) u32x2_t*)((const __attribute__((address_space(3))) char*)lds_base +
                                                                 byte_off);
+}
+
+// Transposing 8-byte read of 8-bit elements: within each block of 16 lanes, result lane i, byte j is byte i%8 of
+// the 8 bytes addressed by lane 2*j + i/8 of the block (measured on gfx950).
+__device__ __forceinline__ u32x2_t lds_read_tr8(const uint8_t* __restrict__ lds_base, uint32_t byte_off) {
+  typedef int i32x2_t __attribute__((ext_vector_type(2)));
+  i32x2_t t = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+      (__attribute__((address_space(3))) i32x2_t*)((__attribute__((address_space(3))) const char*)lds_base + byte_off));
+  return __builtin_bit_cast(u32x2_t, t);
 }
 
 // Transposing 8-byte LDS read (see the layout note at the top of this file).

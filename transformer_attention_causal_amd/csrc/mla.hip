@@ -24,11 +24,14 @@
 //     instruction of a latent row takes its token from the list (a lane read of the tile's index vector into the
 //     scalar offset), the rope rows take theirs per lane; list entries outside [0, L) are masked like the tail.
 //   * 8-bit latent cache (FP8 E4M3 or int8 codes with per-channel scales; DeepSeek 32K to 256K long context,
-//     tqpw.cn, section 2.5; 7 anti-patterns of DeepSeek attention optimisation, lpnh.cn, section 3.3): codes are
-//     staged in LDS, widened exactly into the bf16 tile by all waves between two barriers, and the product code
-//     above runs unchanged; key scales fold into the query, value scales multiply the output channels.
+//     tqpw.cn, section 2.5; 7 anti-patterns of DeepSeek attention optimisation, lpnh.cn, section 3.3); key scales
+//     fold into the query, value scales multiply the output channels. FP8 codes go straight to the FP8 matrix
+//     cores (mla_split_fp8mma_kernel, below). int8 codes are staged in LDS, widened exactly into the bf16 tile by
+//     all waves between two barriers, and the product code above runs unchanged.
 // HBM-bound in principle (about 240 flop per byte) but close to the MFMA ridge, so both matter; measured, the
 // LDS fragment reads (three in flight per wave) are what bound it.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 
@@ -39,6 +42,10 @@ constexpr int kC = 512;             // kv_lora_rank
 constexpr int kR = 64;              // rope dim
 constexpr int kDK = kC + kR;        // key width
 constexpr int kTargetBlocks = 256;  // one workgroup per compute unit on MI355X
+// FP8 latent caches on the FP8 matrix cores (1), or widened into bf16 tiles like int8 (0).
+#ifndef ATTN_MLA_FP8_MMA
+#define ATTN_MLA_FP8_MMA 1
+#endif
 #ifndef ATTN_MLA_COPY_AUX
 #define ATTN_MLA_COPY_AUX 2         // tile copies non-temporal: every cache row is read once (measured 3-7% faster)
 #endif
@@ -452,6 +459,342 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(MlaArgs a) {
   if (g4 == 0) a.ws_lse[slot] = (SPARSE && lt == 0.f) ? -INFINITY : m * a.scale + logf(lt);
 }
 
+// ---- FP8 latent cache on the FP8 matrix cores.
+// The codes stay 8-bit all the way: tiles of 64 tokens are copied into LDS as codes, and both products run on
+// v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 x E4M3, unit scales). The bf16 query and the probabilities are carried
+// as two E4M3 terms each (hi = e4m3(x), lo = e4m3(x - hi): about 8 significant bits, like bf16), so the matrix-core
+// time equals the bf16 kernel's (FP8 runs at twice the bf16 rate), while the LDS fragment bytes and the HBM bytes
+// halve and the widening pass disappears.
+//   * Query: q' = q * c_scale (a key channel's scale folds into the query) times a power of two per head, 2^k,
+//     that brings the head's largest |q'| into [128, 256), then split; scores come out multiplied by 2^k, and that
+//     head's softmax constant is scale * log2(e) / 2^k.
+//   * Scores S^T (16 tokens x 16 heads per MFMA) take the query's hi and lo terms in two MFMAs over the same key
+//     fragment. K positions: K-step ks (128 of the 512 latent channels) gives lane group g the 16-channel chunks
+//     4ks + 2(g>>1) + 16(g&1) + e, e = 0, 1; the rope K-step holds the 64 rope channels twice (A: the codes twice;
+//     B: the hi term in groups 0-1, the lo term in groups 2-3). Lane holds head n = l%16, tokens 16tb + 4g + r.
+//   * O^T = V^T P^T in one MFMA per 16 latent channels and tile: lane group g's 32 K positions are its own 16
+//     tokens twice, 4tb + r for the hi term of token 16tb + 4g + r and 16 + 4tb + r for its lo term, so P^T is
+//     packed straight from the score registers and V^T needs two ds_read_b64_tr_b8 reads, used twice.
+//   * LDS: latent rows of 512 codes at a 528-byte pitch, 16-byte chunk c of row r stored at chunk c ^ 8*((r>>4)&1);
+//     rope rows of 64 codes, chunk c at c ^ ((r>>2)&1). Both read patterns are conflict-free under the measured
+//     bank model (checked exhaustively on the CPU), and each read is a per-lane base plus an immediate.
+//   * Probabilities are carried as 2^7 * exp(s - m) with the reference max m moved whenever the max grows by more
+//     than a factor of 2, so they stay below 256 (E4M3 reaches 448) and the subnormal range of the lo term starts
+//     2^13 below the largest probability; the factor cancels in O = sum p v / sum p.
+//   * The tile loop's LDS reads are inline assembly, each pair with its own wait: compiled reads got a vmcnt wait
+//     for every next-tile copy in flight (the compiler cannot tell the copies fill the other buffer). A fragment is
+//     read right after the products of the previous one are issued, so its latency overlaps those products. The
+//     register file is full (252 of 256 at two waves per SIMD: the 512 x 16 output, the split query), which rules
+//     out deeper read-ahead. Measured 0.295 ms against 0.301 ms for the widening kernel on the same box.
+constexpr int kRowsF8 = 64;                            // tokens per tile
+constexpr float kRescaleLog2F8 = 1.0f;                 // lazy-rescale threshold (log2 units)
+constexpr float kPExpF8 = 7.0f;                        // probabilities carried times 2^7
+constexpr int kLatPitch = 528;                         // LDS bytes per latent row (512 codes + 16)
+constexpr int kLatBytes = kRowsF8 * kLatPitch;
+constexpr int kPeBytesF8 = kRowsF8 * kR;
+constexpr int kLatCopies = kLatBytes / 1024;          // 33 copy instructions of 1 KiB
+constexpr int kCopiesF8 = kLatCopies + kPeBytesF8 / 1024;   // + 4 for the rope rows
+static_assert(kLatBytes % 1024 == 0 && kPeBytesF8 % 1024 == 0, "tiles split into 1 KiB copy instructions");
+
+// Copy instruction ci (wave-uniform) of a tile: latent instructions fill LDS bytes [1024 ci, 1024 ci + 1024) of the
+// padded latent tile (pad bytes read out of range: zeros), rope instructions 16 rope rows each. Rows past the
+// resources (the end of the split) read zeros.
+__device__ __forceinline__ void mla_f8_copy(uint8_t* lat, uint8_t* pe, const buf_rsrc_t& rc, const buf_rsrc_t& rp,
+                                            int ci, int lane) {
+  if (ci < kLatCopies) {
+    const uint32_t at = uint32_t(1024 * ci + 16 * lane);
+    const uint32_t row = at / kLatPitch, col = at - row * kLatPitch;
+    const uint32_t chunk = (col >> 4) ^ (((row >> 4) & 1u) << 3);
+    load_lds16<ATTN_MLA_COPY_AUX>(rc, col < 512u ? row * 512u + 16u * chunk : 0x80000000u, lat + 1024 * ci);
+  } else {
+    const int i = ci - kLatCopies;
+    const uint32_t row = uint32_t(16 * i + (lane >> 2));
+    const uint32_t chunk = uint32_t(lane & 3) ^ ((row >> 2) & 1u);
+    load_lds16<ATTN_MLA_COPY_AUX>(rp, row * 64u + 16u * chunk, pe + 1024 * i);
+  }
+}
+
+// Resources over the codes of tokens t_tile .. min(t_tile + 64, t_end) - 1 of sequence b.
+__device__ __forceinline__ void mla_rsrc_f8(const MlaArgs& a, int b, int t_tile, int t_end, buf_rsrc_t& rc,
+                                            buf_rsrc_t& rp) {
+  const int rows = max(0, min(kRowsF8, t_end - t_tile));
+  const int64_t tok0 = int64_t(b) * a.max_len + min(t_tile, max(t_end - 1, 0));
+  rc = make_buf_rsrc(reinterpret_cast<const uint8_t*>(a.c_kv) + tok0 * kC, uint32_t(rows * kC));
+  rp = make_buf_rsrc(reinterpret_cast<const uint8_t*>(a.k_pe) + tok0 * kR, uint32_t(rows * kR));
+}
+
+// LDS reads of the FP8 kernel, written out in inline assembly with their own lgkmcnt(0) wait: compiled reads
+// after an in-flight direct-to-LDS copy get a vmcnt(0) wait for that copy (the compiler cannot tell that the copy
+// fills the other tile buffer), which serialised every next-tile copy behind the reads.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) char*)p));
+}
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+// 32 bytes: 16 at addr + OFF and 16 at addr + OFF + STEP.
+template <int OFF, int STEP>
+__device__ __forceinline__ i32x8_t lds_read32_asm(uint32_t addr) {
+  u32x4_t x, y;
+  asm volatile("ds_read_b128 %0, %2 offset:%3\n\tds_read_b128 %1, %2 offset:%4\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(x), "=&v"(y)
+               : "v"(addr), "n"(OFF), "n"(OFF + STEP)
+               : "memory");
+  return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// 32 bytes: 16 at a0 + OFF and 16 at a1 + OFF.
+template <int OFF>
+__device__ __forceinline__ i32x8_t lds_read32_asm2(uint32_t a0, uint32_t a1) {
+  u32x4_t x, y;
+  asm volatile("ds_read_b128 %0, %2 offset:%4\n\tds_read_b128 %1, %3 offset:%4\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(x), "=&v"(y)
+               : "v"(a0), "v"(a1), "n"(OFF)
+               : "memory");
+  return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// V^T operand: transposing 8-byte reads at addr + OFF and addr + OFF + STEP, each used twice (hi and lo positions).
+template <int OFF, int STEP>
+__device__ __forceinline__ i32x8_t lds_read_v_asm(uint32_t addr) {
+  u32x2_t x, y;
+  asm volatile("ds_read_b64_tr_b8 %0, %2 offset:%3\n\tds_read_b64_tr_b8 %1, %2 offset:%4\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(x), "=&v"(y)
+               : "v"(addr), "n"(OFF), "n"(OFF + STEP)
+               : "memory");
+  return i32x8_t{int(x[0]), int(x[1]), int(y[0]), int(y[1]), int(x[0]), int(x[1]), int(y[0]), int(y[1])};
+}
+
+// 16 fp32 values (scaled) -> their hi and lo E4M3 terms, four dwords each, in order.
+__device__ __forceinline__ void split_e4m3_16(const float (&v)[16], uint32_t* hi, uint32_t* lo) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    uint32_t hw = f32x2_to_fp8(0u, v[4 * d], v[4 * d + 1], false);
+    hw = f32x2_to_fp8(hw, v[4 * d + 2], v[4 * d + 3], true);
+    const f32x2_t d0 = fp8x2_to_f32(hw, false), d1 = fp8x2_to_f32(hw, true);
+    uint32_t lw = f32x2_to_fp8(0u, v[4 * d] - d0[0], v[4 * d + 1] - d0[1], false);
+    lw = f32x2_to_fp8(lw, v[4 * d + 2] - d1[0], v[4 * d + 3] - d1[1], true);
+    hi[d] = hw;
+    lo[d] = lw;
+  }
+}
+
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void mla_split_fp8mma_kernel(MlaArgs a) {
+  constexpr int NC = (kCopiesF8 + NW - 1) / NW;       // copy instructions per wave per tile
+  __shared__ __attribute__((aligned(16))) uint8_t lat[2][kLatBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t pe[2][kPeBytesF8];
+  // the rope K-step's query operand (32 bytes per lane) waits in LDS, two 16-byte planes per wave: registers are
+  // the limit of this kernel
+  __shared__ __attribute__((aligned(16))) uint8_t qrl[NW][2][64 * 16];
+  const int split = blockIdx.x, b = blockIdx.y;
+  const int wave = int(unsigned(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) % unsigned(NW));
+  const int lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int L = max(0, min(a.seq_lens[b], a.max_len));
+  const int t_begin = split * a.split_len;
+  if (t_begin >= L) return;                            // uniform over the workgroup
+  const int t_end = min(L, t_begin + a.split_len);
+  const int ntiles = (t_end - t_begin + kRowsF8 - 1) / kRowsF8;
+  const int h = wave * kHeadsPerWave + n;
+  {
+    buf_rsrc_t rc, rp;
+    mla_rsrc_f8(a, b, t_begin, t_end, rc, rp);
+#pragma unroll
+    for (int k = 0; k < NC; ++k)
+      if (wave + k * NW < kCopiesF8) mla_f8_copy(lat[0], pe[0], rc, rp, wave + k * NW, lane);
+  }
+
+  // ---- query: hi and lo E4M3 terms of q * scale * 2^k
+  const uint16_t* qlat = a.q_lat + (int64_t(b) * a.heads + h) * kC;
+  const uint16_t* qpe = a.q_pe + (int64_t(b) * a.heads + h) * kR;
+  auto lat_chunk = [&](int ks, int e) { return 4 * ks + 2 * (g >> 1) + 16 * (g & 1) + e; };
+  auto qvals = [&](const uint16_t* q, const float* sc, int c, float mul, float (&v)[16]) {
+    const u32x4_t w0 = *reinterpret_cast<const u32x4_t*>(q + c), w1 = *reinterpret_cast<const u32x4_t*>(q + c + 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(sc + c + 4 * i);
+      const uint32_t wa = i < 2 ? w0[2 * i] : w1[2 * i - 4], wb = i < 2 ? w0[2 * i + 1] : w1[2 * i - 3];
+      v[4 * i] = bf16lo_to_f32(wa) * sv[0] * mul;
+      v[4 * i + 1] = bf16hi_to_f32(wa) * sv[1] * mul;
+      v[4 * i + 2] = bf16lo_to_f32(wb) * sv[2] * mul;
+      v[4 * i + 3] = bf16hi_to_f32(wb) * sv[3] * mul;
+    }
+  };
+  float mx = 0.f;
+  {
+    float v[16];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        qvals(qlat, a.c_scale, 16 * lat_chunk(ks, e), 1.f, v);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(v[i]));
+      }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      qvals(qpe, a.pe_scale, 32 * (g & 1) + 16 * e, 1.f, v);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(v[i]));
+    }
+  }
+  mx = fmaxf(mx, xor_lanes(mx, 16));
+  mx = fmaxf(mx, xor_lanes(mx, 32));
+  int ex = 0;
+  (void)frexpf(mx, &ex);
+  const int kexp = mx > 0.f ? max(-64, min(64, 8 - ex)) : 0;
+  const float up = ldexpf(1.f, kexp);
+  const float c = ldexpf(a.scale * kLog2e, -kexp);      // softmax constant in the scaled score units
+  i32x8_t qh[4], qlo[4];
+  {
+    float v[16];
+    uint32_t hw[8], lw[8];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        qvals(qlat, a.c_scale, 16 * lat_chunk(ks, e), up, v);
+        split_e4m3_16(v, hw + 4 * e, lw + 4 * e);
+      }
+      qh[ks] = i32x8_t{int(hw[0]), int(hw[1]), int(hw[2]), int(hw[3]), int(hw[4]), int(hw[5]), int(hw[6]), int(hw[7])};
+      qlo[ks] = i32x8_t{int(lw[0]), int(lw[1]), int(lw[2]), int(lw[3]), int(lw[4]), int(lw[5]), int(lw[6]), int(lw[7])};
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      qvals(qpe, a.pe_scale, 32 * (g & 1) + 16 * e, up, v);
+      split_e4m3_16(v, hw + 4 * e, lw + 4 * e);
+    }
+    const uint32_t* t = g < 2 ? hw : lw;
+    *reinterpret_cast<u32x4_t*>(&qrl[wave][0][16 * lane]) = u32x4_t{t[0], t[1], t[2], t[3]};
+    *reinterpret_cast<u32x4_t*>(&qrl[wave][1][16 * lane]) = u32x4_t{t[4], t[5], t[6], t[7]};
+  }
+
+  f32x4_t oacc[kC / 16];
+#pragma unroll
+  for (int db = 0; db < kC / 16; ++db) oacc[db] = f32x4_t{};
+  float m = -INFINITY, l = 0.f;
+
+  // lane-fixed LDS read bases (layout above)
+  const uint32_t kb = uint32_t(kLatPitch * n + 32 * (g >> 1) + 256 * (g & 1));     // latent K reads
+  const uint32_t q2 = uint32_t((n >> 2) & 1);
+  const uint32_t rb0 = uint32_t(64 * n + 32 * (g & 1)) + 16u * q2;                   // rope K reads, e = 0
+  const uint32_t rb1 = uint32_t(64 * n + 32 * (g & 1)) + 16u * (1u - q2);            // e = 1
+  const int jp = (lane & 15) >> 1, vs = jp >> 2;                                     // V^T reads
+  const uint32_t vrow = uint32_t((16 * vs + 4 * g + (jp & 3)) * kLatPitch + 8 * (lane & 1));
+  const uint32_t va = vrow + 128u * uint32_t(vs), vb = vrow - 128u * uint32_t(vs);
+  const uint32_t qa = lds_u32(&qrl[0][0][0]) + uint32_t(2048 * wave + 16 * lane);    // this lane's rope query
+
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmem();
+    __syncthreads();                                   // tile t visible to all; buffer (t+1)&1 free
+    const int tok0 = t_begin + t * kRowsF8;
+    buf_rsrc_t rcn, rpn;
+    mla_rsrc_f8(a, b, tok0 + kRowsF8, t_end, rcn, rpn);
+    const uint8_t* Lt = lat[t & 1];
+    const uint8_t* Pt = pe[t & 1];
+    uint8_t* Ln = lat[(t + 1) & 1];
+    uint8_t* Pn = pe[(t + 1) & 1];
+    f32x4_t sacc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sacc[i] = f32x4_t{};
+    const uint32_t lk = lds_u32(Lt) + kb, lr0 = lds_u32(Pt) + rb0, lr1 = lds_u32(Pt) + rb1;
+    static_for<4>([&](auto tbc) {
+      constexpr int tb = decltype(tbc)::value;
+      // key fragment of K-step ks: row 16tb + n, chunk (4ks + ...) ^ 8 * (tb & 1) (see the layout)
+      constexpr int k0 = 16 * kLatPitch * tb + ((tb & 1) ? 128 : 0);
+      i32x8_t cur = lds_read32_asm<k0, 16>(lk);
+      static_for<4>([&](auto ksc) {
+        constexpr int ks = decltype(ksc)::value;
+        sacc[tb] = mfma16x16x128_fp8(cur, qh[ks], sacc[tb]);
+        sacc[tb] = mfma16x16x128_fp8(cur, qlo[ks], sacc[tb]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ks < 3) {
+          constexpr int kn = 16 * kLatPitch * tb + 64 * (ks + 1) + ((tb & 1) ? (ks + 1 < 2 ? 128 : -128) : 0);
+          cur = lds_read32_asm<kn, 16>(lk);
+        }
+      });
+      const i32x8_t rf = lds_read32_asm2<1024 * tb>(lr0, lr1);
+      const i32x8_t qr = lds_read32_asm<0, 1024>(qa);
+      sacc[tb] = mfma16x16x128_fp8(rf, qr, sacc[tb]);
+      __builtin_amdgcn_sched_barrier(0);
+      // next tile's copies, spread over the score products
+      if (t + 1 < ntiles) {
+#pragma unroll
+        for (int k = 0; k < NC; ++k)
+          if (k % 4 == tb && wave + k * NW < kCopiesF8) mla_f8_copy(Ln, Pn, rcn, rpn, wave + k * NW, lane);
+      }
+    });
+    if (tok0 + kRowsF8 > t_end) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sacc[tb][r] = tok0 + 16 * tb + 4 * g + r >= t_end ? -INFINITY : sacc[tb][r];
+    }
+    float hm = -INFINITY;
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) hm = fmaxf(hm, sacc[tb][r]);
+    hm = fmaxf(hm, xor_lanes(hm, 16));
+    hm = fmaxf(hm, xor_lanes(hm, 32));
+    if (__any((hm - m) * c > kRescaleLog2F8)) {
+      const float m_new = fmaxf(m, hm);
+      const float alpha = fast_exp2((m - m_new) * c);
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < kC / 16; ++db) oacc[db] *= alpha;
+      m = m_new;
+    }
+    const float mc = m * c - kPExpF8;
+    uint32_t ph[4], pl[4];                             // P^T: hi and lo codes, one dword per 16-token block
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = fast_exp2(fmaf(sacc[tb][r], c, -mc));
+        l += p[r];
+      }
+      uint32_t hw = f32x2_to_fp8(0u, p[0], p[1], false);
+      hw = f32x2_to_fp8(hw, p[2], p[3], true);
+      const f32x2_t d0 = fp8x2_to_f32(hw, false), d1 = fp8x2_to_f32(hw, true);
+      const uint32_t lw = f32x2_to_fp8(0u, p[0] - d0[0], p[1] - d0[1], false);
+      ph[tb] = hw;
+      pl[tb] = f32x2_to_fp8(lw, p[2] - d1[0], p[3] - d1[1], true);
+    }
+    const i32x8_t bp = i32x8_t{int(ph[0]), int(ph[1]), int(ph[2]), int(ph[3]), int(pl[0]), int(pl[1]), int(pl[2]),
+                               int(pl[3])};
+    // O^T += V^T P^T: 16 latent channels per MFMA; the two V^T reads (16 tokens) serve the hi and lo positions
+    const uint32_t lva = lds_u32(Lt) + va, lvb = lds_u32(Lt) + vb;
+    i32x8_t vf = lds_read_v_asm<0, 32 * kLatPitch>(lva);
+    static_for<kC / 16>([&](auto dbc) {
+      constexpr int db = decltype(dbc)::value;
+      oacc[db] = mfma16x16x128_fp8(vf, bp, oacc[db]);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (db + 1 < kC / 16) {
+        if constexpr (((db + 1) & 8) != 0) vf = lds_read_v_asm<16 * (db + 1), 32 * kLatPitch>(lvb);
+        else vf = lds_read_v_asm<16 * (db + 1), 32 * kLatPitch>(lva);
+      }
+    });
+  }
+
+  float lt = l + xor_lanes(l, 16);
+  lt += xor_lanes(lt, 32);
+  const float inv = 1.f / lt;
+  const int64_t slot = (int64_t(b) * a.heads + h) * a.n_split + split;
+  float* wo = a.ws_o + slot * kC + 4 * g;
+#pragma unroll
+  for (int db = 0; db < kC / 16; ++db) {
+    f32x4_t v = {oacc[db][0] * inv, oacc[db][1] * inv, oacc[db][2] * inv, oacc[db][3] * inv};
+    v *= *reinterpret_cast<const f32x4_t*>(a.c_scale + 16 * db + 4 * g);   // code * s
+    *reinterpret_cast<f32x4_t*>(wo + 16 * db) = v;
+  }
+  if (g == 0) a.ws_lse[slot] = m * ldexpf(a.scale, -kexp) + logf(lt) - kPExpF8 * 0.6931471805599453f;
+}
+
 // Merge splits: M = max lse_s, w_s = exp(lse_s - M), O = sum w_s O_s / sum w_s; length 0 -> O = 0, lse = -inf.
 __global__ __launch_bounds__(256) void mla_combine_kernel(const float* __restrict__ ws_o,
     const float* __restrict__ ws_lse, const int32_t* __restrict__ seq_lens, uint16_t* __restrict__ o,
@@ -581,15 +924,24 @@ hipError_t launch_mla_decode_q8(const void* q_latent, const void* q_pe, const vo
   if (max_seqlen_kv > 0) {
     const dim3 grid(unsigned(a.n_split), unsigned(batch)), block(64 * (n_heads / kHeadsPerWave));
     const bool fp8 = kind == kKvFp8;
-    switch (n_heads / kHeadsPerWave) {
-      case 2: fp8 ? mla_split_kernel<2, false, kKvFp8><<<grid, block, 0, stream>>>(a)
-                  : mla_split_kernel<2, false, kKvInt8><<<grid, block, 0, stream>>>(a); break;
-      case 4: fp8 ? mla_split_kernel<4, false, kKvFp8><<<grid, block, 0, stream>>>(a)
-                  : mla_split_kernel<4, false, kKvInt8><<<grid, block, 0, stream>>>(a); break;
-      case 6: fp8 ? mla_split_kernel<6, false, kKvFp8><<<grid, block, 0, stream>>>(a)
-                  : mla_split_kernel<6, false, kKvInt8><<<grid, block, 0, stream>>>(a); break;
-      default: fp8 ? mla_split_kernel<8, false, kKvFp8><<<grid, block, 0, stream>>>(a)
-                   : mla_split_kernel<8, false, kKvInt8><<<grid, block, 0, stream>>>(a); break;
+    if (fp8 && ATTN_MLA_FP8_MMA) {
+      switch (n_heads / kHeadsPerWave) {
+        case 2: mla_split_fp8mma_kernel<2><<<grid, block, 0, stream>>>(a); break;
+        case 4: mla_split_fp8mma_kernel<4><<<grid, block, 0, stream>>>(a); break;
+        case 6: mla_split_fp8mma_kernel<6><<<grid, block, 0, stream>>>(a); break;
+        default: mla_split_fp8mma_kernel<8><<<grid, block, 0, stream>>>(a); break;
+      }
+    } else {
+      switch (n_heads / kHeadsPerWave) {
+        case 2: fp8 ? mla_split_kernel<2, false, kKvFp8><<<grid, block, 0, stream>>>(a)
+                    : mla_split_kernel<2, false, kKvInt8><<<grid, block, 0, stream>>>(a); break;
+        case 4: fp8 ? mla_split_kernel<4, false, kKvFp8><<<grid, block, 0, stream>>>(a)
+                    : mla_split_kernel<4, false, kKvInt8><<<grid, block, 0, stream>>>(a); break;
+        case 6: fp8 ? mla_split_kernel<6, false, kKvFp8><<<grid, block, 0, stream>>>(a)
+                    : mla_split_kernel<6, false, kKvInt8><<<grid, block, 0, stream>>>(a); break;
+        default: fp8 ? mla_split_kernel<8, false, kKvFp8><<<grid, block, 0, stream>>>(a)
+                     : mla_split_kernel<8, false, kKvInt8><<<grid, block, 0, stream>>>(a); break;
+      }
     }
   }
   mla_combine_kernel<<<dim3(unsigned(n_heads), unsigned(batch)), dim3(kC / 2), 0, stream>>>(
