@@ -481,11 +481,12 @@ __global__ __launch_bounds__(64 * NW) void mla_split_kernel(MlaArgs a) {
 //   * Probabilities are carried as 2^7 * exp(s - m) with the reference max m moved whenever the max grows by more
 //     than a factor of 2, so they stay below 256 (E4M3 reaches 448) and the subnormal range of the lo term starts
 //     2^13 below the largest probability; the factor cancels in O = sum p v / sum p.
-//   * The tile loop's LDS reads are inline assembly, each pair with its own wait: compiled reads got a vmcnt wait
-//     for every next-tile copy in flight (the compiler cannot tell the copies fill the other buffer). A fragment is
-//     read right after the products of the previous one are issued, so its latency overlaps those products. The
-//     register file is full (252 of 256 at two waves per SIMD: the 512 x 16 output, the split query), which rules
-//     out deeper read-ahead. Measured 0.295 ms against 0.301 ms for the widening kernel on the same box.
+//   * The tile loop's LDS reads are inline assembly, each block with its own wait: compiled reads got a vmcnt wait
+//     for every next-tile copy in flight (the compiler cannot tell the copies fill the other buffer). A block reads
+//     the fragments of two K-steps (four products) or four 16-channel value blocks (four products) and is issued
+//     right after the previous block's products, so its latency overlaps them. The register file is full (256 at
+//     two waves per SIMD: the 512 x 16 output and the split query take 192), which bounds the blocks. Measured
+//     0.281-0.285 ms against 0.304 ms for the widening kernel on the same box (one read per product: 0.295).
 constexpr int kRowsF8 = 64;                            // tokens per tile
 constexpr float kRescaleLog2F8 = 1.0f;                 // lazy-rescale threshold (log2 units)
 constexpr float kPExpF8 = 7.0f;                        // probabilities carried times 2^7
@@ -565,6 +566,71 @@ __device__ __forceinline__ i32x8_t lds_read_v_asm(uint32_t addr) {
                : "v"(addr), "n"(OFF), "n"(OFF + STEP)
                : "memory");
   return i32x8_t{int(x[0]), int(x[1]), int(y[0]), int(y[1]), int(x[0]), int(x[1]), int(y[0]), int(y[1])};
+}
+
+// Two 32-byte key fragments (K-steps at OFF0 and OFF1: 16 bytes there and 16 bytes after).
+template <int OFF0, int OFF1>
+__device__ __forceinline__ void lds_read_k2_asm(uint32_t addr, i32x8_t& f0, i32x8_t& f1) {
+  u32x4_t a, b, c, d;
+  asm volatile("ds_read_b128 %0, %4 offset:%5\n\tds_read_b128 %1, %4 offset:%6\n\t"
+               "ds_read_b128 %2, %4 offset:%7\n\tds_read_b128 %3, %4 offset:%8\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
+               : "v"(addr), "n"(OFF0), "n"(OFF0 + 16), "n"(OFF1), "n"(OFF1 + 16)
+               : "memory");
+  f0 = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+  f1 = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(c, d, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// The rope key fragment (16 bytes at r0 + OFF and r1 + OFF) and the rope query operand (q and q + 1024).
+template <int OFF>
+__device__ __forceinline__ void lds_read_rq_asm(uint32_t r0, uint32_t r1, uint32_t q, i32x8_t& rf, i32x8_t& qf) {
+  u32x4_t a, b, c, d;
+  asm volatile("ds_read_b128 %0, %4 offset:%7\n\tds_read_b128 %1, %5 offset:%7\n\t"
+               "ds_read_b128 %2, %6\n\tds_read_b128 %3, %6 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
+               : "v"(r0), "v"(r1), "v"(q), "n"(OFF)
+               : "memory");
+  rf = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+  qf = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(c, d, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// Two V^T operands (latent chunks at a0 + OFF0 and a1 + OFF1): each is two transposing reads (tokens 0-31 and
+// 32-63 of the tile, STEP apart) read twice, for the hi and the lo K positions.
+template <int OFF0, int OFF1, int STEP>
+__device__ __forceinline__ void lds_read_v2_asm(uint32_t a0, uint32_t a1, i32x8_t& v0, i32x8_t& v1) {
+  u32x2_t w0, w1, w2, w3, w4, w5, w6, w7;
+  asm volatile("ds_read_b64_tr_b8 %0, %8 offset:%10\n\tds_read_b64_tr_b8 %1, %8 offset:%11\n\t"
+               "ds_read_b64_tr_b8 %2, %8 offset:%10\n\tds_read_b64_tr_b8 %3, %8 offset:%11\n\t"
+               "ds_read_b64_tr_b8 %4, %9 offset:%12\n\tds_read_b64_tr_b8 %5, %9 offset:%13\n\t"
+               "ds_read_b64_tr_b8 %6, %9 offset:%12\n\tds_read_b64_tr_b8 %7, %9 offset:%13\n\ts_waitcnt lgkmcnt(0)"
+               : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(w4), "=&v"(w5), "=&v"(w6), "=&v"(w7)
+               : "v"(a0), "v"(a1), "n"(OFF0), "n"(OFF0 + STEP), "n"(OFF1), "n"(OFF1 + STEP)
+               : "memory");
+  v0 = i32x8_t{int(w0[0]), int(w0[1]), int(w1[0]), int(w1[1]), int(w2[0]), int(w2[1]), int(w3[0]), int(w3[1])};
+  v1 = i32x8_t{int(w4[0]), int(w4[1]), int(w5[0]), int(w5[1]), int(w6[0]), int(w6[1]), int(w7[0]), int(w7[1])};
+}
+
+// Four V^T operands (latent chunks at a + OFF + 16 i, i = 0..3, all on one side of the swizzle's 128-byte shift).
+template <int OFF, int STEP>
+__device__ __forceinline__ void lds_read_v4_asm(uint32_t a, i32x8_t (&v)[4]) {
+  u32x2_t w[16];
+  asm volatile("ds_read_b64_tr_b8 %0, %16 offset:%17\n\tds_read_b64_tr_b8 %1, %16 offset:%18\n\t"
+               "ds_read_b64_tr_b8 %2, %16 offset:%17\n\tds_read_b64_tr_b8 %3, %16 offset:%18\n\t"
+               "ds_read_b64_tr_b8 %4, %16 offset:%19\n\tds_read_b64_tr_b8 %5, %16 offset:%20\n\t"
+               "ds_read_b64_tr_b8 %6, %16 offset:%19\n\tds_read_b64_tr_b8 %7, %16 offset:%20\n\t"
+               "ds_read_b64_tr_b8 %8, %16 offset:%21\n\tds_read_b64_tr_b8 %9, %16 offset:%22\n\t"
+               "ds_read_b64_tr_b8 %10, %16 offset:%21\n\tds_read_b64_tr_b8 %11, %16 offset:%22\n\t"
+               "ds_read_b64_tr_b8 %12, %16 offset:%23\n\tds_read_b64_tr_b8 %13, %16 offset:%24\n\t"
+               "ds_read_b64_tr_b8 %14, %16 offset:%23\n\tds_read_b64_tr_b8 %15, %16 offset:%24\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]), "=&v"(w[6]),
+                 "=&v"(w[7]), "=&v"(w[8]), "=&v"(w[9]), "=&v"(w[10]), "=&v"(w[11]), "=&v"(w[12]), "=&v"(w[13]),
+                 "=&v"(w[14]), "=&v"(w[15])
+               : "v"(a), "n"(OFF), "n"(OFF + STEP), "n"(OFF + 16), "n"(OFF + 16 + STEP), "n"(OFF + 32),
+                 "n"(OFF + 32 + STEP), "n"(OFF + 48), "n"(OFF + 48 + STEP)
+               : "memory");
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    v[i] = i32x8_t{int(w[4 * i][0]), int(w[4 * i][1]), int(w[4 * i + 1][0]), int(w[4 * i + 1][1]),
+                   int(w[4 * i + 2][0]), int(w[4 * i + 2][1]), int(w[4 * i + 3][0]), int(w[4 * i + 3][1])};
 }
 
 // 16 fp32 values (scaled) -> their hi and lo E4M3 terms, four dwords each, in order.
@@ -703,21 +769,24 @@ __global__ __launch_bounds__(64 * NW) void mla_split_fp8mma_kernel(MlaArgs a) {
     const uint32_t lk = lds_u32(Lt) + kb, lr0 = lds_u32(Pt) + rb0, lr1 = lds_u32(Pt) + rb1;
     static_for<4>([&](auto tbc) {
       constexpr int tb = decltype(tbc)::value;
-      // key fragment of K-step ks: row 16tb + n, chunk (4ks + ...) ^ 8 * (tb & 1) (see the layout)
-      constexpr int k0 = 16 * kLatPitch * tb + ((tb & 1) ? 128 : 0);
-      i32x8_t cur = lds_read32_asm<k0, 16>(lk);
-      static_for<4>([&](auto ksc) {
-        constexpr int ks = decltype(ksc)::value;
-        sacc[tb] = mfma16x16x128_fp8(cur, qh[ks], sacc[tb]);
-        sacc[tb] = mfma16x16x128_fp8(cur, qlo[ks], sacc[tb]);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (ks < 3) {
-          constexpr int kn = 16 * kLatPitch * tb + 64 * (ks + 1) + ((tb & 1) ? (ks + 1 < 2 ? 128 : -128) : 0);
-          cur = lds_read32_asm<kn, 16>(lk);
-        }
-      });
-      const i32x8_t rf = lds_read32_asm2<1024 * tb>(lr0, lr1);
-      const i32x8_t qr = lds_read32_asm<0, 1024>(qa);
+      // key fragment of K-step ks: row 16tb + n, chunk (4ks + ...) ^ 8 * (tb & 1) (see the layout); two K-steps per
+      // read block, so a block's wait overlaps the four products of the previous one
+      constexpr int kt = 16 * kLatPitch * tb, kodd = (tb & 1) ? 128 : 0;
+      i32x8_t f0, f1;
+      lds_read_k2_asm<kt + kodd, kt + 64 + kodd>(lk, f0, f1);
+      sacc[tb] = mfma16x16x128_fp8(f0, qh[0], sacc[tb]);
+      sacc[tb] = mfma16x16x128_fp8(f0, qlo[0], sacc[tb]);
+      sacc[tb] = mfma16x16x128_fp8(f1, qh[1], sacc[tb]);
+      sacc[tb] = mfma16x16x128_fp8(f1, qlo[1], sacc[tb]);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_read_k2_asm<kt + 128 - kodd, kt + 192 - kodd>(lk, f0, f1);
+      sacc[tb] = mfma16x16x128_fp8(f0, qh[2], sacc[tb]);
+      sacc[tb] = mfma16x16x128_fp8(f0, qlo[2], sacc[tb]);
+      sacc[tb] = mfma16x16x128_fp8(f1, qh[3], sacc[tb]);
+      sacc[tb] = mfma16x16x128_fp8(f1, qlo[3], sacc[tb]);
+      __builtin_amdgcn_sched_barrier(0);
+      i32x8_t rf, qr;
+      lds_read_rq_asm<1024 * tb>(lr0, lr1, qa, rf, qr);
       sacc[tb] = mfma16x16x128_fp8(rf, qr, sacc[tb]);
       __builtin_amdgcn_sched_barrier(0);
       // next tile's copies, spread over the score products
@@ -769,15 +838,13 @@ __global__ __launch_bounds__(64 * NW) void mla_split_fp8mma_kernel(MlaArgs a) {
                                int(pl[3])};
     // O^T += V^T P^T: 16 latent channels per MFMA; the two V^T reads (16 tokens) serve the hi and lo positions
     const uint32_t lva = lds_u32(Lt) + va, lvb = lds_u32(Lt) + vb;
-    i32x8_t vf = lds_read_v_asm<0, 32 * kLatPitch>(lva);
-    static_for<kC / 16>([&](auto dbc) {
-      constexpr int db = decltype(dbc)::value;
-      oacc[db] = mfma16x16x128_fp8(vf, bp, oacc[db]);
+    static_for<kC / 64>([&](auto dqc) {
+      constexpr int d0 = 4 * decltype(dqc)::value;     // four 16-channel blocks per read block
+      i32x8_t v[4];
+      lds_read_v4_asm<16 * d0, 32 * kLatPitch>((d0 & 8) ? lvb : lva, v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[d0 + i] = mfma16x16x128_fp8(v[i], bp, oacc[d0 + i]);
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (db + 1 < kC / 16) {
-        if constexpr (((db + 1) & 8) != 0) vf = lds_read_v_asm<16 * (db + 1), 32 * kLatPitch>(lvb);
-        else vf = lds_read_v_asm<16 * (db + 1), 32 * kLatPitch>(lva);
-      }
     });
   }
 
