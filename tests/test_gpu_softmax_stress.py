@@ -84,21 +84,59 @@ def test_paged_decode_rescale_across_blocks(kind, slope):
     check("lse", lse.cpu().numpy(), lse_ref, BF16_MAX, BF16_MEAN)
 
 
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
 @pytest.mark.parametrize("slope", [0.03, -0.03])
-def test_mla_rescale_across_tiles(slope):
+def test_mla_rescale_across_tiles(kind, slope):
+    """The FP8 latent cache runs on its own kernel (FP8 products, probabilities carried x 2^7 with the reference
+    max moved whenever the max doubles), so it gets the same stress: the ramp moves the max by more than that at
+    every 64-token tile."""
     ta = require_gpu()
     w = WORKLOADS["mla_decode_b32"]
     lens = [2000, 700]
-    say(f"mla stress slope={slope}")
+    say(f"mla stress kind={kind} slope={slope}")
     inp = mla_inputs(w, seed=152, batch=2, seqlen=2048, seq_lens=lens)
     qp = bits_to_f32(inp["q_pe"]).copy(); kp = bits_to_f32(inp["k_pe"]).copy()
     qp[..., -1] = 8.0
     kp[:, :, -1] += ramp(2048, slope)[None]
     qpb, kpb = f32_to_bf16_bits(qp), f32_to_bf16_bits(kp)
-    o, lse = ta.attn_mla_decode(dev_bf16(inp["q_lat"]), dev_bf16(qpb), dev_bf16(inp["c_kv"]), dev_bf16(kpb),
-                                dev(inp["seq_lens"]), w.scale, return_lse=True)
-    torch.cuda.synchronize()
     f = bits_to_f32
-    o_ref, lse_ref = oracle.mla_decode(f(inp["q_lat"]), f(qpb), f(inp["c_kv"]), f(kpb), inp["seq_lens"], w.scale)
+    if kind == "bf16":
+        o, lse = ta.attn_mla_decode(dev_bf16(inp["q_lat"]), dev_bf16(qpb), dev_bf16(inp["c_kv"]), dev_bf16(kpb),
+                                    dev(inp["seq_lens"]), w.scale, return_lse=True)
+        ckv_ref, kpe_ref = f(inp["c_kv"]), f(kpb)
+    else:   # FP8 codes with unit scales (the ramp reaches about 61, within E4M3's 448)
+        c8, k8 = f32_to_e4m3_bits(f(inp["c_kv"])), f32_to_e4m3_bits(f(kpb))
+        o, lse = ta.attn_mla_decode_q8(dev_bf16(inp["q_lat"]), dev_bf16(qpb), dev(c8), dev(k8),
+                                       dev(np.ones(w.latent, np.float32)), dev(np.ones(w.rope, np.float32)), "fp8",
+                                       dev(inp["seq_lens"]), w.scale, return_lse=True)
+        ckv_ref, kpe_ref = oracle.fp8_e4m3_decode(c8), oracle.fp8_e4m3_decode(k8)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.mla_decode(f(inp["q_lat"]), f(qpb), ckv_ref, kpe_ref, inp["seq_lens"], w.scale)
     check_bf16("o", host_bf16(o), o_ref)
     check("lse", lse.cpu().numpy(), lse_ref, BF16_MAX, BF16_MEAN)
+
+
+def test_mla_fp8_query_scales_span_many_binades():
+    """The FP8 kernel brings each head's query into E4M3 range with its own power of two: heads whose queries
+    differ by factors up to 2^16 (from uniform attention to a score spread of about 4) all match the oracle. The
+    range stops there because the query enters the products as two E4M3 terms (about 8 significant bits of
+    query x scale), so each score carries a relative error near 2^-9: harmless at ordinary score sizes, but with
+    scores spread over tens of units (this workload's query x 2^5) the output moves by about 0.04."""
+    ta = require_gpu()
+    w = dataclasses.replace(WORKLOADS["mla_decode_b32"], heads=64)
+    inp = mla_inputs(w, seed=153, batch=2, seqlen=900, seq_lens=[900, 333], kv="fp8")
+    f = bits_to_f32
+    mult = (2.0 ** np.linspace(-14, 2, w.heads)).astype(np.float32)[None, :, None]
+    ql = f32_to_bf16_bits(f(inp["q_lat"]) * mult)
+    qp = f32_to_bf16_bits(f(inp["q_pe"]) * mult)
+    o, lse = ta.attn_mla_decode_q8(dev_bf16(ql), dev_bf16(qp), dev(inp["c_kv"]), dev(inp["k_pe"]),
+                                   dev(inp["c_scale"]), dev(inp["pe_scale"]), "fp8", dev(inp["seq_lens"]), w.scale,
+                                   return_lse=True)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.mla_decode_q8(f(ql), f(qp), inp["c_kv"], inp["k_pe"], inp["c_scale"], inp["pe_scale"],
+                                          "fp8", inp["seq_lens"], w.scale)
+    check_bf16("o", host_bf16(o), o_ref)
+    lse = lse.cpu().numpy()
+    rel = np.abs(lse - lse_ref) / np.maximum(np.abs(lse_ref), 1.0)
+    say(f"  lse: max relative difference {rel.max():.3e}")
+    assert rel.max() <= 1e-3, rel.max()
