@@ -34,9 +34,8 @@ def run_oracle(w, inp):
 
 
 @pytest.mark.parametrize("kind", ["fp8", "int8"])
-# FP8 waves take two KV heads at head dim 128 (four at 64) when the KV head count divides, one otherwise; int8
-# always one. The cases cover both forms at both head dims: odd KV head counts (12/3, 5/5 at 128) and a count that
-# 4 does not divide (8/2 at 64) fall back to one head per wave.
+# One KV head per wave; the cases cover head-group counts that 8 (the XCD grouping of the unit order) divides
+# and ones it does not (12/3, 5/5, 16/1), at both head dims.
 @pytest.mark.parametrize("hq,hkv,page,d", [(32, 8, 64, 128), (32, 8, 16, 128), (32, 2, 128, 128), (8, 8, 32, 128),
                                          (12, 4, 64, 128), (12, 3, 64, 128), (5, 5, 16, 128), (32, 8, 64, 64),
                                          (32, 8, 16, 64), (16, 1, 128, 64), (12, 4, 32, 64), (8, 2, 64, 64)])
@@ -137,3 +136,40 @@ def test_full_size_q8_decode(kind):
     o_ref, lse_ref = run_oracle(w, compact(inp, seqs))
     check_bf16("o", o[seqs], o_ref)
     check("lse", lse[seqs], lse_ref, BF16_MAX, BF16_MEAN)
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8", "int8"])
+def test_many_sequences_with_empty_ones(kind):
+    """150 sequences (the 8-bit kernels enumerate the (sequence, chunk) pairs that hold keys 64 sequences at a
+    time), lengths from 0 to 2500 with empty sequences between long ones: every head of every sequence against the
+    oracle, empty sequences give O = 0 and lse = -inf."""
+    ta = require_gpu()
+    w = dataclasses.replace(WORKLOADS["paged_decode_b64"], batch=150, hq=8, hkv=2, page_size=16)
+    lens = np.random.default_rng(85).integers(1, 2500, 150)
+    lens[::7] = 0
+    lens[[63, 64, 127, 128]] = [0, 2500, 1025, 0]
+    say(f"{kind} decode, 150 sequences, {int((lens == 0).sum())} empty")
+    inp = paged_decode_inputs(w, seed=85, seq_lens=lens.tolist(), max_len=2500, kv=kind)
+    q = dev_bf16(inp["q"])
+    ta.attn_rope_apply(q, dev(inp["positions"]), w.theta)
+    if kind == "bf16":
+        o, lse = ta.attn_decode_paged(q, dev_bf16(inp["k_cache"]), dev_bf16(inp["v_cache"]), dev(inp["block_table"]),
+                                      dev(inp["seq_lens"]), inp["max_len"], softmax_scale=w.scale, return_lse=True)
+    else:
+        o, lse = ta.attn_decode_paged_q8(q, dev(inp["k_cache"]), dev(inp["v_cache"]), dev(inp["k_scale"]),
+                                         dev(inp["v_scale"]), kind, dev(inp["block_table"]), dev(inp["seq_lens"]),
+                                         inp["max_len"], softmax_scale=w.scale, return_lse=True)
+    torch.cuda.synchronize()
+    o, lse = host_bf16(o), lse.cpu().numpy()
+    qr = oracle.rope(bits_to_f32(inp["q"])[:, None], inp["positions"][:, None], w.theta)[:, 0]
+    full = lens > 0
+    if kind == "bf16":
+        o_ref, lse_ref = oracle.decode_paged(qr[full], bits_to_f32(inp["k_cache"]), bits_to_f32(inp["v_cache"]),
+                                             inp["block_table"][full], inp["seq_lens"][full], w.scale)
+    else:
+        o_ref, lse_ref = oracle.decode_paged_q8(qr[full], inp["k_cache"], inp["v_cache"], inp["k_scale"],
+                                                inp["v_scale"], kind, inp["block_table"][full], inp["seq_lens"][full],
+                                                w.scale)
+    check_bf16("o", o[full], o_ref)
+    check("lse", lse[full], lse_ref, BF16_MAX, BF16_MEAN)
+    assert np.all(o[~full] == 0) and np.all(np.isneginf(lse[~full]))

@@ -74,12 +74,66 @@ struct DecodeArgs {
 
 __device__ __forceinline__ int clamp_len(int L, int max_len, int cap) { return max(0, min(L, min(max_len, cap))); }
 
-// Workgroup -> (KV-head group g, chunk, sequence b): grid (head groups, n_chunks, batch), head groups fastest, so
-// the head groups of one chunk are consecutive workgroups and read interleaved slices of the same page slots.
-// (Measured: all head groups of a chunk on one XCD instead, a 1-D grid over XCD-strided workgroups, ran 6% slower
-// for bf16 and 3% faster for FP8.)
-__device__ __forceinline__ void decode_unit(int& g, int& chunk, int& b) {
-  g = blockIdx.x; chunk = blockIdx.y; b = blockIdx.z;
+// Workgroup -> (KV-head group g, chunk, sequence b). The 1-D grid holds n_hg x n_chunks x batch workgroups (every
+// sequence at the maximum length). The hardware hands workgroup i to XCD i mod 8 and shader engine i mod 32, and
+// to a free slot within that engine; the order decides how the units' keys spread over the engines.
+//   kOrderGrid: workgroup i is head group i mod n_hg of chunk (i / n_hg) mod n_chunks of sequence
+//     i / (n_hg n_chunks); the head groups of one chunk are consecutive and read interleaved slices of the same
+//     page slots; pairs past a sequence's length exit at once.
+//   kOrderDense, kOrderDenseXcd: unit k counts only the (sequence, chunk) pairs that hold keys, sequence by
+//     sequence, and workgroups past the last unit exit. Dense: head group i mod n_hg of unit i / n_hg. DenseXcd:
+//     the head groups of one unit go to one XCD (workgroups i, i + 8, ...): head group (i / 8) mod n_hg of unit
+//     8 (i / (8 n_hg)) + i mod 8.
+// Measured on the 64-sequence workload (lengths 3.6k-32.6k): bf16 is fastest in grid order (dense 2.5% slower),
+// the 8-bit caches with the dense orders (grid order left the engines' key shares up to 20% apart).
+constexpr int kOrderGrid = 0, kOrderDense = 1, kOrderDenseXcd = 2;
+#ifndef ATTN_DECODE_ORDER_BF16
+#define ATTN_DECODE_ORDER_BF16 0
+#endif
+#ifndef ATTN_DECODE_ORDER_Q8
+#define ATTN_DECODE_ORDER_Q8 2
+#endif
+
+template <int ORDER>
+__device__ __forceinline__ bool decode_unit(const DecodeArgs& a, int& g, int& chunk, int& b) {
+  const int id = blockIdx.x;
+  if constexpr (ORDER == kOrderGrid) {
+    g = id % a.n_hg;
+    chunk = (id / a.n_hg) % a.n_chunks;
+    b = id / (a.n_hg * a.n_chunks);
+    return b < a.batch;
+  } else {
+    int k;
+    if constexpr (ORDER == kOrderDense) {
+      g = id % a.n_hg;
+      k = id / a.n_hg;
+    } else {
+      g = (id >> 3) % a.n_hg;
+      k = 8 * (id / (8 * a.n_hg)) + (id & 7);
+    }
+    const int lane = threadIdx.x;
+    const int cap = a.max_pages << a.page_shift;
+    for (int base = 0; base < a.batch; base += 64) {
+      const int bb = base + lane;
+      const int L = bb < a.batch ? clamp_len(a.seq_lens[bb], a.max_len, cap) : 0;
+      const int nc = (L + a.chunk - 1) / a.chunk;
+      int incl = nc;                                    // inclusive prefix sum of the chunk counts over the lanes
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      const int total = __builtin_amdgcn_readlane(incl, 63);
+      if (k < total) {
+        const int j = __builtin_ctzll(__ballot(incl > k));       // first sequence whose chunks reach past k
+        b = base + j;
+        chunk = k - (__builtin_amdgcn_readlane(incl, j) - __builtin_amdgcn_readlane(nc, j));
+        return true;
+      }
+      k -= total;
+    }
+    return false;
+  }
 }
 
 // Copy cache policy: non-temporal, every cache byte is read once (measured: cached copies 7% slower).
@@ -246,9 +300,15 @@ __device__ __forceinline__ void block_ring(int t_begin, int t_end, Copy& copy, R
 #ifndef ATTN_DECODE_RING_BF16
 #define ATTN_DECODE_RING_BF16 2
 #endif
+// 8-bit caches: ring depth by kind and head dim (one KV head per wave, 8 KiB blocks). Measured: three buffers
+// 0.8% faster for FP8 at head dim 128, 3.5% (FP8) and 2.5% (int8) at 64, 1.5% slower for int8 at 128.
 #ifndef ATTN_DECODE_RING_Q8
-#define ATTN_DECODE_RING_Q8 2
+#define ATTN_DECODE_RING_Q8 0
 #endif
+template <int KV, int D>
+constexpr int q8_ring_depth() {
+  return ATTN_DECODE_RING_Q8 > 0 ? ATTN_DECODE_RING_Q8 : (KV == kKvInt8 && D == 128) ? 2 : 3;
+}
 
 // Element j (0..7) of each of the 8 rows in vv, packed in row order: the A operand for dimension offset j.
 __device__ __forceinline__ bf16x8_t transpose_pick(const u32x4_t* vv, int j) {
@@ -350,7 +410,7 @@ __global__ __launch_bounds__(64) void decode_paged_lds_kernel(DecodeArgs a) {
   ATTN_RING_BUFFERS(uint16_t, kl, 32 * D)
   ATTN_RING_BUFFERS(uint16_t, vl, 32 * D)
   int g, chunk, b;
-  decode_unit(g, chunk, b);
+  if (!decode_unit<ATTN_DECODE_ORDER_BF16>(a, g, chunk, b)) return;
   Chunk ck;
   if (!load_chunk(a, b, chunk, ck)) return;
   const int t_begin = ck.t_begin, t_end = ck.t_end;
@@ -483,11 +543,11 @@ __global__ __launch_bounds__(64) void decode_paged_q8_kernel(DecodeArgs a) {
   constexpr int kCopies = 32 / kRowsPerCopy; // copy instructions per tensor per block
   constexpr int kKs = D / 32;                // k-steps of S^T = K Q^T
   constexpr int kHk = D / 64;                // 16-byte K pieces per lane, key and head
-  constexpr int NB = ATTN_DECODE_RING_Q8;
+  constexpr int NB = q8_ring_depth<KV, D>();
   ATTN_RING_BUFFERS(uint8_t, k8, 32 * RL)
   ATTN_RING_BUFFERS(uint8_t, v8, 32 * RL)
   int gw, chunk, b;
-  decode_unit(gw, chunk, b);
+  if (!decode_unit<ATTN_DECODE_ORDER_Q8>(a, gw, chunk, b)) return;
   const int g0 = gw * HPW;                   // the wave's first KV head
   Chunk ck;
   if (!load_chunk(a, b, chunk, ck)) return;
@@ -663,24 +723,28 @@ size_t decode_paged_workspace_bytes(int batch, int hq, int head_dim, int max_seq
 }
 
 namespace {
-#ifndef ATTN_DECODE_Q8_HPW
-#define ATTN_DECODE_Q8_HPW 2
-#endif
 template <class Kernel>
 void launch_grid(Kernel kernel, DecodeArgs a, int hpw, hipStream_t stream) {
   a.n_hg = a.hkv / hpw;
-  const dim3 grid{unsigned(a.n_hg), unsigned(a.n_chunks), unsigned(a.batch)};   // head-major
-  kernel<<<grid, dim3(64), 0, stream>>>(a);
+  // every possible unit, rounded up to whole groups of 8 x n_hg workgroups (the XCD-grouped order maps those onto
+  // units bijectively; the extra workgroups exit)
+  const unsigned group = 8u * unsigned(a.n_hg);
+  const unsigned units = unsigned(a.n_hg) * unsigned(a.n_chunks) * unsigned(a.batch);
+  kernel<<<dim3((units + group - 1) / group * group), dim3(64), 0, stream>>>(a);
 }
 
-// FP8 caches: a wave takes several KV heads when that makes its rows at least 256 bytes. Measured on the 64-sequence
-// workload: FP8 at head dim 128 streams 4.95 TB/s with one head per wave (128-byte rows) and 5.10 with two; at head
-// dim 64, 2.94 with one and 3.59 with four. Int8 stays at one head per wave: its code conversion takes more
-// instructions, and with the fewer waves per CU of the multi-head kernel it ran slower (3.45 vs 4.77 TB/s at 128).
+// One KV head per wave for both 8-bit kinds (128- or 64-byte rows), in the XCD-grouped dense order. Measured on the
+// 64-sequence workload at head dim 128 (64): in grid order FP8 streamed 4.95 (2.94) TB/s with one head per wave and
+// 5.10 (3.59) with two (four), which made rows of 256 bytes; with the head groups of a chunk on one XCD, one head
+// per wave streams 5.62 (4.02) TB/s for FP8 and 5.25 (3.71) for int8. The multi-head instances
+// (decode_paged_q8_kernel<KV, D, HPW > 1>) remain selectable for other layouts.
+#ifndef ATTN_DECODE_Q8_HPW
+#define ATTN_DECODE_Q8_HPW 1
+#endif
 template <int KV, int D>
 void launch_q8(const DecodeArgs& a, hipStream_t stream) {
-  constexpr int H = KV == kKvInt8 ? 1 : D == 128 ? ATTN_DECODE_Q8_HPW : 4;
-  if constexpr (H > 1) {
+  constexpr int H = KV == kKvInt8 ? 1 : ATTN_DECODE_Q8_HPW;
+  if constexpr (H > 1 && H * D >= 256) {
     if (a.hkv % H == 0) return launch_grid(decode_paged_q8_kernel<KV, D, H>, a, H, stream);
   }
   launch_grid(decode_paged_q8_kernel<KV, D, 1>, a, 1, stream);
@@ -703,6 +767,7 @@ hipError_t launch_decode(int kind, const void* q, const void* k_cache, const voi
   const int chunk = max(kDecodeChunk, min(want, 64 * page_size));
   const int n_chunks = max(1, (max_seqlen_kv + chunk - 1) / chunk);
   const size_t slots = size_t(batch) * size_t(hq) * size_t(n_chunks);
+  if (size_t(hkv) * size_t(n_chunks) * size_t(batch) + 8 * size_t(hkv) > size_t(INT32_MAX)) return hipErrorInvalidValue;
   const size_t o_bytes = (slots * size_t(head_dim) * sizeof(float) + 255) & ~size_t(255);
   DecodeArgs a = {};
   a.q = static_cast<const uint16_t*>(q);
