@@ -92,9 +92,10 @@ __device__ __forceinline__ uint32_t codes_to_bf16x2(uint32_t w, bool hi) {
     return __builtin_bit_cast(uint32_t, hi ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)
                                            : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
   } else {
-    const uint32_t u = w ^ 0x80808080u;               // biased bytes: code + 128
+    // Each byte sign-extended and converted in one instruction (a byte-select of the convert's source), then
+    // packed: 1.5 instructions per code, against 3 for converting the biased byte and subtracting 128.
     const int sh = hi ? 16 : 0;
-    return pack_bf16x2(float((u >> sh) & 255u) - 128.f, float((u >> (sh + 8)) & 255u) - 128.f);
+    return pack_bf16x2(float(int8_t(w >> sh)), float(int8_t(w >> (sh + 8))));
   }
 }
 
