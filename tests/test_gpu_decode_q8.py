@@ -173,3 +173,41 @@ def test_many_sequences_with_empty_ones(kind):
     check_bf16("o", o[full], o_ref)
     check("lse", lse[full], lse_ref, BF16_MAX, BF16_MEAN)
     assert np.all(o[~full] == 0) and np.all(np.isneginf(lse[~full]))
+
+
+def every_code(shape, kind, seed):
+    """Cache bytes taking every code value: seeded permutations of all 256 bytes, repeated. For int8 this includes
+    0x80 (-128), which the generator's [-127, 127] never produces; for FP8 the two NaN codes are replaced by the
+    largest finite ones (every other E4M3 code, subnormals included, occurs)."""
+    r = np.random.default_rng(seed)
+    n = int(np.prod(shape))
+    b = np.concatenate([r.permutation(256) for _ in range((n + 255) // 256)])[:n].astype(np.uint8)
+    if kind == "fp8":
+        b[b == 0x7F] = 0x7E
+        b[b == 0xFF] = 0xFE
+    return b.reshape(shape)
+
+
+def unit_range_scales(shape, kind, seed):
+    """Per-channel scales that put the largest code near magnitude 1 (0.5x to 1.5x, seeded per channel)."""
+    top = 448.0 if kind == "fp8" else 128.0
+    return (np.random.default_rng(seed).uniform(0.5, 1.5, shape) / top).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["fp8", "int8"])
+@pytest.mark.parametrize("d", [128, 64])
+def test_q8_decode_every_code_value(kind, d):
+    """Every code byte through the GPU's code conversion (int8 sign extension including -128; every finite E4M3
+    code) against the oracle's decoding of the same bytes."""
+    ta = require_gpu()
+    w = dataclasses.replace(WORKLOADS["paged_decode_b64"], head_dim=d, scale=1.0 / np.sqrt(d))
+    say(f"q8 decode every code value {kind} d={d}")
+    inp = paged_decode_inputs(w, seed=83, seq_lens=[300, 1, 700, 64], max_len=768, kv=kind)
+    inp["k_cache"] = every_code(inp["k_cache"].shape, kind, 1)
+    inp["v_cache"] = every_code(inp["v_cache"].shape, kind, 2)
+    inp["k_scale"] = unit_range_scales(inp["k_scale"].shape, kind, 3)
+    inp["v_scale"] = unit_range_scales(inp["v_scale"].shape, kind, 4)
+    o, lse = run_gpu(ta, w, inp)
+    o_ref, lse_ref = run_oracle(w, inp)
+    check_bf16("o", o, o_ref)
+    check("lse", lse, lse_ref, BF16_MAX, BF16_MEAN)

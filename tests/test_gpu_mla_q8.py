@@ -114,3 +114,27 @@ def test_full_size_mla_q8_decode(kind):
     o_ref, lse_ref = run_oracle(w, sub)
     check_bf16("o", o[seqs], o_ref)
     check("lse", lse[seqs], lse_ref, BF16_MAX, BF16_MEAN)
+
+
+@pytest.mark.parametrize("kind", ["fp8", "int8"])
+def test_mla_q8_every_code_value(kind):
+    """Every code byte of the latent and rope caches (int8 including -128, every finite E4M3 code with subnormals)
+    against the oracle's decoding of the same bytes; per-channel scales put the largest code near magnitude 1."""
+    ta = require_gpu()
+    w = WORKLOADS["mla_decode_b32"]
+    say(f"mla q8 every code value {kind}")
+    inp = mla_inputs(w, seed=43, batch=2, seqlen=320, seq_lens=[320, 129], kv=kind)
+    r = np.random.default_rng(5)
+    top = 448.0 if kind == "fp8" else 128.0
+    for name, sc in (("c_kv", "c_scale"), ("k_pe", "pe_scale")):
+        n = inp[name].size
+        b = np.concatenate([r.permutation(256) for _ in range((n + 255) // 256)])[:n].astype(np.uint8)
+        if kind == "fp8":
+            b[b == 0x7F] = 0x7E
+            b[b == 0xFF] = 0xFE
+        inp[name] = b.reshape(inp[name].shape)
+        inp[sc] = (r.uniform(0.5, 1.5, inp[sc].shape) / top).astype(np.float32)
+    o, lse = run_gpu(ta, w, inp)
+    o_ref, lse_ref = run_oracle(w, inp)
+    check_bf16("o", o, o_ref)
+    check("lse", lse, lse_ref, BF16_MAX, BF16_MEAN)
