@@ -537,37 +537,6 @@ __device__ __forceinline__ void static_for(F&& f) {
     static_for<N, I + 1>(f);
   }
 }
-// 32 bytes: 16 at addr + OFF and 16 at addr + OFF + STEP.
-template <int OFF, int STEP>
-__device__ __forceinline__ i32x8_t lds_read32_asm(uint32_t addr) {
-  u32x4_t x, y;
-  asm volatile("ds_read_b128 %0, %2 offset:%3\n\tds_read_b128 %1, %2 offset:%4\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(x), "=&v"(y)
-               : "v"(addr), "n"(OFF), "n"(OFF + STEP)
-               : "memory");
-  return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-// 32 bytes: 16 at a0 + OFF and 16 at a1 + OFF.
-template <int OFF>
-__device__ __forceinline__ i32x8_t lds_read32_asm2(uint32_t a0, uint32_t a1) {
-  u32x4_t x, y;
-  asm volatile("ds_read_b128 %0, %2 offset:%4\n\tds_read_b128 %1, %3 offset:%4\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(x), "=&v"(y)
-               : "v"(a0), "v"(a1), "n"(OFF)
-               : "memory");
-  return __builtin_bit_cast(i32x8_t, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-// V^T operand: transposing 8-byte reads at addr + OFF and addr + OFF + STEP, each used twice (hi and lo positions).
-template <int OFF, int STEP>
-__device__ __forceinline__ i32x8_t lds_read_v_asm(uint32_t addr) {
-  u32x2_t x, y;
-  asm volatile("ds_read_b64_tr_b8 %0, %2 offset:%3\n\tds_read_b64_tr_b8 %1, %2 offset:%4\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(x), "=&v"(y)
-               : "v"(addr), "n"(OFF), "n"(OFF + STEP)
-               : "memory");
-  return i32x8_t{int(x[0]), int(x[1]), int(y[0]), int(y[1]), int(x[0]), int(x[1]), int(y[0]), int(y[1])};
-}
-
 // Two 32-byte key fragments (K-steps at OFF0 and OFF1: 16 bytes there and 16 bytes after).
 template <int OFF0, int OFF1>
 __device__ __forceinline__ void lds_read_k2_asm(uint32_t addr, i32x8_t& f0, i32x8_t& f1) {
@@ -592,45 +561,26 @@ __device__ __forceinline__ void lds_read_rq_asm(uint32_t r0, uint32_t r1, uint32
   rf = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
   qf = __builtin_bit_cast(i32x8_t, __builtin_shufflevector(c, d, 0, 1, 2, 3, 4, 5, 6, 7));
 }
-// Two V^T operands (latent chunks at a0 + OFF0 and a1 + OFF1): each is two transposing reads (tokens 0-31 and
-// 32-63 of the tile, STEP apart) read twice, for the hi and the lo K positions.
-template <int OFF0, int OFF1, int STEP>
-__device__ __forceinline__ void lds_read_v2_asm(uint32_t a0, uint32_t a1, i32x8_t& v0, i32x8_t& v1) {
-  u32x2_t w0, w1, w2, w3, w4, w5, w6, w7;
-  asm volatile("ds_read_b64_tr_b8 %0, %8 offset:%10\n\tds_read_b64_tr_b8 %1, %8 offset:%11\n\t"
-               "ds_read_b64_tr_b8 %2, %8 offset:%10\n\tds_read_b64_tr_b8 %3, %8 offset:%11\n\t"
-               "ds_read_b64_tr_b8 %4, %9 offset:%12\n\tds_read_b64_tr_b8 %5, %9 offset:%13\n\t"
-               "ds_read_b64_tr_b8 %6, %9 offset:%12\n\tds_read_b64_tr_b8 %7, %9 offset:%13\n\ts_waitcnt lgkmcnt(0)"
-               : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(w4), "=&v"(w5), "=&v"(w6), "=&v"(w7)
-               : "v"(a0), "v"(a1), "n"(OFF0), "n"(OFF0 + STEP), "n"(OFF1), "n"(OFF1 + STEP)
-               : "memory");
-  v0 = i32x8_t{int(w0[0]), int(w0[1]), int(w1[0]), int(w1[1]), int(w2[0]), int(w2[1]), int(w3[0]), int(w3[1])};
-  v1 = i32x8_t{int(w4[0]), int(w4[1]), int(w5[0]), int(w5[1]), int(w6[0]), int(w6[1]), int(w7[0]), int(w7[1])};
-}
-
 // Four V^T operands (latent chunks at a + OFF + 16 i, i = 0..3, all on one side of the swizzle's 128-byte shift).
+// Each operand is two transposing reads (tokens 0-31 and 32-63 of the tile, STEP apart); its second half, the lo
+// K positions, repeats the first (register copies, not a second pair of reads).
 template <int OFF, int STEP>
 __device__ __forceinline__ void lds_read_v4_asm(uint32_t a, i32x8_t (&v)[4]) {
-  u32x2_t w[16];
-  asm volatile("ds_read_b64_tr_b8 %0, %16 offset:%17\n\tds_read_b64_tr_b8 %1, %16 offset:%18\n\t"
-               "ds_read_b64_tr_b8 %2, %16 offset:%17\n\tds_read_b64_tr_b8 %3, %16 offset:%18\n\t"
-               "ds_read_b64_tr_b8 %4, %16 offset:%19\n\tds_read_b64_tr_b8 %5, %16 offset:%20\n\t"
-               "ds_read_b64_tr_b8 %6, %16 offset:%19\n\tds_read_b64_tr_b8 %7, %16 offset:%20\n\t"
-               "ds_read_b64_tr_b8 %8, %16 offset:%21\n\tds_read_b64_tr_b8 %9, %16 offset:%22\n\t"
-               "ds_read_b64_tr_b8 %10, %16 offset:%21\n\tds_read_b64_tr_b8 %11, %16 offset:%22\n\t"
-               "ds_read_b64_tr_b8 %12, %16 offset:%23\n\tds_read_b64_tr_b8 %13, %16 offset:%24\n\t"
-               "ds_read_b64_tr_b8 %14, %16 offset:%23\n\tds_read_b64_tr_b8 %15, %16 offset:%24\n\t"
+  u32x2_t w[8];
+  asm volatile("ds_read_b64_tr_b8 %0, %8 offset:%9\n\tds_read_b64_tr_b8 %1, %8 offset:%10\n\t"
+               "ds_read_b64_tr_b8 %2, %8 offset:%11\n\tds_read_b64_tr_b8 %3, %8 offset:%12\n\t"
+               "ds_read_b64_tr_b8 %4, %8 offset:%13\n\tds_read_b64_tr_b8 %5, %8 offset:%14\n\t"
+               "ds_read_b64_tr_b8 %6, %8 offset:%15\n\tds_read_b64_tr_b8 %7, %8 offset:%16\n\t"
                "s_waitcnt lgkmcnt(0)"
                : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(w[4]), "=&v"(w[5]), "=&v"(w[6]),
-                 "=&v"(w[7]), "=&v"(w[8]), "=&v"(w[9]), "=&v"(w[10]), "=&v"(w[11]), "=&v"(w[12]), "=&v"(w[13]),
-                 "=&v"(w[14]), "=&v"(w[15])
+                 "=&v"(w[7])
                : "v"(a), "n"(OFF), "n"(OFF + STEP), "n"(OFF + 16), "n"(OFF + 16 + STEP), "n"(OFF + 32),
                  "n"(OFF + 32 + STEP), "n"(OFF + 48), "n"(OFF + 48 + STEP)
                : "memory");
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    v[i] = i32x8_t{int(w[4 * i][0]), int(w[4 * i][1]), int(w[4 * i + 1][0]), int(w[4 * i + 1][1]),
-                   int(w[4 * i + 2][0]), int(w[4 * i + 2][1]), int(w[4 * i + 3][0]), int(w[4 * i + 3][1])};
+    v[i] = i32x8_t{int(w[2 * i][0]), int(w[2 * i][1]), int(w[2 * i + 1][0]), int(w[2 * i + 1][1]),
+                   int(w[2 * i][0]), int(w[2 * i][1]), int(w[2 * i + 1][0]), int(w[2 * i + 1][1])};
 }
 
 // 16 fp32 values (scaled) -> their hi and lo E4M3 terms, four dwords each, in order.
